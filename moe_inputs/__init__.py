@@ -1,0 +1,208 @@
+"""Seeded synthetic inputs for the MoE expert layer.
+
+This module is the only code shared by the HIP path (tests, bench) and the CPU
+oracle. It draws random tensors and holds none of the layer's arithmetic: no
+gating, routing, quantisation, GEMM or reduction happens here.
+
+Workloads are named by what they are. Their shapes follow the models the source
+pages optimise (Qwen3-MoE on Atlas A3/950 and LongCat-Flash on Atlas A3); the
+values are synthetic because trained weights are not available.
+
+Distributions ("N(0, s)" means standard deviation s):
+  * router logits: fp32 N(0,1); the skewed prefill workload adds a per-expert
+    bias N(0,1.5) drawn once per seed (heavy expert load imbalance);
+  * hidden states x and residual: N(0,1) rounded to the activation dtype;
+  * bf16/fp32 expert weights: N(0, w_std) rounded to the weight dtype;
+  * MXFP4 expert weights: e2m1 codes drawn uniformly over all 16 codes and e8m0
+    block scales drawn uniformly from {119, 120, 121} (2^-8..2^-6), which gives
+    an element RMS of about 0.012..0.046, close to N(0, 0.02).
+
+Generation uses torch's seeded generator on the requested device, so the same
+(workload, seed, device) always gives the same tensors; the CPU oracle receives
+host copies of exactly the tensors the GPU path consumes.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import torch
+
+__all__ = ["MoEShape", "WORKLOADS", "get_workload", "generate", "seed_for",
+           "scaled"]
+
+
+@dataclass(frozen=True)
+class MoEShape:
+    name: str
+    T: int            # tokens
+    H: int            # hidden size (GEMM1 K, GEMM2 N)
+    I: int            # per-expert intermediate size
+    n_ffn: int        # FFN experts, ids [0, n_ffn)
+    n_zero: int       # identity ("zero-compute") experts, ids [n_ffn, n_ffn+n_zero)
+    top_k: int
+    local_begin: int  # expert range [local_begin, local_end) handled by the call
+    local_end: int
+    act: str          # "f32" | "bf16"  (x, residual, y, out)
+    wt: str           # "f32" | "bf16" | "mxfp4"
+    act_q: str        # "none" | "mxfp8" (dynamic activation quantisation)
+    w_std: float = 0.02
+    logit_bias_std: float = 0.0
+    residual: bool = False
+
+    @property
+    def E_tot(self) -> int:
+        return self.n_ffn + self.n_zero
+
+    @property
+    def ffn_begin(self) -> int:
+        return min(self.local_begin, self.n_ffn)
+
+    @property
+    def ffn_end(self) -> int:
+        return min(self.local_end, self.n_ffn)
+
+    @property
+    def E_loc(self) -> int:
+        """FFN experts whose weights the call holds."""
+        return max(0, self.ffn_end - self.ffn_begin)
+
+    def replace(self, **kw) -> "MoEShape":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, MoEShape] = {
+    s.name: s for s in [
+        MoEShape("tiny_fp32", T=16, H=64, I=32, n_ffn=8, n_zero=0, top_k=2,
+                 local_begin=0, local_end=8, act="f32", wt="f32", act_q="none",
+                 w_std=0.05),
+        MoEShape("qwen3_30b_a3b_decode_bf16", T=32, H=2048, I=768, n_ffn=128,
+                 n_zero=0, top_k=8, local_begin=0, local_end=128, act="bf16",
+                 wt="bf16", act_q="none"),
+        MoEShape("qwen3_30b_a3b_prefill_skewed_bf16", T=4096, H=2048, I=768,
+                 n_ffn=128, n_zero=0, top_k=8, local_begin=0, local_end=128,
+                 act="bf16", wt="bf16", act_q="none", logit_bias_std=1.5,
+                 residual=True),
+        MoEShape("longcat_flash_zero_experts_bf16", T=1024, H=6144, I=2048,
+                 n_ffn=512, n_zero=256, top_k=12, local_begin=0, local_end=768,
+                 act="bf16", wt="bf16", act_q="none"),
+        MoEShape("qwen3_235b_a22b_ep_rank_w4a8", T=4096, H=4096, I=1536,
+                 n_ffn=128, n_zero=0, top_k=8, local_begin=32, local_end=64,
+                 act="bf16", wt="mxfp4", act_q="mxfp8"),
+    ]
+}
+
+
+def get_workload(name: str) -> MoEShape:
+    return WORKLOADS[name]
+
+
+def scaled(shape: MoEShape, **kw) -> MoEShape:
+    """A smaller copy of a workload (same dtypes and structure)."""
+    return shape.replace(name=shape.name + "_small", **kw)
+
+
+def seed_for(shape: MoEShape, seed: int, role: int, index: int = 0) -> int:
+    """Deterministic 63-bit seed for (workload, seed, tensor role, index)."""
+    h = 1469598103934665603
+    for ch in shape.name.encode():
+        h = ((h ^ ch) * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+    for v in (seed, role, index):
+        h = ((h ^ (v & 0xFFFFFFFF)) * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+        h ^= h >> 29
+    return h & 0x7FFFFFFFFFFFFFFF
+
+
+def _gen(device, s: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(s)
+    return g
+
+
+def _normal(shape, std, dtype, device, s) -> torch.Tensor:
+    t = torch.randn(shape, generator=_gen(device, s), device=device,
+                    dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(dtype)
+
+
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+ROLE_LOGITS, ROLE_BIAS, ROLE_X, ROLE_RES, ROLE_W13, ROLE_W2 = range(6)
+ROLE_W13_SCALE, ROLE_W2_SCALE = 6, 7
+
+
+def generate(shape: MoEShape, seed: int = 0, device="cpu",
+             weights: bool = True) -> Dict[str, Optional[torch.Tensor]]:
+    """Draw one input set.
+
+    Returns a dict with
+      logits   fp32 [T, E_tot]
+      x        act  [T, H]
+      residual act  [T, H] or None
+      w13      [E_loc, H, 2I] (f32/bf16) | uint8 [E_loc, 2I, H/2] (mxfp4 codes)
+      w13_scale None | uint8 [E_loc, 2I, H/32]
+      w2       [E_loc, I, H] (f32/bf16) | uint8 [E_loc, H, I/2]
+      w2_scale None | uint8 [E_loc, H, I/32]
+    Weights are drawn per expert (seeded by global expert id), so an expert's
+    weights do not depend on the local range.
+    """
+    dev = torch.device(device)
+    T, H, I, E = shape.T, shape.H, shape.I, shape.E_tot
+    out: Dict[str, Optional[torch.Tensor]] = {}
+    logits = _normal((T, E), 1.0, torch.float32, dev,
+                     seed_for(shape, seed, ROLE_LOGITS))
+    if shape.logit_bias_std:
+        bias = _normal((E,), shape.logit_bias_std, torch.float32, dev,
+                       seed_for(shape, seed, ROLE_BIAS))
+        logits += bias[None, :]
+    out["logits"] = logits.contiguous()
+    adt = _DT[shape.act]
+    out["x"] = _normal((T, H), 1.0, adt, dev, seed_for(shape, seed, ROLE_X))
+    out["residual"] = (_normal((T, H), 1.0, adt, dev,
+                               seed_for(shape, seed, ROLE_RES))
+                       if shape.residual else None)
+    out["w13"] = out["w2"] = out["w13_scale"] = out["w2_scale"] = None
+    if not weights:
+        return out
+    El = shape.E_loc
+    experts = range(shape.ffn_begin, shape.ffn_end)
+    if shape.wt in ("f32", "bf16"):
+        wdt = _DT[shape.wt]
+        w13 = torch.empty((El, H, 2 * I), dtype=wdt, device=dev)
+        w2 = torch.empty((El, I, H), dtype=wdt, device=dev)
+        for i, e in enumerate(experts):
+            w13[i] = _normal((H, 2 * I), shape.w_std, wdt, dev,
+                             seed_for(shape, seed, ROLE_W13, e))
+            w2[i] = _normal((I, H), shape.w_std, wdt, dev,
+                            seed_for(shape, seed, ROLE_W2, e))
+        out["w13"], out["w2"] = w13, w2
+    elif shape.wt == "mxfp4":
+        assert H % 32 == 0 and I % 32 == 0
+        w13 = torch.empty((El, 2 * I, H // 2), dtype=torch.uint8, device=dev)
+        w2 = torch.empty((El, H, I // 2), dtype=torch.uint8, device=dev)
+        s13 = torch.empty((El, 2 * I, H // 32), dtype=torch.uint8, device=dev)
+        s2 = torch.empty((El, H, I // 32), dtype=torch.uint8, device=dev)
+        for i, e in enumerate(experts):
+            w13[i] = torch.randint(0, 256, (2 * I, H // 2), device=dev,
+                                   dtype=torch.int32,
+                                   generator=_gen(dev, seed_for(shape, seed, ROLE_W13, e))
+                                   ).to(torch.uint8)
+            w2[i] = torch.randint(0, 256, (H, I // 2), device=dev,
+                                  dtype=torch.int32,
+                                  generator=_gen(dev, seed_for(shape, seed, ROLE_W2, e))
+                                  ).to(torch.uint8)
+            s13[i] = torch.randint(119, 122, (2 * I, H // 32), device=dev,
+                                   dtype=torch.int32,
+                                   generator=_gen(dev, seed_for(shape, seed, ROLE_W13_SCALE, e))
+                                   ).to(torch.uint8)
+            s2[i] = torch.randint(119, 122, (H, I // 32), device=dev,
+                                  dtype=torch.int32,
+                                  generator=_gen(dev, seed_for(shape, seed, ROLE_W2_SCALE, e))
+                                  ).to(torch.uint8)
+        out["w13"], out["w2"], out["w13_scale"], out["w2_scale"] = w13, w2, s13, s2
+    else:
+        raise ValueError(shape.wt)
+    return out

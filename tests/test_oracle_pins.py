@@ -1,0 +1,346 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+hand-worked fixtures (tests/golden), closed forms, library routines (scipy
+softmax, torch float8 conversion, torch SiLU / chunk), invariants, and brute
+force on tiny inputs. No GPU needed."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------- gate
+
+
+def test_gate_golden_cases():
+    for c in _load("gate_cases.json")["cases"]:
+        L = np.array([c["logits"]], dtype=np.float32)
+        ids, w = O.gate_topk(L, c["k"])
+        assert ids[0].tolist() == c["ids"]
+        if "w" in c:
+            np.testing.assert_allclose(w[0], c["w"], rtol=0, atol=1e-7)
+    # the formula case: three logits of 7 and one of 0
+    L = np.array([[-5, 7, -5, 7, 0, 7]], dtype=np.float32)
+    _, w = O.gate_topk(L, 4)
+    d = 3 * math.exp(7) + 1
+    np.testing.assert_allclose(w[0], [math.exp(7) / d] * 3 + [1 / d], rtol=1e-14)
+
+
+def test_gate_full_k_is_scipy_softmax():
+    rng = np.random.default_rng(1)
+    L = rng.standard_normal((7, 12)).astype(np.float32)
+    ids, w = O.gate_topk(L, 12)
+    ref = scipy.special.softmax(L.astype(np.float64), axis=1)
+    np.testing.assert_allclose(w, np.take_along_axis(ref, ids.astype(np.int64), 1),
+                               rtol=1e-13)
+    # ids are a permutation in descending-logit order
+    for t in range(7):
+        assert sorted(ids[t].tolist()) == list(range(12))
+        assert np.all(np.diff(L[t, ids[t]]) <= 0)
+
+
+def test_gate_topk_then_softmax_equals_softmax_then_renormalise():
+    rng = np.random.default_rng(2)
+    for E, k in [(8, 2), (128, 8), (768, 12)]:
+        L = rng.standard_normal((5, E)).astype(np.float32)
+        ids, w = O.gate_topk(L, k)
+        full = scipy.special.softmax(L.astype(np.float64), axis=1)
+        sel = np.take_along_axis(full, ids.astype(np.int64), 1)
+        np.testing.assert_allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-12)
+        np.testing.assert_allclose(w.sum(1), 1.0, rtol=0, atol=1e-14)
+
+
+def test_gate_bruteforce_selection():
+    rng = np.random.default_rng(3)
+    # integer logits force many ties
+    L = rng.integers(-3, 4, size=(40, 9)).astype(np.float32)
+    for k in (1, 3, 9):
+        ids, _ = O.gate_topk(L, k)
+        for t in range(L.shape[0]):
+            # brute force: repeatedly take the best remaining (value desc, id asc)
+            left = list(range(9))
+            want = []
+            for _ in range(k):
+                best = left[0]
+                for e in left[1:]:
+                    if L[t, e] > L[t, best]:
+                        best = e
+                want.append(best)
+                left.remove(best)
+            assert ids[t].tolist() == want
+
+
+def test_gate_signed_zero_is_a_tie():
+    L = np.array([[-0.0, 0.0, -1.0]], dtype=np.float32)
+    ids, w = O.gate_topk(L, 2)
+    assert ids[0].tolist() == [0, 1]
+    np.testing.assert_allclose(w[0], [0.5, 0.5], rtol=0, atol=0)
+
+
+# ----------------------------------------------------------------- routing
+
+
+def test_routing_golden():
+    g = _load("routing_small.json")
+    counts, offsets, sc, cp = O.init_routing(np.array(g["topk_ids"]), g["n_experts"])
+    assert counts.tolist() == g["counts"]
+    assert offsets.tolist() == g["offsets"]
+    assert sc.tolist() == g["sorted_copy"]
+    assert cp.tolist() == g["copy_pos"]
+
+
+def _routing_bruteforce(ids, E):
+    flat = [int(v) for v in np.asarray(ids).reshape(-1)]
+    counts = [0] * E
+    for e in flat:
+        counts[e] += 1
+    sorted_copy = [c for e in range(E) for c in range(len(flat)) if flat[c] == e]
+    pos = [0] * len(flat)
+    for i, c in enumerate(sorted_copy):
+        pos[c] = i
+    offs = [0]
+    for e in range(E):
+        offs.append(offs[-1] + counts[e])
+    return counts, offs, sorted_copy, pos
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (5, 4, 2), (16, 8, 2), (13, 24, 5), (0, 3, 1)])
+def test_routing_bruteforce(T, E, k):
+    rng = np.random.default_rng(T * 100 + E)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]) if T else np.zeros((0, k), int)
+    counts, offsets, sc, cp = O.init_routing(ids, E)
+    bc, bo, bs, bp = _routing_bruteforce(ids, E)
+    assert counts.tolist() == bc and offsets.tolist() == bo
+    assert sc.tolist() == bs and cp.tolist() == bp
+    # invariants
+    assert counts.sum() == T * k
+    flat = ids.reshape(-1)
+    if T:
+        assert np.all(np.diff(flat[sc]) >= 0)
+        assert np.array_equal(cp[sc], np.arange(T * k))
+        for e in range(E):
+            seg = sc[offsets[e]:offsets[e + 1]]
+            assert np.all(np.diff(seg) > 0)
+
+
+def test_routing_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        O.init_routing(np.array([[0, 5]]), 5)
+
+
+# ----------------------------------------------------------------- MX formats
+
+
+def test_e4m3_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().double().numpy()
+    got = O.e4m3_decode(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert nan.sum() == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    # sign of zero
+    assert np.signbit(got[128]) and not np.signbit(got[0])
+
+
+def test_e4m3_encode_matches_torch_rne_in_range():
+    # every finite code value, every midpoint between neighbours, and random
+    # values, all within [-448, 448] where torch's conversion is plain RNE
+    vals = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    pos = np.unique(vals[(vals >= 0) & np.isfinite(vals)])
+    mids = (pos[1:] + pos[:-1]) / 2
+    rng = np.random.default_rng(4)
+    rnd = rng.standard_normal(20000) * np.exp2(rng.integers(-12, 9, 20000))
+    rnd = rnd[np.abs(rnd) <= 448]
+    v = np.concatenate([pos, mids, -pos, -mids, rnd]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_encode(v.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_encode_saturates():
+    assert O.e4m3_encode(np.array([500.0, 1e9, -1e9, 449.0]))[:].tolist() == [126, 126, 254, 126]
+
+
+def test_e2m1_table_and_midpoints():
+    # OCP MX v1.0 e2m1 values for codes 0..7 (sign in bit 3)
+    assert O.e2m1_decode(np.arange(8)).tolist() == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    assert O.e2m1_decode(np.arange(8, 16)).tolist() == [-0.0, -0.5, -1, -1.5, -2, -3, -4, -6]
+    # ties to even mantissa, saturation at 6
+    mid = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0,
+           5.0: 4.0, 7.0: 6.0, 100.0: 6.0}
+    got = O.e2m1_decode(O.e2m1_encode(np.array(list(mid))))
+    assert got.tolist() == list(mid.values())
+    for c in range(16):
+        assert O.e2m1_encode(O.e2m1_decode(np.array([c])))[0] == (0 if c == 8 else c) or c == 8
+
+
+def test_mx_golden_blocks():
+    for c in _load("mx_blocks.json")["cases"]:
+        v = np.full(32, c["rest"], dtype=np.float64)
+        v[0] = c["first"]
+        codes, sc = O.mx_quant(v[None, :], c["fmt"])
+        assert int(sc[0, 0]) == c["scale"], c
+        assert int(codes[0, 0]) == c["code_first"], c
+        assert np.all(codes[0, 1:] == c["code_rest"]), c
+
+
+def test_mx_roundtrip_and_error_bound():
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((64, 256)) * np.exp2(rng.integers(-20, 20, (64, 1)))
+    v = O.round_bf16(v)
+    codes, sc = O.mx_quant(v, "e4m3")
+    d = O.mx_dequant(codes, sc, "e4m3")
+    # per block: |error| <= half an e4m3 ulp at the scaled magnitude
+    s = O.e8m0_decode(sc).repeat(32, axis=1)
+    q = np.abs(v) / s
+    ulp = np.exp2(np.maximum(np.floor(np.log2(np.maximum(q, 1e-300))), -6) - 3)
+    sat = q > 448
+    assert np.all(np.abs(d - v)[~sat] <= 0.5 * ulp[~sat] * s[~sat] * (1 + 1e-12))
+    # decode(encode(decode(c))) == decode(c): representable values round-trip
+    codes2, sc2 = O.mx_quant(d, "e4m3")
+    assert np.array_equal(O.mx_dequant(codes2, sc2, "e4m3"), d)
+
+
+def test_mxfp4_unpack_nibble_order():
+    packed = np.array([[0x21, 0xF7]], dtype=np.uint8)
+    assert O.mxfp4_unpack(packed).tolist() == [[1, 2, 7, 15]]
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(6)
+    v = (rng.standard_normal(50000) * np.exp2(rng.integers(-30, 30, 50000))).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).float().double().numpy()
+    assert np.array_equal(O.round_bf16(v.astype(np.float64)), ref)
+
+
+# ----------------------------------------------------------------- FFN / layer
+
+
+def test_silu_closed_forms():
+    np.testing.assert_allclose(O.silu(np.array([0.0, 1.0, -1.0])),
+                               [0.0, 1 / (1 + math.exp(-1)), -1 / (1 + math.exp(1))],
+                               rtol=1e-15)
+
+
+def _tiny(T=6, H=32, I=16, n_ffn=4, n_zero=0, k=2, lb=0, le=None, seed=0, residual=False):
+    rng = np.random.default_rng(seed)
+    E = n_ffn + n_zero
+    le = E if le is None else le
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    x = rng.standard_normal((T, H))
+    W13 = rng.standard_normal((n_ffn, H, 2 * I)) * 0.1
+    W2 = rng.standard_normal((n_ffn, I, H)) * 0.1
+    res = rng.standard_normal((T, H)) if residual else None
+    kw = dict(logits=logits, x=x, get_weights=lambda e: (W13[e], W2[e]), T=T, H=H,
+              I=I, n_ffn=n_ffn, n_zero=n_zero, top_k=k, local_begin=lb,
+              local_end=le, residual=res)
+    return kw, W13, W2
+
+
+def test_single_expert_is_dense_swiglu_ffn_torch():
+    # E=1, k=1: the layer is one dense FFN; compare with torch's chunk + silu
+    kw, W13, W2 = _tiny(T=9, n_ffn=1, k=1)
+    out = O.moe_layer(act="f32", exact=True, **kw)["out"]
+    x = torch.from_numpy(kw["x"])
+    g, u = torch.chunk(x @ torch.from_numpy(W13[0]), 2, -1)
+    ref = (torch.nn.functional.silu(g) * u) @ torch.from_numpy(W2[0])
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(),
+    dict(n_ffn=8, k=3, T=11, residual=True),
+    dict(n_ffn=5, n_zero=3, k=4, T=10),
+    dict(n_ffn=6, n_zero=2, k=2, lb=2, le=7, T=12),
+])
+def test_routed_equals_pertoken_and_dense(cfg):
+    kw, _, _ = _tiny(**cfg)
+    routed = O.moe_layer(act="f32", exact=True, **kw)["out"]
+    per_tok = O.moe_tokens(range(kw["T"]), act="f32", exact=True, **kw)
+    dense = O.moe_dense(**kw)
+    np.testing.assert_allclose(routed, dense, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(per_tok, dense, rtol=1e-12, atol=1e-12)
+
+
+def test_routed_equals_pertoken_with_roundings():
+    for act, act_q in [("bf16", "none"), ("f32", "none"), ("bf16", "mxfp8")]:
+        kw, _, _ = _tiny(T=10, H=64, I=32, n_ffn=6, n_zero=2, k=3, residual=True)
+        routed = O.moe_layer(act=act, act_q=act_q, **kw)["out"]
+        per_tok = O.moe_tokens(range(10), act=act, act_q=act_q, **kw)
+        assert np.array_equal(routed, per_tok)
+
+
+def test_zero_gate_columns_give_residual():
+    # SiLU(0) = 0: with zero gate weights every expert output is 0
+    kw, W13, W2 = _tiny(residual=True)
+    W13[:, :, :16] = 0.0
+    out = O.moe_layer(act="f32", exact=True, **kw)["out"]
+    np.testing.assert_array_equal(out, kw["residual"])
+
+
+def test_identity_experts_only_return_input():
+    # bias the logits so only identity experts win: MoE(x) = x
+    kw, _, _ = _tiny(T=7, n_ffn=4, n_zero=3, k=3, residual=True)
+    kw["logits"][:, 4:] += 100.0
+    for act in ("bf16", "f32"):
+        xa = O.round_to(kw["x"], act)
+        ra = O.round_to(kw["residual"], act)
+        # without residual the weights sum to 1 and the output is x itself
+        out = O.moe_layer(act=act, **dict(kw, x=xa, residual=None))["out"]
+        np.testing.assert_array_equal(out, xa)
+        # with residual: x + residual, rounded once (to within one ulp, since
+        # the fp64 weights sum to 1 only up to rounding and x + r may be a tie)
+        out = O.moe_layer(act=act, **dict(kw, x=xa, residual=ra))["out"]
+        ref = xa + ra
+        ulp = np.exp2(np.floor(np.log2(np.abs(ref) + 1e-30)) - (7 if act == "bf16" else 23))
+        assert np.all(np.abs(out - ref) <= ulp + 1e-15 * np.abs(xa))
+
+
+def test_expert_range_partial_sums_add_up():
+    kw, _, _ = _tiny(T=12, n_ffn=8, n_zero=4, k=4)
+    full = O.moe_layer(act="f32", exact=True, **kw)["out"]
+    parts = [O.moe_layer(act="f32", exact=True, **dict(kw, local_begin=b, local_end=e))["out"]
+             for b, e in [(0, 3), (3, 8), (8, 10), (10, 12)]]
+    np.testing.assert_allclose(sum(parts), full, rtol=1e-12, atol=1e-12)
+
+
+def test_gemm_inputs_are_the_routed_rows():
+    kw, _, _ = _tiny(T=8, n_ffn=4, n_zero=2, k=2, lb=1, le=4)
+    r = O.moe_layer(act="f32", exact=True, **kw)
+    ids = r["topk_ids"].reshape(-1)
+    # rows of x_perm are x of the copies whose expert lies in [1, 4), sorted
+    want = [c for e in range(1, 4) for c in range(ids.size) if ids[c] == e]
+    np.testing.assert_array_equal(r["x_perm"], kw["x"][np.array(want, int) // 2])
+    assert r["R"] == len(want)
+
+
+def test_mx_activation_codes_are_rowwise():
+    rng = np.random.default_rng(7)
+    x = O.round_bf16(rng.standard_normal((5, 64)))
+    codes, sc = O.mx_quant(x, "e4m3")
+    for t in range(5):
+        c1, s1 = O.mx_quant(x[t:t + 1], "e4m3")
+        assert np.array_equal(c1[0], codes[t]) and np.array_equal(s1[0], sc[t])
+
+
+def test_mxfp4_weights_dequant_exact():
+    # dequantised MXFP4 weights are exact fp64 numbers: code value * 2^(s-127)
+    packed = np.array([[0x71, 0x8F] * 16], dtype=np.uint8)      # K = 64
+    scales = np.array([[120, 127]], dtype=np.uint8)
+    w = O.mxfp4_dequant_rows(packed, scales)
+    assert w.shape == (1, 64)
+    assert w[0, :4].tolist() == [0.5 * 2**-7, 6.0 * 2**-7, -6.0 * 2**-7, -0.0]
+    assert w[0, 32:36].tolist() == [0.5, 6.0, -6.0, -0.0]
