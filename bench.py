@@ -1,0 +1,239 @@
+"""Benchmark of the MoE expert layer on one MI355X.
+
+One step = one pass of the whole layer (gate top-k softmax, routing, gather,
+GEMM1 + SwiGLU, GEMM2, finalize) over one batch of synthetic inputs that are
+already resident in HBM, through the library's C ABI (moe_layer_traced, which
+records an event around every stage on the launch stream).
+
+Prints ONE JSON line: whole-step tokens/s plus
+  roofline     the dominant kernel (GEMM1 + SwiGLU) measured with the stage
+               events over the timed steps, against the MI355X peak of the
+               bound it hits (HBM 8 TB/s for decode-size batches, dense MFMA
+               for prefill-size batches);
+  cpu_baseline the CPU oracle timed on the host on a bounded sample of the
+               same workload (a reported baseline, not the target).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("MoE layer tokens/s; grouped-GEMM % of MFMA peak (prefill) / "
+          "% HBM BW (decode)")
+DEFAULT_WORKLOAD = "qwen3_30b_a3b_decode_bf16"
+
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "mx": 5000.0, "f32": 157.3}
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def _routing_stats(m, p, shape, inp):
+    """Touched experts and routed rows of the local range, read back once
+    after the timed region from the library's own routing calls."""
+    import torch
+    ids, _ = m.gate_topk(p, inp["logits"])
+    r = m.init_routing(p, ids, inp["x"])
+    counts = r["counts"].cpu().numpy()
+    loc = counts[shape.ffn_begin:shape.ffn_end]
+    torch.cuda.synchronize()
+    return int((loc > 0).sum()), int(loc.sum())
+
+
+def _gemm1_units(shape, touched, R):
+    """Algorithmic work of one GEMM1 + SwiGLU launch."""
+    H, I = shape.H, shape.I
+    if shape.wt == "mxfp4":
+        wbytes = touched * (2 * I * H // 2 + 2 * I * H // 32)
+        abytes = R * (H + H // 32) + R * (I + I // 32)
+    else:
+        eb = 4 if shape.wt == "f32" else 2
+        wbytes = touched * H * 2 * I * eb
+        abytes = R * H * eb + R * I * eb
+    flops = 2.0 * R * H * 2 * I
+    return wbytes + abytes, flops
+
+
+def _bound(shape, R, touched):
+    """Decode-size batches stream weights (HBM bound); prefill-size batches
+    are MFMA bound. Chosen by arithmetic intensity of GEMM1 against the
+    ridge point of the format's peak."""
+    nbytes, flops = _gemm1_units(shape, touched, R)
+    kind = "mx" if shape.wt == "mxfp4" else ("f32" if shape.wt == "f32" else "bf16")
+    ridge = PEAK_TFLOPS[kind] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    return ("mfma" if flops / nbytes > ridge else "hbm"), kind
+
+
+def _cpu_baseline(shape, inp, target_s):
+    """The oracle as it stands, on the host, over a bounded token sample."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    cores = max(blas, torch.get_num_threads())
+    host = {k: (None if v is None else v.cpu()) for k, v in inp.items()}
+    fb = shape.ffn_begin
+    if shape.wt == "mxfp4":
+        def get(e):
+            i = e - fb
+            a = O.mxfp4_dequant_rows(host["w13"][i].numpy(), host["w13_scale"][i].numpy())
+            b = O.mxfp4_dequant_rows(host["w2"][i].numpy(), host["w2_scale"][i].numpy())
+            return a.T.copy(), b.T.copy()
+    else:
+        def get(e):
+            i = e - fb
+            return (host["w13"][i].double().numpy(), host["w2"][i].double().numpy())
+    kw = dict(logits=host["logits"].numpy(), x=host["x"].double().numpy(),
+              residual=None if host["residual"] is None else host["residual"].double().numpy(),
+              get_weights=get, T=shape.T, H=shape.H, I=shape.I,
+              n_ffn=shape.n_ffn, n_zero=shape.n_zero, top_k=shape.top_k,
+              local_begin=shape.local_begin, local_end=shape.local_end,
+              act=shape.act, act_q=shape.act_q)
+    # sample: whole layer when small enough, else a growing prefix of tokens
+    # evaluated per token (weights fetched once per expert)
+    done, t0 = 0, time.perf_counter()
+    if shape.T <= 64:
+        reps = 0
+        while True:
+            O.moe_layer(**kw)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= target_s or reps >= 5:
+                break
+        done = reps * shape.T
+        sample = f"whole layer ({shape.T} tokens) x{reps} via the routed oracle"
+    else:
+        rng = np.random.default_rng(0)
+        toks = rng.permutation(shape.T)
+        n = 8
+        while True:
+            O.moe_tokens(toks[done:done + n], cache_weights=False, **kw)
+            done += n
+            el = time.perf_counter() - t0
+            if el >= target_s or done >= shape.T:
+                break
+            n = min(2 * n, shape.T - done)
+        sample = f"{done} of {shape.T} tokens via the per-token oracle"
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle", "sample": sample, "seconds": round(el, 2)}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU "
+              "path (the expert-parallel case is one rank's expert range on "
+              "one GPU). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import moe_expert_layer_gate_amd as m
+    from moe_inputs import generate, get_workload
+
+    m.lib()
+    shape = get_workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = generate(shape, seed=args.seed, device=dev)
+    p = m.problem(shape)
+    ws = torch.empty(max(m.layer_workspace_bytes(p), 1), dtype=torch.uint8, device=dev)
+    dt = torch.float32 if shape.act == "f32" else torch.bfloat16
+    out = torch.empty((shape.T, shape.H), dtype=dt, device=dev)
+    nst = len(m.STAGES) + 1
+
+    def step(events):
+        m.layer_traced(p, inp["logits"], inp["x"], inp["w13"], inp["w2"],
+                       events, inp["w13_scale"], inp["w2_scale"],
+                       residual=inp["residual"], out=out, workspace=ws)
+
+    none = [None] * nst
+    for _ in range(args.warmup):
+        step(none)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    stage_us = {}
+    for s, name in enumerate(m.STAGES):
+        d = [ev[i][s].elapsed_time(ev[i][s + 1]) * 1e3 for i in range(args.steps)]
+        stage_us[name] = round(sum(d) / len(d), 2)
+    gpu_step_us = sum(ev[i][0].elapsed_time(ev[i][nst - 1]) * 1e3
+                      for i in range(args.steps)) / args.steps
+
+    touched, R = _routing_stats(m, p, shape, inp)
+    bound, kind = _bound(shape, R, touched)
+    nbytes, flops = _gemm1_units(shape, touched, R)
+    dur = stage_us["gemm1_swiglu"] * 1e-6
+    if bound == "hbm":
+        ach = nbytes / dur / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": None}
+    else:
+        ach = flops / dur / 1e12
+        peak = PEAK_TFLOPS[kind]
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None}
+    roof.update({"kernel": "gemm1_swiglu", "avg_us": stage_us["gemm1_swiglu"],
+                 "algorithmic_bytes": int(nbytes), "algorithmic_flops": flops,
+                 "touched_experts": touched, "routed_rows": R})
+    rec = {
+        "metric": METRIC,
+        "value": round(shape.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "mxfp4": "mxfp8xmxfp4"}[shape.wt],
+        "data": "synthetic",
+        "config": {"workload": shape.name, "T": shape.T, "H": shape.H,
+                   "I": shape.I, "n_ffn": shape.n_ffn, "n_zero": shape.n_zero,
+                   "top_k": shape.top_k,
+                   "local_experts": [shape.local_begin, shape.local_end],
+                   "act": shape.act, "wt": shape.wt, "act_q": shape.act_q,
+                   "residual": shape.residual, "seed": args.seed},
+        "gpu_step_us": round(gpu_step_us, 2),
+        "stages_us": stage_us,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = _cpu_baseline(shape, inp, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+/*
+ * moe_mi355x.h -- C ABI of the MI355X (gfx950) MoE expert-layer library.
+ *
+ * The layer: router logits -> gating top-k softmax -> routing (expert
+ * histogram, stable permutation of token copies, gather) -> grouped GEMM over
+ * the merged gate/up weights w13 with a fused SwiGLU -> grouped GEMM over the
+ * down weights w2 -> finalize (weighted un-permute and sum, identity experts,
+ * optional residual).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "Qwen3-MoE low-latency inference on Atlas A3 / 950 clusters"
+ *   [P2] "LongCat-Flash inference on Atlas A3 clusters"
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers to memory the caller allocated
+ *     and owns. The library never allocates, frees, copies to the host or
+ *     synchronises; it only enqueues kernels on `stream` (a hipStream_t; NULL
+ *     is the null stream). Outputs are overwritten, never accumulated into.
+ *   - Every array is row-major and contiguous. Sizes are element counts.
+ *   - Argument checks run on the host before any launch. A failed check
+ *     returns an error and enqueues nothing. A launch failure returns
+ *     MOE_ERR_HIP. Faults inside kernels surface at the caller's next
+ *     synchronisation. Nothing is printed; no call aborts.
+ *   - Calls keep no mutable global state and may run concurrently on
+ *     different streams with different buffers.
+ *   - Workspace (hipcub style): when `workspace` is NULL the call stores the
+ *     bytes it needs in *workspace_bytes, returns MOE_OK and launches nothing.
+ *     Otherwise *workspace_bytes is the size of `workspace`; a buffer that is
+ *     too small gives MOE_ERR_WORKSPACE. Workspace must be 256-byte aligned.
+ *
+ * Expert ids: FFN experts are [0, n_ffn); identity ("zero-compute") experts
+ * are [n_ffn, n_ffn + n_zero) and return their input, MoE(x) = x ([P2]
+ * "MoE模块 / Decode阶段优化"). E_tot = n_ffn + n_zero. A call handles the ids
+ * in [local_begin, local_end) -- one expert-parallel rank's share ([P1] "MoE
+ * EP优化 / AllGather方案": routing keeps only the copies of this rank's
+ * experts and finalize yields a partial sum). Copies of experts outside the
+ * range contribute 0. The FFN experts of the range, [fb, fe) with
+ * fb = min(local_begin, n_ffn) and fe = min(local_end, n_ffn), are the ones
+ * whose weights the call receives, indexed by e - fb (E_loc = fe - fb).
+ *
+ * Limits: 1 <= top_k <= min(E_tot, 64); E_tot <= 2048; H and I multiples of
+ * 32; T*top_k < 2^31. Status MOE_ERR_UNSUPPORTED otherwise.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad range            */
+  MOE_ERR_UNSUPPORTED = 2, /* valid problem outside this library's limits  */
+  MOE_ERR_WORKSPACE = 3,   /* workspace smaller than required              */
+  MOE_ERR_HIP = 4          /* a HIP launch failed                           */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_MXFP8_E4M3 = 2, /* e4m3fn codes + one e8m0 scale per 32 along K      */
+  MOE_MXFP4_E2M1 = 3  /* e2m1 codes, 2 per byte (low nibble = even k),
+                         + one e8m0 scale per 32 along K                    */
+} moe_dtype;
+
+typedef struct moe_problem {
+  int32_t T;           /* tokens                                            */
+  int32_t H;           /* hidden size                                       */
+  int32_t I;           /* per-expert intermediate size                      */
+  int32_t n_ffn;       /* FFN experts                                       */
+  int32_t n_zero;      /* identity experts                                  */
+  int32_t top_k;       /* experts per token                                 */
+  int32_t local_begin; /* expert-id range handled by the call              */
+  int32_t local_end;
+  int32_t act;   /* MOE_F32 | MOE_BF16: x, residual, y, out, h (unquantised) */
+  int32_t wt;    /* MOE_F32 | MOE_BF16 | MOE_MXFP4_E2M1                     */
+  int32_t act_q; /* == act (no quantisation) | MOE_MXFP8_E4M3 (dynamic)     */
+} moe_problem;
+
+/* Supported combinations: (act, wt, act_q) = (F32, F32, F32),
+ * (BF16, BF16, BF16), (BF16, MXFP4_E2M1, MXFP8_E4M3).
+ *
+ * Weight layouts (E_loc experts, weights of expert e at index e - fb):
+ *   F32 / BF16:  w13 [E_loc, H, 2I]   columns [0, I) = gate, [I, 2I) = up
+ *                w2  [E_loc, I, H]
+ *                (the merged gate/up matrix of [P1] "MoE TP优化 / 计算分解")
+ *   MXFP4_E2M1:  w13 [E_loc, 2I, H/2] bytes, K (= H) contiguous per output
+ *                column; rows [0, I) gate, [I, 2I) up
+ *                w13_scale [E_loc, 2I, H/32] e8m0
+ *                w2  [E_loc, H, I/2] bytes, w2_scale [E_loc, H, I/32] e8m0
+ * Scale pointers must be NULL unless wt is MXFP4_E2M1.
+ */
+
+/* Gating: [P1] "GMM使能和Routing优化 / 快速选择专家" (fused top-k + softmax
+ * replacing topk-then-softmax); [P2] "MoE模块 / Router" (sort router output,
+ * take the top-k experts).
+ *   logits      fp32 [T, E_tot]
+ *   topk_ids    int32 [T, top_k]  the k largest logits per token, descending,
+ *                                 ties to the lower expert id
+ *   topk_weight fp32  [T, top_k]  softmax over the k selected logits (the
+ *                                 full softmax renormalised over the top-k)
+ * Uses all E_tot experts regardless of the local range. */
+MOE_API moe_status moe_gate_topk(const moe_problem* p, const float* logits,
+                         int32_t* topk_ids, float* topk_weight, void* stream);
+
+/* Routing: [P1] "高效排序和token路由" (init_routing sorts the token copies by
+ * expert, compute_expert_tokens counts each expert's tokens); [P1] "MoE
+ * EP优化 / AllGather方案" (MXFP8 quantisation of the hidden states and
+ * routing restricted to the local expert range).
+ * Copies are numbered c = t * top_k + j.
+ *   topk_ids          int32 [T, top_k]; ids outside [0, E_tot) are ignored
+ *                     (not counted; their copy_pos is -1)
+ *   x                 act [T, H]
+ *   tokens_per_expert int32 [E_tot]   copies routed to each expert
+ *   offsets           int32 [E_tot+1] exclusive prefix sum; offsets[E_tot]
+ *                     is the number of valid copies
+ *   sorted_copy       int32 [T*top_k] copies sorted by (expert id, c)
+ *   copy_pos          int32 [T*top_k] inverse: sorted position of copy c
+ *   x_perm            rows r = 0 .. R-1, R = offsets[fe] - offsets[fb]:
+ *                     x_perm[r] = x[sorted_copy[offsets[fb] + r] / top_k];
+ *                     act [T*top_k, H] or, when act_q is MXFP8_E4M3, e4m3
+ *                     codes uint8 [T*top_k, H]. Rows >= R are not written.
+ *   x_perm_scale      e8m0 uint8 [T*top_k, H/32] when act_q is MXFP8_E4M3,
+ *                     else must be NULL.
+ *   workspace         scratch (see conventions). */
+MOE_API moe_status moe_init_routing(const moe_problem* p, const int32_t* topk_ids,
+                            const void* x, int32_t* tokens_per_expert,
+                            int32_t* offsets, int32_t* sorted_copy,
+                            int32_t* copy_pos, void* x_perm,
+                            uint8_t* x_perm_scale, void* workspace,
+                            size_t* workspace_bytes, void* stream);
+
+/* Grouped expert FFN: [P1] "MoE TP优化 / 计算分解" (expert =
+ * down(SiLU(gate(x)) * up(x)); npu_swiglu halves the last axis and returns
+ * SiLU(first) * second) and "高性能专家计算" (all experts' matmuls in one
+ * grouped operator). For every FFN expert e in [fb, fe) with rows
+ * [offsets[e] - offsets[fb], offsets[e+1] - offsets[fb]) of x_perm:
+ *   h = SwiGLU(x_perm_rows @ w13[e])   fp32 accumulation; stored in act
+ *                                      dtype, or MXFP8 (one e8m0 per 32
+ *                                      along I) when act_q is MXFP8_E4M3
+ *   y = h @ w2[e]                      fp32 accumulation, stored in act
+ * Experts with no rows never read their weights.
+ *   offsets  int32 [E_tot+1] as produced by moe_init_routing
+ *   y        act [T*top_k, H]; rows >= R are not written
+ * moe_ffn_up and moe_ffn_down are the two halves (h buffer explicit):
+ *   h        act [T*top_k, I], or e4m3 codes uint8 [T*top_k, I]
+ *   h_scale  e8m0 uint8 [T*top_k, I/32] when act_q is MXFP8_E4M3 else NULL */
+MOE_API moe_status moe_grouped_ffn(const moe_problem* p, const int32_t* offsets,
+                           const void* x_perm, const uint8_t* x_perm_scale,
+                           const void* w13, const uint8_t* w13_scale,
+                           const void* w2, const uint8_t* w2_scale, void* y,
+                           void* workspace, size_t* workspace_bytes,
+                           void* stream);
+
+MOE_API moe_status moe_ffn_up(const moe_problem* p, const int32_t* offsets,
+                      const void* x_perm, const uint8_t* x_perm_scale,
+                      const void* w13, const uint8_t* w13_scale, void* h,
+                      uint8_t* h_scale, void* workspace,
+                      size_t* workspace_bytes, void* stream);
+
+MOE_API moe_status moe_ffn_down(const moe_problem* p, const int32_t* offsets,
+                        const void* h, const uint8_t* h_scale, const void* w2,
+                        const uint8_t* w2_scale, void* y, void* workspace,
+                        size_t* workspace_bytes, void* stream);
+
+/* Finalize: [P1] "高效排序和token路由" (finalize_routing restores token order
+ * and takes the weighted sum) and [P2] "Decode阶段优化" (identity experts).
+ *   out[t] = residual[t] + sum_{j=0..k-1} topk_weight[t,j] * v(t,j)
+ *   v = y[copy_pos[t*k+j] - offsets[fb]]  FFN expert in the range
+ *     = x[t]                              identity expert in the range
+ *     = 0                                 expert outside the range
+ * Summed in fp32 in the order j = 0..k-1 starting from the residual,
+ * rounded once to act.
+ *   residual act [T, H] or NULL; x act [T, H]; y as from moe_grouped_ffn;
+ *   out act [T, H]. */
+MOE_API moe_status moe_finalize(const moe_problem* p, const int32_t* topk_ids,
+                        const float* topk_weight, const int32_t* copy_pos,
+                        const int32_t* offsets, const void* y, const void* x,
+                        const void* residual, void* out, void* stream);
+
+/* The whole layer in one call: gate, routing, grouped FFN, finalize. All
+ * intermediates live in `workspace`. Same result as the five calls above in
+ * sequence. */
+MOE_API moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
+                     const void* residual, const void* w13,
+                     const uint8_t* w13_scale, const void* w2,
+                     const uint8_t* w2_scale, void* out, void* workspace,
+                     size_t* workspace_bytes, void* stream);
+
+/* moe_layer with stage timing: when stage_events is non-NULL, entry i (a
+ * hipEvent_t or NULL) is recorded on `stream` right before stage i is
+ * enqueued, for i < n_events, with stages 0 gate, 1 expert histogram,
+ * 2 scan (+ GEMM tile list), 3 permutation, 4 gather (+ MXFP8), 5 GEMM1 +
+ * SwiGLU, 6 GEMM2, 7 finalize, and entry 8 after the last. Each of stages
+ * 0-7 is exactly one kernel launch (a stage with nothing to do launches
+ * nothing), so events i and i+1 bracket one kernel. For performance tooling;
+ * results are identical to moe_layer. */
+MOE_API moe_status moe_layer_traced(const moe_problem* p, const float* logits,
+                                    const void* x, const void* residual,
+                                    const void* w13, const uint8_t* w13_scale,
+                                    const void* w2, const uint8_t* w2_scale,
+                                    void* out, void* workspace,
+                                    size_t* workspace_bytes, void* stream,
+                                    void* const* stage_events, int32_t n_events);
+
+/* Static strings; never NULL. */
+MOE_API const char* moe_status_string(moe_status s);
+/* Library ABI version (major * 100 + minor). */
+MOE_API int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,283 @@
+"""Python binding of the MI355X MoE expert-layer library (libmoe_mi355x.so).
+
+Argument marshalling only: torch tensors supply device pointers and torch's
+current HIP stream supplies the stream; every step of the layer runs in the
+library's HIP kernels. The library must be built (``__graft_entry__.build()``
+or ``python moe_expert_layer_gate_amd/build.py``); importing the binding
+without it raises, there is no fallback.
+
+Calls mirror the C ABI in include/moe_mi355x.h:
+  gate_topk, init_routing, ffn_up, ffn_down, grouped_ffn, finalize, layer.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "MoeProblem", "MoeError", "lib", "problem", "gate_topk",
+    "init_routing", "ffn_up", "ffn_down", "grouped_ffn", "finalize", "layer",
+    "layer_workspace_bytes", "layer_traced", "SYMBOLS", "STAGES",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+
+MOE_F32, MOE_BF16, MOE_MXFP8_E4M3, MOE_MXFP4_E2M1 = 0, 1, 2, 3
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8_E4M3,
+       "mxfp4": MOE_MXFP4_E2M1}
+
+SYMBOLS = ["moe_gate_topk", "moe_init_routing", "moe_grouped_ffn", "moe_ffn_up",
+           "moe_ffn_down", "moe_finalize", "moe_layer", "moe_layer_traced",
+           "moe_status_string", "moe_abi_version"]
+
+# stages of moe_layer_traced, in launch order
+STAGES = ["gate_topk", "route_count", "route_scan", "route_scatter",
+          "route_gather", "gemm1_swiglu", "gemm2", "finalize"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class MoeProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "T", "H", "I", "n_ffn", "n_zero", "top_k", "local_begin", "local_end",
+        "act", "wt", "act_q")]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_sz = ctypes.POINTER(ctypes.c_size_t)
+_pp = ctypes.POINTER(MoeProblem)
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "moe_gate_topk": [_pp, _vp, _vp, _vp, _vp],
+        "moe_init_routing": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _sz, _vp],
+        "moe_grouped_ffn": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                            _sz, _vp],
+        "moe_ffn_up": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+        "moe_ffn_down": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+        "moe_finalize": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+        "moe_layer": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                      _vp],
+        "moe_layer_traced": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _sz, _vp, ctypes.POINTER(ctypes.c_void_p),
+                             ctypes.c_int32],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    L.moe_status_string.argtypes = [ctypes.c_int]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_abi_version.argtypes = []
+    L.moe_abi_version.restype = ctypes.c_int32
+    _lib = L
+    return L
+
+
+def problem(shape=None, **kw) -> MoeProblem:
+    """Build a MoeProblem from an object with the shape attributes (T, H, I,
+    n_ffn, n_zero, top_k, local_begin, local_end, act, wt, act_q with dtype
+    names "f32" / "bf16" / "mxfp4" / "mxfp8" / "none") and/or keywords."""
+    vals = {}
+    for n in ("T", "H", "I", "n_ffn", "n_zero", "top_k", "local_begin",
+              "local_end", "act", "wt", "act_q"):
+        if n in kw:
+            vals[n] = kw[n]
+        elif shape is not None:
+            vals[n] = getattr(shape, n)
+    if vals.get("act_q") in (None, "none"):
+        vals["act_q"] = vals["act"]
+    for n in ("act", "wt", "act_q"):
+        if isinstance(vals[n], str):
+            vals[n] = _DT[vals[n]]
+    return MoeProblem(**vals)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(st: int):
+    if st != 0:
+        raise MoeError(st, lib().moe_status_string(st).decode())
+
+
+def _ws_query(fn, *args) -> int:
+    n = ctypes.c_size_t(0)
+    _check(fn(*args, None, ctypes.byref(n), None))
+    return n.value
+
+
+def _act_dtype(p: MoeProblem):
+    return torch.float32 if p.act == MOE_F32 else torch.bfloat16
+
+
+def gate_topk(p: MoeProblem, logits, topk_ids=None, topk_weight=None):
+    dev = logits.device
+    if topk_ids is None:
+        topk_ids = torch.empty((p.T, p.top_k), dtype=torch.int32, device=dev)
+    if topk_weight is None:
+        topk_weight = torch.empty((p.T, p.top_k), dtype=torch.float32, device=dev)
+    _check(lib().moe_gate_topk(ctypes.byref(p), _ptr(logits), _ptr(topk_ids),
+                               _ptr(topk_weight), _stream()))
+    return topk_ids, topk_weight
+
+
+def init_routing(p: MoeProblem, topk_ids, x):
+    dev = x.device
+    E = p.n_ffn + p.n_zero
+    N = p.T * p.top_k
+    mx = p.act_q == MOE_MXFP8_E4M3
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_copy = torch.empty(N, dtype=torch.int32, device=dev)
+    copy_pos = torch.empty(N, dtype=torch.int32, device=dev)
+    if mx:
+        x_perm = torch.empty((N, p.H), dtype=torch.uint8, device=dev)
+        x_scale = torch.empty((N, p.H // 32), dtype=torch.uint8, device=dev)
+    else:
+        x_perm = torch.empty((N, p.H), dtype=_act_dtype(p), device=dev)
+        x_scale = None
+    L = lib()
+    args = (ctypes.byref(p), _ptr(topk_ids), _ptr(x), _ptr(counts),
+            _ptr(offsets), _ptr(sorted_copy), _ptr(copy_pos), _ptr(x_perm),
+            _ptr(x_scale))
+    nb = _ws_query(L.moe_init_routing, *args)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    n = ctypes.c_size_t(ws.numel())
+    _check(L.moe_init_routing(*args, _ptr(ws), ctypes.byref(n), _stream()))
+    return dict(counts=counts, offsets=offsets, sorted_copy=sorted_copy,
+                copy_pos=copy_pos, x_perm=x_perm, x_perm_scale=x_scale,
+                workspace=ws)
+
+
+def _h_buffers(p: MoeProblem, dev):
+    N = p.T * p.top_k
+    if p.act_q == MOE_MXFP8_E4M3:
+        return (torch.empty((N, p.I), dtype=torch.uint8, device=dev),
+                torch.empty((N, p.I // 32), dtype=torch.uint8, device=dev))
+    return torch.empty((N, p.I), dtype=_act_dtype(p), device=dev), None
+
+
+def ffn_up(p: MoeProblem, offsets, x_perm, x_perm_scale, w13, w13_scale=None):
+    dev = offsets.device
+    h, hs = _h_buffers(p, dev)
+    L = lib()
+    args = (ctypes.byref(p), _ptr(offsets), _ptr(x_perm), _ptr(x_perm_scale),
+            _ptr(w13), _ptr(w13_scale), _ptr(h), _ptr(hs))
+    nb = _ws_query(L.moe_ffn_up, *args)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    n = ctypes.c_size_t(ws.numel())
+    _check(L.moe_ffn_up(*args, _ptr(ws), ctypes.byref(n), _stream()))
+    return h, hs
+
+
+def ffn_down(p: MoeProblem, offsets, h, h_scale, w2, w2_scale=None):
+    dev = offsets.device
+    y = torch.empty((p.T * p.top_k, p.H), dtype=_act_dtype(p), device=dev)
+    L = lib()
+    args = (ctypes.byref(p), _ptr(offsets), _ptr(h), _ptr(h_scale), _ptr(w2),
+            _ptr(w2_scale), _ptr(y))
+    nb = _ws_query(L.moe_ffn_down, *args)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    n = ctypes.c_size_t(ws.numel())
+    _check(L.moe_ffn_down(*args, _ptr(ws), ctypes.byref(n), _stream()))
+    return y
+
+
+def grouped_ffn(p: MoeProblem, offsets, x_perm, x_perm_scale, w13, w2,
+                w13_scale=None, w2_scale=None):
+    dev = offsets.device
+    y = torch.empty((p.T * p.top_k, p.H), dtype=_act_dtype(p), device=dev)
+    L = lib()
+    args = (ctypes.byref(p), _ptr(offsets), _ptr(x_perm), _ptr(x_perm_scale),
+            _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), _ptr(y))
+    nb = _ws_query(L.moe_grouped_ffn, *args)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    n = ctypes.c_size_t(ws.numel())
+    _check(L.moe_grouped_ffn(*args, _ptr(ws), ctypes.byref(n), _stream()))
+    return y
+
+
+def finalize(p: MoeProblem, topk_ids, topk_weight, copy_pos, offsets, y, x,
+             residual=None, out=None):
+    if out is None:
+        out = torch.empty((p.T, p.H), dtype=_act_dtype(p), device=x.device)
+    _check(lib().moe_finalize(ctypes.byref(p), _ptr(topk_ids),
+                              _ptr(topk_weight), _ptr(copy_pos), _ptr(offsets),
+                              _ptr(y), _ptr(x), _ptr(residual), _ptr(out),
+                              _stream()))
+    return out
+
+
+def layer_workspace_bytes(p: MoeProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_layer(ctypes.byref(p), None, None, None, None, None, None,
+                           None, None, None, ctypes.byref(n), None))
+    return n.value
+
+
+def layer_traced(p: MoeProblem, logits, x, w13, w2, events, w13_scale=None,
+                 w2_scale=None, residual=None, out=None, workspace=None):
+    """moe_layer with torch.cuda.Event objects (len(STAGES) + 1 of them, or
+    None entries) recorded on the current stream around each stage."""
+    if out is None:
+        out = torch.empty((p.T, p.H), dtype=_act_dtype(p), device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(layer_workspace_bytes(p), 1),
+                                dtype=torch.uint8, device=x.device)
+    arr = (ctypes.c_void_p * len(events))(
+        *[None if e is None else e.cuda_event for e in events])
+    n = ctypes.c_size_t(workspace.numel())
+    _check(lib().moe_layer_traced(ctypes.byref(p), _ptr(logits), _ptr(x),
+                                  _ptr(residual), _ptr(w13), _ptr(w13_scale),
+                                  _ptr(w2), _ptr(w2_scale), _ptr(out),
+                                  _ptr(workspace), ctypes.byref(n), _stream(),
+                                  arr, len(events)))
+    return out
+
+
+def layer(p: MoeProblem, logits, x, w13, w2, w13_scale=None, w2_scale=None,
+          residual=None, out=None, workspace=None):
+    """The whole layer in one library call. `workspace` (uint8 CUDA tensor of
+    at least layer_workspace_bytes(p)) may be passed to avoid reallocating."""
+    if out is None:
+        out = torch.empty((p.T, p.H), dtype=_act_dtype(p), device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(layer_workspace_bytes(p), 1),
+                                dtype=torch.uint8, device=x.device)
+    n = ctypes.c_size_t(workspace.numel())
+    _check(lib().moe_layer(ctypes.byref(p), _ptr(logits), _ptr(x),
+                           _ptr(residual), _ptr(w13), _ptr(w13_scale), _ptr(w2),
+                           _ptr(w2_scale), _ptr(out), _ptr(workspace),
+                           ctypes.byref(n), _stream()))
+    return out

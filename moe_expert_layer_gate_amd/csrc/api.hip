@@ -1,0 +1,403 @@
+// C ABI of the MoE expert layer: argument checks, workspace layout and the
+// launch sequence. No allocation, no host synchronisation, no global state.
+#include "../../include/moe_mi355x.h"
+#include "launch.h"
+
+namespace {
+
+using moe::Tile;
+
+constexpr int kMaxE = 2048;
+constexpr int kMaxK = 64;
+
+struct Prob {
+  int T, H, I, nffn, nzero, k, lb, le, act, wt, actq;
+  int E, fb, fe, El;
+  long long N;  // T * k copies
+  bool mx;
+};
+
+moe_status check(const moe_problem* p, Prob* q) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  Prob r{};
+  r.T = p->T; r.H = p->H; r.I = p->I; r.nffn = p->n_ffn; r.nzero = p->n_zero;
+  r.k = p->top_k; r.lb = p->local_begin; r.le = p->local_end;
+  r.act = p->act; r.wt = p->wt; r.actq = p->act_q;
+  if (r.T < 0 || r.H <= 0 || r.I <= 0 || r.nffn < 0 || r.nzero < 0)
+    return MOE_ERR_INVALID_ARG;
+  r.E = r.nffn + r.nzero;
+  if (r.E < 1 || r.k < 1 || r.k > r.E) return MOE_ERR_INVALID_ARG;
+  if (r.lb < 0 || r.lb >= r.le || r.le > r.E) return MOE_ERR_INVALID_ARG;
+  if (r.E > kMaxE || r.k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (r.H % 32 || r.I % 32) return MOE_ERR_UNSUPPORTED;
+  r.N = (long long)r.T * r.k;
+  if (r.N >= (1LL << 31) || (long long)r.N * r.H >= (1LL << 40))
+    return MOE_ERR_UNSUPPORTED;
+  const bool f32 = r.act == MOE_F32 && r.wt == MOE_F32 && r.actq == MOE_F32;
+  const bool bf16 = r.act == MOE_BF16 && r.wt == MOE_BF16 && r.actq == MOE_BF16;
+  r.mx = r.act == MOE_BF16 && r.wt == MOE_MXFP4_E2M1 && r.actq == MOE_MXFP8_E4M3;
+  if (!f32 && !bf16 && !r.mx) return MOE_ERR_UNSUPPORTED;
+  if (r.mx && (r.H % 128 || r.I % 128)) return MOE_ERR_UNSUPPORTED;
+  r.fb = r.lb < r.nffn ? r.lb : r.nffn;
+  r.fe = r.le < r.nffn ? r.le : r.nffn;
+  r.El = r.fe - r.fb;
+  *q = r;
+  return MOE_OK;
+}
+
+size_t act_bytes(const Prob& q) { return q.act == MOE_F32 ? 4 : 2; }
+
+// Tile height of the grouped GEMM chosen for the problem.
+int tile_rows(const Prob& q) {
+  if (q.act == MOE_F32) return 32;
+  const long long avg = q.E ? q.N / q.E : 0;  // expected rows per expert
+  return avg <= 12 ? 16 : 32;
+}
+
+long long max_tiles(const Prob& q, int mt) {
+  if (q.El == 0 || q.N == 0) return 0;
+  long long ne = q.El < q.N ? q.El : q.N;
+  return ne + q.N / mt + 1;
+}
+
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base((char*)b) {}
+  template <class T>
+  T* take(size_t n) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+moe_status hip_status(hipError_t e) {
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+#define MOE_TRY(expr)                                 \
+  do {                                                \
+    hipError_t _e = (expr);                           \
+    if (_e != hipSuccess) return MOE_ERR_HIP;         \
+  } while (0)
+
+// ---------------------------------------------------------------- FFN halves
+
+struct FfnWs {
+  Tile* tiles;
+  int32_t* tile_count;
+};
+
+FfnWs carve_ffn_ws(Carve& c, const Prob& q, int mt) {
+  FfnWs w;
+  w.tiles = c.take<Tile>((size_t)max_tiles(q, mt) + 1);
+  w.tile_count = c.take<int32_t>(1);
+  return w;
+}
+
+moe_status run_up(const Prob& q, int mt, const Tile* tiles,
+                  const int32_t* tile_count, const void* xp, const uint8_t* xs,
+                  const void* w13, const uint8_t* w13s, void* h, uint8_t* hs,
+                  hipStream_t s) {
+  const int mtl = (int)max_tiles(q, mt);
+  if (mtl == 0) return MOE_OK;
+  if (q.act == MOE_F32)
+    MOE_TRY(moe::launch_gemm_f32(true, tiles, tile_count, mtl, (const float*)xp,
+                                 (const float*)w13, (float*)h, q.H, 2 * q.I,
+                                 q.I, s));
+  else if (q.mx)
+    MOE_TRY(moe::launch_gemm_mx(true, mt / 16, tiles, tile_count, mtl,
+                                (const uint8_t*)xp, xs, (const uint8_t*)w13,
+                                w13s, h, hs, q.H, 2 * q.I, q.I, s));
+  else
+    MOE_TRY(moe::launch_gemm_bf16_stream(
+        true, mt / 16, tiles, tile_count, mtl, (const uint16_t*)xp,
+        (const uint16_t*)w13, (uint16_t*)h, q.H, 2 * q.I, q.I, s));
+  return MOE_OK;
+}
+
+moe_status run_down(const Prob& q, int mt, const Tile* tiles,
+                    const int32_t* tile_count, const void* h,
+                    const uint8_t* hs, const void* w2, const uint8_t* w2s,
+                    void* y, hipStream_t s) {
+  const int mtl = (int)max_tiles(q, mt);
+  if (mtl == 0) return MOE_OK;
+  if (q.act == MOE_F32)
+    MOE_TRY(moe::launch_gemm_f32(false, tiles, tile_count, mtl,
+                                 (const float*)h, (const float*)w2, (float*)y,
+                                 q.I, q.H, q.H, s));
+  else if (q.mx)
+    MOE_TRY(moe::launch_gemm_mx(false, mt / 16, tiles, tile_count, mtl,
+                                (const uint8_t*)h, hs, (const uint8_t*)w2, w2s,
+                                y, nullptr, q.I, q.H, q.H, s));
+  else
+    MOE_TRY(moe::launch_gemm_bf16_stream(
+        false, mt / 16, tiles, tile_count, mtl, (const uint16_t*)h,
+        (const uint16_t*)w2, (uint16_t*)y, q.I, q.H, q.H, s));
+  return MOE_OK;
+}
+
+moe_status check_weights(const Prob& q, const void* w13, const uint8_t* w13s,
+                         const void* w2, const uint8_t* w2s, bool need13,
+                         bool need2) {
+  if (q.El == 0) return MOE_OK;  // no FFN expert in range: weights unused
+  if ((need13 && !w13) || (need2 && !w2)) return MOE_ERR_INVALID_ARG;
+  if (q.mx) {
+    if ((need13 && !w13s) || (need2 && !w2s)) return MOE_ERR_INVALID_ARG;
+  } else if (w13s || w2s) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside library limits";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch failed";
+  }
+  return "unknown moe_status";
+}
+
+int32_t moe_abi_version(void) { return 100; }
+
+moe_status moe_gate_topk(const moe_problem* p, const float* logits,
+                         int32_t* topk_ids, float* topk_weight, void* stream) {
+  Prob q;
+  moe_status st = check(p, &q);
+  if (st != MOE_OK) return st;
+  if (q.T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_weight) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_gate_topk(logits, q.T, q.E, q.k, topk_ids,
+                                          topk_weight, (hipStream_t)stream));
+}
+
+moe_status moe_init_routing(const moe_problem* p, const int32_t* topk_ids,
+                            const void* x, int32_t* tokens_per_expert,
+                            int32_t* offsets, int32_t* sorted_copy,
+                            int32_t* copy_pos, void* x_perm,
+                            uint8_t* x_perm_scale, void* workspace,
+                            size_t* workspace_bytes, void* stream) {
+  Prob q;
+  moe_status st = check(p, &q);
+  if (st != MOE_OK) return st;
+  if (!workspace_bytes) return MOE_ERR_INVALID_ARG;
+  const int nch = moe::route_num_chunks((int)q.N);
+  Carve c(workspace);
+  int32_t* cc = c.take<int32_t>((size_t)nch * q.E + 1);
+  if (!workspace) { *workspace_bytes = c.off; return MOE_OK; }
+  if (*workspace_bytes < c.off) return MOE_ERR_WORKSPACE;
+  if (!tokens_per_expert || !offsets) return MOE_ERR_INVALID_ARG;
+  if (q.N > 0 && (!topk_ids || !sorted_copy || !copy_pos)) return MOE_ERR_INVALID_ARG;
+  if (q.El > 0 && q.N > 0 && (!x || !x_perm)) return MOE_ERR_INVALID_ARG;
+  if (q.mx ? (q.El > 0 && q.N > 0 && !x_perm_scale) : (x_perm_scale != nullptr))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (q.N > 0) MOE_TRY(moe::launch_route_count(topk_ids, (int)q.N, q.E, cc, s));
+  MOE_TRY(moe::launch_route_scan(cc, nch, q.E, tokens_per_expert, offsets,
+                                 q.fb, q.fe, 0, nullptr, 0, nullptr, s));
+  if (q.N > 0) {
+    MOE_TRY(moe::launch_route_scatter(topk_ids, (int)q.N, q.E, cc, offsets,
+                                      sorted_copy, copy_pos, s));
+    MOE_TRY(moe::launch_route_gather(x, q.act == MOE_F32 ? 0 : 1, q.mx ? 1 : 0,
+                                     q.H, q.k, sorted_copy, offsets, q.fb,
+                                     q.fe, (int)q.N, x_perm, x_perm_scale, s));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_ffn_up(const moe_problem* p, const int32_t* offsets,
+                      const void* x_perm, const uint8_t* x_perm_scale,
+                      const void* w13, const uint8_t* w13_scale, void* h,
+                      uint8_t* h_scale, void* workspace,
+                      size_t* workspace_bytes, void* stream) {
+  Prob q;
+  moe_status st = check(p, &q);
+  if (st != MOE_OK) return st;
+  if (!workspace_bytes) return MOE_ERR_INVALID_ARG;
+  const int mt = tile_rows(q);
+  Carve c(workspace);
+  FfnWs fw = carve_ffn_ws(c, q, mt);
+  if (!workspace) { *workspace_bytes = c.off; return MOE_OK; }
+  if (*workspace_bytes < c.off) return MOE_ERR_WORKSPACE;
+  if ((st = check_weights(q, w13, w13_scale, nullptr, nullptr, true, false)) != MOE_OK)
+    return st;
+  if (q.El == 0 || q.N == 0) return MOE_OK;
+  if (!offsets || !x_perm || !h) return MOE_ERR_INVALID_ARG;
+  if (q.mx ? (!x_perm_scale || !h_scale) : (x_perm_scale || h_scale))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  MOE_TRY(moe::launch_build_tiles(offsets, q.fb, q.fe, mt, fw.tiles,
+                                  (int)max_tiles(q, mt), fw.tile_count, s));
+  return run_up(q, mt, fw.tiles, fw.tile_count, x_perm, x_perm_scale, w13,
+                w13_scale, h, h_scale, s);
+}
+
+moe_status moe_ffn_down(const moe_problem* p, const int32_t* offsets,
+                        const void* h, const uint8_t* h_scale, const void* w2,
+                        const uint8_t* w2_scale, void* y, void* workspace,
+                        size_t* workspace_bytes, void* stream) {
+  Prob q;
+  moe_status st = check(p, &q);
+  if (st != MOE_OK) return st;
+  if (!workspace_bytes) return MOE_ERR_INVALID_ARG;
+  const int mt = tile_rows(q);
+  Carve c(workspace);
+  FfnWs fw = carve_ffn_ws(c, q, mt);
+  if (!workspace) { *workspace_bytes = c.off; return MOE_OK; }
+  if (*workspace_bytes < c.off) return MOE_ERR_WORKSPACE;
+  if ((st = check_weights(q, nullptr, nullptr, w2, w2_scale, false, true)) != MOE_OK)
+    return st;
+  if (q.El == 0 || q.N == 0) return MOE_OK;
+  if (!offsets || !h || !y) return MOE_ERR_INVALID_ARG;
+  if (q.mx ? !h_scale : (h_scale != nullptr)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  MOE_TRY(moe::launch_build_tiles(offsets, q.fb, q.fe, mt, fw.tiles,
+                                  (int)max_tiles(q, mt), fw.tile_count, s));
+  return run_down(q, mt, fw.tiles, fw.tile_count, h, h_scale, w2, w2_scale, y,
+                  s);
+}
+
+moe_status moe_grouped_ffn(const moe_problem* p, const int32_t* offsets,
+                           const void* x_perm, const uint8_t* x_perm_scale,
+                           const void* w13, const uint8_t* w13_scale,
+                           const void* w2, const uint8_t* w2_scale, void* y,
+                           void* workspace, size_t* workspace_bytes,
+                           void* stream) {
+  Prob q;
+  moe_status st = check(p, &q);
+  if (st != MOE_OK) return st;
+  if (!workspace_bytes) return MOE_ERR_INVALID_ARG;
+  const int mt = tile_rows(q);
+  Carve c(workspace);
+  FfnWs fw = carve_ffn_ws(c, q, mt);
+  void* h = c.take<char>((size_t)q.N * q.I * (q.mx ? 1 : act_bytes(q)));
+  uint8_t* hs = q.mx ? c.take<uint8_t>((size_t)q.N * (q.I / 32)) : nullptr;
+  if (!workspace) { *workspace_bytes = c.off; return MOE_OK; }
+  if (*workspace_bytes < c.off) return MOE_ERR_WORKSPACE;
+  if ((st = check_weights(q, w13, w13_scale, w2, w2_scale, true, true)) != MOE_OK)
+    return st;
+  if (q.El == 0 || q.N == 0) return MOE_OK;
+  if (!offsets || !x_perm || !y) return MOE_ERR_INVALID_ARG;
+  if (q.mx ? !x_perm_scale : (x_perm_scale != nullptr)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  MOE_TRY(moe::launch_build_tiles(offsets, q.fb, q.fe, mt, fw.tiles,
+                                  (int)max_tiles(q, mt), fw.tile_count, s));
+  st = run_up(q, mt, fw.tiles, fw.tile_count, x_perm, x_perm_scale, w13,
+              w13_scale, h, hs, s);
+  if (st != MOE_OK) return st;
+  return run_down(q, mt, fw.tiles, fw.tile_count, h, hs, w2, w2_scale, y, s);
+}
+
+moe_status moe_finalize(const moe_problem* p, const int32_t* topk_ids,
+                        const float* topk_weight, const int32_t* copy_pos,
+                        const int32_t* offsets, const void* y, const void* x,
+                        const void* residual, void* out, void* stream) {
+  Prob q;
+  moe_status st = check(p, &q);
+  if (st != MOE_OK) return st;
+  if (q.T == 0) return MOE_OK;
+  if (!topk_ids || !topk_weight || !copy_pos || !offsets || !x || !out)
+    return MOE_ERR_INVALID_ARG;
+  if (q.El > 0 && !y) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_finalize(
+      topk_ids, topk_weight, copy_pos, offsets, q.fb, q.nffn, q.lb, q.le, y, x,
+      residual, out, q.act == MOE_F32 ? 0 : 1, q.T, q.H, q.k,
+      (hipStream_t)stream));
+}
+
+moe_status moe_layer_traced(const moe_problem* p, const float* logits,
+                            const void* x, const void* residual,
+                            const void* w13, const uint8_t* w13_scale,
+                            const void* w2, const uint8_t* w2_scale, void* out,
+                            void* workspace, size_t* workspace_bytes,
+                            void* stream, void* const* stage_events,
+                            int32_t n_events) {
+  Prob q;
+  moe_status st = check(p, &q);
+  if (st != MOE_OK) return st;
+  if (!workspace_bytes || n_events < 0) return MOE_ERR_INVALID_ARG;
+  const int mt = tile_rows(q);
+  const size_t N = (size_t)q.N;
+  const int nch = moe::route_num_chunks((int)q.N);
+  Carve c(workspace);
+  int32_t* ids = c.take<int32_t>(N);
+  float* wts = c.take<float>(N);
+  int32_t* counts = c.take<int32_t>(q.E);
+  int32_t* offsets = c.take<int32_t>(q.E + 1);
+  int32_t* cc = c.take<int32_t>((size_t)nch * q.E + 1);
+  int32_t* sorted_copy = c.take<int32_t>(N);
+  int32_t* copy_pos = c.take<int32_t>(N);
+  FfnWs fw = carve_ffn_ws(c, q, mt);
+  const size_t ab = q.mx ? 1 : act_bytes(q);
+  void* xp = c.take<char>(q.El ? N * q.H * ab : 0);
+  uint8_t* xs = q.mx ? c.take<uint8_t>(q.El ? N * (q.H / 32) : 0) : nullptr;
+  void* h = c.take<char>(q.El ? N * q.I * ab : 0);
+  uint8_t* hs = q.mx ? c.take<uint8_t>(q.El ? N * (q.I / 32) : 0) : nullptr;
+  void* y = c.take<char>(q.El ? N * q.H * act_bytes(q) : 0);
+  if (!workspace) { *workspace_bytes = c.off; return MOE_OK; }
+  if (*workspace_bytes < c.off) return MOE_ERR_WORKSPACE;
+  if ((st = check_weights(q, w13, w13_scale, w2, w2_scale, true, true)) != MOE_OK)
+    return st;
+  if (q.T == 0) return MOE_OK;
+  if (!logits || !x || !out) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  auto mark = [&](int i) -> hipError_t {
+    if (stage_events && i < n_events && stage_events[i])
+      return hipEventRecord((hipEvent_t)stage_events[i], s);
+    return hipSuccess;
+  };
+  MOE_TRY(mark(0));
+  MOE_TRY(moe::launch_gate_topk(logits, q.T, q.E, q.k, ids, wts, s));
+  MOE_TRY(mark(1));
+  MOE_TRY(moe::launch_route_count(ids, (int)q.N, q.E, cc, s));
+  const int mtl = (int)max_tiles(q, mt);
+  MOE_TRY(mark(2));
+  MOE_TRY(moe::launch_route_scan(cc, nch, q.E, counts, offsets, q.fb, q.fe, mt,
+                                 mtl ? fw.tiles : nullptr, mtl, fw.tile_count,
+                                 s));
+  MOE_TRY(mark(3));
+  MOE_TRY(moe::launch_route_scatter(ids, (int)q.N, q.E, cc, offsets,
+                                    sorted_copy, copy_pos, s));
+  MOE_TRY(mark(4));
+  if (q.El > 0)
+    MOE_TRY(moe::launch_route_gather(x, q.act == MOE_F32 ? 0 : 1, q.mx ? 1 : 0,
+                                     q.H, q.k, sorted_copy, offsets, q.fb,
+                                     q.fe, (int)q.N, xp, xs, s));
+  MOE_TRY(mark(5));
+  if (q.El > 0) {
+    st = run_up(q, mt, fw.tiles, fw.tile_count, xp, xs, w13, w13_scale, h, hs,
+                s);
+    if (st != MOE_OK) return st;
+  }
+  MOE_TRY(mark(6));
+  if (q.El > 0) {
+    st = run_down(q, mt, fw.tiles, fw.tile_count, h, hs, w2, w2_scale, y, s);
+    if (st != MOE_OK) return st;
+  }
+  MOE_TRY(mark(7));
+  MOE_TRY(moe::launch_finalize(ids, wts, copy_pos, offsets, q.fb, q.nffn, q.lb,
+                               q.le, y, x, residual, out,
+                               q.act == MOE_F32 ? 0 : 1, q.T, q.H, q.k, s));
+  MOE_TRY(mark(8));
+  return MOE_OK;
+}
+
+moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
+                     const void* residual, const void* w13,
+                     const uint8_t* w13_scale, const void* w2,
+                     const uint8_t* w2_scale, void* out, void* workspace,
+                     size_t* workspace_bytes, void* stream) {
+  return moe_layer_traced(p, logits, x, residual, w13, w13_scale, w2, w2_scale,
+                          out, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+}  // extern "C"

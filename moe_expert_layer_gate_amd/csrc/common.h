@@ -1,0 +1,102 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_DEV __device__ __forceinline__
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 bits
+
+MOE_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+MOE_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
+MOE_DEV uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- wave ops
+
+MOE_DEV int lane_id() { return __lane_id(); }
+
+MOE_DEV uint64_t ballot(bool p) { return __ballot(p); }
+
+MOE_DEV int popc64(uint64_t m) { return __popcll(m); }
+
+MOE_DEV uint64_t lanemask_lt() {
+  int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// ---------------------------------------------------------------- MX encode
+//
+// e8m0 shared exponent of an MX block (OCP MX v1.0): floor(log2(amax)) minus
+// the element format's emax (8 for e4m3), clamped to [-127, 127], stored with
+// bias 127. An all-zero block gets code 0. Computed from the fp32 bits.
+MOE_DEV int floor_log2_f32(float a) {  // a > 0, finite
+  uint32_t u = __float_as_uint(a);
+  int ex = (int)((u >> 23) & 0xFF);
+  if (ex) return ex - 127;
+  uint32_t m = u & 0x7FFFFFu;  // subnormal: m * 2^-149
+  return (31 - __clz((int)m)) - 149;
+}
+
+MOE_DEV int mx_e4m3_scale_exp(float amax) {
+  if (!(amax > 0.f)) return -127;
+  int s = floor_log2_f32(amax) - 8;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// Round-to-nearest-even right shift of a non-negative integer.
+MOE_DEV uint32_t rne_shift(uint32_t m, int sh) {
+  if (sh <= 0) return m << (-sh);
+  if (sh >= 32) return 0;
+  uint32_t q = m >> sh;
+  uint32_t rem = m & ((1u << sh) - 1u);
+  uint32_t half = 1u << (sh - 1);
+  if (rem > half || (rem == half && (q & 1u))) ++q;
+  return q;
+}
+
+// e4m3fn code of v * 2^-s, rounded to nearest (ties to even), saturating at
+// 448, sign kept. Exact integer arithmetic on the fp32 bits of v.
+MOE_DEV uint32_t e4m3_encode_scaled(float v, int s) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  int ex = (int)((u >> 23) & 0xFF);
+  uint32_t M = u & 0x7FFFFFu;
+  if (ex) M |= 0x800000u; else ex = 1;
+  if (M == 0) return sign;
+  int p = ex - 150 - s;                      // |v| * 2^-s = M * 2^p
+  int nb = 32 - __clz((int)M);               // bit length of M
+  int e = nb - 1 + p;                        // floor(log2(|v| 2^-s))
+  if (e >= -6) {                             // e4m3 normal range
+    uint32_t r = rne_shift(M, nb - 4);       // 4 significant bits, in [8,16]
+    if (r == 16) { r = 8; ++e; }
+    if (e > 8 || (e == 8 && r > 14)) return sign | 0x7Eu;   // saturate 448
+    return sign | ((uint32_t)(e + 7) << 3) | (r - 8);
+  }
+  // subnormal: multiples of 2^-9; rounding up to 8 lands on the min normal
+  uint32_t n = rne_shift(M, -(p + 9));
+  return sign | n;
+}
+
+// ---------------------------------------------------------------- misc
+
+MOE_DEV float silu(float z) { return z / (1.0f + expf(-z)); }
+
+}  // namespace moe

@@ -1,0 +1,242 @@
+// Grouped GEMM, bf16 x bf16 -> fp32 on MFMA, weight-streaming schedule.
+//
+// [P1] "Qwen3-MoE low-latency inference on Atlas A3 / 950 clusters", section
+// MoE TP优化 / 计算分解 (expert = down(SiLU(gate(x)) * up(x)); merged gate/up
+// matrix; npu_swiglu = SiLU(first half) * second half) and section
+// 高性能专家计算 (one grouped operator for all experts). [P2] "LongCat-Flash
+// inference on Atlas A3 clusters" notes that on the FFN side the grouped
+// matmuls of decode are memory-bound.
+//
+// Decode-size batches give each expert a handful of rows, so every weight byte
+// is used by at most 16*RG rows and the kernel is bound by streaming weights
+// from HBM. The schedule keeps weights out of LDS entirely:
+//   * weights are [K, N] with N contiguous. Lane l of a wave loads an 8x8
+//     block -- rows k0 + 8*(l/16) + 0..7, columns col + 8*(l%16) + 0..7 -- as
+//     eight 16-byte loads (16 lanes cover 256 contiguous bytes of a row), and
+//     transposes it in registers (v_perm) into eight K-packed fragments, one
+//     per column offset i. Fragment i is the B operand of a
+//     v_mfma_f32_16x16x32_bf16 whose 16 "columns" are {col + 8g + i}, g=0..15.
+//   * each lane carries two such column groups: for GEMM1 the gate columns
+//     and the matching up columns (so SwiGLU is lane-local in the epilogue),
+//     for GEMM2 two halves of a 256-column slab.
+//   * A rows (activations, K contiguous) are loaded straight into the
+//     fragment layout: row 16*rg + l%16, k0 + 8*(l/16) + 0..7.
+//   * KSPLIT waves of a block split K; partial sums meet in LDS 16 registers
+//     at a time; wave 0 applies SwiGLU / converts and stores 16 bytes per
+//     row and lane.
+// Output D of each MFMA: lane l holds rows 4*(l/16) + 0..3 at column
+// col + 8*(l%16) + i, so a lane owns 8 consecutive columns of 4 rows.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+MOE_DEV f32x4 mfma_bf16_16x16x32(u32x4_t a, u32x4_t b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c, 0,
+      0, 0);
+}
+
+// Column i (0..7) of an 8x8 bf16 block held as 8 rows of uint4: K-packed.
+MOE_DEV u32x4_t column_frag(const uint4 (&r)[8], int i) {
+  const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+  auto dw = [&](int row) -> uint32_t {
+    const uint4 v = r[row];
+    const int d = i >> 1;
+    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+  };
+  u32x4_t f;
+  f.x = __builtin_amdgcn_perm(dw(1), dw(0), sel);
+  f.y = __builtin_amdgcn_perm(dw(3), dw(2), sel);
+  f.z = __builtin_amdgcn_perm(dw(5), dw(4), sel);
+  f.w = __builtin_amdgcn_perm(dw(7), dw(6), sel);
+  return f;
+}
+
+template <bool GLU, int RG, int KSPLIT>
+__global__ __launch_bounds__(64 * KSPLIT) void gemm_bf16_stream_kernel(
+    const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ w,
+    uint16_t* __restrict__ out, int K, int Nw, int Nout) {
+  if ((int)blockIdx.x >= tile_count[0]) return;
+  const Tile tl = tiles[blockIdx.x];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane & 15, kq = lane >> 4;
+  // two column groups per lane
+  constexpr int SLAB = GLU ? 128 : 256;
+  const int c0 = blockIdx.y * SLAB;
+  const int colA = c0 + 8 * g;
+  const int colB = GLU ? Nout + colA : colA + 128;
+  const bool okA = colA < Nout;
+  const bool okB = GLU ? okA : (colA + 128 < Nout);
+  const uint16_t* we = w + (size_t)tl.expert * K * Nw;
+  const int nsteps = K / 32;
+  const int s_begin = wave * nsteps / KSPLIT;
+  const int s_end = (wave + 1) * nsteps / KSPLIT;
+
+  const uint16_t* arow[RG];
+  bool aok[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    int r = 16 * rg + g;
+    aok[rg] = r < tl.rows;
+    arow[rg] = a + (size_t)(tl.row0 + (aok[rg] ? r : 0)) * K + 8 * kq;
+  }
+
+  f32x4 acc[2][RG][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][rg][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
+  for (int s = s_begin; s < s_end; ++s) {
+    const int k0 = s * 32;
+    uint4 bA[8], bB[8];
+    const uint16_t* pA = we + (size_t)(k0 + 8 * kq) * Nw + colA;
+    const uint16_t* pB = we + (size_t)(k0 + 8 * kq) * Nw + colB;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      bA[r] = okA ? *(const uint4*)(pA + (size_t)r * Nw) : z4;
+      bB[r] = okB ? *(const uint4*)(pB + (size_t)r * Nw) : z4;
+    }
+    u32x4_t af[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      uint4 v = aok[rg] ? *(const uint4*)(arow[rg] + k0) : z4;
+      af[rg] = u32x4_t{v.x, v.y, v.z, v.w};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u32x4_t fA = column_frag(bA, i);
+      u32x4_t fB = column_frag(bB, i);
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        acc[0][rg][i] = mfma_bf16_16x16x32(af[rg], fA, acc[0][rg][i]);
+        acc[1][rg][i] = mfma_bf16_16x16x32(af[rg], fB, acc[1][rg][i]);
+      }
+    }
+  }
+
+  // cross-wave reduction of the split-K partial sums, 16 registers a round
+  if (KSPLIT > 1) {
+    __shared__ float red[(KSPLIT > 1 ? KSPLIT - 1 : 1) * 16 * 64];
+    constexpr int NREG = 2 * RG * 8 * 4;
+#pragma unroll
+    for (int q = 0; q < NREG / 16; ++q) {
+      if (wave > 0) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int rgi = q * 16 + j;
+          const int h = rgi / (RG * 32), rg = (rgi / 32) % RG;
+          const int i = (rgi / 4) % 8, e = rgi % 4;
+          red[((wave - 1) * 16 + j) * 64 + lane] = acc[h][rg][i][e];
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int rgi = q * 16 + j;
+          const int h = rgi / (RG * 32), rg = (rgi / 32) % RG;
+          const int i = (rgi / 4) % 8, e = rgi % 4;
+          float sum = acc[h][rg][i][e];
+#pragma unroll
+          for (int ww = 0; ww < KSPLIT - 1; ++ww)
+            sum += red[(ww * 16 + j) * 64 + lane];
+          acc[h][rg][i][e] = sum;
+        }
+      }
+      __syncthreads();
+    }
+    if (wave > 0) return;
+  }
+
+  // epilogue: lane owns rows 16*rg + 4*kq + e, columns colA + 0..7 (+ colB)
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rg + 4 * kq + e;
+      if (r >= tl.rows) continue;
+      uint16_t* orow = out + (size_t)(tl.row0 + r) * Nout;
+      if (GLU) {
+        if (okA) {
+          float hv[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            hv[i] = silu(acc[0][rg][i][e]) * acc[1][rg][i][e];
+          uint4 o;
+          o.x = pack_bf16x2(hv[0], hv[1]);
+          o.y = pack_bf16x2(hv[2], hv[3]);
+          o.z = pack_bf16x2(hv[4], hv[5]);
+          o.w = pack_bf16x2(hv[6], hv[7]);
+          *(uint4*)(orow + colA) = o;
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (h == 0 ? !okA : !okB) continue;
+          uint4 o;
+          o.x = pack_bf16x2(acc[h][rg][0][e], acc[h][rg][1][e]);
+          o.y = pack_bf16x2(acc[h][rg][2][e], acc[h][rg][3][e]);
+          o.z = pack_bf16x2(acc[h][rg][4][e], acc[h][rg][5][e]);
+          o.w = pack_bf16x2(acc[h][rg][6][e], acc[h][rg][7][e]);
+          *(uint4*)(orow + (h == 0 ? colA : colB)) = o;
+        }
+      }
+    }
+  }
+}
+
+template <bool GLU, int RG>
+static hipError_t launch_stream(int ksplit, dim3 grid, const Tile* tiles,
+                                const int32_t* tile_count, const uint16_t* a,
+                                const uint16_t* w, uint16_t* out, int K, int Nw,
+                                int Nout, hipStream_t s) {
+  switch (ksplit) {
+    case 1:
+      hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 1>), grid, dim3(64),
+                         0, s, tiles, tile_count, a, w, out, K, Nw, Nout);
+      break;
+    case 2:
+      hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 2>), grid,
+                         dim3(128), 0, s, tiles, tile_count, a, w, out, K, Nw,
+                         Nout);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 4>), grid,
+                         dim3(256), 0, s, tiles, tile_count, a, w, out, K, Nw,
+                         Nout);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
+                                   const int32_t* tile_count, int max_tiles,
+                                   const uint16_t* a, const uint16_t* w,
+                                   uint16_t* out, int K, int Nw, int Nout,
+                                   hipStream_t s) {
+  if (max_tiles == 0) return hipSuccess;
+  const int slab = glu ? 128 : 256;
+  dim3 grid(max_tiles, (Nout + slab - 1) / slab);
+  // split K so each wave streams at least ~16 steps of 32
+  int steps = K / 32;
+  int ksplit = steps >= 64 ? 4 : steps >= 32 ? 2 : 1;
+  if (glu)
+    return rg == 1 ? launch_stream<true, 1>(ksplit, grid, tiles, tile_count, a,
+                                            w, out, K, Nw, Nout, s)
+                   : launch_stream<true, 2>(ksplit, grid, tiles, tile_count, a,
+                                            w, out, K, Nw, Nout, s);
+  return rg == 1 ? launch_stream<false, 1>(ksplit, grid, tiles, tile_count, a,
+                                           w, out, K, Nw, Nout, s)
+                 : launch_stream<false, 2>(ksplit, grid, tiles, tile_count, a,
+                                           w, out, K, Nw, Nout, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,75 @@
+// Host-side launchers of the kernels (one per .hip file), used by api.cpp.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tile of a grouped GEMM: local expert index and first row (relative to the
+// expert's first row). Built on the device from the routing offsets.
+struct Tile {
+  int32_t expert;  // e - fb
+  int32_t row0;    // row of x_perm where the tile starts (absolute)
+  int32_t rows;    // rows in the tile (<= tile height)
+  int32_t pad;
+};
+
+hipError_t launch_gate_topk(const float* logits, int T, int E, int k,
+                            int32_t* ids, float* w, hipStream_t s);
+
+// Routing. chunk_counts has route_num_chunks(N) * E ints.
+int route_num_chunks(int N);
+hipError_t launch_route_count(const int32_t* ids, int N, int E,
+                              int32_t* chunk_counts, hipStream_t s);
+// Scans chunk counts (in place, to per-chunk bases), writes counts and
+// offsets. When tiles != NULL also builds the GEMM tile list for the FFN
+// experts [fb, fe) with tile height mt (tile_count[0] = number of tiles).
+hipError_t launch_route_scan(int32_t* chunk_counts, int nchunks, int E,
+                             int32_t* counts, int32_t* offsets, int fb, int fe,
+                             int mt, Tile* tiles, int max_tiles,
+                             int32_t* tile_count, hipStream_t s);
+hipError_t launch_build_tiles(const int32_t* offsets, int fb, int fe, int mt,
+                              Tile* tiles, int max_tiles, int32_t* tile_count,
+                              hipStream_t s);
+hipError_t launch_route_scatter(const int32_t* ids, int N, int E,
+                                const int32_t* chunk_base,
+                                const int32_t* offsets, int32_t* sorted_copy,
+                                int32_t* copy_pos, hipStream_t s);
+// act: 0 f32, 1 bf16. mx: quantise rows to MXFP8 (bf16 input only).
+hipError_t launch_route_gather(const void* x, int act, int mx, int H, int k,
+                               const int32_t* sorted_copy,
+                               const int32_t* offsets, int fb, int fe,
+                               int max_rows, void* x_perm, uint8_t* x_scale,
+                               hipStream_t s);
+
+// Grouped GEMMs. glu: GEMM1 with SwiGLU epilogue (N = 2*I weight columns,
+// I outputs), else GEMM2 (N outputs). Tiles come from the tile list.
+// bf16 activations / bf16 weights [E_loc, K, N].
+hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
+                                   const int32_t* tile_count, int max_tiles,
+                                   const uint16_t* a, const uint16_t* w,
+                                   uint16_t* out, int K, int Nw, int Nout,
+                                   hipStream_t s);
+// fp32 activations / fp32 weights [E_loc, K, N], VALU.
+hipError_t launch_gemm_f32(bool glu, const Tile* tiles,
+                           const int32_t* tile_count, int max_tiles,
+                           const float* a, const float* w, float* out, int K,
+                           int Nw, int Nout, hipStream_t s);
+// MXFP8 activations [rows, K] + e8m0 [rows, K/32]; MXFP4 weights
+// [E_loc, N, K/2] + e8m0 [E_loc, N, K/32]. glu: output MXFP8 h (+ scales);
+// else bf16 y.
+hipError_t launch_gemm_mx(bool glu, int rg, const Tile* tiles,
+                          const int32_t* tile_count, int max_tiles,
+                          const uint8_t* a, const uint8_t* a_scale,
+                          const uint8_t* w, const uint8_t* w_scale, void* out,
+                          uint8_t* out_scale, int K, int Nw, int Nout,
+                          hipStream_t s);
+
+hipError_t launch_finalize(const int32_t* ids, const float* w,
+                           const int32_t* copy_pos, const int32_t* offsets,
+                           int fb, int n_ffn, int lb, int le, const void* y,
+                           const void* x, const void* residual, void* out,
+                           int act, int T, int H, int k, hipStream_t s);
+
+}  // namespace moe

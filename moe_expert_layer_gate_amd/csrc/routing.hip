@@ -1,0 +1,302 @@
+// Routing: expert histogram, offsets, stable permutation, gather (+ MXFP8).
+//
+// [P1] "Qwen3-MoE low-latency inference on Atlas A3 / 950 clusters",
+// section 高效排序和token路由: sort the token copies by expert (init_routing)
+// and count the tokens of each expert (compute_expert_tokens); section MoE
+// EP优化 / AllGather方案(W4A8量化): quantise hidden states to MXFP8 and keep
+// only the copies of the local expert range.
+//
+// Copies c = t * k + j are cut into chunks of 256 (one wavefront each).
+//   count   : per-chunk LDS histogram -> chunk_counts[chunk][E]
+//   scan    : one block; per expert an exclusive scan over chunks (in place,
+//             giving each chunk its first slot inside the expert), the
+//             expert totals, their exclusive scan (offsets) and, optionally,
+//             the GEMM tile list of the local FFN experts
+//   scatter : each wave re-reads its chunk 64 copies at a time in order and
+//             ranks equal ids with ballot + popcount (one pass per distinct
+//             id in the 64), so copies of one expert keep ascending c: the
+//             sort key is (expert, c) and the result is deterministic
+//   gather  : one wave per routed row copies (or MXFP8-quantises) x[t]
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int kChunk = 256;
+constexpr int kMaxE = 2048;
+
+int route_num_chunks(int N) { return (N + kChunk - 1) / kChunk; }
+
+__global__ __launch_bounds__(256) void route_count_kernel(
+    const int32_t* __restrict__ ids, int N, int E, int nchunks,
+    int32_t* __restrict__ cc) {
+  extern __shared__ int32_t sh[];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + w;
+  int32_t* h = sh + w * E;
+  for (int e = lane; e < E; e += 64) h[e] = 0;
+  __syncthreads();
+  if (c < nchunks) {
+#pragma unroll
+    for (int it = 0; it < kChunk / 64; ++it) {
+      int i = c * kChunk + it * 64 + lane;
+      if (i < N) {
+        int e = ids[i];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+      }
+    }
+  }
+  __syncthreads();
+  if (c < nchunks)
+    for (int e = lane; e < E; e += 64) cc[(size_t)c * E + e] = h[e];
+}
+
+// Exclusive scan of a[0..n) in LDS by a block of 1024 threads, n <= 2048.
+// Returns the total to every thread.
+__device__ int block_exclusive_scan(int32_t* a, int n, int32_t* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i0 = 2 * tid, i1 = i0 + 1;
+  int v0 = i0 < n ? a[i0] : 0;
+  int v1 = i1 < n ? a[i1] : 0;
+  int s = v0 + v1, x = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int z = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      int y = __shfl_up(z, off);
+      if (lane >= off) z += y;
+    }
+    if (lane < 16) wsum[lane] = z;
+  }
+  __syncthreads();
+  int base = (w ? wsum[w - 1] : 0) + x - s;
+  int total = wsum[15];
+  if (i0 < n) a[i0] = base;
+  if (i1 < n) a[i1] = base + v0;
+  __syncthreads();
+  return total;
+}
+
+// Tile list of the FFN experts [fb, fe): expert e gets ceil(count/mt) tiles.
+__device__ void build_tiles_block(const int32_t* cnt_lds, const int32_t* off_lds,
+                                  int fb, int fe, int mt, Tile* tiles,
+                                  int max_tiles, int32_t* tile_count,
+                                  int32_t* tmp, int32_t* wsum) {
+  const int El = fe - fb;
+  for (int i = threadIdx.x; i < El; i += blockDim.x)
+    tmp[i] = (cnt_lds[fb + i] + mt - 1) / mt;
+  __syncthreads();
+  int total = block_exclusive_scan(tmp, El, wsum);
+  const int r0 = off_lds[fb];
+  for (int i = threadIdx.x; i < El; i += blockDim.x) {
+    int n = cnt_lds[fb + i];
+    int start = tmp[i];
+    for (int m = 0; m * mt < n; ++m) {
+      int ti = start + m;
+      if (ti >= max_tiles) break;
+      Tile tl;
+      tl.expert = i;
+      tl.row0 = off_lds[fb + i] - r0 + m * mt;
+      tl.rows = min(mt, n - m * mt);
+      tl.pad = 0;
+      tiles[ti] = tl;
+    }
+  }
+  if (threadIdx.x == 0) tile_count[0] = min(total, max_tiles);
+}
+
+__global__ __launch_bounds__(1024) void route_scan_kernel(
+    int32_t* __restrict__ cc, int nchunks, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int fb, int fe, int mt, Tile* tiles,
+    int max_tiles, int32_t* tile_count) {
+  __shared__ int32_t cnt[kMaxE];
+  __shared__ int32_t off[kMaxE + 1];
+  __shared__ int32_t tmp[kMaxE];
+  __shared__ int32_t wsum[16];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      size_t idx = (size_t)c * E + e;
+      int v = cc[idx];
+      cc[idx] = run;
+      run += v;
+    }
+    cnt[e] = run;
+    off[e] = run;
+    counts[e] = run;
+  }
+  __syncthreads();
+  int total = block_exclusive_scan(off, E, wsum);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) offsets[e] = off[e];
+  if (threadIdx.x == 0) { offsets[E] = total; off[E] = total; }
+  __syncthreads();
+  if (tiles) build_tiles_block(cnt, off, fb, fe, mt, tiles, max_tiles,
+                               tile_count, tmp, wsum);
+}
+
+__global__ __launch_bounds__(1024) void build_tiles_kernel(
+    const int32_t* __restrict__ offsets, int fb, int fe, int mt, Tile* tiles,
+    int max_tiles, int32_t* tile_count) {
+  __shared__ int32_t cnt[kMaxE];
+  __shared__ int32_t off[kMaxE + 1];
+  __shared__ int32_t tmp[kMaxE];
+  __shared__ int32_t wsum[16];
+  for (int e = fb + threadIdx.x; e <= fe; e += blockDim.x) {
+    off[e] = offsets[e];
+    if (e < fe) cnt[e] = offsets[e + 1] - offsets[e];
+  }
+  __syncthreads();
+  build_tiles_block(cnt, off, fb, fe, mt, tiles, max_tiles, tile_count, tmp,
+                    wsum);
+}
+
+__global__ __launch_bounds__(256) void route_scatter_kernel(
+    const int32_t* __restrict__ ids, int N, int E, int nchunks,
+    const int32_t* __restrict__ cc, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_copy, int32_t* __restrict__ copy_pos) {
+  extern __shared__ int32_t sh[];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + w;
+  volatile int32_t* base = sh + w * E;
+  if (c < nchunks)
+    for (int e = lane; e < E; e += 64)
+      base[e] = offsets[e] + cc[(size_t)c * E + e];
+  __syncthreads();
+  if (c >= nchunks) return;
+  const uint64_t lt = lanemask_lt();
+  for (int it = 0; it < kChunk / 64; ++it) {
+    const int i = c * kChunk + it * 64 + lane;
+    const int e = i < N ? ids[i] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    if (i < N && !valid) copy_pos[i] = -1;
+    uint64_t rem = ballot(valid);
+    while (rem) {
+      const int leader = __ffsll((long long)rem) - 1;
+      const int ek = __shfl(e, leader);
+      const bool mine = valid && e == ek;
+      const uint64_t m = ballot(mine);
+      const int b = base[ek];
+      if (mine) {
+        int pos = b + popc64(m & lt);
+        sorted_copy[pos] = i;
+        copy_pos[i] = pos;
+      }
+      if (lane == leader) base[ek] = b + popc64(m);
+      rem &= ~m;
+    }
+  }
+}
+
+// One wave per routed row. bf16 rows move as 16-byte chunks of 8 values.
+template <int ACT, bool MX>
+__global__ __launch_bounds__(256) void route_gather_kernel(
+    const void* __restrict__ x, int H, int k,
+    const int32_t* __restrict__ sorted_copy,
+    const int32_t* __restrict__ offsets, int fb, int fe,
+    void* __restrict__ xp, uint8_t* __restrict__ xs) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int r0 = offsets[fb];
+  const int R = offsets[fe] - r0;
+  if (r >= R) return;
+  const int t = sorted_copy[r0 + r] / k;
+  if (ACT == 0) {  // fp32: 8 floats = two 16-byte chunks per step
+    const uint4* src = (const uint4*)((const float*)x + (size_t)t * H);
+    uint4* dst = (uint4*)((float*)xp + (size_t)r * H);
+    for (int c = lane; c < H / 4; c += 64) dst[c] = src[c];
+    return;
+  }
+  const uint4* src = (const uint4*)((const uint16_t*)x + (size_t)t * H);
+  if (!MX) {
+    uint4* dst = (uint4*)((uint16_t*)xp + (size_t)r * H);
+    for (int c = lane; c < H / 8; c += 64) dst[c] = src[c];
+    return;
+  }
+  uint8_t* dst = (uint8_t*)xp + (size_t)r * H;
+  uint8_t* dsc = xs + (size_t)r * (H / 32);
+  for (int c = lane; c < H / 8; c += 64) {  // H % 32 == 0: 4-lane groups whole
+    uint4 v = src[c];
+    float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const int s = mx_e4m3_scale_exp(amax);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= e4m3_encode_scaled(f[i], s) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= e4m3_encode_scaled(f[4 + i], s) << (8 * i);
+    *(uint2*)(dst + (size_t)c * 8) = make_uint2(lo, hi);
+    if ((c & 3) == 0) dsc[c >> 2] = (uint8_t)(s + 127);
+  }
+}
+
+hipError_t launch_route_count(const int32_t* ids, int N, int E,
+                              int32_t* chunk_counts, hipStream_t s) {
+  int nch = route_num_chunks(N);
+  if (nch == 0) return hipSuccess;
+  hipLaunchKernelGGL(route_count_kernel, dim3((nch + 3) / 4), dim3(256),
+                     4 * E * sizeof(int32_t), s, ids, N, E, nch, chunk_counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_scan(int32_t* chunk_counts, int nchunks, int E,
+                             int32_t* counts, int32_t* offsets, int fb, int fe,
+                             int mt, Tile* tiles, int max_tiles,
+                             int32_t* tile_count, hipStream_t s) {
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s,
+                     chunk_counts, nchunks, E, counts, offsets, fb, fe, mt,
+                     tiles, max_tiles, tile_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, int fb, int fe, int mt,
+                              Tile* tiles, int max_tiles, int32_t* tile_count,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets,
+                     fb, fe, mt, tiles, max_tiles, tile_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_scatter(const int32_t* ids, int N, int E,
+                                const int32_t* chunk_base,
+                                const int32_t* offsets, int32_t* sorted_copy,
+                                int32_t* copy_pos, hipStream_t s) {
+  int nch = route_num_chunks(N);
+  if (nch == 0) return hipSuccess;
+  hipLaunchKernelGGL(route_scatter_kernel, dim3((nch + 3) / 4), dim3(256),
+                     4 * E * sizeof(int32_t), s, ids, N, E, nch, chunk_base,
+                     offsets, sorted_copy, copy_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_gather(const void* x, int act, int mx, int H, int k,
+                               const int32_t* sorted_copy,
+                               const int32_t* offsets, int fb, int fe,
+                               int max_rows, void* x_perm, uint8_t* x_scale,
+                               hipStream_t s) {
+  if (max_rows == 0 || fe <= fb) return hipSuccess;
+  dim3 grid((max_rows + 3) / 4), block(256);
+  if (act == 0)
+    hipLaunchKernelGGL((route_gather_kernel<0, false>), grid, block, 0, s, x,
+                       H, k, sorted_copy, offsets, fb, fe, x_perm, x_scale);
+  else if (!mx)
+    hipLaunchKernelGGL((route_gather_kernel<1, false>), grid, block, 0, s, x,
+                       H, k, sorted_copy, offsets, fb, fe, x_perm, x_scale);
+  else
+    hipLaunchKernelGGL((route_gather_kernel<1, true>), grid, block, 0, s, x,
+                       H, k, sorted_copy, offsets, fb, fe, x_perm, x_scale);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -415,11 +415,14 @@ def finalize(*, ids, w, copy_pos, row0, y, x, n_ffn, local_begin, local_end,
 
 def moe_tokens(tokens: Sequence[int], *, logits, x, get_weights: WeightFn, T, H,
                I, n_ffn, n_zero, top_k, local_begin, local_end, act,
-               act_q="none", residual=None, exact=False) -> np.ndarray:
+               act_q="none", residual=None, exact=False,
+               cache_weights=True) -> np.ndarray:
     """Brute-force per-token evaluation (no routing structures): for each token
     t in `tokens`, out[t] = residual[t] + sum_j w_j * FFN_{e_j}(x[t]) with the
     same storage roundings as moe_layer. Every step of the layer is row-local,
-    so this equals the routed result row by row. Returns [len(tokens), H]."""
+    so this equals the routed result row by row. Returns [len(tokens), H].
+    cache_weights=False fetches an expert's weights anew for every use (for
+    workloads whose fp64 weights do not fit in host memory)."""
     _check_problem(T, H, I, n_ffn, n_zero, top_k, local_begin, local_end)
     x = np.asarray(x, dtype=np.float64)
     L = np.asarray(logits)
@@ -436,10 +439,14 @@ def moe_tokens(tokens: Sequence[int], *, logits, x, get_weights: WeightFn, T, H,
             if e >= n_ffn:
                 acc = acc + w[0, j] * x[t]
                 continue
-            if e not in cache:
-                cache[e] = get_weights(e)
+            if e in cache:
+                we = cache[e]
+            else:
+                we = get_weights(e)
+                if cache_weights:
+                    cache[e] = we
             a, _ = _act_rows(x[t:t + 1], act_q)
-            _, _, ye = expert_ffn(a, *cache[e], act=act, act_q=act_q, exact=exact)
+            _, _, ye = expert_ffn(a, *we, act=act, act_q=act_q, exact=exact)
             acc = acc + w[0, j] * ye[0]
         outs.append(acc if exact else round_to(acc, act))
     return np.stack(outs) if outs else np.zeros((0, H))

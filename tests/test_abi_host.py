@@ -1,0 +1,113 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports
+every symbol the header declares, and rejects bad arguments on the host
+before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_expert_layer_gate_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(m.LIB_PATH):
+        from moe_expert_layer_gate_amd import build
+        build.build(verbose=False)
+    return m.lib()
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*MOE_API\s+(?:moe_status|const char\*|int32_t)\s+(moe_\w+)\s*\(",
+                                 txt, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("moe_gate_topk", "moe_init_routing", "moe_grouped_ffn",
+              "moe_finalize", "moe_layer"):
+        assert n in names
+    assert set(names) == set(m.SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    for s in range(5):
+        assert L.moe_status_string(s)
+    assert L.moe_status_string(99) == b"unknown moe_status"
+    assert L.moe_abi_version() >= 100
+
+
+def _p(**kw):
+    base = dict(T=32, H=2048, I=768, n_ffn=128, n_zero=0, top_k=8,
+                local_begin=0, local_end=128, act="bf16", wt="bf16", act_q="none")
+    base.update(kw)
+    return m.problem(**base)
+
+
+def _query(L, p):
+    n = ctypes.c_size_t(0)
+    st = L.moe_layer(ctypes.byref(p), None, None, None, None, None, None, None,
+                     None, None, ctypes.byref(n), None)
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=0), 1), (dict(top_k=129), 1), (dict(T=-1), 1), (dict(H=0), 1),
+    (dict(local_begin=5, local_end=5), 1), (dict(local_end=129), 1),
+    (dict(n_ffn=0, n_zero=0), 1), (dict(H=2000), 2), (dict(I=100), 2),
+    (dict(n_ffn=4096, local_end=4096), 2), (dict(top_k=65, n_ffn=128), 2),
+    (dict(act="f32"), 2), (dict(wt="mxfp4"), 2),
+    (dict(wt="mxfp4", act_q="mxfp8", H=2048 + 32), 2),
+])
+def test_invalid_problems_rejected_on_host(L, kw, status):
+    st, _ = _query(L, _p(**kw))
+    assert st == status
+
+
+def test_workspace_query_and_too_small(L):
+    p = _p()
+    st, need = _query(L, p)
+    assert st == 0 and need > 0
+    # grows with T; W4A8 needs its MX buffers
+    _, need2 = _query(L, _p(T=64))
+    assert need2 > need
+    st, _ = _query(L, _p(wt="mxfp4", act_q="mxfp8", H=4096, I=1536,
+                         local_begin=32, local_end=64))
+    assert st == 0
+    # a buffer smaller than required is refused before any launch
+    n = ctypes.c_size_t(need - 1)
+    st = L.moe_layer(ctypes.byref(p), None, None, None, None, None, None, None,
+                     None, ctypes.c_void_p(1 << 20), ctypes.byref(n), None)
+    assert st == 3
+
+
+def test_missing_pointers_rejected(L):
+    p = _p()
+    _, need = _query(L, p)
+    n = ctypes.c_size_t(need)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: checks come first
+    st = L.moe_layer(ctypes.byref(p), None, fake, None, fake, None, fake, None,
+                     fake, fake, ctypes.byref(n), None)
+    assert st == 1  # logits missing
+    st = L.moe_layer(ctypes.byref(p), fake, fake, None, fake, fake, fake, None,
+                     fake, fake, ctypes.byref(n), None)
+    assert st == 1  # scale given for bf16 weights
+    st = L.moe_gate_topk(ctypes.byref(p), None, fake, fake, None)
+    assert st == 1
+    st = L.moe_finalize(ctypes.byref(p), fake, fake, None, fake, fake, fake,
+                        None, fake, None)
+    assert st == 1
+
+
+def test_null_problem(L):
+    assert L.moe_gate_topk(None, None, None, None, None) == 1

@@ -1,0 +1,363 @@
+"""GPU parity of the HIP library against the CPU oracle, through the C ABI.
+
+Integer outputs (ids, counts, offsets, permutation, gathered rows and MX codes)
+must be bit-exact; floating outputs meet the layer tolerances (fp32 rel-L2
+<= 1e-5; bf16 / W4A8 rel-L2 <= 1e-2 and max-abs <= 5e-2 * RMS(ref)); router
+weights within 1e-6."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from moe_inputs import WORKLOADS, generate, get_workload, scaled
+from _moe_util import (assert_close, bits, np_to_act_bits, oracle_kwargs, to64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _m():
+    import moe_expert_layer_gate_amd as m
+    m.lib()  # raises if the HIP library is missing: no fallback
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# Small shapes of each workload: several tiles and ragged tails, fast oracle.
+SMALL = {
+    "tiny_fp32": get_workload("tiny_fp32"),
+    "tiny_fp32_ragged": scaled(get_workload("tiny_fp32"), T=37, H=96, I=64,
+                               n_ffn=5, local_end=5, top_k=3),
+    "decode_bf16_small": scaled(get_workload("qwen3_30b_a3b_decode_bf16"), T=32,
+                                H=512, I=384, n_ffn=16, local_end=16, top_k=4),
+    "prefill_skewed_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_bf16"),
+                                   T=300, H=256, I=160, n_ffn=12, local_end=12,
+                                   top_k=4),
+    "zero_experts_small": scaled(get_workload("longcat_flash_zero_experts_bf16"),
+                                 T=64, H=512, I=256, n_ffn=24, n_zero=12,
+                                 local_end=36, top_k=6),
+    "ep_w4a8_small": scaled(get_workload("qwen3_235b_a22b_ep_rank_w4a8"), T=200,
+                            H=512, I=256, n_ffn=16, local_begin=4, local_end=8,
+                            top_k=4),
+}
+
+
+def _oracle_layer(shape, inp, **kw):
+    return O.moe_layer(**oracle_kwargs(shape, inp), **kw)
+
+
+# ------------------------------------------------------------------ gate
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_gate_topk_full_size(name):
+    m = _m()
+    shape = get_workload(name)
+    _say("gate", name)
+    inp = generate(shape, seed=1, device=DEV, weights=False)
+    ids, w = m.gate_topk(m.problem(shape), inp["logits"])
+    torch.cuda.synchronize()
+    rid, rw = O.gate_topk(inp["logits"].cpu().numpy(), shape.top_k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.max(np.abs(w.cpu().double().numpy() - rw)) <= 1e-6
+    assert np.max(np.abs(w.cpu().double().numpy().sum(1) - 1.0)) <= 1e-6
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 64), (128, 8), (768, 12), (100, 7),
+                                 (2048, 16), (1, 1)])
+def test_gate_topk_ties(E, k):
+    m = _m()
+    g = torch.Generator().manual_seed(E * 7 + k)
+    T = 203
+    L = torch.randint(-2, 3, (T, E), generator=g).float()  # many ties
+    L[0] = 0.0                                               # all tied
+    L[1, ::2] = -0.0
+    logits = L.to(DEV)
+    p = m.problem(T=T, H=32, I=32, n_ffn=E, n_zero=0, top_k=k, local_begin=0,
+                  local_end=E, act="bf16", wt="bf16", act_q="none")
+    ids, w = m.gate_topk(p, logits)
+    torch.cuda.synchronize()
+    rid, rw = O.gate_topk(L.numpy(), k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.max(np.abs(w.cpu().double().numpy() - rw)) <= 1e-6
+
+
+# ------------------------------------------------------------------ routing
+
+
+def _routing_case(shape, seed):
+    m = _m()
+    inp = generate(shape, seed=seed, device=DEV, weights=False)
+    rid, _ = O.gate_topk(inp["logits"].cpu().numpy(), shape.top_k)
+    ids = torch.from_numpy(rid).to(DEV)
+    r = m.init_routing(m.problem(shape), ids, inp["x"])
+    torch.cuda.synchronize()
+    counts, offsets, sc, cp = O.init_routing(rid, shape.E_tot)
+    assert np.array_equal(r["counts"].cpu().numpy(), counts)
+    assert np.array_equal(r["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(r["sorted_copy"].cpu().numpy(), sc)
+    assert np.array_equal(r["copy_pos"].cpu().numpy(), cp)
+    fb, fe = shape.ffn_begin, shape.ffn_end
+    r0, r1 = int(offsets[fb]), int(offsets[fe])
+    tok = sc[r0:r1] // shape.top_k
+    x = inp["x"].cpu()
+    if shape.act_q == "mxfp8":
+        codes, scl = O.mx_quant(x.double().numpy()[tok], "e4m3")
+        assert np.array_equal(r["x_perm"][: r1 - r0].cpu().numpy(), codes)
+        assert np.array_equal(r["x_perm_scale"][: r1 - r0].cpu().numpy(), scl)
+    else:
+        assert np.array_equal(bits(r["x_perm"][: r1 - r0]), bits(x[torch.from_numpy(tok)]))
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_init_routing_full_size(name):
+    _say("routing", name)
+    _routing_case(get_workload(name), seed=2)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_init_routing_small(name):
+    _say("routing small", name)
+    _routing_case(SMALL[name], seed=3)
+
+
+def test_init_routing_invalid_ids_are_ignored():
+    m = _m()
+    shape = SMALL["decode_bf16_small"]
+    inp = generate(shape, seed=0, device=DEV, weights=False)
+    rid, _ = O.gate_topk(inp["logits"].cpu().numpy(), shape.top_k)
+    rid = rid.copy()
+    rid[3, 1] = -5
+    rid[7, 0] = shape.E_tot + 3
+    r = m.init_routing(m.problem(shape), torch.from_numpy(rid).to(DEV), inp["x"])
+    torch.cuda.synchronize()
+    cp = r["copy_pos"].cpu().numpy()
+    assert cp[3 * shape.top_k + 1] == -1 and cp[7 * shape.top_k] == -1
+    assert int(r["offsets"][-1]) == rid.size - 2
+
+
+# ------------------------------------------------------------------ FFN, finalize
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_grouped_ffn_on_oracle_routing(name):
+    """moe_grouped_ffn fed the oracle's routing and x_perm; y vs oracle y."""
+    m = _m()
+    shape = SMALL[name]
+    _say("ffn", name)
+    inp = generate(shape, seed=4, device=DEV)
+    ref = _oracle_layer(shape, inp)
+    R = ref["R"]
+    p = m.problem(shape)
+    offsets = torch.from_numpy(ref["offsets"].astype(np.int32)).to(DEV)
+    N = shape.T * shape.top_k
+    if shape.act_q == "mxfp8":
+        xp = torch.zeros((N, shape.H), dtype=torch.uint8)
+        xs = torch.zeros((N, shape.H // 32), dtype=torch.uint8)
+        xp[:R] = torch.from_numpy(ref["x_perm_codes"])
+        xs[:R] = torch.from_numpy(ref["x_perm_scale"])
+        xp, xs = xp.to(DEV), xs.to(DEV)
+    else:
+        dt = torch.float32 if shape.act == "f32" else torch.bfloat16
+        xp = torch.zeros((N, shape.H), dtype=dt)
+        xp[:R] = torch.from_numpy(ref["x_perm"]).to(dt)
+        xp, xs = xp.to(DEV), None
+    y = m.grouped_ffn(p, offsets, xp, xs, inp["w13"], inp["w2"],
+                      inp["w13_scale"], inp["w2_scale"])
+    torch.cuda.synchronize()
+    assert_close(to64(y[:R]), ref["y"], shape, "y")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_finalize_on_oracle_inputs(name):
+    m = _m()
+    shape = SMALL[name]
+    inp = generate(shape, seed=5, device=DEV)
+    ref = _oracle_layer(shape, inp)
+    p = m.problem(shape)
+    N = shape.T * shape.top_k
+    dt = torch.float32 if shape.act == "f32" else torch.bfloat16
+    y = torch.zeros((N, shape.H), dtype=dt)
+    y[:ref["R"]] = torch.from_numpy(ref["y"]).to(dt)
+    out = m.finalize(p, torch.from_numpy(ref["topk_ids"]).to(DEV),
+                     torch.from_numpy(ref["topk_weight"].astype(np.float32)).to(DEV),
+                     torch.from_numpy(ref["copy_pos"].astype(np.int32)).to(DEV),
+                     torch.from_numpy(ref["offsets"].astype(np.int32)).to(DEV),
+                     y.to(DEV), inp["x"], inp["residual"])
+    torch.cuda.synchronize()
+    assert_close(to64(out), ref["out"], shape, "out")
+
+
+# ------------------------------------------------------------------ whole layer
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_small(name, seed):
+    m = _m()
+    shape = SMALL[name]
+    _say("layer", name, seed)
+    inp = generate(shape, seed=seed, device=DEV)
+    out = m.layer(m.problem(shape), inp["logits"], inp["x"], inp["w13"],
+                  inp["w2"], inp["w13_scale"], inp["w2_scale"],
+                  residual=inp["residual"])
+    torch.cuda.synchronize()
+    ref = _oracle_layer(shape, inp)["out"]
+    assert_close(to64(out), ref, shape, f"{name} seed {seed}")
+
+
+def test_layer_split_calls_equal_fused():
+    """The five calls in sequence give the same bits as moe_layer."""
+    m = _m()
+    for name in ("prefill_skewed_small", "ep_w4a8_small", "tiny_fp32"):
+        shape = SMALL[name]
+        inp = generate(shape, seed=6, device=DEV)
+        p = m.problem(shape)
+        fused = m.layer(p, inp["logits"], inp["x"], inp["w13"], inp["w2"],
+                        inp["w13_scale"], inp["w2_scale"], residual=inp["residual"])
+        ids, w = m.gate_topk(p, inp["logits"])
+        r = m.init_routing(p, ids, inp["x"])
+        h, hs = m.ffn_up(p, r["offsets"], r["x_perm"], r["x_perm_scale"],
+                         inp["w13"], inp["w13_scale"])
+        y = m.ffn_down(p, r["offsets"], h, hs, inp["w2"], inp["w2_scale"])
+        out = m.finalize(p, ids, w, r["copy_pos"], r["offsets"], y, inp["x"],
+                         inp["residual"])
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), bits(fused)), name
+
+
+def test_layer_deterministic():
+    m = _m()
+    shape = SMALL["prefill_skewed_small"]
+    inp = generate(shape, seed=7, device=DEV)
+    p = m.problem(shape)
+    a = m.layer(p, inp["logits"], inp["x"], inp["w13"], inp["w2"],
+                residual=inp["residual"])
+    b = m.layer(p, inp["logits"], inp["x"], inp["w13"], inp["w2"],
+                residual=inp["residual"])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(a), bits(b))
+
+
+def test_expert_range_partials_add_up():
+    """One call per expert-parallel share; the partial sums add up to the
+    full-range layer (the single-GPU stand-in for the reduce-scatter)."""
+    m = _m()
+    base = SMALL["ep_w4a8_small"]
+    full = base.replace(local_begin=0, local_end=base.n_ffn)
+    inp = generate(full, seed=8, device=DEV)
+    p = m.problem(full)
+    ref = m.layer(p, inp["logits"], inp["x"], inp["w13"], inp["w2"],
+                  inp["w13_scale"], inp["w2_scale"]).double()
+    total = torch.zeros_like(ref)
+    q = full.n_ffn // 4
+    for i in range(4):
+        sh = full.replace(local_begin=i * q, local_end=(i + 1) * q)
+        sl = slice(i * q, (i + 1) * q)
+        part = m.layer(m.problem(sh), inp["logits"], inp["x"],
+                       inp["w13"][sl].contiguous(), inp["w2"][sl].contiguous(),
+                       inp["w13_scale"][sl].contiguous(),
+                       inp["w2_scale"][sl].contiguous())
+        total += part.double()
+    torch.cuda.synchronize()
+    assert_close(total.cpu().numpy(), ref.cpu().numpy(), full, "partials")
+
+
+# ------------------------------------------------------------------ edge cases
+
+
+def _layer_vs_oracle(shape, seed=0, logit_fn=None):
+    m = _m()
+    inp = generate(shape, seed=seed, device=DEV)
+    if logit_fn is not None:
+        inp["logits"] = logit_fn(inp["logits"]).contiguous()
+    out = m.layer(m.problem(shape), inp["logits"], inp["x"], inp["w13"],
+                  inp["w2"], inp["w13_scale"], inp["w2_scale"],
+                  residual=inp["residual"])
+    torch.cuda.synchronize()
+    ref = _oracle_layer(shape, inp)["out"]
+    if shape.T:
+        assert_close(to64(out), ref, shape, shape.name)
+    return out
+
+
+def test_edge_single_token_and_k_equals_E():
+    b = SMALL["decode_bf16_small"]
+    _layer_vs_oracle(b.replace(T=1))
+    _layer_vs_oracle(b.replace(T=5, top_k=b.n_ffn))
+    _layer_vs_oracle(SMALL["tiny_fp32"].replace(top_k=1))
+
+
+def test_edge_zero_tokens():
+    m = _m()
+    shape = SMALL["decode_bf16_small"].replace(T=0)
+    inp = generate(shape, seed=0, device=DEV)
+    out = m.layer(m.problem(shape), inp["logits"], inp["x"], inp["w13"], inp["w2"])
+    torch.cuda.synchronize()
+    assert out.shape == (0, shape.H)
+
+
+def test_edge_identity_experts_only():
+    b = SMALL["zero_experts_small"]
+    # every token routes only to identity experts: out = x (weights sum to 1)
+    _layer_vs_oracle(b, logit_fn=lambda L: torch.cat(
+        [L[:, : b.n_ffn] - 100.0, L[:, b.n_ffn:]], 1))
+    # a range holding only identity experts: no FFN expert in range at all
+    _layer_vs_oracle(b.replace(local_begin=b.n_ffn, local_end=b.E_tot))
+
+
+def test_edge_hot_expert_many_tiles():
+    # one expert takes every token: one expert with T rows, many tiles
+    b = SMALL["prefill_skewed_small"].replace(T=700)
+    _layer_vs_oracle(b, logit_fn=lambda L: L + torch.nn.functional.one_hot(
+        torch.full((L.shape[0],), 3, device=L.device), L.shape[1]).float() * 50)
+
+
+def test_edge_range_drops_everything():
+    b = SMALL["ep_w4a8_small"]
+    # logits steer every token away from the local range: partial sum is 0
+    out = _layer_vs_oracle(b, logit_fn=lambda L: torch.cat(
+        [L[:, : b.local_begin], L[:, b.local_begin: b.local_end] - 100.0,
+         L[:, b.local_end:]], 1))
+    assert float(out.abs().max()) == 0.0
+
+
+# ------------------------------------------------------------------ full size
+
+
+def _sample_tokens(T, n, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(T, size=min(n, T), replace=False))
+
+
+FULL_SAMPLES = {"tiny_fp32": 16, "qwen3_30b_a3b_decode_bf16": 32,
+                "qwen3_30b_a3b_prefill_skewed_bf16": 48,
+                "longcat_flash_zero_experts_bf16": 6,
+                "qwen3_235b_a22b_ep_rank_w4a8": 48}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_layer_full_size_sampled(name):
+    """Full-size workload through moe_layer (the benchmark's call); sampled
+    tokens checked against the oracle's per-token evaluation."""
+    m = _m()
+    shape = get_workload(name)
+    _say("full", name)
+    inp = generate(shape, seed=0, device=DEV)
+    out = m.layer(m.problem(shape), inp["logits"], inp["x"], inp["w13"],
+                  inp["w2"], inp["w13_scale"], inp["w2_scale"],
+                  residual=inp["residual"])
+    torch.cuda.synchronize()
+    toks = _sample_tokens(shape.T, FULL_SAMPLES[name])
+    kw = oracle_kwargs(shape, inp)
+    ref = O.moe_tokens(toks, cache_weights=name != "longcat_flash_zero_experts_bf16", **kw)
+    got = to64(out)[toks]
+    assert_close(got, ref, shape, name)
+    # every output row is finite
+    assert torch.isfinite(out.float()).all()
