@@ -178,6 +178,9 @@ def main():
         step(none)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst)]
           for _ in range(args.steps)]
+    for row in ev:  # torch creates the HIP event on first record
+        for e in row:
+            e.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):

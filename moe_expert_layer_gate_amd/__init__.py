@@ -255,8 +255,12 @@ def layer_traced(p: MoeProblem, logits, x, w13, w2, events, w13_scale=None,
     if workspace is None:
         workspace = torch.empty(max(layer_workspace_bytes(p), 1),
                                 dtype=torch.uint8, device=x.device)
-    arr = (ctypes.c_void_p * len(events))(
-        *[None if e is None else e.cuda_event for e in events])
+    handles = []
+    for e in events:
+        if e is not None and not e.cuda_event:
+            e.record()  # torch creates the HIP event lazily, on first record
+        handles.append(None if e is None else e.cuda_event)
+    arr = (ctypes.c_void_p * len(events))(*handles)
     n = ctypes.c_size_t(workspace.numel())
     _check(lib().moe_layer_traced(ctypes.byref(p), _ptr(logits), _ptr(x),
                                   _ptr(residual), _ptr(w13), _ptr(w13_scale),

@@ -94,32 +94,42 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_bf16_stream_kernel(
       for (int i = 0; i < 8; ++i) acc[h][rg][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint4 z4 = make_uint4(0, 0, 0, 0);
-  for (int s = s_begin; s < s_end; ++s) {
-    const int k0 = s * 32;
+  // one K step: 8 rows x (8 + 8) columns of weights and the A fragments
+  struct Stage {
     uint4 bA[8], bB[8];
+    u32x4_t af[RG];
+  };
+  auto load = [&](Stage& st, int s) {
+    const int k0 = s * 32;
     const uint16_t* pA = we + (size_t)(k0 + 8 * kq) * Nw + colA;
     const uint16_t* pB = we + (size_t)(k0 + 8 * kq) * Nw + colB;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      bA[r] = okA ? *(const uint4*)(pA + (size_t)r * Nw) : z4;
-      bB[r] = okB ? *(const uint4*)(pB + (size_t)r * Nw) : z4;
+      st.bA[r] = okA ? *(const uint4*)(pA + (size_t)r * Nw) : z4;
+      st.bB[r] = okB ? *(const uint4*)(pB + (size_t)r * Nw) : z4;
     }
-    u32x4_t af[RG];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
       uint4 v = aok[rg] ? *(const uint4*)(arow[rg] + k0) : z4;
-      af[rg] = u32x4_t{v.x, v.y, v.z, v.w};
+      st.af[rg] = u32x4_t{v.x, v.y, v.z, v.w};
     }
+  };
+  auto compute = [&](const Stage& st) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      u32x4_t fA = column_frag(bA, i);
-      u32x4_t fB = column_frag(bB, i);
+      u32x4_t fA = column_frag(st.bA, i);
+      u32x4_t fB = column_frag(st.bB, i);
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
-        acc[0][rg][i] = mfma_bf16_16x16x32(af[rg], fA, acc[0][rg][i]);
-        acc[1][rg][i] = mfma_bf16_16x16x32(af[rg], fB, acc[1][rg][i]);
+        acc[0][rg][i] = mfma_bf16_16x16x32(st.af[rg], fA, acc[0][rg][i]);
+        acc[1][rg][i] = mfma_bf16_16x16x32(st.af[rg], fB, acc[1][rg][i]);
       }
     }
+  };
+  for (int s = s_begin; s < s_end; ++s) {
+    Stage st;
+    load(st, s);
+    compute(st);
   }
 
   // cross-wave reduction of the split-K partial sums, 16 registers a round
@@ -225,9 +235,9 @@ hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
   if (max_tiles == 0) return hipSuccess;
   const int slab = glu ? 128 : 256;
   dim3 grid(max_tiles, (Nout + slab - 1) / slab);
-  // split K so each wave streams at least ~16 steps of 32
+  // split K across 4 waves unless a wave would get fewer than 4 steps of 32
   int steps = K / 32;
-  int ksplit = steps >= 64 ? 4 : steps >= 32 ? 2 : 1;
+  int ksplit = steps >= 16 ? 4 : steps >= 8 ? 2 : 1;
   if (glu)
     return rg == 1 ? launch_stream<true, 1>(ksplit, grid, tiles, tile_count, a,
                                             w, out, K, Nw, Nout, s)

@@ -7,11 +7,15 @@
 // (expert = down(SiLU(gate(x)) * up(x)), merged gate/up).
 //
 // v_mfma_scale_f32_16x16x128_f8f6f4 with A = e4m3 (format 0) and B = e2m1
-// (format 4). Lane l supplies row l%16 of A and column l%16 of B over the
-// 32-element K block l/16 of the 128-wide K step, together with that block's
-// e8m0 scales, so a block scale applies exactly to the 32 products it
-// multiplies. Both operands are K-contiguous in memory: A rows are 32 bytes,
-// B columns 16 bytes per lane and step, loaded straight into registers.
+// (format 4). Operand layout on gfx950 (measured with an in-bounds probe of
+// one instruction): with q = l/16 and a 128-wide K step,
+//   B (e2m1, 4 VGPRs): lane l holds column l%16, K [32q, 32q+32);
+//   A (e4m3, 8 VGPRs): lane l holds row l%16, K [16q, 16q+16) in bytes 0-15
+//                      and K [64+16q, 64+16q+16) in bytes 16-31;
+//   scales: lane l holds the e8m0 scale of row / column l%16 for the K block
+//           [32q, 32q+32), whichever lanes hold that block's data.
+// Both operands are K-contiguous in memory, so every lane issues 16-byte
+// loads straight into registers: two for A, one for B per step.
 //
 // GEMM1 (glu): each lane carries 4 gate groups and the 4 matching up groups of
 // 16 columns (64 h columns per wave); the epilogue forms h = SiLU(g) * u in
@@ -74,14 +78,14 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_mx_kernel(
   const int s_begin = wave * nsteps / KSPLIT;
   const int s_end = (wave + 1) * nsteps / KSPLIT;
   for (int s = s_begin; s < s_end; ++s) {
-    const int kblk = s * 4 + kb;  // this lane's 32-wide K block
+    const int kblk = s * 4 + kb;  // K block of this lane's scales and B data
     i32x8 af[RG];
     int asc[RG];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      const uint4* p = (const uint4*)(a + (size_t)arow[rg] * K + kblk * 32);
-      uint4 v0 = aok[rg] ? p[0] : make_uint4(0, 0, 0, 0);
-      uint4 v1 = aok[rg] ? p[1] : make_uint4(0, 0, 0, 0);
+      const uint8_t* p = a + (size_t)arow[rg] * K + s * 128 + 16 * kb;
+      uint4 v0 = aok[rg] ? *(const uint4*)p : make_uint4(0, 0, 0, 0);
+      uint4 v1 = aok[rg] ? *(const uint4*)(p + 64) : make_uint4(0, 0, 0, 0);
       af[rg] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
                      (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
       asc[rg] = aok[rg] ? as[(size_t)arow[rg] * KB + kblk] : 0;

@@ -12,9 +12,10 @@
 //             giving each chunk its first slot inside the expert), the
 //             expert totals, their exclusive scan (offsets) and, optionally,
 //             the GEMM tile list of the local FFN experts
-//   scatter : each wave re-reads its chunk 64 copies at a time in order and
-//             ranks equal ids with ballot + popcount (one pass per distinct
-//             id in the 64), so copies of one expert keep ascending c: the
+//   scatter : each wave re-reads its chunk 64 copies at a time in order; the
+//             lanes holding equal ids are found by intersecting one ballot
+//             per bit of the id, and a copy's rank is the number of equal
+//             lanes below it, so copies of one expert keep ascending c: the
 //             sort key is (expert, c) and the result is deterministic
 //   gather  : one wave per routed row copies (or MXFP8-quantises) x[t]
 #include "common.h"
@@ -171,25 +172,26 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(
   __syncthreads();
   if (c >= nchunks) return;
   const uint64_t lt = lanemask_lt();
+  const uint64_t gt = ~lt & ~(1ull << lane);
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
   for (int it = 0; it < kChunk / 64; ++it) {
     const int i = c * kChunk + it * 64 + lane;
     const int e = i < N ? ids[i] : -1;
     const bool valid = (unsigned)e < (unsigned)E;
     if (i < N && !valid) copy_pos[i] = -1;
-    uint64_t rem = ballot(valid);
-    while (rem) {
-      const int leader = __ffsll((long long)rem) - 1;
-      const int ek = __shfl(e, leader);
-      const bool mine = valid && e == ek;
-      const uint64_t m = ballot(mine);
-      const int b = base[ek];
-      if (mine) {
-        int pos = b + popc64(m & lt);
-        sorted_copy[pos] = i;
-        copy_pos[i] = pos;
-      }
-      if (lane == leader) base[ek] = b + popc64(m);
-      rem &= ~m;
+    // lanes holding the same expert id: intersect one ballot per id bit
+    uint64_t m = ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = ballot(valid && bit);
+      m &= bit ? ones : ~ones;
+    }
+    if (valid) {
+      const int b0 = base[e];  // every reader sees the value before this step
+      const int pos = b0 + popc64(m & lt);
+      sorted_copy[pos] = i;
+      copy_pos[i] = pos;
+      if ((m & gt) == 0) base[e] = b0 + popc64(m);  // last lane of its group
     }
   }
 }
