@@ -47,10 +47,13 @@ moe_status check(const moe_problem* p, Prob* q) {
 
 size_t act_bytes(const Prob& q) { return q.act == MOE_F32 ? 4 : 2; }
 
-// Tile height of the grouped GEMM chosen for the problem.
+// Tile height of the grouped GEMM chosen for the problem, from the expected
+// rows per expert: weight-streaming tiles of 16 or 32 rows for decode-size
+// batches, 128-row LDS-tiled MFMA tiles for prefill-size batches.
 int tile_rows(const Prob& q) {
   if (q.act == MOE_F32) return 32;
   const long long avg = q.E ? q.N / q.E : 0;  // expected rows per expert
+  if (avg >= 64) return 128;
   return avg <= 12 ? 16 : 32;
 }
 
@@ -107,10 +110,19 @@ moe_status run_up(const Prob& q, int mt, const Tile* tiles,
     MOE_TRY(moe::launch_gemm_f32(true, tiles, tile_count, mtl, (const float*)xp,
                                  (const float*)w13, (float*)h, q.H, 2 * q.I,
                                  q.I, s));
+  else if (q.mx && mt == 128)
+    MOE_TRY(moe::launch_gemm_mx_tiled(true, tiles, tile_count, mtl,
+                                      (const uint8_t*)xp, xs,
+                                      (const uint8_t*)w13, w13s, h, hs, q.H,
+                                      2 * q.I, q.I, s));
   else if (q.mx)
     MOE_TRY(moe::launch_gemm_mx(true, mt / 16, tiles, tile_count, mtl,
                                 (const uint8_t*)xp, xs, (const uint8_t*)w13,
                                 w13s, h, hs, q.H, 2 * q.I, q.I, s));
+  else if (mt == 128)
+    MOE_TRY(moe::launch_gemm_bf16_tiled(
+        true, tiles, tile_count, mtl, (const uint16_t*)xp,
+        (const uint16_t*)w13, (uint16_t*)h, q.H, 2 * q.I, q.I, s));
   else
     MOE_TRY(moe::launch_gemm_bf16_stream(
         true, mt / 16, tiles, tile_count, mtl, (const uint16_t*)xp,
@@ -128,10 +140,19 @@ moe_status run_down(const Prob& q, int mt, const Tile* tiles,
     MOE_TRY(moe::launch_gemm_f32(false, tiles, tile_count, mtl,
                                  (const float*)h, (const float*)w2, (float*)y,
                                  q.I, q.H, q.H, s));
+  else if (q.mx && mt == 128)
+    MOE_TRY(moe::launch_gemm_mx_tiled(false, tiles, tile_count, mtl,
+                                      (const uint8_t*)h, hs,
+                                      (const uint8_t*)w2, w2s, y, nullptr,
+                                      q.I, q.H, q.H, s));
   else if (q.mx)
     MOE_TRY(moe::launch_gemm_mx(false, mt / 16, tiles, tile_count, mtl,
                                 (const uint8_t*)h, hs, (const uint8_t*)w2, w2s,
                                 y, nullptr, q.I, q.H, q.H, s));
+  else if (mt == 128)
+    MOE_TRY(moe::launch_gemm_bf16_tiled(
+        false, tiles, tile_count, mtl, (const uint16_t*)h,
+        (const uint16_t*)w2, (uint16_t*)y, q.I, q.H, q.H, s));
   else
     MOE_TRY(moe::launch_gemm_bf16_stream(
         false, mt / 16, tiles, tile_count, mtl, (const uint16_t*)h,

@@ -71,6 +71,12 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_bf16_stream_kernel(
   const int colB = GLU ? Nout + colA : colA + 128;
   const bool okA = colA < Nout;
   const bool okB = GLU ? okA : (colA + 128 < Nout);
+  // Columns past N and rows past the tile only feed outputs that are never
+  // stored (each output column / row depends on its own B column / A row),
+  // so their loads are redirected to column / row 0 instead of being
+  // predicated: every load stays an unconditional 16-byte load.
+  const int ldA = okA ? colA : 0;
+  const int ldB = okB ? colB : 0;
   const uint16_t* we = w + (size_t)tl.expert * K * Nw;
   const int nsteps = K / 32;
   const int s_begin = wave * nsteps / KSPLIT;
@@ -93,7 +99,6 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_bf16_stream_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[h][rg][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
   // one K step: 8 rows x (8 + 8) columns of weights and the A fragments
   struct Stage {
     uint4 bA[8], bB[8];
@@ -101,16 +106,16 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_bf16_stream_kernel(
   };
   auto load = [&](Stage& st, int s) {
     const int k0 = s * 32;
-    const uint16_t* pA = we + (size_t)(k0 + 8 * kq) * Nw + colA;
-    const uint16_t* pB = we + (size_t)(k0 + 8 * kq) * Nw + colB;
+    const uint16_t* pA = we + (size_t)(k0 + 8 * kq) * Nw + ldA;
+    const uint16_t* pB = we + (size_t)(k0 + 8 * kq) * Nw + ldB;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      st.bA[r] = okA ? *(const uint4*)(pA + (size_t)r * Nw) : z4;
-      st.bB[r] = okB ? *(const uint4*)(pB + (size_t)r * Nw) : z4;
+      st.bA[r] = *(const uint4*)(pA + (size_t)r * Nw);
+      st.bB[r] = *(const uint4*)(pB + (size_t)r * Nw);
     }
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      uint4 v = aok[rg] ? *(const uint4*)(arow[rg] + k0) : z4;
+      uint4 v = *(const uint4*)(arow[rg] + k0);
       st.af[rg] = u32x4_t{v.x, v.y, v.z, v.w};
     }
   };
@@ -126,10 +131,27 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_bf16_stream_kernel(
       }
     }
   };
-  for (int s = s_begin; s < s_end; ++s) {
-    Stage st;
-    load(st, s);
-    compute(st);
+  if (RG == 1) {
+    // two register stages: the loads of step s+1 are in flight while step s
+    // is transposed and multiplied
+    Stage st0, st1;
+    if (s_begin < s_end) load(st0, s_begin);
+    for (int s = s_begin; s < s_end; s += 2) {
+      if (s + 1 < s_end) load(st1, s + 1);
+      compute(st0);
+      if (s + 1 < s_end) {
+        if (s + 2 < s_end) load(st0, s + 2);
+        compute(st1);
+      }
+    }
+  } else {
+    // 32-row tiles carry twice the accumulators: one stage, loads of a step
+    // still issued together before its MFMAs
+    for (int s = s_begin; s < s_end; ++s) {
+      Stage st;
+      load(st, s);
+      compute(st);
+    }
   }
 
   // cross-wave reduction of the split-K partial sums, 16 registers a round
@@ -218,6 +240,11 @@ static hipError_t launch_stream(int ksplit, dim3 grid, const Tile* tiles,
                          dim3(128), 0, s, tiles, tile_count, a, w, out, K, Nw,
                          Nout);
       break;
+    case 3:
+      hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 3>), grid,
+                         dim3(192), 0, s, tiles, tile_count, a, w, out, K, Nw,
+                         Nout);
+      break;
     default:
       hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 4>), grid,
                          dim3(256), 0, s, tiles, tile_count, a, w, out, K, Nw,
@@ -225,6 +252,27 @@ static hipError_t launch_stream(int ksplit, dim3 grid, const Tile* tiles,
       break;
   }
   return hipGetLastError();
+}
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+// Waves per block that split K. Decode launches have few (tile, slab) blocks;
+// splitting K across up to 4 waves fills the chip, but only as far as every
+// wave stays resident in one round (3 waves per SIMD for 16-row tiles, 2 for
+// 32-row tiles) and keeps at least 4 steps of 32.
+int stream_ksplit(long long blocks, int steps, int rg) {
+  const long long slots = (long long)device_cus() * 4 * (rg == 1 ? 3 : 2);
+  int ks = 1;
+  for (int k = 2; k <= 4; ++k)
+    if (blocks * k <= slots && steps / k >= 4) ks = k;
+  return ks;
 }
 
 hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
@@ -235,9 +283,7 @@ hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
   if (max_tiles == 0) return hipSuccess;
   const int slab = glu ? 128 : 256;
   dim3 grid(max_tiles, (Nout + slab - 1) / slab);
-  // split K across 4 waves unless a wave would get fewer than 4 steps of 32
-  int steps = K / 32;
-  int ksplit = steps >= 16 ? 4 : steps >= 8 ? 2 : 1;
+  const int ksplit = stream_ksplit((long long)grid.x * grid.y, K / 32, rg);
   if (glu)
     return rg == 1 ? launch_stream<true, 1>(ksplit, grid, tiles, tile_count, a,
                                             w, out, K, Nw, Nout, s)

@@ -83,18 +83,19 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_mx_kernel(
     int asc[RG];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
+      // rows past the tile read row 0 of the tile: their outputs are dropped
       const uint8_t* p = a + (size_t)arow[rg] * K + s * 128 + 16 * kb;
-      uint4 v0 = aok[rg] ? *(const uint4*)p : make_uint4(0, 0, 0, 0);
-      uint4 v1 = aok[rg] ? *(const uint4*)(p + 64) : make_uint4(0, 0, 0, 0);
+      uint4 v0 = *(const uint4*)p;
+      uint4 v1 = *(const uint4*)(p + 64);
       af[rg] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
                      (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-      asc[rg] = aok[rg] ? as[(size_t)arow[rg] * KB + kblk] : 0;
+      asc[rg] = as[(size_t)arow[rg] * KB + kblk];
     }
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      uint4 v = cok[gi] ? *(const uint4*)(we + (size_t)col[gi] * (K / 2) + kblk * 16)
-                        : make_uint4(0, 0, 0, 0);
-      int bsc = cok[gi] ? wse[(size_t)col[gi] * KB + kblk] : 0;
+      // columns past N read column 0: their outputs are never stored
+      uint4 v = *(const uint4*)(we + (size_t)col[gi] * (K / 2) + kblk * 16);
+      int bsc = wse[(size_t)col[gi] * KB + kblk];
       i32x8 bf = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg)

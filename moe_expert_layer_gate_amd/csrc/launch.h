@@ -51,6 +51,12 @@ hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
                                    const uint16_t* a, const uint16_t* w,
                                    uint16_t* out, int K, int Nw, int Nout,
                                    hipStream_t s);
+// Same operands, 128-row LDS-tiled MFMA tiles (tile list built with mt=128).
+hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
+                                  const int32_t* tile_count, int max_tiles,
+                                  const uint16_t* a, const uint16_t* w,
+                                  uint16_t* out, int K, int Nw, int Nout,
+                                  hipStream_t s);
 // fp32 activations / fp32 weights [E_loc, K, N], VALU.
 hipError_t launch_gemm_f32(bool glu, const Tile* tiles,
                            const int32_t* tile_count, int max_tiles,
@@ -65,6 +71,14 @@ hipError_t launch_gemm_mx(bool glu, int rg, const Tile* tiles,
                           const uint8_t* w, const uint8_t* w_scale, void* out,
                           uint8_t* out_scale, int K, int Nw, int Nout,
                           hipStream_t s);
+
+// Same operands, 128-row LDS-tiled scaled-MFMA tiles (tile list mt=128).
+hipError_t launch_gemm_mx_tiled(bool glu, const Tile* tiles,
+                                const int32_t* tile_count, int max_tiles,
+                                const uint8_t* a, const uint8_t* a_scale,
+                                const uint8_t* w, const uint8_t* w_scale,
+                                void* out, uint8_t* out_scale, int K, int Nw,
+                                int Nout, hipStream_t s);
 
 hipError_t launch_finalize(const int32_t* ids, const float* w,
                            const int32_t* copy_pos, const int32_t* offsets,

@@ -45,6 +45,11 @@ SMALL = {
     "ep_w4a8_small": scaled(get_workload("qwen3_235b_a22b_ep_rank_w4a8"), T=200,
                             H=512, I=256, n_ffn=16, local_begin=4, local_end=8,
                             top_k=4),
+    # enough rows per expert for the 128-row LDS-tiled scaled-MFMA kernel;
+    # H = 384 leaves a ragged 256-column slab in GEMM2
+    "ep_w4a8_prefill_small": scaled(get_workload("qwen3_235b_a22b_ep_rank_w4a8"),
+                                    T=384, H=384, I=256, n_ffn=16, local_begin=4,
+                                    local_end=12, top_k=4),
 }
 
 
@@ -215,7 +220,8 @@ def test_layer_small(name, seed):
 def test_layer_split_calls_equal_fused():
     """The five calls in sequence give the same bits as moe_layer."""
     m = _m()
-    for name in ("prefill_skewed_small", "ep_w4a8_small", "tiny_fp32"):
+    for name in ("prefill_skewed_small", "ep_w4a8_small", "ep_w4a8_prefill_small",
+                 "tiny_fp32", "decode_bf16_small"):
         shape = SMALL[name]
         inp = generate(shape, seed=6, device=DEV)
         p = m.problem(shape)
