@@ -10,9 +10,13 @@
 // Block = 256 threads (2 x 2 waves) computing a 128-row x 256-weight-column
 // tile of one expert, K in steps of 32 through double-buffered LDS:
 //   * A (activation rows, K contiguous) is copied to LDS as [row][k];
-//   * B (weights [K, N], N contiguous) is loaded as 4x8 blocks (4 rows x 16
-//     bytes per thread, 128 contiguous bytes per 8 threads) and transposed in
-//     registers into [n][k] so both MFMA operands are single 16-byte LDS reads;
+//   * B (weights [K, N], N contiguous) is copied to LDS unchanged, [k][n],
+//     with 512 contiguous bytes per row and 16-byte stores, and read back
+//     K-packed with ds_read_b64_tr_b16: within each group of 16 lanes, source
+//     lane s supplies row kb + s/4, columns n0 + 4*(s%4) .. +3, and lane j
+//     receives column n0 + j at rows kb .. kb+3 (transpose semantics measured
+//     with an in-bounds probe of the instruction); two such reads give the
+//     8 consecutive K of an MFMA B fragment;
 //   * v_mfma_f32_32x32x16_bf16: each wave owns 64 rows x 128 weight columns
 //     (2 x 4 blocks of 32 x 32, 128 fp32 accumulators);
 //   * GEMM1 tiles hold 128 gate columns and the 128 matching up columns; a
@@ -31,8 +35,11 @@ namespace moe {
 namespace {
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BNW = 256, BK = 32, LDK = BK + 8;  // LDS row: 80 B
+constexpr int BM = 128, BNW = 256, BK = 32;
+constexpr int LDK = BK + 8;      // A row in LDS: 80 B
+constexpr int LDN = BNW + 16;    // B row in LDS: 544 B
 
 MOE_DEV f32x16 mfma32(u32x4_t a, u32x4_t b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -40,9 +47,14 @@ MOE_DEV f32x16 mfma32(u32x4_t a, u32x4_t b, f32x16 c) {
       0, 0);
 }
 
+MOE_DEV v4i16_t lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16_t*)(p));
+}
+
 struct Smem {
   uint16_t a[2][BM][LDK];
-  uint16_t b[2][BNW][LDK];
+  uint16_t b[2][BK][LDN];
 };
 
 }  // namespace
@@ -77,11 +89,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
     const int r = (tid >> 2) + 64 * j;
     a_src[j] = a + (size_t)(tl.row0 + (r < tl.rows ? r : 0)) * K + 8 * a_kc;
   }
-  // B: weight columns 8*cg .. +8 of the tile, rows 4*kg .. +4 of the step
-  const int cg = tid >> 3, kg = tid & 7;
+  // B: 16-byte pieces p = tid + 256*j: row p/32 of the step, tile columns
+  // 8*(p%32) .. +8 (32 lanes per 512-byte row)
+  const int bc = tid & 31, bk = tid >> 5;
   int bcol;
   {
-    const int j = 8 * cg;  // tile column
+    const int j = 8 * bc;  // tile column
     int col, oc;
     if (GLU) {
       oc = c0 + (j & (BNW / 2 - 1));
@@ -92,35 +105,30 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
     }
     bcol = oc < Nout ? col : 0;  // unused columns read column 0
   }
-  const uint16_t* b_src = we + (size_t)(4 * kg) * Nw + bcol;
+  const uint16_t* b_src = we + (size_t)bk * Nw + bcol;
 
-  uint4 ra[2], rb[4];
-  auto gload = [&](int s) {
-    const int k0 = s * BK;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) ra[j] = *(const uint4*)(a_src[j] + k0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      rb[r] = *(const uint4*)(b_src + (size_t)(k0 + r) * Nw);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      *(uint4*)&sm.a[buf][(tid >> 2) + 64 * j][8 * a_kc] = ra[j];
-    // transpose 4 rows x 8 columns -> 8 columns x 4 k (8 bytes each)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-      auto dw = [&](int r) -> uint32_t {
-        const int d = i >> 1;
-        return d == 0 ? rb[r].x : d == 1 ? rb[r].y : d == 2 ? rb[r].z : rb[r].w;
-      };
-      uint2 v;
-      v.x = __builtin_amdgcn_perm(dw(1), dw(0), sel);
-      v.y = __builtin_amdgcn_perm(dw(3), dw(2), sel);
-      *(uint2*)&sm.b[buf][8 * cg + i][4 * kg] = v;
-    }
-  };
+  // the prefetch registers are plain locals written and read in fully
+  // unrolled code (no lambda captures), so they stay in VGPRs
+#define MOE_TILED_GLOAD(s_)                                                 \
+  do {                                                                      \
+    const int k0_ = (s_) * BK;                                              \
+    ra0 = *(const uint4*)(a_src[0] + k0_);                                  \
+    ra1 = *(const uint4*)(a_src[1] + k0_);                                  \
+    rb0 = *(const uint4*)(b_src + (size_t)(k0_ + 0) * Nw);                  \
+    rb1 = *(const uint4*)(b_src + (size_t)(k0_ + 8) * Nw);                  \
+    rb2 = *(const uint4*)(b_src + (size_t)(k0_ + 16) * Nw);                 \
+    rb3 = *(const uint4*)(b_src + (size_t)(k0_ + 24) * Nw);                 \
+  } while (0)
+#define MOE_TILED_LSTORE(buf_)                                              \
+  do {                                                                      \
+    *(uint4*)&sm.a[buf_][(tid >> 2)][8 * a_kc] = ra0;                       \
+    *(uint4*)&sm.a[buf_][(tid >> 2) + 64][8 * a_kc] = ra1;                  \
+    *(uint4*)&sm.b[buf_][bk + 0][8 * bc] = rb0;                             \
+    *(uint4*)&sm.b[buf_][bk + 8][8 * bc] = rb1;                             \
+    *(uint4*)&sm.b[buf_][bk + 16][8 * bc] = rb2;                            \
+    *(uint4*)&sm.b[buf_][bk + 24][8 * bc] = rb3;                            \
+  } while (0)
+  uint4 ra0, ra1, rb0, rb1, rb2, rb3;
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -136,6 +144,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
     return wn * 128 + nbk * 32;
   };
   const int lr = lane & 31, lk = 8 * (lane >> 5);
+  // transpose-read coordinates: group g = lane/16, source lane s = lane%16
+  const int tr_k = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_n = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
@@ -147,8 +158,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
       }
 #pragma unroll
       for (int nbk = 0; nbk < 4; ++nbk) {
-        uint4 v = *(const uint4*)&sm.b[buf][bblock(nbk) + lr][kk * 16 + lk];
-        fb[nbk] = u32x4_t{v.x, v.y, v.z, v.w};
+        const uint16_t* p = &sm.b[buf][kk * 16 + tr_k][bblock(nbk) + tr_n];
+        const v4i16_t lo = lds_read_tr(p);
+        const v4i16_t hi = lds_read_tr(p + 4 * LDN);
+        fb[nbk] = __builtin_bit_cast(
+            u32x4_t, (short __attribute__((ext_vector_type(8)))){
+                         lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -159,16 +174,18 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
   };
 
   const int nsteps = K / BK;
-  gload(0);
-  lstore(0);
+  MOE_TILED_GLOAD(0);
+  MOE_TILED_LSTORE(0);
   __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nsteps) gload(s + 1);
+    if (s + 1 < nsteps) MOE_TILED_GLOAD(s + 1);
     compute(buf);
-    if (s + 1 < nsteps) lstore(buf ^ 1);
+    if (s + 1 < nsteps) MOE_TILED_LSTORE(buf ^ 1);
     __syncthreads();
   }
+#undef MOE_TILED_GLOAD
+#undef MOE_TILED_LSTORE
 
   // epilogue through LDS: each wave stages 32 rows at a time in its own
   // region of the (now free) B buffers

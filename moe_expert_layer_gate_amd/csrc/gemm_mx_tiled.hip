@@ -70,42 +70,73 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   const uint8_t* we = w + (size_t)tl.expert * Nw * (K / 2);
   const uint8_t* wse = ws + (size_t)tl.expert * Nw * KB;
 
-  // global -> register assignment. A: row tid/2, 64 bytes at 64*(tid%2).
-  const int ar = tid >> 1, ah = tid & 1;
-  const int arow = tl.row0 + (ar < tl.rows ? ar : 0);
-  const uint8_t* a_src = a + (size_t)arow * K + 64 * ah;
-  const uint32_t* as_src = (const uint32_t*)(as + (size_t)arow * KB);
-  // B: column tid, 64 bytes (128 K values) per step
-  int col, oc;
-  if (GLU) {
-    oc = c0 + (tid & (MBNW / 2 - 1));
-    col = tid < MBNW / 2 ? oc : Nout + oc;
-  } else {
-    oc = c0 + tid;
-    col = oc;
+  // global -> register assignment, 16-byte pieces p = tid + 256*j (j < 4):
+  // A piece p = row p/8, bytes 16*(p%8) of the step (8 lanes per 128-byte
+  // row); B piece p = tile column p/4, bytes 16*(p%4) (4 lanes per 64-byte
+  // column slice). Scales: one 4-byte word per row (tid < 128) and column.
+  size_t a_off[4];
+  int b_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = tid + 256 * j;
+    const int r = p >> 3;
+    a_off[j] = (size_t)(tl.row0 + (r < tl.rows ? r : 0)) * K + 16 * (p & 7);
+    const int t = p >> 2;
+    int oc, col;
+    if (GLU) {
+      oc = c0 + (t & (MBNW / 2 - 1));
+      col = t < MBNW / 2 ? oc : Nout + oc;
+    } else {
+      oc = c0 + t;
+      col = oc;
+    }
+    if (oc >= Nout) col = 0;  // unused columns read column 0
+    b_off[j] = col * (K / 2) + 16 * (p & 3);
   }
-  if (oc >= Nout) col = 0;  // unused columns read column 0
-  const uint8_t* b_src = we + (size_t)col * (K / 2);
-  const uint32_t* bs_src = (const uint32_t*)(wse + (size_t)col * KB);
+  const int sr = tid & (MBM - 1);
+  const uint32_t* as_src = (const uint32_t*)(as + (size_t)(tl.row0 + (sr < tl.rows ? sr : 0)) * KB);
+  int scol, soc;
+  if (GLU) {
+    soc = c0 + (tid & (MBNW / 2 - 1));
+    scol = tid < MBNW / 2 ? soc : Nout + soc;
+  } else {
+    soc = c0 + tid;
+    scol = soc;
+  }
+  if (soc >= Nout) scol = 0;
+  const uint32_t* bs_src = (const uint32_t*)(wse + (size_t)scol * KB);
 
-  uint4 ra[4], rb[4];
-  uint32_t rsa = 0, rsb;
-  auto gload = [&](int s) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ra[j] = *(const uint4*)(a_src + s * MBK + 16 * j);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) rb[j] = *(const uint4*)(b_src + s * (MBK / 2) + 16 * j);
-    if (ah == 0) rsa = as_src[s];
-    rsb = bs_src[s];
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *(uint4*)&sm.a[buf][ar][64 * ah + 16 * j] = ra[j];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *(uint4*)&sm.b[buf][tid][16 * j] = rb[j];
-    if (ah == 0) sm.as[buf][ar] = rsa;
-    sm.bs[buf][tid] = rsb;
-  };
+  // prefetch registers: plain locals in fully unrolled code (no lambda
+  // captures), so they stay in VGPRs
+  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+  uint32_t rsa = 0, rsb = 0;
+#define MOE_MX_GLOAD(s_)                                                    \
+  do {                                                                      \
+    const int so_ = (s_);                                                   \
+    ra0 = *(const uint4*)(a + a_off[0] + so_ * MBK);                        \
+    ra1 = *(const uint4*)(a + a_off[1] + so_ * MBK);                        \
+    ra2 = *(const uint4*)(a + a_off[2] + so_ * MBK);                        \
+    ra3 = *(const uint4*)(a + a_off[3] + so_ * MBK);                        \
+    rb0 = *(const uint4*)(we + (size_t)b_off[0] + so_ * (MBK / 2));         \
+    rb1 = *(const uint4*)(we + (size_t)b_off[1] + so_ * (MBK / 2));         \
+    rb2 = *(const uint4*)(we + (size_t)b_off[2] + so_ * (MBK / 2));         \
+    rb3 = *(const uint4*)(we + (size_t)b_off[3] + so_ * (MBK / 2));         \
+    if (tid < MBM) rsa = as_src[so_];                                       \
+    rsb = bs_src[so_];                                                      \
+  } while (0)
+#define MOE_MX_LSTORE(buf_)                                                 \
+  do {                                                                      \
+    *(uint4*)&sm.a[buf_][(tid >> 3)][16 * (tid & 7)] = ra0;                 \
+    *(uint4*)&sm.a[buf_][(tid >> 3) + 32][16 * (tid & 7)] = ra1;            \
+    *(uint4*)&sm.a[buf_][(tid >> 3) + 64][16 * (tid & 7)] = ra2;            \
+    *(uint4*)&sm.a[buf_][(tid >> 3) + 96][16 * (tid & 7)] = ra3;            \
+    *(uint4*)&sm.b[buf_][(tid >> 2)][16 * (tid & 3)] = rb0;                 \
+    *(uint4*)&sm.b[buf_][(tid >> 2) + 64][16 * (tid & 3)] = rb1;            \
+    *(uint4*)&sm.b[buf_][(tid >> 2) + 128][16 * (tid & 3)] = rb2;           \
+    *(uint4*)&sm.b[buf_][(tid >> 2) + 192][16 * (tid & 3)] = rb3;           \
+    if (tid < MBM) sm.as[buf_][tid] = rsa;                                  \
+    sm.bs[buf_][tid] = rsb;                                                 \
+  } while (0)
 
   f32x4 acc[4][8];
 #pragma unroll
@@ -144,16 +175,18 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   };
 
   const int nsteps = K / MBK;
-  gload(0);
-  lstore(0);
+  MOE_MX_GLOAD(0);
+  MOE_MX_LSTORE(0);
   __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
     const int buf = s & 1;
-    if (s + 1 < nsteps) gload(s + 1);
+    if (s + 1 < nsteps) MOE_MX_GLOAD(s + 1);
     compute(buf);
-    if (s + 1 < nsteps) lstore(buf ^ 1);
+    if (s + 1 < nsteps) MOE_MX_LSTORE(buf ^ 1);
     __syncthreads();
   }
+#undef MOE_MX_GLOAD
+#undef MOE_MX_LSTORE
 
   // epilogue, staged per wave in the (free) operand buffers
   if (GLU) {
