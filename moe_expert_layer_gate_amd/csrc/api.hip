@@ -57,6 +57,17 @@ int tile_rows(const Prob& q) {
   return avg <= 12 ? 16 : 32;
 }
 
+// moe_layer fuses the gather into GEMM1's activation loads for bf16 (the
+// tiled kernel addresses x with 32-bit offsets, so x must span < 4 GB).
+// Up to this many tokens the gate runs inside the single-block routing kernel
+// (16 waves, each scoring a token at a time).
+constexpr int64_t kSmallGateTokens = 64;
+
+bool fused_gather(const Prob& q) {
+  return q.act == MOE_BF16 && !q.mx &&
+         (unsigned long long)q.T * q.H * 2 < (1ull << 32);
+}
+
 long long max_tiles(const Prob& q, int mt) {
   if (q.El == 0 || q.N == 0) return 0;
   long long ne = q.El < q.N ? q.El : q.N;
@@ -100,10 +111,13 @@ FfnWs carve_ffn_ws(Carve& c, const Prob& q, int mt) {
   return w;
 }
 
+// gidx/gbase: fused gather (bf16 only) -- activation row of sorted copy i is
+// row gidx[gbase[0] + i] / top_k of xp (= x); NULL: xp holds permuted rows.
 moe_status run_up(const Prob& q, int mt, const Tile* tiles,
                   const int32_t* tile_count, const void* xp, const uint8_t* xs,
                   const void* w13, const uint8_t* w13s, void* h, uint8_t* hs,
-                  hipStream_t s) {
+                  hipStream_t s, const int32_t* gidx = nullptr,
+                  const int32_t* gbase = nullptr) {
   const int mtl = (int)max_tiles(q, mt);
   if (mtl == 0) return MOE_OK;
   if (q.act == MOE_F32)
@@ -122,11 +136,13 @@ moe_status run_up(const Prob& q, int mt, const Tile* tiles,
   else if (mt == 128)
     MOE_TRY(moe::launch_gemm_bf16_tiled(
         true, tiles, tile_count, mtl, (const uint16_t*)xp,
-        (const uint16_t*)w13, (uint16_t*)h, q.H, 2 * q.I, q.I, s));
+        (const uint16_t*)w13, (uint16_t*)h, q.H, 2 * q.I, q.I, gidx, gbase,
+        q.k, s));
   else
     MOE_TRY(moe::launch_gemm_bf16_stream(
         true, mt / 16, tiles, tile_count, mtl, (const uint16_t*)xp,
-        (const uint16_t*)w13, (uint16_t*)h, q.H, 2 * q.I, q.I, s));
+        (const uint16_t*)w13, (uint16_t*)h, q.H, 2 * q.I, q.I, gidx, gbase,
+        q.k, s));
   return MOE_OK;
 }
 
@@ -152,11 +168,13 @@ moe_status run_down(const Prob& q, int mt, const Tile* tiles,
   else if (mt == 128)
     MOE_TRY(moe::launch_gemm_bf16_tiled(
         false, tiles, tile_count, mtl, (const uint16_t*)h,
-        (const uint16_t*)w2, (uint16_t*)y, q.I, q.H, q.H, s));
+        (const uint16_t*)w2, (uint16_t*)y, q.I, q.H, q.H, nullptr, nullptr,
+        q.k, s));
   else
     MOE_TRY(moe::launch_gemm_bf16_stream(
         false, mt / 16, tiles, tile_count, mtl, (const uint16_t*)h,
-        (const uint16_t*)w2, (uint16_t*)y, q.I, q.H, q.H, s));
+        (const uint16_t*)w2, (uint16_t*)y, q.I, q.H, q.H, nullptr, nullptr,
+        q.k, s));
   return MOE_OK;
 }
 
@@ -222,12 +240,21 @@ moe_status moe_init_routing(const moe_problem* p, const int32_t* topk_ids,
   if (q.mx ? (q.El > 0 && q.N > 0 && !x_perm_scale) : (x_perm_scale != nullptr))
     return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  if (q.N > 0) MOE_TRY(moe::launch_route_count(topk_ids, (int)q.N, q.E, cc, s));
-  MOE_TRY(moe::launch_route_scan(cc, nch, q.E, tokens_per_expert, offsets,
-                                 q.fb, q.fe, 0, nullptr, 0, nullptr, s));
+  if (moe::route_small_ok((int)q.N, q.E)) {
+    MOE_TRY(moe::launch_route_small(nullptr, q.T, q.k,
+                                    const_cast<int32_t*>(topk_ids), nullptr,
+                                    (int)q.N, q.E, tokens_per_expert, offsets,
+                                    sorted_copy, copy_pos, q.fb, q.fe, 0,
+                                    nullptr, 0, nullptr, s));
+  } else {
+    if (q.N > 0) MOE_TRY(moe::launch_route_count(topk_ids, (int)q.N, q.E, cc, s));
+    MOE_TRY(moe::launch_route_scan(cc, nch, q.E, tokens_per_expert, offsets,
+                                   q.fb, q.fe, 0, nullptr, 0, nullptr, s));
+    if (q.N > 0)
+      MOE_TRY(moe::launch_route_scatter(topk_ids, (int)q.N, q.E, cc, offsets,
+                                        sorted_copy, copy_pos, s));
+  }
   if (q.N > 0) {
-    MOE_TRY(moe::launch_route_scatter(topk_ids, (int)q.N, q.E, cc, offsets,
-                                      sorted_copy, copy_pos, s));
     MOE_TRY(moe::launch_route_gather(x, q.act == MOE_F32 ? 0 : 1, q.mx ? 1 : 0,
                                      q.H, q.k, sorted_copy, offsets, q.fb,
                                      q.fe, (int)q.N, x_perm, x_perm_scale, s));
@@ -359,7 +386,9 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
   int32_t* copy_pos = c.take<int32_t>(N);
   FfnWs fw = carve_ffn_ws(c, q, mt);
   const size_t ab = q.mx ? 1 : act_bytes(q);
-  void* xp = c.take<char>(q.El ? N * q.H * ab : 0);
+  // bf16: GEMM1 reads its rows straight from x (no permuted copy)
+  const bool gather = fused_gather(q);
+  void* xp = c.take<char>(q.El && !gather ? N * q.H * ab : 0);
   uint8_t* xs = q.mx ? c.take<uint8_t>(q.El ? N * (q.H / 32) : 0) : nullptr;
   void* h = c.take<char>(q.El ? N * q.I * ab : 0);
   uint8_t* hs = q.mx ? c.take<uint8_t>(q.El ? N * (q.I / 32) : 0) : nullptr;
@@ -376,27 +405,43 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
       return hipEventRecord((hipEvent_t)stage_events[i], s);
     return hipSuccess;
   };
-  MOE_TRY(mark(0));
-  MOE_TRY(moe::launch_gate_topk(logits, q.T, q.E, q.k, ids, wts, s));
-  MOE_TRY(mark(1));
-  MOE_TRY(moe::launch_route_count(ids, (int)q.N, q.E, cc, s));
+  // small problems route in one block; the tiniest also run the gate there
+  const bool small = moe::route_small_ok((int)q.N, q.E);
+  const bool small_gate = small && q.T <= kSmallGateTokens;
   const int mtl = (int)max_tiles(q, mt);
+  MOE_TRY(mark(0));
+  if (!small_gate)
+    MOE_TRY(moe::launch_gate_topk(logits, q.T, q.E, q.k, ids, wts, s));
+  MOE_TRY(mark(1));
+  if (small) {
+    MOE_TRY(moe::launch_route_small(small_gate ? logits : nullptr, q.T, q.k,
+                                    ids, wts, (int)q.N, q.E, counts, offsets,
+                                    sorted_copy, copy_pos, q.fb, q.fe, mt,
+                                    mtl ? fw.tiles : nullptr, mtl,
+                                    fw.tile_count, s));
+  } else {
+    MOE_TRY(moe::launch_route_count(ids, (int)q.N, q.E, cc, s));
+  }
   MOE_TRY(mark(2));
-  MOE_TRY(moe::launch_route_scan(cc, nch, q.E, counts, offsets, q.fb, q.fe, mt,
-                                 mtl ? fw.tiles : nullptr, mtl, fw.tile_count,
-                                 s));
+  if (!small)
+    MOE_TRY(moe::launch_route_scan(cc, nch, q.E, counts, offsets, q.fb, q.fe,
+                                   mt, mtl ? fw.tiles : nullptr, mtl,
+                                   fw.tile_count, s));
   MOE_TRY(mark(3));
-  MOE_TRY(moe::launch_route_scatter(ids, (int)q.N, q.E, cc, offsets,
-                                    sorted_copy, copy_pos, s));
+  if (!small)
+    MOE_TRY(moe::launch_route_scatter(ids, (int)q.N, q.E, cc, offsets,
+                                      sorted_copy, copy_pos, s));
   MOE_TRY(mark(4));
-  if (q.El > 0)
+  if (q.El > 0 && !gather)
     MOE_TRY(moe::launch_route_gather(x, q.act == MOE_F32 ? 0 : 1, q.mx ? 1 : 0,
                                      q.H, q.k, sorted_copy, offsets, q.fb,
                                      q.fe, (int)q.N, xp, xs, s));
   MOE_TRY(mark(5));
   if (q.El > 0) {
-    st = run_up(q, mt, fw.tiles, fw.tile_count, xp, xs, w13, w13_scale, h, hs,
-                s);
+    st = gather ? run_up(q, mt, fw.tiles, fw.tile_count, x, nullptr, w13,
+                         w13_scale, h, hs, s, sorted_copy, offsets + q.fb)
+                : run_up(q, mt, fw.tiles, fw.tile_count, xp, xs, w13,
+                         w13_scale, h, hs, s);
     if (st != MOE_OK) return st;
   }
   MOE_TRY(mark(6));

@@ -20,7 +20,9 @@
 //     and the matching up columns (so SwiGLU is lane-local in the epilogue),
 //     for GEMM2 two halves of a 256-column slab.
 //   * A rows (activations, K contiguous) are loaded straight into the
-//     fragment layout: row 16*rg + l%16, k0 + 8*(l/16) + 0..7.
+//     fragment layout: row 16*rg + l%16, k0 + 8*(l/16) + 0..7. With a gather
+//     index the rows are read from x itself (row of sorted copy i = token
+//     sorted_copy[i] / k), so the permuted copy of x is never written.
 //   * KSPLIT waves of a block split K; partial sums meet in LDS 16 registers
 //     at a time; wave 0 applies SwiGLU / converts and stores 16 bytes per
 //     row and lane.
@@ -59,7 +61,9 @@ template <bool GLU, int RG, int KSPLIT>
 __global__ __launch_bounds__(64 * KSPLIT) void gemm_bf16_stream_kernel(
     const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ w,
-    uint16_t* __restrict__ out, int K, int Nw, int Nout) {
+    uint16_t* __restrict__ out, int K, int Nw, int Nout,
+    const int32_t* __restrict__ gidx, const int32_t* __restrict__ gbase,
+    int gk) {
   if ((int)blockIdx.x >= tile_count[0]) return;
   const Tile tl = tiles[blockIdx.x];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -88,7 +92,10 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_bf16_stream_kernel(
   for (int rg = 0; rg < RG; ++rg) {
     int r = 16 * rg + g;
     aok[rg] = r < tl.rows;
-    arow[rg] = a + (size_t)(tl.row0 + (aok[rg] ? r : 0)) * K + 8 * kq;
+    int src = tl.row0 + (aok[rg] ? r : 0);
+    // fused gather: the row of the sorted copy is its token's row of x
+    if (gidx) src = gidx[gbase[0] + src] / gk;
+    arow[rg] = a + (size_t)src * K + 8 * kq;
   }
 
   f32x4 acc[2][RG][8];
@@ -229,26 +236,27 @@ template <bool GLU, int RG>
 static hipError_t launch_stream(int ksplit, dim3 grid, const Tile* tiles,
                                 const int32_t* tile_count, const uint16_t* a,
                                 const uint16_t* w, uint16_t* out, int K, int Nw,
-                                int Nout, hipStream_t s) {
+                                int Nout, const int32_t* gidx,
+                                const int32_t* gbase, int gk, hipStream_t s) {
   switch (ksplit) {
     case 1:
       hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 1>), grid, dim3(64),
-                         0, s, tiles, tile_count, a, w, out, K, Nw, Nout);
+                         0, s, tiles, tile_count, a, w, out, K, Nw, Nout, gidx, gbase, gk);
       break;
     case 2:
       hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 2>), grid,
                          dim3(128), 0, s, tiles, tile_count, a, w, out, K, Nw,
-                         Nout);
+                         Nout, gidx, gbase, gk);
       break;
     case 3:
       hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 3>), grid,
                          dim3(192), 0, s, tiles, tile_count, a, w, out, K, Nw,
-                         Nout);
+                         Nout, gidx, gbase, gk);
       break;
     default:
       hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 4>), grid,
                          dim3(256), 0, s, tiles, tile_count, a, w, out, K, Nw,
-                         Nout);
+                         Nout, gidx, gbase, gk);
       break;
   }
   return hipGetLastError();
@@ -279,20 +287,21 @@ hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
                                    const int32_t* tile_count, int max_tiles,
                                    const uint16_t* a, const uint16_t* w,
                                    uint16_t* out, int K, int Nw, int Nout,
-                                   hipStream_t s) {
+                                   const int32_t* gidx, const int32_t* gbase,
+                                   int gk, hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
   const int slab = glu ? 128 : 256;
   dim3 grid(max_tiles, (Nout + slab - 1) / slab);
   const int ksplit = stream_ksplit((long long)grid.x * grid.y, K / 32, rg);
   if (glu)
     return rg == 1 ? launch_stream<true, 1>(ksplit, grid, tiles, tile_count, a,
-                                            w, out, K, Nw, Nout, s)
+                                            w, out, K, Nw, Nout, gidx, gbase, gk, s)
                    : launch_stream<true, 2>(ksplit, grid, tiles, tile_count, a,
-                                            w, out, K, Nw, Nout, s);
+                                            w, out, K, Nw, Nout, gidx, gbase, gk, s);
   return rg == 1 ? launch_stream<false, 1>(ksplit, grid, tiles, tile_count, a,
-                                           w, out, K, Nw, Nout, s)
+                                           w, out, K, Nw, Nout, gidx, gbase, gk, s)
                  : launch_stream<false, 2>(ksplit, grid, tiles, tile_count, a,
-                                           w, out, K, Nw, Nout, s);
+                                           w, out, K, Nw, Nout, gidx, gbase, gk, s);
 }
 
 }  // namespace moe

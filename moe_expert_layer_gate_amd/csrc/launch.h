@@ -36,6 +36,15 @@ hipError_t launch_route_scatter(const int32_t* ids, int N, int E,
                                 const int32_t* chunk_base,
                                 const int32_t* offsets, int32_t* sorted_copy,
                                 int32_t* copy_pos, hipStream_t s);
+// Single-block routing (count + scan + tile list + scatter, optionally the
+// gate too when logits != NULL) for N <= 16384 copies and E <= 1024.
+bool route_small_ok(int N, int E);
+hipError_t launch_route_small(const float* logits, int T, int k, int32_t* ids,
+                              float* wts, int N, int E, int32_t* counts,
+                              int32_t* offsets, int32_t* sorted_copy,
+                              int32_t* copy_pos, int fb, int fe, int mt,
+                              Tile* tiles, int max_tiles, int32_t* tile_count,
+                              hipStream_t s);
 // act: 0 f32, 1 bf16. mx: quantise rows to MXFP8 (bf16 input only).
 hipError_t launch_route_gather(const void* x, int act, int mx, int H, int k,
                                const int32_t* sorted_copy,
@@ -45,18 +54,23 @@ hipError_t launch_route_gather(const void* x, int act, int mx, int H, int k,
 
 // Grouped GEMMs. glu: GEMM1 with SwiGLU epilogue (N = 2*I weight columns,
 // I outputs), else GEMM2 (N outputs). Tiles come from the tile list.
-// bf16 activations / bf16 weights [E_loc, K, N].
+// bf16 activations / bf16 weights [E_loc, K, N]. When gidx is non-NULL the
+// activation row of tile row i is row gidx[gbase[0] + i] / gk of `a` (the
+// gather from x fused into the A loads); otherwise row i of `a`.
 hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
                                    const int32_t* tile_count, int max_tiles,
                                    const uint16_t* a, const uint16_t* w,
                                    uint16_t* out, int K, int Nw, int Nout,
-                                   hipStream_t s);
+                                   const int32_t* gidx, const int32_t* gbase,
+                                   int gk, hipStream_t s);
 // Same operands, 128-row LDS-tiled MFMA tiles (tile list built with mt=128).
+// With gidx, `a` must span less than 4 GB.
 hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
                                   const int32_t* tile_count, int max_tiles,
                                   const uint16_t* a, const uint16_t* w,
                                   uint16_t* out, int K, int Nw, int Nout,
-                                  hipStream_t s);
+                                  const int32_t* gidx, const int32_t* gbase,
+                                  int gk, hipStream_t s);
 // fp32 activations / fp32 weights [E_loc, K, N], VALU.
 hipError_t launch_gemm_f32(bool glu, const Tile* tiles,
                            const int32_t* tile_count, int max_tiles,

@@ -19,6 +19,7 @@
 //             sort key is (expert, c) and the result is deterministic
 //   gather  : one wave per routed row copies (or MXFP8-quantises) x[t]
 #include "common.h"
+#include "gate_wave.h"
 #include "launch.h"
 
 namespace moe {
@@ -121,19 +122,35 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
   __shared__ int32_t off[kMaxE + 1];
   __shared__ int32_t tmp[kMaxE];
   __shared__ int32_t wsum[16];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      size_t idx = (size_t)c * E + e;
-      int v = cc[idx];
-      cc[idx] = run;
-      run += v;
+  __shared__ int32_t part[1024];
+  // tpe threads per expert split the chunks into contiguous ranges: sum each
+  // range (independent loads), scan the ranges in LDS, then rewrite every
+  // chunk count as its exclusive prefix within the expert
+  int tpe = 1;
+  while (tpe * 2 * E <= (int)blockDim.x) tpe *= 2;
+  const int per = (nchunks + tpe - 1) / tpe;
+  for (int e0 = 0; e0 < E; e0 += blockDim.x / tpe) {
+    const int e = e0 + (int)threadIdx.x / tpe, q = threadIdx.x % tpe;
+    const bool act = e < E && (int)threadIdx.x / tpe < (int)blockDim.x / tpe;
+    const int c0 = q * per, c1 = min(nchunks, c0 + per);
+    int sum = 0;
+    if (act)
+      for (int c = c0; c < c1; ++c) sum += cc[(size_t)c * E + e];
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    if (act) {
+      int base = 0;
+      for (int j = 0; j < q; ++j) base += part[threadIdx.x - q + j];
+      if (q == tpe - 1) { cnt[e] = base + sum; off[e] = base + sum; counts[e] = base + sum; }
+      for (int c = c0; c < c1; ++c) {
+        const size_t idx = (size_t)c * E + e;
+        const int v = cc[idx];
+        cc[idx] = base;
+        base += v;
+      }
     }
-    cnt[e] = run;
-    off[e] = run;
-    counts[e] = run;
+    __syncthreads();
   }
-  __syncthreads();
   int total = block_exclusive_scan(off, E, wsum);
   for (int e = threadIdx.x; e < E; e += blockDim.x) offsets[e] = off[e];
   if (threadIdx.x == 0) { offsets[E] = total; off[E] = total; }
@@ -192,6 +209,100 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(
       sorted_copy[pos] = i;
       copy_pos[i] = pos;
       if ((m & gt) == 0) base[e] = b0 + popc64(m);  // last lane of its group
+    }
+  }
+}
+
+// Single-block routing for small problems (N <= 16384 copies, E <= 1024):
+// optional gate (VPL > 0: waves take tokens t = wave, wave + 16, ...),
+// per-wave histograms over contiguous chunks of copies, the scans, the GEMM
+// tile list and the stable scatter, all in one launch with the counts kept
+// in LDS. Same results as gate + count + scan + scatter.
+constexpr int kSmallMaxN = 16384, kSmallMaxE = 1024;
+
+template <int VPL>
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const float* __restrict__ logits, int T, int k, int32_t* __restrict__ ids,
+    float* __restrict__ wts, int N, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_copy,
+    int32_t* __restrict__ copy_pos, int fb, int fe, int mt, Tile* tiles,
+    int max_tiles, int32_t* tile_count) {
+  __shared__ int32_t hist[16][kSmallMaxE];
+  __shared__ int32_t cnt[kSmallMaxE];
+  __shared__ int32_t off[kSmallMaxE + 1];
+  __shared__ int32_t tmp[kSmallMaxE];
+  __shared__ int32_t wsum[16];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if constexpr (VPL > 0) {
+    __shared__ uint2 gslot[16][64];
+    for (int t = w; t < T; t += 16)
+      topk_softmax_wave<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
+                             wts + (size_t)t * k, gslot[w]);
+    __syncthreads();  // ids written by other waves of this block are visible
+  }
+  // wave w owns copies [c0, c1), a multiple of 64 long
+  const int C = ((N + 16 * 64 - 1) / (16 * 64)) * 64;
+  const int c0 = min(N, w * C), c1 = min(N, c0 + C);
+  // the wave's ids stay in registers: all loads issue back to back, and the
+  // count and the scatter both read them from there
+  constexpr int kPerLane = kSmallMaxN / (16 * 64);
+  int idr[kPerLane];
+#pragma unroll
+  for (int it = 0; it < kPerLane; ++it) {
+    const int i = c0 + it * 64 + lane;
+    const int v = N > 0 ? ids[min(i, N - 1)] : -1;
+    idr[it] = i < c1 ? v : -1;
+  }
+  for (int e = lane; e < E; e += 64) hist[w][e] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < kPerLane; ++it)
+    if ((unsigned)idr[it] < (unsigned)E) atomicAdd(&hist[w][idr[it]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int run = 0;
+#pragma unroll
+    for (int ww = 0; ww < 16; ++ww) {
+      const int v = hist[ww][e];
+      hist[ww][e] = run;
+      run += v;
+    }
+    cnt[e] = run;
+    off[e] = run;
+    counts[e] = run;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(off, E, wsum);
+  for (int e = threadIdx.x; e < E; e += blockDim.x) offsets[e] = off[e];
+  if (threadIdx.x == 0) { offsets[E] = total; off[E] = total; }
+  __syncthreads();
+  if (tiles) build_tiles_block(cnt, off, fb, fe, mt, tiles, max_tiles,
+                               tile_count, tmp, wsum);
+  // this wave's first slot of each expert, then the stable scatter
+  volatile int32_t* base = hist[w];
+  for (int e = lane; e < E; e += 64) base[e] = base[e] + off[e];
+  const uint64_t lt = lanemask_lt();
+  const uint64_t gt = ~lt & ~(1ull << lane);
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+#pragma unroll
+  for (int it = 0; it < kPerLane; ++it) {
+    if (c0 + it * 64 >= c1) break;
+    const int i = c0 + it * 64 + lane;
+    const int e = idr[it];
+    const bool valid = (unsigned)e < (unsigned)E;
+    if (i < c1 && !valid) copy_pos[i] = -1;
+    uint64_t m = ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t ones = ballot(valid && bit);
+      m &= bit ? ones : ~ones;
+    }
+    if (valid) {
+      const int b0 = base[e];
+      const int pos = b0 + popc64(m & lt);
+      sorted_copy[pos] = i;
+      copy_pos[i] = pos;
+      if ((m & gt) == 0) base[e] = b0 + popc64(m);
     }
   }
 }
@@ -280,6 +391,34 @@ hipError_t launch_route_scatter(const int32_t* ids, int N, int E,
                      4 * E * sizeof(int32_t), s, ids, N, E, nch, chunk_base,
                      offsets, sorted_copy, copy_pos);
   return hipGetLastError();
+}
+
+bool route_small_ok(int N, int E) { return N <= kSmallMaxN && E <= kSmallMaxE; }
+
+hipError_t launch_route_small(const float* logits, int T, int k, int32_t* ids,
+                              float* wts, int N, int E, int32_t* counts,
+                              int32_t* offsets, int32_t* sorted_copy,
+                              int32_t* copy_pos, int fb, int fe, int mt,
+                              Tile* tiles, int max_tiles, int32_t* tile_count,
+                              hipStream_t s) {
+  const int vpl = logits ? (E + 63) / 64 : 0;
+#define MOE_SMALL_CASE(V)                                                      \
+  if (vpl <= V) {                                                              \
+    hipLaunchKernelGGL(route_small_kernel<V>, dim3(1), dim3(1024), 0, s,       \
+                       logits, T, k, ids, wts, N, E, counts, offsets,          \
+                       sorted_copy, copy_pos, fb, fe, mt, tiles, max_tiles,    \
+                       tile_count);                                            \
+    return hipGetLastError();                                                  \
+  }
+  MOE_SMALL_CASE(0)
+  MOE_SMALL_CASE(1)
+  MOE_SMALL_CASE(2)
+  MOE_SMALL_CASE(4)
+  MOE_SMALL_CASE(8)
+  MOE_SMALL_CASE(12)
+  MOE_SMALL_CASE(16)
+#undef MOE_SMALL_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_route_gather(const void* x, int act, int mx, int H, int k,
