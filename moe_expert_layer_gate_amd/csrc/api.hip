@@ -128,7 +128,7 @@ moe_status run_up(const Prob& q, int mt, const Tile* tiles,
     MOE_TRY(moe::launch_gemm_mx_tiled(true, tiles, tile_count, mtl,
                                       (const uint8_t*)xp, xs,
                                       (const uint8_t*)w13, w13s, h, hs, q.H,
-                                      2 * q.I, q.I, s));
+                                      2 * q.I, q.I, gidx, gbase, q.k, s));
   else if (q.mx)
     MOE_TRY(moe::launch_gemm_mx(true, mt / 16, tiles, tile_count, mtl,
                                 (const uint8_t*)xp, xs, (const uint8_t*)w13,
@@ -160,7 +160,8 @@ moe_status run_down(const Prob& q, int mt, const Tile* tiles,
     MOE_TRY(moe::launch_gemm_mx_tiled(false, tiles, tile_count, mtl,
                                       (const uint8_t*)h, hs,
                                       (const uint8_t*)w2, w2s, y, nullptr,
-                                      q.I, q.H, q.H, s));
+                                      q.I, q.H, q.H, nullptr, nullptr, q.k,
+                                      s));
   else if (q.mx)
     MOE_TRY(moe::launch_gemm_mx(false, mt / 16, tiles, tile_count, mtl,
                                 (const uint8_t*)h, hs, (const uint8_t*)w2, w2s,
@@ -388,8 +389,12 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
   const size_t ab = q.mx ? 1 : act_bytes(q);
   // bf16: GEMM1 reads its rows straight from x (no permuted copy)
   const bool gather = fused_gather(q);
-  void* xp = c.take<char>(q.El && !gather ? N * q.H * ab : 0);
-  uint8_t* xs = q.mx ? c.take<uint8_t>(q.El ? N * (q.H / 32) : 0) : nullptr;
+  // MXFP8 with the tiled GEMM: x is quantised once per token and GEMM1 reads
+  // the token rows of the codes
+  const bool mx_tok = q.mx && mt == 128 && (int64_t)q.T * q.H < (int64_t(1) << 31);
+  const size_t xrows = mx_tok ? (size_t)q.T : N;
+  void* xp = c.take<char>(q.El && !gather ? xrows * q.H * ab : 0);
+  uint8_t* xs = q.mx ? c.take<uint8_t>(q.El ? xrows * (q.H / 32) : 0) : nullptr;
   void* h = c.take<char>(q.El ? N * q.I * ab : 0);
   uint8_t* hs = q.mx ? c.take<uint8_t>(q.El ? N * (q.I / 32) : 0) : nullptr;
   void* y = c.take<char>(q.El ? N * q.H * act_bytes(q) : 0);
@@ -432,16 +437,23 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
     MOE_TRY(moe::launch_route_scatter(ids, (int)q.N, q.E, cc, offsets,
                                       sorted_copy, copy_pos, s));
   MOE_TRY(mark(4));
-  if (q.El > 0 && !gather)
+  if (q.El > 0 && mx_tok)
+    MOE_TRY(moe::launch_quantize_mx(x, (int)q.T, q.H, (uint8_t*)xp, xs, s));
+  else if (q.El > 0 && !gather)
     MOE_TRY(moe::launch_route_gather(x, q.act == MOE_F32 ? 0 : 1, q.mx ? 1 : 0,
                                      q.H, q.k, sorted_copy, offsets, q.fb,
                                      q.fe, (int)q.N, xp, xs, s));
   MOE_TRY(mark(5));
   if (q.El > 0) {
-    st = gather ? run_up(q, mt, fw.tiles, fw.tile_count, x, nullptr, w13,
-                         w13_scale, h, hs, s, sorted_copy, offsets + q.fb)
-                : run_up(q, mt, fw.tiles, fw.tile_count, xp, xs, w13,
-                         w13_scale, h, hs, s);
+    if (gather)
+      st = run_up(q, mt, fw.tiles, fw.tile_count, x, nullptr, w13, w13_scale,
+                  h, hs, s, sorted_copy, offsets + q.fb);
+    else if (mx_tok)
+      st = run_up(q, mt, fw.tiles, fw.tile_count, xp, xs, w13, w13_scale, h,
+                  hs, s, sorted_copy, offsets + q.fb);
+    else
+      st = run_up(q, mt, fw.tiles, fw.tile_count, xp, xs, w13, w13_scale, h,
+                  hs, s);
     if (st != MOE_OK) return st;
   }
   MOE_TRY(mark(6));

@@ -31,12 +31,12 @@
 //     the same XCD and share its L2.
 #include "common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace moe {
 
 namespace {
 
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
@@ -52,41 +52,10 @@ MOE_DEV f32x16 mfma32(u32x4_t a, u32x4_t b, f32x16 c) {
       0, 0);
 }
 
-MOE_DEV u32x4_t lds_read_b128(uint32_t a) {
-  return *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)a;
-}
-
 MOE_DEV v4i16_t lds_read_tr(uint32_t a) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) v4i16_t*)(uintptr_t)a);
 }
-
-// 16 bytes per lane, global (base + 32-bit lane offset) -> LDS at
-// lds_wave_base + 16 * lane. Issued as inline assembly so that the compiler
-// does not track it as an LDS write: it would otherwise drain every
-// outstanding copy (vmcnt(0)) before each barrier and LDS read, serialising
-// the ring. Completion is ordered by hand with MOE_WAIT_VMCNT before the
-// barrier that publishes a stage. M0 holds the wave-uniform LDS destination;
-// nothing else in these kernels uses M0. The base is a wave-uniform 64-bit
-// SGPR pair, so advancing a step costs scalar adds only.
-MOE_DEV void g2lds(const void* base, uint32_t voff, uint32_t lds_wave_base) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(base), "s"(lds_wave_base)
-      : "memory");
-}
-
-MOE_DEV uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum)
-#define MOE_WAIT_VMCNT(n) \
-  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | 0x0F70)
 
 MOE_DEV int swz_a(int row) { return (row >> 2) & 3; }
 MOE_DEV int swz_b(int k) { return 4 * (k & 3); }
@@ -208,52 +177,114 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
                       16 * ((col >> 3) ^ swz_b(kr)) + 2 * (col & 7);
     }
 
-#define MOE_TILED_COMPUTE(st_)                                                \
+  // fragments of one half step (16 K): A for the wave's two 32-row blocks,
+  // B for its four 32-column blocks; two register sets so that the LDS reads
+  // of the next half step overlap the MFMAs of the current one
+#define MOE_TILED_READ(fa_, fb_, st_, kk_)                                    \
   do {                                                                        \
-    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                        \
-      u32x4_t fa[2], fb[4];                                                   \
-      _Pragma("unroll") for (int mb = 0; mb < 2; ++mb) {                      \
-        fa[mb] = lds_read_b128(a_rd[kk][mb] + (st_) * STAGE_BYTES);           \
-      }                                                                       \
-      _Pragma("unroll") for (int nbk = 0; nbk < 4; ++nbk) {                   \
-        const uint32_t p_ = b_rd[kk][nbk] + (st_) * STAGE_BYTES;              \
-        const v4i16_t lo = lds_read_tr(p_);                                   \
-        const v4i16_t hi = lds_read_tr(p_ + 4 * B_ROW);                       \
-        fb[nbk] = __builtin_bit_cast(                                         \
-            u32x4_t, v8i16_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}); \
-      }                                                                       \
-      _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                        \
-        _Pragma("unroll") for (int nbk = 0; nbk < 4; ++nbk)                   \
-          acc[mb][nbk] = mfma32(fa[mb], fb[nbk], acc[mb][nbk]);               \
+    _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                          \
+      fa_[mb] = lds_read_b128(a_rd[kk_][mb] + (st_) * STAGE_BYTES);           \
+    _Pragma("unroll") for (int nbk = 0; nbk < 4; ++nbk) {                     \
+      const uint32_t p_ = b_rd[kk_][nbk] + (st_) * STAGE_BYTES;               \
+      const v4i16_t lo = lds_read_tr(p_);                                     \
+      const v4i16_t hi = lds_read_tr(p_ + 4 * B_ROW);                         \
+      fb_[nbk] = __builtin_bit_cast(                                          \
+          u32x4_t, v8i16_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}); \
     }                                                                         \
   } while (0)
+  // NMB_: 32-row blocks of this wave that hold tile rows (blocks past the
+  // tile's rows feed no stored output and are skipped)
+#define MOE_TILED_MMA(fa_, fb_, NMB_)                                         \
+  do {                                                                        \
+    _Pragma("unroll") for (int mb = 0; mb < (NMB_); ++mb)                     \
+      _Pragma("unroll") for (int nbk = 0; nbk < 4; ++nbk)                     \
+        acc[mb][nbk] = mfma32(fa_[mb], fb_[nbk], acc[mb][nbk]);               \
+  } while (0)
 
-  // one K step t in stage st_: wait for its copies (at most one later step,
-  // 6 copies per wave, still in flight), publish it, multiply, and refill
-  // the stage read one step earlier with step t + 2
-#define MOE_TILED_STEP(t_, st_)                                               \
+  // K step t_ held in stage st_; fragments of its first half are in f0*.
+  // While the second half is read, the first is multiplied; then, once the
+  // copies of step t+1 have landed (at most step t+2's 6 copies per wave
+  // still in flight) and every wave is past its reads of stage st_, that
+  // stage is refilled with step t+3 and the first half of step t+1 is read
+  // while the second half of step t is multiplied. The steady-state form
+  // (t + 3 < nsteps) has no branches, so the compiler's wait counts stay
+  // exact; the last steps take the guarded form.
+#define MOE_TILED_STEP_FULL(t_, st_, NMB_)                                    \
+  do {                                                                        \
+    MOE_TILED_READ(f1a, f1b, st_, 1);                                         \
+    MOE_TILED_MMA(f0a, f0b, NMB_);                                            \
+    MOE_TILED_ORDER(NMB_);                                                    \
+    MOE_WAIT_VMCNT(6);                                                        \
+    __syncthreads();                                                          \
+    MOE_TILED_ISSUE((t_) + 3, st_);                                           \
+    MOE_TILED_READ(f0a, f0b, ((st_) + 1) % NSTAGE, 0);                        \
+    MOE_TILED_MMA(f1a, f1b, NMB_);                                            \
+    MOE_TILED_ORDER(NMB_);                                                    \
+  } while (0)
+  // scheduling order of a half step: all LDS reads of the next fragments
+  // first, then the MFMAs on the current ones (otherwise the scheduler sinks
+  // each read next to its use and the LDS latency is exposed)
+#define MOE_TILED_ORDER(NMB_)                                                 \
+  do {                                                                        \
+    if ((NMB_) > 0) {                                                         \
+      __builtin_amdgcn_sched_group_barrier(0x100, (NMB_) + 8, 0);             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * (NMB_), 0);             \
+    }                                                                         \
+  } while (0)
+#define MOE_TILED_STEP(t_, st_, NMB_)                                         \
   do {                                                                        \
     const int t = (t_);                                                       \
-    if (t + 1 < nsteps) MOE_WAIT_VMCNT(6);                                    \
-    else MOE_WAIT_VMCNT(0);                                                   \
-    __syncthreads();                                                          \
-    MOE_TILED_COMPUTE(st_);                                                   \
-    if (t + 2 < nsteps) MOE_TILED_ISSUE(t + 2, ((st_) + 2) % NSTAGE);         \
+    if (t < nsteps) {                                                         \
+      MOE_TILED_READ(f1a, f1b, st_, 1);                                       \
+      MOE_TILED_MMA(f0a, f0b, NMB_);                                          \
+      if (t + 1 < nsteps) {                                                   \
+        if (t + 2 < nsteps) MOE_WAIT_VMCNT(6);                                \
+        else MOE_WAIT_VMCNT(0);                                               \
+        __syncthreads();                                                      \
+        if (t + 3 < nsteps) MOE_TILED_ISSUE(t + 3, st_);                      \
+        MOE_TILED_READ(f0a, f0b, ((st_) + 1) % NSTAGE, 0);                    \
+      }                                                                       \
+      MOE_TILED_MMA(f1a, f1b, NMB_);                                          \
+    }                                                                         \
+  } while (0)
+#define MOE_TILED_PIPE(NMB_)                                                  \
+  do {                                                                        \
+    int s = 0;                                                                \
+    for (; s + 5 < nsteps; s += NSTAGE) {                                     \
+      MOE_TILED_STEP_FULL(s, 0, NMB_);                                        \
+      MOE_TILED_STEP_FULL(s + 1, 1, NMB_);                                    \
+      MOE_TILED_STEP_FULL(s + 2, 2, NMB_);                                    \
+    }                                                                         \
+    MOE_TILED_STEP(s, 0, NMB_);                                               \
+    MOE_TILED_STEP(s + 1, 1, NMB_);                                           \
+    MOE_TILED_STEP(s + 2, 2, NMB_);                                           \
+    MOE_TILED_STEP(s + 3, 0, NMB_);                                           \
+    MOE_TILED_STEP(s + 4, 1, NMB_);                                           \
   } while (0)
 
   const int nsteps = K / BK;
+  // rows of this wave's 64-row half (wave-uniform)
+  const int mrows = __builtin_amdgcn_readfirstlane(tl.rows - wm * 64);
+  u32x4_t f0a[2], f0b[4], f1a[2], f1b[4];
   MOE_TILED_ISSUE(0, 0);
-  if (nsteps > 1) MOE_TILED_ISSUE(1, 1);
-  int s = 0;
-  for (; s + NSTAGE <= nsteps; s += NSTAGE) {
-    MOE_TILED_STEP(s, 0);
-    MOE_TILED_STEP(s + 1, 1);
-    MOE_TILED_STEP(s + 2, 2);
+  if (nsteps > 1) {
+    MOE_TILED_ISSUE(1, 1);
+    MOE_WAIT_VMCNT(6);
+  } else {
+    MOE_WAIT_VMCNT(0);
   }
-  if (s < nsteps) MOE_TILED_STEP(s, 0);
-  if (s + 1 < nsteps) MOE_TILED_STEP(s + 1, 1);
+  __syncthreads();
+  if (nsteps > 2) MOE_TILED_ISSUE(2, 2);
+  MOE_TILED_READ(f0a, f0b, 0, 0);
+  if (mrows > 32) MOE_TILED_PIPE(2);
+  else if (mrows > 0) MOE_TILED_PIPE(1);
+  else MOE_TILED_PIPE(0);
+#undef MOE_TILED_PIPE
+#undef MOE_TILED_STEP_FULL
+#undef MOE_TILED_ORDER
 #undef MOE_TILED_STEP
-#undef MOE_TILED_COMPUTE
+#undef MOE_TILED_MMA
+#undef MOE_TILED_READ
 #undef MOE_TILED_ISSUE
   __syncthreads();
 

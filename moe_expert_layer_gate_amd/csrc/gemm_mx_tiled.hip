@@ -8,14 +8,22 @@
 // of MoE TP优化 / 计算分解 (down(SiLU(gate(x)) * up(x)), merged gate/up).
 //
 // Block = 256 threads (2 x 2 waves), tile = 128 rows x 256 weight columns of
-// one expert, K steps of 128 through double-buffered LDS. Both operands are
-// K-contiguous in HBM and in LDS ([row][128 B] for e4m3 activations,
-// [column][64 B] for e2m1 weights, plus one 4-byte word of e8m0 scales per
-// row / column and step), so no transposition is needed anywhere.
+// one expert, K steps of 128 through a two-stage LDS ring filled by direct
+// global -> LDS copies (16 bytes per lane, no VGPRs involved). Both operands
+// are K-contiguous in HBM and in LDS, so nothing is transposed:
+//   * A (e4m3 codes): LDS [row][8 x 16 B], the 16-byte piece index XOR-ed
+//     with row % 8 so that the 16 rows one MFMA operand read touches fall on
+//     distinct bank groups;
+//   * B (e2m1 codes): LDS [column][4 x 16 B], piece index XOR-ed with
+//     (column / 4) % 4 for the same reason;
+//   * the e8m0 scales (one word = the step's four 32-K blocks per row or
+//     column) ride along in the same stage, 4 bytes per lane, and each lane
+//     reads back the byte of its K block.
 // v_mfma_scale_f32_16x16x128_f8f6f4 operand layout (lane l, q = l/16; see the
 // streaming MX kernel): A row l%16 bytes from K [16q,+16) and [64+16q,+16); B
 // column l%16 bytes from K [32q,+32); scales of K block q. Each wave owns
-// 64 rows x 128 weight columns: 4 x 8 MFMAs per step, 128 fp32 accumulators.
+// 64 rows x 128 weight columns: 4 x 8 MFMAs per step, 128 fp32 accumulators;
+// 32-row halves past the tile's rows are skipped.
 // GEMM1 tiles hold 128 gate and the 128 matching up columns; a wave takes 64
 // of each so SwiGLU and the MXFP8 quantisation of h (amax over 32 columns =
 // 16 lanes x 2 groups) stay inside the wave. Epilogues stage through LDS and
@@ -23,21 +31,30 @@
 // tiled kernel.
 #include "common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace moe {
 
 namespace {
 
 constexpr int MBM = 128, MBNW = 256, MBK = 128;
-constexpr int LDA = MBK + 16;      // 144 B per activation row in LDS
-constexpr int LDB = MBK / 2 + 16;  // 80 B per weight column in LDS
+constexpr int MA_BYTES = MBM * MBK;           // 16 KB of e4m3
+constexpr int MB_BYTES = MBNW * MBK / 2;      // 16 KB of e2m1
+constexpr int MSA = MA_BYTES + MB_BYTES;      // row scale words (512 B)
+constexpr int MSB = MSA + MBM * 4;            // column scale words (1 KB)
+constexpr int MSTAGE = MSB + MBNW * 4;        // 33.5 KB
 
-struct MxSmem {
-  uint8_t a[2][MBM][LDA];
-  uint8_t b[2][MBNW][LDB];
-  uint32_t as[2][MBM];
-  uint32_t bs[2][MBNW];
-};
+// 4 bytes per lane, global (base + lane offset) -> LDS at lds_wave_base +
+// 4 * lane; same conventions as g2lds
+MOE_DEV void g2lds4(const void* base, uint32_t voff, uint32_t lds_wave_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds_wave_base)
+      : "memory");
+}
 
 MOE_DEV f32x4 mfma_mx(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa,
@@ -47,14 +64,15 @@ MOE_DEV f32x4 mfma_mx(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
 }  // namespace
 
 template <bool GLU>
-// two blocks per CU: 2 waves per SIMD, LDS for two double-buffered tiles
+// two blocks per CU: 2 waves per SIMD, 64 KB of LDS each
 __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
     const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws,
     void* __restrict__ out, uint8_t* __restrict__ os, int K, int Nw, int Nout,
-    int nslabs) {
-  __shared__ __align__(16) MxSmem sm;
+    int nslabs, const int32_t* __restrict__ gidx,
+    const int32_t* __restrict__ gbase, int gk) {
+  __shared__ __align__(1024) uint8_t smem[2 * MSTAGE];
   const int nb = tile_count[0] * nslabs;
   const int b = blockIdx.x;
   if (b >= nb) return;
@@ -69,19 +87,15 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   const int KB = K / 32;
   const uint8_t* we = w + (size_t)tl.expert * Nw * (K / 2);
   const uint8_t* wse = ws + (size_t)tl.expert * Nw * KB;
+  // A rows: the tile's rows of the permuted codes, or with a gather index
+  // the token rows of the per-token codes (32-bit offsets, checked by the
+  // host)
+  const uint8_t* a_tile = gidx ? a : a + (size_t)tl.row0 * K;
+  const uint8_t* as_tile = gidx ? as : as + (size_t)tl.row0 * KB;
+  const int32_t* grow = gidx ? gidx + gbase[0] + tl.row0 : nullptr;
 
-  // global -> register assignment, 16-byte pieces p = tid + 256*j (j < 4):
-  // A piece p = row p/8, bytes 16*(p%8) of the step (8 lanes per 128-byte
-  // row); B piece p = tile column p/4, bytes 16*(p%4) (4 lanes per 64-byte
-  // column slice). Scales: one 4-byte word per row (tid < 128) and column.
-  size_t a_off[4];
-  int b_off[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = tid + 256 * j;
-    const int r = p >> 3;
-    a_off[j] = (size_t)(tl.row0 + (r < tl.rows ? r : 0)) * K + 16 * (p & 7);
-    const int t = p >> 2;
+  // weight column of tile column t (0..255); columns past Nout read column 0
+  auto wcol = [&](int t) -> int {
     int oc, col;
     if (GLU) {
       oc = c0 + (t & (MBNW / 2 - 1));
@@ -90,53 +104,74 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
       oc = c0 + t;
       col = oc;
     }
-    if (oc >= Nout) col = 0;  // unused columns read column 0
-    b_off[j] = col * (K / 2) + 16 * (p & 3);
-  }
-  const int sr = tid & (MBM - 1);
-  const uint32_t* as_src = (const uint32_t*)(as + (size_t)(tl.row0 + (sr < tl.rows ? sr : 0)) * KB);
-  int scol, soc;
-  if (GLU) {
-    soc = c0 + (tid & (MBNW / 2 - 1));
-    scol = tid < MBNW / 2 ? soc : Nout + soc;
-  } else {
-    soc = c0 + tid;
-    scol = soc;
-  }
-  if (soc >= Nout) scol = 0;
-  const uint32_t* bs_src = (const uint32_t*)(wse + (size_t)scol * KB);
+    return oc < Nout ? col : 0;
+  };
+  // tile rows past the tile read its row 0 (their outputs are never stored)
+  auto arow = [&](int r) -> int {
+    const int rr = r < tl.rows ? r : 0;
+    return grow ? grow[rr] / gk : rr;
+  };
 
-  // prefetch registers: plain locals in fully unrolled code (no lambda
-  // captures), so they stay in VGPRs
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-  uint32_t rsa = 0, rsb = 0;
-#define MOE_MX_GLOAD(s_)                                                    \
-  do {                                                                      \
-    const int so_ = (s_);                                                   \
-    ra0 = *(const uint4*)(a + a_off[0] + so_ * MBK);                        \
-    ra1 = *(const uint4*)(a + a_off[1] + so_ * MBK);                        \
-    ra2 = *(const uint4*)(a + a_off[2] + so_ * MBK);                        \
-    ra3 = *(const uint4*)(a + a_off[3] + so_ * MBK);                        \
-    rb0 = *(const uint4*)(we + (size_t)b_off[0] + so_ * (MBK / 2));         \
-    rb1 = *(const uint4*)(we + (size_t)b_off[1] + so_ * (MBK / 2));         \
-    rb2 = *(const uint4*)(we + (size_t)b_off[2] + so_ * (MBK / 2));         \
-    rb3 = *(const uint4*)(we + (size_t)b_off[3] + so_ * (MBK / 2));         \
-    if (tid < MBM) rsa = as_src[so_];                                       \
-    rsb = bs_src[so_];                                                      \
+  // ---- copy assignment: instruction j (0..3) of a wave moves 1 KB.
+  // A: rows 8*(4j + wave) + lane/8, physical piece lane%8 <- logical piece
+  //    (lane%8) ^ (row%8); row % 8 = lane/8 here.
+  // B: columns 16*(4j + wave) + lane/4, physical piece lane%4 <- logical
+  //    piece (lane%4) ^ ((column/4)%4); (column/4)%4 = (lane/16)%4 here.
+  uint32_t a_off[4], b_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 8 * (4 * j + wave) + (lane >> 3);
+    a_off[j] = (uint32_t)arow(r) * K + 16 * ((lane & 7) ^ (lane >> 3));
+    const int t = 16 * (4 * j + wave) + (lane >> 2);
+    b_off[j] = (uint32_t)wcol(t) * (K / 2) + 16 * ((lane & 3) ^ (lane >> 4));
+  }
+  const uint32_t lds0 = lds_addr(smem);
+  const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds0 + 8 * wave * MBK);
+  const uint32_t b_dst =
+      __builtin_amdgcn_readfirstlane(lds0 + MA_BYTES + 16 * wave * (MBK / 2));
+
+  // scale words: waves 0-1 copy rows 64*wave + lane, every wave copies
+  // tile columns 64*wave + lane
+  const uint32_t sa_doff = (uint32_t)arow((64 * wave + lane) & (MBM - 1)) * KB;
+  const uint32_t sb_doff = (uint32_t)wcol(64 * wave + lane) * KB;
+  const uint32_t sa_dst =
+      __builtin_amdgcn_readfirstlane(lds0 + MSA + 64 * 4 * (wave & 1));
+  const uint32_t sb_dst = __builtin_amdgcn_readfirstlane(lds0 + MSB + 64 * 4 * wave);
+
+  // loads of K step s_ into stage st_ (9 or 10 instructions per wave)
+#define MOE_MX_ISSUE(s_, st_)                                                 \
+  do {                                                                        \
+    const uint8_t* ab_ = a_tile + (size_t)(s_) * MBK;                         \
+    const uint8_t* bb_ = we + (size_t)(s_) * (MBK / 2);                       \
+    const uint32_t o_ = (st_) * MSTAGE;                                       \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
+      g2lds(ab_, a_off[j], a_dst + o_ + 32 * j * MBK);                        \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
+      g2lds(bb_, b_off[j], b_dst + o_ + 64 * j * (MBK / 2));                  \
+    if (wave < 2) g2lds4(as_tile + 4 * (s_), sa_doff, sa_dst + o_);           \
+    g2lds4(wse + 4 * (s_), sb_doff, sb_dst + o_);                             \
   } while (0)
-#define MOE_MX_LSTORE(buf_)                                                 \
-  do {                                                                      \
-    *(uint4*)&sm.a[buf_][(tid >> 3)][16 * (tid & 7)] = ra0;                 \
-    *(uint4*)&sm.a[buf_][(tid >> 3) + 32][16 * (tid & 7)] = ra1;            \
-    *(uint4*)&sm.a[buf_][(tid >> 3) + 64][16 * (tid & 7)] = ra2;            \
-    *(uint4*)&sm.a[buf_][(tid >> 3) + 96][16 * (tid & 7)] = ra3;            \
-    *(uint4*)&sm.b[buf_][(tid >> 2)][16 * (tid & 3)] = rb0;                 \
-    *(uint4*)&sm.b[buf_][(tid >> 2) + 64][16 * (tid & 3)] = rb1;            \
-    *(uint4*)&sm.b[buf_][(tid >> 2) + 128][16 * (tid & 3)] = rb2;           \
-    *(uint4*)&sm.b[buf_][(tid >> 2) + 192][16 * (tid & 3)] = rb3;           \
-    if (tid < MBM) sm.as[buf_][tid] = rsa;                                  \
-    sm.bs[buf_][tid] = rsb;                                                 \
-  } while (0)
+
+  // ---- operand reads. A of 16-row block mb: row wm*64 + 16*mb + lane%16,
+  // logical pieces q and 4+q; B of group g: tile column bcol(g), piece q.
+  const int lr = lane & 15, q = lane >> 4;
+  uint32_t a_rd[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    a_rd[h] = lds0 + (wm * 64 + lr) * MBK + 16 * ((4 * h + q) ^ (lr & 7));
+  auto bcol = [&](int g) -> int {
+    if (GLU) return (g < 4 ? 0 : MBNW / 2) + wn * 64 + (g & 3) * 16 + lr;
+    return wn * 128 + g * 16 + lr;
+  };
+  const uint32_t b_rd =
+      lds0 + MA_BYTES + bcol(0) * (MBK / 2) + 16 * (q ^ (lr >> 2));
+
+  // scale bytes of this lane: row wm*64 + 16*mb + lane%16 and tile column
+  // bcol(g), byte q (K block 4s + q)
+  const uint32_t sa_rd = lds0 + MSA + (wm * 64 + lr) * 4 + q;
+  const uint32_t sb_rd = lds0 + MSB + bcol(0) * 4 + q;
+#define MOE_MX_LDS_U8(a_) \
+  ((int)*(const __attribute__((address_space(3))) uint8_t*)(uintptr_t)(a_))
 
   f32x4 acc[4][8];
 #pragma unroll
@@ -144,54 +179,83 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int lr = lane & 15, q = lane >> 4;
-  // tile column of wave column wn, group g (0..7)
-  auto bcolumn = [&](int g) -> int {
-    if (GLU) return (g < 4 ? 0 : MBNW / 2) + wn * 64 + (g & 3) * 16 + lr;
-    return wn * 128 + g * 16 + lr;
-  };
-  auto compute = [&](int buf) {
-    i32x8 fa[4];
-    int sa[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int r = wm * 64 + mb * 16 + lr;
-      const uint4 v0 = *(const uint4*)&sm.a[buf][r][16 * q];
-      const uint4 v1 = *(const uint4*)&sm.a[buf][r][64 + 16 * q];
-      fa[mb] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                     (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-      sa[mb] = (sm.as[buf][r] >> (8 * q)) & 0xFF;
-    }
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int c = bcolumn(g);
-      const uint4 v = *(const uint4*)&sm.b[buf][c][16 * q];
-      const i32x8 fb = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      const int sb = (sm.bs[buf][c] >> (8 * q)) & 0xFF;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        acc[mb][g] = mfma_mx(fa[mb], fb, acc[mb][g], sa[mb], sb);
-    }
-  };
+  // one K step from stage st_ with scale words sa_/sb_; NMB_ 16-row blocks.
+  // Two halves of four column groups each: the A fragments and the first
+  // half's B fragments are read before its MFMAs, the second half's B while
+  // they run.
+#define MOE_MX_HALF(st_, NMB_, G0_)                                 \
+  do {                                                                        \
+    u32x4_t fb[4];                                                            \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g)                             \
+      fb[g] = lds_read_b128(b_rd + (st_) * MSTAGE +                           \
+                            (bcol((G0_) + g) - bcol(0)) * (MBK / 2));         \
+    if ((NMB_) > 0) {                                                         \
+      __builtin_amdgcn_sched_group_barrier(0x100, (G0_) ? 8 : 3 * (NMB_) + 8, 0); \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * (NMB_), 0);             \
+    }                                                                         \
+    _Pragma("unroll") for (int g = 0; g < 4; ++g) {                           \
+      const i32x8 b8 = i32x8{(int)fb[g].x, (int)fb[g].y, (int)fb[g].z,        \
+                             (int)fb[g].w, 0, 0, 0, 0};                       \
+      const int sbv = MOE_MX_LDS_U8(sb_rd + (st_) * MSTAGE +                  \
+                                    (bcol((G0_) + g) - bcol(0)) * 4);         \
+      _Pragma("unroll") for (int mb = 0; mb < (NMB_); ++mb)                   \
+        acc[mb][(G0_) + g] = mfma_mx(fa[mb], b8, acc[mb][(G0_) + g],          \
+                                     sa[mb], sbv);                            \
+    }                                                                         \
+  } while (0)
+#define MOE_MX_COMPUTE(st_, NMB_)                                             \
+  do {                                                                        \
+    i32x8 fa[4];                                                              \
+    int sa[4];                                                                \
+    _Pragma("unroll") for (int mb = 0; mb < (NMB_); ++mb) {                   \
+      const u32x4_t v0 = lds_read_b128(a_rd[0] + (st_) * MSTAGE + mb * 16 * MBK); \
+      const u32x4_t v1 = lds_read_b128(a_rd[1] + (st_) * MSTAGE + mb * 16 * MBK); \
+      fa[mb] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,              \
+                     (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};             \
+      sa[mb] = MOE_MX_LDS_U8(sa_rd + (st_) * MSTAGE + mb * 16 * 4);           \
+    }                                                                         \
+    MOE_MX_HALF(st_, NMB_, 0);                                                \
+    MOE_MX_HALF(st_, NMB_, 4);                                                \
+  } while (0)
+
+  // step t_: its copies landed (issued one step earlier) and every wave is
+  // done with the other stage; refill that stage with step t+1, multiply.
+#define MOE_MX_STEP(t_, st_, NMB_)                                            \
+  do {                                                                        \
+    MOE_WAIT_VMCNT(0);                                                        \
+    __syncthreads();                                                          \
+    if ((t_) + 1 < nsteps) MOE_MX_ISSUE((t_) + 1, (st_) ^ 1);                 \
+    MOE_MX_COMPUTE(st_, NMB_);                                                \
+  } while (0)
+#define MOE_MX_PIPE(NMB_)                                                     \
+  do {                                                                        \
+    int s = 0;                                                                \
+    for (; s + 1 < nsteps; s += 2) {                                          \
+      MOE_MX_STEP(s, 0, NMB_);                                                \
+      MOE_MX_STEP(s + 1, 1, NMB_);                                            \
+    }                                                                         \
+    if (s < nsteps) MOE_MX_STEP(s, 0, NMB_);                                  \
+  } while (0)
 
   const int nsteps = K / MBK;
-  MOE_MX_GLOAD(0);
-  MOE_MX_LSTORE(0);
+  MOE_MX_ISSUE(0, 0);
+  // 16-row blocks of this wave's 64 rows that hold tile rows, in pairs
+  const int mrows = __builtin_amdgcn_readfirstlane(tl.rows - wm * 64);
+  if (mrows > 32) MOE_MX_PIPE(4);
+  else if (mrows > 0) MOE_MX_PIPE(2);
+  else MOE_MX_PIPE(0);
+#undef MOE_MX_PIPE
+#undef MOE_MX_STEP
+#undef MOE_MX_COMPUTE
+#undef MOE_MX_HALF
+#undef MOE_MX_LDS_U8
+#undef MOE_MX_ISSUE
   __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) MOE_MX_GLOAD(s + 1);
-    compute(buf);
-    if (s + 1 < nsteps) MOE_MX_LSTORE(buf ^ 1);
-    __syncthreads();
-  }
-#undef MOE_MX_GLOAD
-#undef MOE_MX_LSTORE
 
   // epilogue, staged per wave in the (free) operand buffers
   if (GLU) {
     // h: 64 rows x 64 columns of e4m3 codes per wave + 2 scales per row
-    uint8_t* st = &sm.a[0][0][0] + wave * (64 * 64);
+    uint8_t* st = smem + wave * (64 * 64);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -227,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
     }
   } else {
     // y: 64 rows x 128 bf16 columns per wave (16 KB), staged 32 rows at a time
-    uint16_t* st = (uint16_t*)(&sm.a[0][0][0]) + wave * (32 * 128);
+    uint16_t* st = (uint16_t*)smem + wave * (32 * 128);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -258,7 +322,8 @@ hipError_t launch_gemm_mx_tiled(bool glu, const Tile* tiles,
                                 const uint8_t* a, const uint8_t* a_scale,
                                 const uint8_t* w, const uint8_t* w_scale,
                                 void* out, uint8_t* out_scale, int K, int Nw,
-                                int Nout, hipStream_t s) {
+                                int Nout, const int32_t* gidx,
+                                const int32_t* gbase, int gk, hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
   const int slab = glu ? MBNW / 2 : MBNW;
   const int nslabs = (Nout + slab - 1) / slab;
@@ -266,11 +331,11 @@ hipError_t launch_gemm_mx_tiled(bool glu, const Tile* tiles,
   if (glu)
     hipLaunchKernelGGL(gemm_mx_tiled_kernel<true>, grid, dim3(256), 0, s, tiles,
                        tile_count, a, a_scale, w, w_scale, out, out_scale, K,
-                       Nw, Nout, nslabs);
+                       Nw, Nout, nslabs, gidx, gbase, gk);
   else
     hipLaunchKernelGGL(gemm_mx_tiled_kernel<false>, grid, dim3(256), 0, s,
                        tiles, tile_count, a, a_scale, w, w_scale, out,
-                       out_scale, K, Nw, Nout, nslabs);
+                       out_scale, K, Nw, Nout, nslabs, gidx, gbase, gk);
   return hipGetLastError();
 }
 

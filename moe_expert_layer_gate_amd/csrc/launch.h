@@ -37,7 +37,7 @@ hipError_t launch_route_scatter(const int32_t* ids, int N, int E,
                                 const int32_t* offsets, int32_t* sorted_copy,
                                 int32_t* copy_pos, hipStream_t s);
 // Single-block routing (count + scan + tile list + scatter, optionally the
-// gate too when logits != NULL) for N <= 16384 copies and E <= 1024.
+// gate too when logits != NULL) for N <= 4096 copies and E <= 1024.
 bool route_small_ok(int N, int E);
 hipError_t launch_route_small(const float* logits, int T, int k, int32_t* ids,
                               float* wts, int N, int E, int32_t* counts,
@@ -46,6 +46,9 @@ hipError_t launch_route_small(const float* logits, int T, int k, int32_t* ids,
                               Tile* tiles, int max_tiles, int32_t* tile_count,
                               hipStream_t s);
 // act: 0 f32, 1 bf16. mx: quantise rows to MXFP8 (bf16 input only).
+// MXFP8 codes and e8m0 scales of the T rows of x (bf16), in token order.
+hipError_t launch_quantize_mx(const void* x, int T, int H, uint8_t* xq,
+                              uint8_t* xq_scale, hipStream_t s);
 hipError_t launch_route_gather(const void* x, int act, int mx, int H, int k,
                                const int32_t* sorted_copy,
                                const int32_t* offsets, int fb, int fe,
@@ -87,12 +90,15 @@ hipError_t launch_gemm_mx(bool glu, int rg, const Tile* tiles,
                           hipStream_t s);
 
 // Same operands, 128-row LDS-tiled scaled-MFMA tiles (tile list mt=128).
+// With gidx non-NULL, A rows (and their scales) are read from the per-token
+// codes: row of sorted copy i = gidx[gbase[0] + i] / gk (offsets < 2^31).
 hipError_t launch_gemm_mx_tiled(bool glu, const Tile* tiles,
                                 const int32_t* tile_count, int max_tiles,
                                 const uint8_t* a, const uint8_t* a_scale,
                                 const uint8_t* w, const uint8_t* w_scale,
                                 void* out, uint8_t* out_scale, int K, int Nw,
-                                int Nout, hipStream_t s);
+                                int Nout, const int32_t* gidx,
+                                const int32_t* gbase, int gk, hipStream_t s);
 
 hipError_t launch_finalize(const int32_t* ids, const float* w,
                            const int32_t* copy_pos, const int32_t* offsets,

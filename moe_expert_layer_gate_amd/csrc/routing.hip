@@ -126,27 +126,41 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
   // tpe threads per expert split the chunks into contiguous ranges: sum each
   // range (independent loads), scan the ranges in LDS, then rewrite every
   // chunk count as its exclusive prefix within the expert
+  // (chunk counts are read 8 at a time so that the loads overlap)
   int tpe = 1;
   while (tpe * 2 * E <= (int)blockDim.x) tpe *= 2;
   const int per = (nchunks + tpe - 1) / tpe;
   for (int e0 = 0; e0 < E; e0 += blockDim.x / tpe) {
     const int e = e0 + (int)threadIdx.x / tpe, q = threadIdx.x % tpe;
-    const bool act = e < E && (int)threadIdx.x / tpe < (int)blockDim.x / tpe;
+    const bool act = e < E;
     const int c0 = q * per, c1 = min(nchunks, c0 + per);
     int sum = 0;
     if (act)
-      for (int c = c0; c < c1; ++c) sum += cc[(size_t)c * E + e];
+      for (int c = c0; c < c1; c += 8) {
+        int v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          v[j] = c + j < c1 ? cc[(size_t)(c + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum += v[j];
+      }
     part[threadIdx.x] = sum;
     __syncthreads();
     if (act) {
       int base = 0;
       for (int j = 0; j < q; ++j) base += part[threadIdx.x - q + j];
       if (q == tpe - 1) { cnt[e] = base + sum; off[e] = base + sum; counts[e] = base + sum; }
-      for (int c = c0; c < c1; ++c) {
-        const size_t idx = (size_t)c * E + e;
-        const int v = cc[idx];
-        cc[idx] = base;
-        base += v;
+      for (int c = c0; c < c1; c += 8) {
+        int v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          v[j] = c + j < c1 ? cc[(size_t)(c + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (c + j < c1) {
+            cc[(size_t)(c + j) * E + e] = base;
+            base += v[j];
+          }
       }
     }
     __syncthreads();
@@ -213,14 +227,14 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(
   }
 }
 
-// Single-block routing for small problems (N <= 16384 copies, E <= 1024):
+// Single-block routing for small problems (N <= 4096 copies, E <= 1024):
 // optional gate (VPL > 0: waves take tokens t = wave, wave + 16, ...),
 // per-wave histograms over contiguous chunks of copies, the scans, the GEMM
 // tile list and the stable scatter, all in one launch with the counts kept
 // in LDS. Same results as gate + count + scan + scatter.
-constexpr int kSmallMaxN = 16384, kSmallMaxE = 1024;
+constexpr int kSmallMaxN = 4096, kSmallMaxE = 1024;
 
-template <int VPL>
+template <int VPL, int PER>
 __global__ __launch_bounds__(1024) void route_small_kernel(
     const float* __restrict__ logits, int T, int k, int32_t* __restrict__ ids,
     float* __restrict__ wts, int N, int E, int32_t* __restrict__ counts,
@@ -245,7 +259,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
   const int c0 = min(N, w * C), c1 = min(N, c0 + C);
   // the wave's ids stay in registers: all loads issue back to back, and the
   // count and the scatter both read them from there
-  constexpr int kPerLane = kSmallMaxN / (16 * 64);
+  constexpr int kPerLane = PER;  // copies per lane: N <= 1024 * PER
   int idr[kPerLane];
 #pragma unroll
   for (int it = 0; it < kPerLane; ++it) {
@@ -291,6 +305,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     const int e = idr[it];
     const bool valid = (unsigned)e < (unsigned)E;
     if (i < c1 && !valid) copy_pos[i] = -1;
+    // lanes holding the same expert id: intersect one ballot per id bit
     uint64_t m = ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -313,13 +328,18 @@ __global__ __launch_bounds__(256) void route_gather_kernel(
     const void* __restrict__ x, int H, int k,
     const int32_t* __restrict__ sorted_copy,
     const int32_t* __restrict__ offsets, int fb, int fe,
-    void* __restrict__ xp, uint8_t* __restrict__ xs) {
+    void* __restrict__ xp, uint8_t* __restrict__ xs, int nrows) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int r0 = offsets[fb];
-  const int R = offsets[fe] - r0;
-  if (r >= R) return;
-  const int t = sorted_copy[r0 + r] / k;
+  // without a permutation row r is token r (rows quantised in place order)
+  int t = r;
+  if (sorted_copy) {
+    const int r0 = offsets[fb];
+    if (r >= offsets[fe] - r0) return;
+    t = sorted_copy[r0 + r] / k;
+  } else if (r >= nrows) {
+    return;
+  }
   if (ACT == 0) {  // fp32: 8 floats = two 16-byte chunks per step
     const uint4* src = (const uint4*)((const float*)x + (size_t)t * H);
     uint4* dst = (uint4*)((float*)xp + (size_t)r * H);
@@ -402,23 +422,40 @@ hipError_t launch_route_small(const float* logits, int T, int k, int32_t* ids,
                               Tile* tiles, int max_tiles, int32_t* tile_count,
                               hipStream_t s) {
   const int vpl = logits ? (E + 63) / 64 : 0;
-#define MOE_SMALL_CASE(V)                                                      \
-  if (vpl <= V) {                                                              \
-    hipLaunchKernelGGL(route_small_kernel<V>, dim3(1), dim3(1024), 0, s,       \
+  const int per = N <= 1024 ? 1 : 4;
+#define MOE_SMALL_CASE(V, P)                                                   \
+  if (vpl <= V && per == P) {                                                  \
+    hipLaunchKernelGGL((route_small_kernel<V, P>), dim3(1), dim3(1024), 0, s,  \
                        logits, T, k, ids, wts, N, E, counts, offsets,          \
                        sorted_copy, copy_pos, fb, fe, mt, tiles, max_tiles,    \
                        tile_count);                                            \
     return hipGetLastError();                                                  \
   }
-  MOE_SMALL_CASE(0)
-  MOE_SMALL_CASE(1)
-  MOE_SMALL_CASE(2)
-  MOE_SMALL_CASE(4)
-  MOE_SMALL_CASE(8)
-  MOE_SMALL_CASE(12)
-  MOE_SMALL_CASE(16)
+  MOE_SMALL_CASE(0, 1)
+  MOE_SMALL_CASE(0, 4)
+  MOE_SMALL_CASE(1, 1)
+  MOE_SMALL_CASE(1, 4)
+  MOE_SMALL_CASE(2, 1)
+  MOE_SMALL_CASE(2, 4)
+  MOE_SMALL_CASE(4, 1)
+  MOE_SMALL_CASE(4, 4)
+  MOE_SMALL_CASE(8, 1)
+  MOE_SMALL_CASE(8, 4)
+  MOE_SMALL_CASE(12, 1)
+  MOE_SMALL_CASE(12, 4)
+  MOE_SMALL_CASE(16, 1)
+  MOE_SMALL_CASE(16, 4)
 #undef MOE_SMALL_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize_mx(const void* x, int T, int H, uint8_t* xq,
+                              uint8_t* xq_scale, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL((route_gather_kernel<1, true>), dim3((T + 3) / 4),
+                     dim3(256), 0, s, x, H, 1, nullptr, nullptr, 0, 0, xq,
+                     xq_scale, T);
+  return hipGetLastError();
 }
 
 hipError_t launch_route_gather(const void* x, int act, int mx, int H, int k,
@@ -430,13 +467,13 @@ hipError_t launch_route_gather(const void* x, int act, int mx, int H, int k,
   dim3 grid((max_rows + 3) / 4), block(256);
   if (act == 0)
     hipLaunchKernelGGL((route_gather_kernel<0, false>), grid, block, 0, s, x,
-                       H, k, sorted_copy, offsets, fb, fe, x_perm, x_scale);
+                       H, k, sorted_copy, offsets, fb, fe, x_perm, x_scale, 0);
   else if (!mx)
     hipLaunchKernelGGL((route_gather_kernel<1, false>), grid, block, 0, s, x,
-                       H, k, sorted_copy, offsets, fb, fe, x_perm, x_scale);
+                       H, k, sorted_copy, offsets, fb, fe, x_perm, x_scale, 0);
   else
     hipLaunchKernelGGL((route_gather_kernel<1, true>), grid, block, 0, s, x,
-                       H, k, sorted_copy, offsets, fb, fe, x_perm, x_scale);
+                       H, k, sorted_copy, offsets, fb, fe, x_perm, x_scale, 0);
   return hipGetLastError();
 }
 
