@@ -38,6 +38,67 @@ PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "mx": 5000.0, "f32": 157.3}
 
 
+# HBM bytes of one launch of the dominant kernel, from two rocprofv3 --pmc
+# runs of this script (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch,
+# averaged over the timed dispatches), each scaled by what the same counter
+# reads for a plain device copy of known size (--copy-calibration): a
+# 256 MiB copy reads FETCH_SIZE = 131080 KiB (factor 2.0) and WRITE_SIZE =
+# 262144 KiB (factor 1.0). An entry holds only while the kernel's sources
+# hash to the recorded value; otherwise traffic is reported as null.
+COPY_FACTORS = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+KERNEL_SOURCES = {
+    "gemm_bf16_stream": ["gemm_bf16_stream.hip", "common.h", "launch.h"],
+    "gemm_bf16_tiled": ["gemm_bf16_tiled.hip", "lds_dma.h", "common.h", "launch.h"],
+    "gemm_mx_tiled": ["gemm_mx_tiled.hip", "lds_dma.h", "common.h", "launch.h"],
+}
+TRAFFIC = {
+    # workload: (kernel source set, sha256[:16] of its sources, FETCH KiB,
+    #            WRITE KiB) per GEMM1 dispatch
+    "qwen3_30b_a3b_decode_bf16":
+        ("gemm_bf16_stream", "dc15f36c5323b571", 342751.7, 384.0),
+    "qwen3_30b_a3b_prefill_skewed_bf16":
+        ("gemm_bf16_tiled", "a4d23f5ad3b14398", 586087.7, 49152.0),
+    "longcat_flash_zero_experts_bf16":
+        ("gemm_bf16_stream", "dc15f36c5323b571", 13270927.4, 32528.0),
+    "qwen3_235b_a22b_ep_rank_w4a8":
+        ("gemm_mx_tiled", "f689ae886ad82391", 197958.9, 12932.8),
+}
+
+
+def _sources_sha(kind):
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_expert_layer_gate_amd", "csrc")
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload):
+    ent = TRAFFIC.get(workload)
+    if ent is None:
+        return None
+    kind, sha, fetch_kib, write_kib = ent
+    if _sources_sha(kind) != sha:
+        return None
+    return int((fetch_kib * COPY_FACTORS["FETCH_SIZE"] +
+                write_kib * COPY_FACTORS["WRITE_SIZE"]) * 1024)
+
+
+def _copy_calibration():
+    """A plain device copy of 256 MiB, five times: the reference dispatch for
+    scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "dispatches": 5}), flush=True)
+
+
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -48,6 +109,10 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the reference copy for counter scaling")
+    ap.add_argument("--print-source-sha", action="store_true",
+                    help="print the source hashes that key the traffic table")
     return ap.parse_args()
 
 
@@ -154,6 +219,12 @@ def main():
               "path (the expert-parallel case is one rank's expert range on "
               "one GPU). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.print_source_sha:
+        print(json.dumps({k: _sources_sha(k) for k in KERNEL_SOURCES}))
+        return
+    if args.copy_calibration:
+        _copy_calibration()
+        return
     import torch
 
     import moe_expert_layer_gate_amd as m
@@ -224,12 +295,13 @@ def main():
         ach = nbytes / dur / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "traffic": None}
+                "traffic": _traffic(shape.name)}
     else:
         ach = flops / dur / 1e12
         peak = PEAK_TFLOPS[kind]
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                "traffic": _traffic(shape.name)}
     roof.update({"kernel": "gemm1_swiglu", "avg_us": round(gemm1_us, 2),
                  "algorithmic_bytes": int(nbytes), "algorithmic_flops": flops,
                  "touched_experts": touched, "routed_rows": R})

@@ -81,7 +81,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
   const int slab = L % nslabs;
   const int c0 = slab * (GLU ? BNW / 2 : BNW);  // first output column
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
   const uint16_t* we = w + (size_t)tl.expert * K * Nw;
 

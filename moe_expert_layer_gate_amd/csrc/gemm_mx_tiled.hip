@@ -82,7 +82,8 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   const int slab = L % nslabs;
   const int c0 = slab * (GLU ? MBNW / 2 : MBNW);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
   const int KB = K / 32;
   const uint8_t* we = w + (size_t)tl.expert * Nw * (K / 2);
