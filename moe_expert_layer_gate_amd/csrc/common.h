@@ -95,8 +95,34 @@ MOE_DEV uint32_t e4m3_encode_scaled(float v, int s) {
   return sign | n;
 }
 
+// Same code as e4m3_encode_scaled, with fp32 arithmetic and no branches:
+// w = v * 2^-s is exact whenever it matters (|w| < 2^9 inside an MX block;
+// results below the fp32 normal range are far under e4m3's smallest step and
+// encode as zero either way). Subnormal range (|w| < 2^-6): the magic-number
+// add rounds |w| * 2^9 to an integer ties-to-even, and 8 lands on the code of
+// the smallest normal. Normal range: rounding the fp32 bits at mantissa bit
+// 20 (ties to even) leaves exponent and 3 mantissa bits, rebiased from 127 to
+// 7; codes past 0x7E (448) saturate.
+MOE_DEV uint32_t e4m3_encode_fast(float v, int s) {
+  const float w = __builtin_amdgcn_ldexpf(v, -s);
+  const uint32_t sign = (__float_as_uint(w) >> 24) & 0x80u;
+  const float a = __builtin_fabsf(w);
+  const uint32_t sub = (uint32_t)((a * 512.0f + 8388608.0f) - 8388608.0f);
+  uint32_t u = __float_as_uint(a);
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  uint32_t nrm = (u >> 20) - (120u << 3);
+  nrm = nrm > 0x7Eu ? 0x7Eu : nrm;
+  return sign | (a < 0.015625f ? sub : nrm);
+}
+
 // ---------------------------------------------------------------- misc
 
 MOE_DEV float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// SiLU with the hardware exp2 and reciprocal (a few ulp; for epilogues whose
+// result is rounded to bf16 or quantised right away).
+MOE_DEV float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 }  // namespace moe

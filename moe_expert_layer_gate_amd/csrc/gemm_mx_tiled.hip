@@ -12,8 +12,8 @@
 // global -> LDS copies (16 bytes per lane, no VGPRs involved). Both operands
 // are K-contiguous in HBM and in LDS, so nothing is transposed:
 //   * A (e4m3 codes): LDS [row][8 x 16 B], the 16-byte piece index XOR-ed
-//     with row % 8 so that the 16 rows one MFMA operand read touches fall on
-//     distinct bank groups;
+//     with (row / 2) % 8: with 128-byte rows, the 16 rows one MFMA operand
+//     read touches then cover all 64 banks once (row parity picks the half);
 //   * B (e2m1 codes): LDS [column][4 x 16 B], piece index XOR-ed with
 //     (column / 4) % 4 for the same reason;
 //   * the e8m0 scales (one word = the step's four 32-K blocks per row or
@@ -115,14 +115,15 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
 
   // ---- copy assignment: instruction j (0..3) of a wave moves 1 KB.
   // A: rows 8*(4j + wave) + lane/8, physical piece lane%8 <- logical piece
-  //    (lane%8) ^ (row%8); row % 8 = lane/8 here.
+  //    (lane%8) ^ ((row/2)%8); (row/2)%8 = 4*(wave%2) + lane/16 here.
   // B: columns 16*(4j + wave) + lane/4, physical piece lane%4 <- logical
   //    piece (lane%4) ^ ((column/4)%4); (column/4)%4 = (lane/16)%4 here.
   uint32_t a_off[4], b_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 8 * (4 * j + wave) + (lane >> 3);
-    a_off[j] = (uint32_t)arow(r) * K + 16 * ((lane & 7) ^ (lane >> 3));
+    a_off[j] = (uint32_t)arow(r) * K +
+               16 * ((lane & 7) ^ (4 * (wave & 1) + (lane >> 4)));
     const int t = 16 * (4 * j + wave) + (lane >> 2);
     b_off[j] = (uint32_t)wcol(t) * (K / 2) + 16 * ((lane & 3) ^ (lane >> 4));
   }
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   uint32_t a_rd[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
-    a_rd[h] = lds0 + (wm * 64 + lr) * MBK + 16 * ((4 * h + q) ^ (lr & 7));
+    a_rd[h] = lds0 + (wm * 64 + lr) * MBK + 16 * ((4 * h + q) ^ (lr >> 1));
   auto bcol = [&](int g) -> int {
     if (GLU) return (g < 4 ? 0 : MBNW / 2) + wn * 64 + (g & 3) * 16 + lr;
     return wn * 128 + g * 16 + lr;
@@ -264,15 +265,15 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
         const int r = mb * 16 + 4 * q + e;  // row within the wave's 64
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) {
-          const float h0 = silu(acc[mb][2 * bb][e]) * acc[mb][2 * bb + 4][e];
-          const float h1 = silu(acc[mb][2 * bb + 1][e]) * acc[mb][2 * bb + 5][e];
+          const float h0 = silu_fast(acc[mb][2 * bb][e]) * acc[mb][2 * bb + 4][e];
+          const float h1 = silu_fast(acc[mb][2 * bb + 1][e]) * acc[mb][2 * bb + 5][e];
           float amax = fmaxf(fabsf(h0), fabsf(h1));
 #pragma unroll
           for (int off = 1; off < 16; off <<= 1)
             amax = fmaxf(amax, __shfl_xor(amax, off));
           const int sx = mx_e4m3_scale_exp(amax);
-          st[r * 64 + 32 * bb + lr] = (uint8_t)e4m3_encode_scaled(h0, sx);
-          st[r * 64 + 32 * bb + 16 + lr] = (uint8_t)e4m3_encode_scaled(h1, sx);
+          st[r * 64 + 32 * bb + lr] = (uint8_t)e4m3_encode_fast(h0, sx);
+          st[r * 64 + 32 * bb + 16 + lr] = (uint8_t)e4m3_encode_fast(h1, sx);
           const int row = wm * 64 + r;
           const int cb = c0 + wn * 64 + 32 * bb;
           if (lr == 0 && row < tl.rows && cb < Nout)
