@@ -6,9 +6,12 @@
 // Atlas A3 clusters", MoE模块 / Decode阶段优化: a zero-compute expert returns
 // its input, MoE(x) = x.
 //
-// One block per token; each thread owns 8 consecutive columns (16 bytes of
-// bf16) and sums in fp32 from the residual, in slot order j = 0..k-1, then
-// rounds once. Copies of experts outside [lb, le) add nothing.
+// One block per token. The token's k slots are resolved once (into LDS) to
+// a source row: its expert output row in y, its own x row for an identity
+// expert, or nothing for an expert outside [lb, le); the slots that add
+// something are compacted in slot order. Each thread owns 8 consecutive
+// columns (16 bytes of bf16), loads the rows of 8 kept slots at a time and
+// sums in fp32 from the residual, in slot order j = 0..k-1, then rounds once.
 #include "common.h"
 #include "launch.h"
 
@@ -29,6 +32,12 @@ MOE_DEV void load8(const void* base, size_t row, int H, int c, float f[8]) {
   }
 }
 
+// Source row of each of a token's k slots, decided once per token: a row of
+// y (>= 0), the token's own x row (kIdentity) or nothing (kDropped).
+constexpr int kIdentity = -1, kDropped = -2;
+constexpr int kMaxSlots = 64;
+constexpr int kBatch = 8;  // slots whose rows are loaded together
+
 template <int ACT>
 __global__ __launch_bounds__(256) void finalize_kernel(
     const int32_t* __restrict__ ids, const float* __restrict__ wts,
@@ -36,8 +45,31 @@ __global__ __launch_bounds__(256) void finalize_kernel(
     int fb, int n_ffn, int lb, int le, const void* __restrict__ y,
     const void* __restrict__ x, const void* __restrict__ residual,
     void* __restrict__ out, int H, int k) {
+  __shared__ int32_t s_row[kMaxSlots];
+  __shared__ float s_w[kMaxSlots];
+  __shared__ int32_t s_n;
   const int t = blockIdx.x;
-  const int r0 = offsets[fb];
+  // wave 0 keeps the slots that add something, in slot order (k <= 64)
+  if (threadIdx.x < 64) {
+    const int j = threadIdx.x;
+    int row = kDropped;
+    float wj = 0.f;
+    if (j < k) {
+      const int e = ids[t * k + j];
+      if (e >= lb && e < le)
+        row = e >= n_ffn ? kIdentity : copy_pos[t * k + j] - offsets[fb];
+      wj = wts[t * k + j];
+    }
+    const uint64_t keep = ballot(row != kDropped);
+    if (row != kDropped) {
+      const int pos = popc64(keep & lanemask_lt());
+      s_row[pos] = row;
+      s_w[pos] = wj;
+    }
+    if (j == 0) s_n = popc64(keep);
+  }
+  __syncthreads();
+  const int n = s_n;
   for (int c = threadIdx.x; c < H / 8; c += blockDim.x) {
     float acc[8];
     if (residual) {
@@ -46,17 +78,27 @@ __global__ __launch_bounds__(256) void finalize_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     }
-    for (int j = 0; j < k; ++j) {
-      const int e = ids[t * k + j];
-      if (e < lb || e >= le) continue;
-      const float wj = wts[t * k + j];
-      float v[8];
-      if (e >= n_ffn)
-        load8<ACT>(x, t, H, c, v);
-      else
-        load8<ACT>(y, (size_t)(copy_pos[t * k + j] - r0), H, c, v);
+    for (int j0 = 0; j0 < n; j0 += kBatch) {
+      // rows of up to kBatch kept slots in flight together (entries past n
+      // re-read the first kept row and are not added), then the fp32 sum in
+      // slot order
+      float v[kBatch][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+      for (int jj = 0; jj < kBatch; ++jj) {
+        const int j = j0 + jj;
+        const int row = s_row[j < n ? j : 0];
+        const bool from_y = row >= 0;
+        load8<ACT>(from_y ? y : x, from_y ? (size_t)row : (size_t)t, H, c,
+                   v[jj]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < kBatch; ++jj) {
+        if (j0 + jj < n) {
+          const float wj = s_w[j0 + jj];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[jj][i], acc[i]);
+        }
+      }
     }
     if (ACT == 0) {
       float4* p = (float4*)((float*)out + (size_t)t * H) + 2 * c;

@@ -7,10 +7,18 @@
 // (all experts in one grouped operator); prefill operators are compute-bound
 // (Prefill优化 / 并行策略选择).
 //
-// Block = 256 threads (2 x 2 waves) computing a 128-row x 256-weight-column
-// tile of one expert, K in steps of 32 through a 3-stage LDS ring filled by
-// direct global->LDS loads (global_load_lds_dwordx4: lane l of a wave lands
-// at the wave's LDS base + 16*l, no VGPRs involved), two steps in flight:
+// Block = 256 threads (2 x 2 waves) computing a (2*WR)-row x 256-weight-column
+// tile of one expert, K in steps of 32 through an LDS ring filled by direct
+// global->LDS loads (global_load_lds_dwordx4: lane l of a wave lands at the
+// wave's LDS base + 16*l, no VGPRs involved). Two shapes:
+//   * WR = 64: 128-row tiles, 3-stage ring (two steps in flight), two blocks
+//     per CU, 128 fp32 accumulators per lane;
+//   * WR = 128: 256-row tiles, 4-stage ring (three steps in flight), one
+//     block per CU, 256 accumulators per lane (in the accumulation registers)
+//     -- half the LDS operand reads and half the L2 -> LDS bytes per flop
+//     of the 128-row shape, which matters because MI355X's MFMA rate per CU
+//     outruns both (the LDS instruction issue of the transposing B reads
+//     most of all).
 //   * A (activation rows, K contiguous): LDS [row][4 x 16 B], the 16-byte
 //     piece index XOR-swizzled with (row/4)%4 so the MFMA reads of 8
 //     consecutive rows hit 8 different bank groups;
@@ -20,8 +28,8 @@
 //     columns n0 + 4*(s%4) .. +3, and lane j receives column n0 + j at rows
 //     kb .. kb+3 (transpose semantics measured with an in-bounds probe); two
 //     such reads form the 8 consecutive K of an MFMA B fragment;
-//   * v_mfma_f32_32x32x16_bf16: each wave owns 64 rows x 128 weight columns
-//     (2 x 4 blocks of 32 x 32, 128 fp32 accumulators);
+//   * v_mfma_f32_32x32x16_bf16: each wave owns WR rows x 128 weight columns
+//     (WR/32 x 4 blocks of 32 x 32);
 //   * GEMM1 tiles hold 128 gate columns and the 128 matching up columns; a
 //     wave takes 64 of each, so SwiGLU is lane-local in the epilogue;
 //   * the epilogue stages each wave's 32-row slice through LDS and writes
@@ -40,11 +48,22 @@ namespace {
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
-constexpr int BM = 128, BNW = 256, BK = 32, NSTAGE = 3;
-constexpr int A_BYTES = BM * BK * 2;            // 8 KB
+constexpr int BNW = 256, BK = 32;
 constexpr int B_BYTES = BK * BNW * 2;           // 16 KB
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;  // 24 KB
 constexpr int B_ROW = BNW * 2;                  // 512 B
+
+// Tile geometry for wave-row count WR (64 or 128).
+template <int WR>
+struct TiledCfg {
+  static constexpr int BM = 2 * WR;                      // tile rows
+  static constexpr int NMB = WR / 32;                    // 32-row blocks per wave
+  static constexpr int NSTAGE = WR == 128 ? 4 : 3;       // LDS ring depth
+  static constexpr int A_BYTES = BM * BK * 2;            // 8 / 16 KB
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;  // 24 / 32 KB
+  static constexpr int NA = BM / 64;                     // A copies per wave
+  static constexpr int NI = NA + 4;                      // copies per wave and step
+  static constexpr int BLOCKS_PER_CU = WR == 128 ? 1 : 2;
+};
 
 MOE_DEV f32x16 mfma32(u32x4_t a, u32x4_t b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -62,21 +81,21 @@ MOE_DEV int swz_b(int k) { return 4 * (k & 3); }
 
 }  // namespace
 
-// two blocks per CU: 2 waves per SIMD, LDS for two 3-stage rings
-template <bool GLU>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
-    const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
+// One (tile, slab) work item L of the grid's list: tile L / nslabs, weight
+// slab L % nslabs. smem is the block's LDS ring; the item starts and ends
+// with every wave past its LDS accesses of the previous item.
+template <bool GLU, int WR>
+MOE_DEV void tiled_item(
+    uint8_t* smem, int L, const Tile* __restrict__ tiles,
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ w,
     uint16_t* __restrict__ out, int K, int Nw, int Nout, int nslabs,
     const int32_t* __restrict__ gidx, const int32_t* __restrict__ gbase,
     int gk) {
-  __shared__ __align__(1024) uint8_t smem[NSTAGE * STAGE_BYTES];
-  // XCD-aware remap of the active blocks (dispatch is round-robin over 8 XCDs)
-  const int nb = tile_count[0] * nslabs;
-  const int b = blockIdx.x;
-  if (b >= nb) return;
-  const int per = nb / 8, rem = nb % 8, xcd = b % 8;
-  const int L = xcd * per + min(xcd, rem) + b / 8;
+  using C = TiledCfg<WR>;
+  constexpr int BM = C::BM, NMB = C::NMB, NSTAGE = C::NSTAGE;
+  constexpr int A_BYTES = C::A_BYTES, STAGE_BYTES = C::STAGE_BYTES;
+  constexpr int NA = C::NA, NI = C::NI;
+  (void)BM;
   const Tile tl = tiles[L / nslabs];
   const int slab = L % nslabs;
   const int c0 = slab * (GLU ? BNW / 2 : BNW);  // first output column
@@ -87,23 +106,19 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
   const uint16_t* we = w + (size_t)tl.expert * K * Nw;
 
   // ---- global -> LDS assignment (per wave instruction: 1 KB contiguous)
-  // A, instruction j (0..1): tile rows 16*(wave + 4j) + lane/4, physical
+  // A, instruction j (0..NA-1): tile rows 16*(wave + 4j) + lane/4, physical
   // piece lane%4 holds logical piece (lane%4) ^ swz_a(row)
   // With a gather index the rows come straight from x (row of sorted copy
   // i = token sorted_copy[i] / k; the host keeps x under 4 GB so 32-bit
   // offsets hold), otherwise from the permuted rows of this tile.
   const uint16_t* a_tile = gidx ? a : a + (size_t)tl.row0 * K;  // uniform
-  uint32_t a_off0, a_off1;
-  {
-    const int r0 = 16 * wave + (lane >> 2), r1 = r0 + 64;
-    int s0 = r0 < tl.rows ? r0 : 0, s1 = r1 < tl.rows ? r1 : 0;
-    if (gidx) {
-      const int g0 = gbase[0] + tl.row0;
-      s0 = gidx[g0 + s0] / gk;
-      s1 = gidx[g0 + s1] / gk;
-    }
-    a_off0 = ((uint32_t)s0 * K + 8 * ((lane & 3) ^ swz_a(r0))) * 2u;
-    a_off1 = ((uint32_t)s1 * K + 8 * ((lane & 3) ^ swz_a(r1))) * 2u;
+  uint32_t a_off[NA];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int r = 16 * (wave + 4 * j) + (lane >> 2);
+    int src = r < tl.rows ? r : 0;
+    if (gidx) src = gidx[gbase[0] + tl.row0 + src] / gk;
+    a_off[j] = ((uint32_t)src * K + 8 * ((lane & 3) ^ swz_a(r))) * 2u;
   }
   // B, instruction j (0..3): k-row 2*(wave + 4j) + lane/32 of the step,
   // physical piece lane%32 holds logical piece (lane%32) ^ swz_b(k); the
@@ -131,23 +146,23 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
   const size_t b_step = (size_t)BK * Nw * 2;     // bytes per K step of B
   const uint32_t b_row8 = 8u * Nw * 2;          // 8 k-rows of B
 
-  // loads of K step s_ into stage st_ (6 instructions per wave)
+  // loads of K step s_ into stage st_ (NI instructions per wave)
 #define MOE_TILED_ISSUE(s_, st_)                                              \
   do {                                                                        \
     const char* ab_ = (const char*)a_tile + (size_t)(s_) * (BK * 2);         \
     const char* bb_ = (const char*)we + (size_t)(s_) * b_step;               \
     const uint32_t o_ = (st_) * STAGE_BYTES;                                  \
-    g2lds(ab_, a_off0, a_dst + o_);                                           \
-    g2lds(ab_, a_off1, a_dst + o_ + 64 * (BK * 2));                           \
+    _Pragma("unroll") for (int j = 0; j < NA; ++j)                            \
+      g2lds(ab_, a_off[j], a_dst + o_ + 64 * j * (BK * 2));                   \
     g2lds(bb_, b_off, b_dst + o_);                                            \
     g2lds(bb_, b_off + b_row8, b_dst + o_ + 8 * B_ROW);                       \
     g2lds(bb_, b_off + 2 * b_row8, b_dst + o_ + 16 * B_ROW);                  \
     g2lds(bb_, b_off + 3 * b_row8, b_dst + o_ + 24 * B_ROW);                  \
   } while (0)
 
-  f32x16 acc[2][4];
+  f32x16 acc[NMB][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NMB; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -155,12 +170,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
 
   // LDS read offsets, loop invariant (stage offsets are immediates below)
   const int lr = lane & 31, lh = lane >> 5;
-  uint32_t a_rd[2][2];  // [kk][mb]
+  uint32_t a_rd[2][NMB];  // [kk][mb]
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int m = wm * 64 + mb * 32 + lr;
+    for (int mb = 0; mb < NMB; ++mb) {
+      const int m = wm * WR + mb * 32 + lr;
       a_rd[kk][mb] = lds_addr(smem) + m * (BK * 2) + 16 * ((kk * 2 + lh) ^ swz_a(m));
     }
   // transpose reads: group g = lane/16, source lane s = lane%16 supplies row
@@ -178,12 +193,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
                       16 * ((col >> 3) ^ swz_b(kr)) + 2 * (col & 7);
     }
 
-  // fragments of one half step (16 K): A for the wave's two 32-row blocks,
+  // fragments of one half step (16 K): A for the wave's 32-row blocks,
   // B for its four 32-column blocks; two register sets so that the LDS reads
   // of the next half step overlap the MFMAs of the current one
 #define MOE_TILED_READ(fa_, fb_, st_, kk_)                                    \
   do {                                                                        \
-    _Pragma("unroll") for (int mb = 0; mb < 2; ++mb)                          \
+    _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb)                        \
       fa_[mb] = lds_read_b128(a_rd[kk_][mb] + (st_) * STAGE_BYTES);           \
     _Pragma("unroll") for (int nbk = 0; nbk < 4; ++nbk) {                     \
       const uint32_t p_ = b_rd[kk_][nbk] + (st_) * STAGE_BYTES;               \
@@ -202,22 +217,23 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
         acc[mb][nbk] = mfma32(fa_[mb], fb_[nbk], acc[mb][nbk]);               \
   } while (0)
 
-  // K step t_ held in stage st_; fragments of its first half are in f0*.
-  // While the second half is read, the first is multiplied; then, once the
-  // copies of step t+1 have landed (at most step t+2's 6 copies per wave
-  // still in flight) and every wave is past its reads of stage st_, that
-  // stage is refilled with step t+3 and the first half of step t+1 is read
-  // while the second half of step t is multiplied. The steady-state form
-  // (t + 3 < nsteps) has no branches, so the compiler's wait counts stay
-  // exact; the last steps take the guarded form.
+  // K step t_ held in stage st_ (= t_ % NSTAGE); fragments of its first half
+  // are in f0*. While the second half is read, the first is multiplied; then,
+  // once the copies of step t+1 have landed (steps t+2 .. t+NSTAGE-1, NI
+  // copies per wave each, may still be in flight) and every wave is past its
+  // reads of stage st_, that stage is refilled with step t+NSTAGE and the
+  // first half of step t+1 is read while the second half of step t is
+  // multiplied. The steady-state form (t + NSTAGE < nsteps) has no branches,
+  // so the compiler's wait counts stay exact; the last steps take the
+  // guarded form.
 #define MOE_TILED_STEP_FULL(t_, st_, NMB_)                                    \
   do {                                                                        \
     MOE_TILED_READ(f1a, f1b, st_, 1);                                         \
     MOE_TILED_MMA(f0a, f0b, NMB_);                                            \
     MOE_TILED_ORDER(NMB_);                                                    \
-    MOE_WAIT_VMCNT(6);                                                        \
+    MOE_WAIT_VMCNT((NSTAGE - 2) * NI);                                        \
     __syncthreads();                                                          \
-    MOE_TILED_ISSUE((t_) + 3, st_);                                           \
+    MOE_TILED_ISSUE((t_) + NSTAGE, st_);                                      \
     MOE_TILED_READ(f0a, f0b, ((st_) + 1) % NSTAGE, 0);                        \
     MOE_TILED_MMA(f1a, f1b, NMB_);                                            \
     MOE_TILED_ORDER(NMB_);                                                    \
@@ -232,6 +248,15 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, 4 * (NMB_), 0);             \
     }                                                                         \
   } while (0)
+  // wait until step t+1 has landed: the copies of steps t+2 .. up to
+  // min(t + NSTAGE - 1, nsteps - 1) may stay in flight
+#define MOE_TILED_WAIT_NEXT(t_)                                               \
+  do {                                                                        \
+    const int pend_ = min(NSTAGE - 2, nsteps - 2 - (t_));                     \
+    if (NSTAGE > 3 && pend_ >= 2) MOE_WAIT_VMCNT(2 * NI);                     \
+    else if (pend_ >= 1) MOE_WAIT_VMCNT(NI);                                  \
+    else MOE_WAIT_VMCNT(0);                                                   \
+  } while (0)
 #define MOE_TILED_STEP(t_, st_, NMB_)                                         \
   do {                                                                        \
     const int t = (t_);                                                       \
@@ -239,10 +264,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
       MOE_TILED_READ(f1a, f1b, st_, 1);                                       \
       MOE_TILED_MMA(f0a, f0b, NMB_);                                          \
       if (t + 1 < nsteps) {                                                   \
-        if (t + 2 < nsteps) MOE_WAIT_VMCNT(6);                                \
-        else MOE_WAIT_VMCNT(0);                                               \
+        MOE_TILED_WAIT_NEXT(t);                                               \
         __syncthreads();                                                      \
-        if (t + 3 < nsteps) MOE_TILED_ISSUE(t + 3, st_);                      \
+        if (t + NSTAGE < nsteps) MOE_TILED_ISSUE(t + NSTAGE, st_);            \
         MOE_TILED_READ(f0a, f0b, ((st_) + 1) % NSTAGE, 0);                    \
       }                                                                       \
       MOE_TILED_MMA(f1a, f1b, NMB_);                                          \
@@ -251,37 +275,36 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
 #define MOE_TILED_PIPE(NMB_)                                                  \
   do {                                                                        \
     int s = 0;                                                                \
-    for (; s + 5 < nsteps; s += NSTAGE) {                                     \
-      MOE_TILED_STEP_FULL(s, 0, NMB_);                                        \
-      MOE_TILED_STEP_FULL(s + 1, 1, NMB_);                                    \
-      MOE_TILED_STEP_FULL(s + 2, 2, NMB_);                                    \
+    for (; s + 2 * NSTAGE - 1 < nsteps; s += NSTAGE) {                        \
+      _Pragma("unroll") for (int i = 0; i < NSTAGE; ++i)                      \
+        MOE_TILED_STEP_FULL(s + i, i, NMB_);                                  \
     }                                                                         \
-    MOE_TILED_STEP(s, 0, NMB_);                                               \
-    MOE_TILED_STEP(s + 1, 1, NMB_);                                           \
-    MOE_TILED_STEP(s + 2, 2, NMB_);                                           \
-    MOE_TILED_STEP(s + 3, 0, NMB_);                                           \
-    MOE_TILED_STEP(s + 4, 1, NMB_);                                           \
+    _Pragma("unroll") for (int i = 0; i < 2 * NSTAGE - 1; ++i)                \
+      MOE_TILED_STEP(s + i, i % NSTAGE, NMB_);                                \
   } while (0)
 
   const int nsteps = K / BK;
-  // rows of this wave's 64-row half (wave-uniform)
-  const int mrows = __builtin_amdgcn_readfirstlane(tl.rows - wm * 64);
-  u32x4_t f0a[2], f0b[4], f1a[2], f1b[4];
+  // rows of this wave's WR-row part of the tile (wave-uniform)
+  const int mrows = __builtin_amdgcn_readfirstlane(tl.rows - wm * WR);
+  u32x4_t f0a[NMB], f0b[4], f1a[NMB], f1b[4];
+  // prologue: steps 0 .. NSTAGE-2 in flight, wait for step 0, then the last
+  // stage gets step NSTAGE-1
   MOE_TILED_ISSUE(0, 0);
-  if (nsteps > 1) {
-    MOE_TILED_ISSUE(1, 1);
-    MOE_WAIT_VMCNT(6);
-  } else {
-    MOE_WAIT_VMCNT(0);
-  }
+#pragma unroll
+  for (int i = 1; i < NSTAGE - 1; ++i)
+    if (nsteps > i) MOE_TILED_ISSUE(i, i);
+  MOE_TILED_WAIT_NEXT(-1);
   __syncthreads();
-  if (nsteps > 2) MOE_TILED_ISSUE(2, 2);
+  if (nsteps > NSTAGE - 1) MOE_TILED_ISSUE(NSTAGE - 1, NSTAGE - 1);
   MOE_TILED_READ(f0a, f0b, 0, 0);
-  if (mrows > 32) MOE_TILED_PIPE(2);
+  if (NMB > 3 && mrows > 96) MOE_TILED_PIPE(4);
+  else if (NMB > 2 && mrows > 64) MOE_TILED_PIPE(3);
+  else if (mrows > 32) MOE_TILED_PIPE(2);
   else if (mrows > 0) MOE_TILED_PIPE(1);
   else MOE_TILED_PIPE(0);
 #undef MOE_TILED_PIPE
 #undef MOE_TILED_STEP_FULL
+#undef MOE_TILED_WAIT_NEXT
 #undef MOE_TILED_ORDER
 #undef MOE_TILED_STEP
 #undef MOE_TILED_MMA
@@ -294,7 +317,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
   const int ncols = GLU ? 64 : 128;  // output columns of this wave
   const int oc0 = c0 + wn * ncols;   // first output column of this wave
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < NMB; ++mb) {
     // acc element e of a 32x32 block: row 8*(e/4) + 4*(lane/32) + e%4,
     // column lane%32
 #pragma unroll
@@ -319,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
     for (int it = 0; it < 32 * (GLU ? 8 : 16) / 64; ++it) {
       const int q = it * 64 + lane;
       const int r = q / chunks, c = q % chunks;
-      const int row = wm * 64 + mb * 32 + r;
+      const int row = wm * WR + mb * 32 + r;
       const int col = oc0 + 8 * c;
       if (row < tl.rows && col < Nout)
         *(uint4*)(out + (size_t)(tl.row0 + row) * Nout + col) =
@@ -328,25 +351,71 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tiled_kernel(
   }
 }
 
-hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
+// Persistent grid of (a multiple of 8) blocks, dispatched round-robin over the
+// 8 XCDs: XCD x owns the contiguous item range [lo_x, hi_x) and its blocks
+// walk it in lockstep, block j taking items lo_x + j, lo_x + j + nj, ...
+// (nj blocks per XCD). The items running at once on an XCD are therefore
+// consecutive: the slabs of a few tiles and the tiles of one expert, whose A
+// rows and weight slabs that XCD's L2 serves to all of them.
+template <bool GLU, int WR>
+__global__ __launch_bounds__(256, TiledCfg<WR>::BLOCKS_PER_CU) void gemm_bf16_tiled_kernel(
+    const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ w,
+    uint16_t* __restrict__ out, int K, int Nw, int Nout, int nslabs,
+    const int32_t* __restrict__ gidx, const int32_t* __restrict__ gbase,
+    int gk) {
+  using C = TiledCfg<WR>;
+  __shared__ __align__(1024) uint8_t smem[C::NSTAGE * C::STAGE_BYTES];
+  const int nb = tile_count[0] * nslabs;
+  const int xcd = blockIdx.x % 8, j = blockIdx.x / 8, nj = gridDim.x / 8;
+  const int per = nb / 8, rem = nb % 8;
+  const int lo = xcd * per + min(xcd, rem);
+  const int hi = lo + per + (xcd < rem ? 1 : 0);
+  for (int L = lo + j; L < hi; L += nj) {
+    tiled_item<GLU, WR>(smem, L, tiles, a, w, out, K, Nw, Nout, nslabs, gidx,
+                        gbase, gk);
+    __syncthreads();  // LDS staging of this item read before the next fills
+  }
+}
+
+template <int WR>
+static hipError_t launch_tiled(bool glu, dim3 grid, const Tile* tiles,
+                               const int32_t* tile_count, const uint16_t* a,
+                               const uint16_t* w, uint16_t* out, int K, int Nw,
+                               int Nout, int nslabs, const int32_t* gidx,
+                               const int32_t* gbase, int gk, hipStream_t s) {
+  if (glu)
+    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<true, WR>), grid, dim3(256), 0,
+                       s, tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
+                       gidx, gbase, gk);
+  else
+    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<false, WR>), grid, dim3(256), 0,
+                       s, tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
+                       gidx, gbase, gk);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_tiled(bool glu, int mt, const Tile* tiles,
                                   const int32_t* tile_count, int max_tiles,
                                   const uint16_t* a, const uint16_t* w,
                                   uint16_t* out, int K, int Nw, int Nout,
                                   const int32_t* gidx, const int32_t* gbase,
                                   int gk, hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
+  if (mt != 128 && mt != 256) return hipErrorInvalidValue;
   const int slab = glu ? BNW / 2 : BNW;
   const int nslabs = (Nout + slab - 1) / slab;
-  dim3 grid((unsigned)max_tiles * nslabs);
-  if (glu)
-    hipLaunchKernelGGL(gemm_bf16_tiled_kernel<true>, grid, dim3(256), 0, s,
-                       tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
-                       gidx, gbase, gk);
-  else
-    hipLaunchKernelGGL(gemm_bf16_tiled_kernel<false>, grid, dim3(256), 0, s,
-                       tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
-                       gidx, gbase, gk);
-  return hipGetLastError();
+  // one resident block per slot, a multiple of 8 (the XCD count), never more
+  // blocks than items
+  const long long items = (long long)max_tiles * nslabs;
+  const long long slots = (long long)device_cus() * (mt == 256 ? 1 : 2);
+  long long nblk = items < slots ? items : slots;
+  nblk = ((nblk + 7) / 8) * 8;
+  dim3 grid((unsigned)nblk);
+  return mt == 256 ? launch_tiled<128>(glu, grid, tiles, tile_count, a, w, out,
+                                       K, Nw, Nout, nslabs, gidx, gbase, gk, s)
+                   : launch_tiled<64>(glu, grid, tiles, tile_count, a, w, out,
+                                      K, Nw, Nout, nslabs, gidx, gbase, gk, s);
 }
 
 }  // namespace moe

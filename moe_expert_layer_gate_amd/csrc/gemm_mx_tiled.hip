@@ -7,10 +7,15 @@
 // the local experts (MoE EP优化 / AllGather方案(W4A8量化)) and the expert FFN
 // of MoE TP优化 / 计算分解 (down(SiLU(gate(x)) * up(x)), merged gate/up).
 //
-// Block = 256 threads (2 x 2 waves), tile = 128 rows x 256 weight columns of
-// one expert, K steps of 128 through a two-stage LDS ring filled by direct
-// global -> LDS copies (16 bytes per lane, no VGPRs involved). Both operands
-// are K-contiguous in HBM and in LDS, so nothing is transposed:
+// Block = WMW x 2 waves, tile = 64*WMW rows x 256 weight columns of one
+// expert, K steps of 128 through an LDS ring filled by direct global -> LDS
+// copies (16 bytes per lane, no VGPRs involved):
+//   * WMW = 2: 128-row tiles, 256 threads, 2-stage ring (one step in
+//     flight), two blocks per CU;
+//   * WMW = 4: 256-row tiles, 512 threads, 3-stage ring (two steps in flight,
+//     150 KB of LDS), one block per CU: 1.5x the bytes in flight per CU and
+//     half the weight bytes per flop of the 128-row shape.
+// Both operands are K-contiguous in HBM and in LDS, so nothing is transposed:
 //   * A (e4m3 codes): LDS [row][8 x 16 B], the 16-byte piece index XOR-ed
 //     with (row / 2) % 8: with 128-byte rows, the 16 rows one MFMA operand
 //     read touches then cover all 64 banks once (row parity picks the half);
@@ -37,12 +42,23 @@ namespace moe {
 
 namespace {
 
-constexpr int MBM = 128, MBNW = 256, MBK = 128;
-constexpr int MA_BYTES = MBM * MBK;           // 16 KB of e4m3
+constexpr int MBNW = 256, MBK = 128;
 constexpr int MB_BYTES = MBNW * MBK / 2;      // 16 KB of e2m1
-constexpr int MSA = MA_BYTES + MB_BYTES;      // row scale words (512 B)
-constexpr int MSB = MSA + MBM * 4;            // column scale words (1 KB)
-constexpr int MSTAGE = MSB + MBNW * 4;        // 33.5 KB
+
+// Tile geometry for WMW 64-row wave groups.
+template <int WMW>
+struct MxCfg {
+  static constexpr int NW = 2 * WMW;                 // waves
+  static constexpr int MBM = 64 * WMW;               // tile rows
+  static constexpr int MA_BYTES = MBM * MBK;         // 16 / 32 KB of e4m3
+  static constexpr int MSA = MA_BYTES + MB_BYTES;    // row scale words
+  static constexpr int MSB = MSA + MBM * 4;          // column scale words
+  static constexpr int MSTAGE = MSB + MBNW * 4;      // 33.5 / 50 KB
+  static constexpr int NSTAGE = WMW == 4 ? 3 : 2;
+  static constexpr int BLOCKS_PER_CU = WMW == 4 ? 1 : 2;
+  // copies per wave and step with WMW == 4: 4 (A) + 2 (B) + 1 (scales)
+  static constexpr int NI = 7;
+};
 
 // 4 bytes per lane, global (base + lane offset) -> LDS at lds_wave_base +
 // 4 * lane; same conventions as g2lds
@@ -63,16 +79,20 @@ MOE_DEV f32x4 mfma_mx(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
 
 }  // namespace
 
-template <bool GLU>
-// two blocks per CU: 2 waves per SIMD, 64 KB of LDS each
-__global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
+template <bool GLU, int WMW>
+__global__ __launch_bounds__(128 * WMW, MxCfg<WMW>::BLOCKS_PER_CU) void gemm_mx_tiled_kernel(
     const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws,
     void* __restrict__ out, uint8_t* __restrict__ os, int K, int Nw, int Nout,
     int nslabs, const int32_t* __restrict__ gidx,
     const int32_t* __restrict__ gbase, int gk) {
-  __shared__ __align__(1024) uint8_t smem[2 * MSTAGE];
+  using C = MxCfg<WMW>;
+  constexpr int NW = C::NW, MBM = C::MBM, MA_BYTES = C::MA_BYTES;
+  constexpr int MSA = C::MSA, MSB = C::MSB, MSTAGE = C::MSTAGE;
+  constexpr int NSTAGE = C::NSTAGE, NI = C::NI;
+  static_assert(NSTAGE == 2 || NW == 8, "a 3-stage ring needs uniform copy counts");
+  __shared__ __align__(1024) uint8_t smem[NSTAGE * MSTAGE];
   const int nb = tile_count[0] * nslabs;
   const int b = blockIdx.x;
   if (b >= nb) return;
@@ -113,18 +133,24 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
     return grow ? grow[rr] / gk : rr;
   };
 
-  // ---- copy assignment: instruction j (0..3) of a wave moves 1 KB.
-  // A: rows 8*(4j + wave) + lane/8, physical piece lane%8 <- logical piece
-  //    (lane%8) ^ ((row/2)%8); (row/2)%8 = 4*(wave%2) + lane/16 here.
-  // B: columns 16*(4j + wave) + lane/4, physical piece lane%4 <- logical
-  //    piece (lane%4) ^ ((column/4)%4); (column/4)%4 = (lane/16)%4 here.
-  uint32_t a_off[4], b_off[4];
+  // ---- copy assignment: each instruction of a wave moves 1 KB.
+  // A (4 per wave, j = 0..3): rows 8*(NW*j + wave) + lane/8, physical piece
+  //    lane%8 <- logical piece (lane%8) ^ ((row/2)%8); (row/2)%8 =
+  //    4*(wave%2) + lane/16 here.
+  // B (16/NW per wave): columns 16*(NW*j + wave) + lane/4, physical piece
+  //    lane%4 <- logical piece (lane%4) ^ ((column/4)%4); (column/4)%4 =
+  //    (lane/16)%4 here.
+  constexpr int NB = 16 / NW;
+  uint32_t a_off[4], b_off[NB];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int r = 8 * (4 * j + wave) + (lane >> 3);
+    const int r = 8 * (NW * j + wave) + (lane >> 3);
     a_off[j] = (uint32_t)arow(r) * K +
                16 * ((lane & 7) ^ (4 * (wave & 1) + (lane >> 4)));
-    const int t = 16 * (4 * j + wave) + (lane >> 2);
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int t = 16 * (NW * j + wave) + (lane >> 2);
     b_off[j] = (uint32_t)wcol(t) * (K / 2) + 16 * ((lane & 3) ^ (lane >> 4));
   }
   const uint32_t lds0 = lds_addr(smem);
@@ -132,26 +158,30 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   const uint32_t b_dst =
       __builtin_amdgcn_readfirstlane(lds0 + MA_BYTES + 16 * wave * (MBK / 2));
 
-  // scale words: waves 0-1 copy rows 64*wave + lane, every wave copies
-  // tile columns 64*wave + lane
+  // scale words: waves w < MBM/64 copy rows 64*w + lane; the last four waves
+  // copy tile columns 64*(w - NW + 4) + lane
+  const bool sa_wave = wave < MBM / 64;
+  const int sbw = wave - (NW - 4);
+  const bool sb_wave = sbw >= 0;
   const uint32_t sa_doff = (uint32_t)arow((64 * wave + lane) & (MBM - 1)) * KB;
-  const uint32_t sb_doff = (uint32_t)wcol(64 * wave + lane) * KB;
-  const uint32_t sa_dst =
-      __builtin_amdgcn_readfirstlane(lds0 + MSA + 64 * 4 * (wave & 1));
-  const uint32_t sb_dst = __builtin_amdgcn_readfirstlane(lds0 + MSB + 64 * 4 * wave);
+  const uint32_t sb_doff = (uint32_t)wcol((64 * sbw + lane) & (MBNW - 1)) * KB;
+  const uint32_t sa_dst = __builtin_amdgcn_readfirstlane(
+      lds0 + MSA + 64 * 4 * (wave & (MBM / 64 - 1)));
+  const uint32_t sb_dst = __builtin_amdgcn_readfirstlane(
+      lds0 + MSB + 64 * 4 * (sbw & 3));
 
-  // loads of K step s_ into stage st_ (9 or 10 instructions per wave)
+  // loads of K step s_ into stage st_
 #define MOE_MX_ISSUE(s_, st_)                                                 \
   do {                                                                        \
     const uint8_t* ab_ = a_tile + (size_t)(s_) * MBK;                         \
     const uint8_t* bb_ = we + (size_t)(s_) * (MBK / 2);                       \
     const uint32_t o_ = (st_) * MSTAGE;                                       \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
-      g2lds(ab_, a_off[j], a_dst + o_ + 32 * j * MBK);                        \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
-      g2lds(bb_, b_off[j], b_dst + o_ + 64 * j * (MBK / 2));                  \
-    if (wave < 2) g2lds4(as_tile + 4 * (s_), sa_doff, sa_dst + o_);           \
-    g2lds4(wse + 4 * (s_), sb_doff, sb_dst + o_);                             \
+      g2lds(ab_, a_off[j], a_dst + o_ + 8 * NW * j * MBK);                    \
+    _Pragma("unroll") for (int j = 0; j < NB; ++j)                            \
+      g2lds(bb_, b_off[j], b_dst + o_ + 16 * NW * j * (MBK / 2));             \
+    if (sa_wave) g2lds4(as_tile + 4 * (s_), sa_doff, sa_dst + o_);            \
+    if (sb_wave) g2lds4(wse + 4 * (s_), sb_doff, sb_dst + o_);                \
   } while (0)
 
   // ---- operand reads. A of 16-row block mb: row wm*64 + 16*mb + lane%16,
@@ -189,8 +219,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   do {                                                                        \
     u32x4_t fb[4];                                                            \
     _Pragma("unroll") for (int g = 0; g < 4; ++g)                             \
-      fb[g] = lds_read_b128(b_rd + (st_) * MSTAGE +                           \
-                            (bcol((G0_) + g) - bcol(0)) * (MBK / 2));         \
+      fb[g] = lds_read_b128(br_ + (bcol((G0_) + g) - bcol(0)) * (MBK / 2));  \
     if ((NMB_) > 0) {                                                         \
       __builtin_amdgcn_sched_group_barrier(0x100, (G0_) ? 8 : 3 * (NMB_) + 8, 0); \
       __builtin_amdgcn_sched_group_barrier(0x008, 4 * (NMB_), 0);             \
@@ -198,8 +227,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
     _Pragma("unroll") for (int g = 0; g < 4; ++g) {                           \
       const i32x8 b8 = i32x8{(int)fb[g].x, (int)fb[g].y, (int)fb[g].z,        \
                              (int)fb[g].w, 0, 0, 0, 0};                       \
-      const int sbv = MOE_MX_LDS_U8(sb_rd + (st_) * MSTAGE +                  \
-                                    (bcol((G0_) + g) - bcol(0)) * 4);         \
+      const int sbv = MOE_MX_LDS_U8(sbr_ + (bcol((G0_) + g) - bcol(0)) * 4);  \
       _Pragma("unroll") for (int mb = 0; mb < (NMB_); ++mb)                   \
         acc[mb][(G0_) + g] = mfma_mx(fa[mb], b8, acc[mb][(G0_) + g],          \
                                      sa[mb], sbv);                            \
@@ -207,40 +235,49 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   } while (0)
 #define MOE_MX_COMPUTE(st_, NMB_)                                             \
   do {                                                                        \
+    /* the stage's read bases, recomputed every step (an opaque offset keeps \
+       the compiler from holding one set of address registers per stage;     \
+       stage offsets past 64 KB do not fit the read's immediate) */          \
+    uint32_t so_ = (st_) * MSTAGE;                                            \
+    asm volatile("" : "+s"(so_));                                             \
+    const uint32_t ar0_ = a_rd[0] + so_, ar1_ = a_rd[1] + so_;                \
+    const uint32_t br_ = b_rd + so_, sar_ = sa_rd + so_, sbr_ = sb_rd + so_;  \
     i32x8 fa[4];                                                              \
     int sa[4];                                                                \
     _Pragma("unroll") for (int mb = 0; mb < (NMB_); ++mb) {                   \
-      const u32x4_t v0 = lds_read_b128(a_rd[0] + (st_) * MSTAGE + mb * 16 * MBK); \
-      const u32x4_t v1 = lds_read_b128(a_rd[1] + (st_) * MSTAGE + mb * 16 * MBK); \
+      const u32x4_t v0 = lds_read_b128(ar0_ + mb * 16 * MBK);                 \
+      const u32x4_t v1 = lds_read_b128(ar1_ + mb * 16 * MBK);                 \
       fa[mb] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,              \
                      (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};             \
-      sa[mb] = MOE_MX_LDS_U8(sa_rd + (st_) * MSTAGE + mb * 16 * 4);           \
+      sa[mb] = MOE_MX_LDS_U8(sar_ + mb * 16 * 4);                             \
     }                                                                         \
     MOE_MX_HALF(st_, NMB_, 0);                                                \
     MOE_MX_HALF(st_, NMB_, 4);                                                \
   } while (0)
 
-  // step t_: its copies landed (issued one step earlier) and every wave is
-  // done with the other stage; refill that stage with step t+1, multiply.
+  // step t_ (stage st_ = t_ % NSTAGE): wait until its copies landed (the
+  // NI copies per wave of step t+1 may still be in flight in a 3-stage
+  // ring), then every wave is done with the stage of step t-1; refill it
+  // with step t + NSTAGE - 1 and multiply.
 #define MOE_MX_STEP(t_, st_, NMB_)                                            \
   do {                                                                        \
-    MOE_WAIT_VMCNT(0);                                                        \
+    if (NSTAGE == 3 && (t_) + 1 < nsteps) MOE_WAIT_VMCNT(NI);                 \
+    else MOE_WAIT_VMCNT(0);                                                   \
     __syncthreads();                                                          \
-    if ((t_) + 1 < nsteps) MOE_MX_ISSUE((t_) + 1, (st_) ^ 1);                 \
+    if ((t_) + NSTAGE - 1 < nsteps)                                           \
+      MOE_MX_ISSUE((t_) + NSTAGE - 1, ((st_) + NSTAGE - 1) % NSTAGE);         \
     MOE_MX_COMPUTE(st_, NMB_);                                                \
   } while (0)
+// one step per iteration, the stage index at run time: unrolling over the
+// ring's stages keeps a set of address registers per stage alive and spills
 #define MOE_MX_PIPE(NMB_)                                                     \
   do {                                                                        \
-    int s = 0;                                                                \
-    for (; s + 1 < nsteps; s += 2) {                                          \
-      MOE_MX_STEP(s, 0, NMB_);                                                \
-      MOE_MX_STEP(s + 1, 1, NMB_);                                            \
-    }                                                                         \
-    if (s < nsteps) MOE_MX_STEP(s, 0, NMB_);                                  \
+    for (int t = 0; t < nsteps; ++t) MOE_MX_STEP(t, t % NSTAGE, NMB_);        \
   } while (0)
 
   const int nsteps = K / MBK;
   MOE_MX_ISSUE(0, 0);
+  if (NSTAGE == 3 && nsteps > 1) MOE_MX_ISSUE(1, 1);
   // 16-row blocks of this wave's 64 rows that hold tile rows, in pairs
   const int mrows = __builtin_amdgcn_readfirstlane(tl.rows - wm * 64);
   if (mrows > 32) MOE_MX_PIPE(4);
@@ -319,7 +356,28 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   }
 }
 
-hipError_t launch_gemm_mx_tiled(bool glu, const Tile* tiles,
+template <int WMW>
+static hipError_t launch_mx(bool glu, dim3 grid, const Tile* tiles,
+                            const int32_t* tile_count, const uint8_t* a,
+                            const uint8_t* a_scale, const uint8_t* w,
+                            const uint8_t* w_scale, void* out,
+                            uint8_t* out_scale, int K, int Nw, int Nout,
+                            int nslabs, const int32_t* gidx,
+                            const int32_t* gbase, int gk, hipStream_t s) {
+  if (glu)
+    hipLaunchKernelGGL((gemm_mx_tiled_kernel<true, WMW>), grid,
+                       dim3(128 * WMW), 0, s, tiles, tile_count, a, a_scale, w,
+                       w_scale, out, out_scale, K, Nw, Nout, nslabs, gidx,
+                       gbase, gk);
+  else
+    hipLaunchKernelGGL((gemm_mx_tiled_kernel<false, WMW>), grid,
+                       dim3(128 * WMW), 0, s, tiles, tile_count, a, a_scale, w,
+                       w_scale, out, out_scale, K, Nw, Nout, nslabs, gidx,
+                       gbase, gk);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mx_tiled(bool glu, int mt, const Tile* tiles,
                                 const int32_t* tile_count, int max_tiles,
                                 const uint8_t* a, const uint8_t* a_scale,
                                 const uint8_t* w, const uint8_t* w_scale,
@@ -327,18 +385,16 @@ hipError_t launch_gemm_mx_tiled(bool glu, const Tile* tiles,
                                 int Nout, const int32_t* gidx,
                                 const int32_t* gbase, int gk, hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
+  if (mt != 128 && mt != 256) return hipErrorInvalidValue;
   const int slab = glu ? MBNW / 2 : MBNW;
   const int nslabs = (Nout + slab - 1) / slab;
   dim3 grid((unsigned)max_tiles * nslabs);
-  if (glu)
-    hipLaunchKernelGGL(gemm_mx_tiled_kernel<true>, grid, dim3(256), 0, s, tiles,
-                       tile_count, a, a_scale, w, w_scale, out, out_scale, K,
-                       Nw, Nout, nslabs, gidx, gbase, gk);
-  else
-    hipLaunchKernelGGL(gemm_mx_tiled_kernel<false>, grid, dim3(256), 0, s,
-                       tiles, tile_count, a, a_scale, w, w_scale, out,
-                       out_scale, K, Nw, Nout, nslabs, gidx, gbase, gk);
-  return hipGetLastError();
+  return mt == 256 ? launch_mx<4>(glu, grid, tiles, tile_count, a, a_scale, w,
+                                  w_scale, out, out_scale, K, Nw, Nout, nslabs,
+                                  gidx, gbase, gk, s)
+                   : launch_mx<2>(glu, grid, tiles, tile_count, a, a_scale, w,
+                                  w_scale, out, out_scale, K, Nw, Nout, nslabs,
+                                  gidx, gbase, gk, s);
 }
 
 }  // namespace moe

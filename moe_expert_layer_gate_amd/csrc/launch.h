@@ -55,6 +55,9 @@ hipError_t launch_route_gather(const void* x, int act, int mx, int H, int k,
                                int max_rows, void* x_perm, uint8_t* x_scale,
                                hipStream_t s);
 
+// Compute units of the current device (256 on MI355X if the query fails).
+int device_cus();
+
 // Grouped GEMMs. glu: GEMM1 with SwiGLU epilogue (N = 2*I weight columns,
 // I outputs), else GEMM2 (N outputs). Tiles come from the tile list.
 // bf16 activations / bf16 weights [E_loc, K, N]. When gidx is non-NULL the
@@ -66,9 +69,9 @@ hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
                                    uint16_t* out, int K, int Nw, int Nout,
                                    const int32_t* gidx, const int32_t* gbase,
                                    int gk, hipStream_t s);
-// Same operands, 128-row LDS-tiled MFMA tiles (tile list built with mt=128).
-// With gidx, `a` must span less than 4 GB.
-hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
+// Same operands, LDS-tiled MFMA tiles of mt = 128 or 256 rows (the tile list
+// built with the same mt). With gidx, `a` must span less than 4 GB.
+hipError_t launch_gemm_bf16_tiled(bool glu, int mt, const Tile* tiles,
                                   const int32_t* tile_count, int max_tiles,
                                   const uint16_t* a, const uint16_t* w,
                                   uint16_t* out, int K, int Nw, int Nout,
@@ -89,10 +92,11 @@ hipError_t launch_gemm_mx(bool glu, int rg, const Tile* tiles,
                           uint8_t* out_scale, int K, int Nw, int Nout,
                           hipStream_t s);
 
-// Same operands, 128-row LDS-tiled scaled-MFMA tiles (tile list mt=128).
-// With gidx non-NULL, A rows (and their scales) are read from the per-token
-// codes: row of sorted copy i = gidx[gbase[0] + i] / gk (offsets < 2^31).
-hipError_t launch_gemm_mx_tiled(bool glu, const Tile* tiles,
+// Same operands, LDS-tiled scaled-MFMA tiles of mt = 128 or 256 rows (tile
+// list built with the same mt). With gidx non-NULL, A rows (and their scales)
+// are read from the per-token codes: row of sorted copy i =
+// gidx[gbase[0] + i] / gk (offsets < 2^31).
+hipError_t launch_gemm_mx_tiled(bool glu, int mt, const Tile* tiles,
                                 const int32_t* tile_count, int max_tiles,
                                 const uint8_t* a, const uint8_t* a_scale,
                                 const uint8_t* w, const uint8_t* w_scale,

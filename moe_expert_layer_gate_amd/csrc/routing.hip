@@ -26,6 +26,7 @@ namespace moe {
 
 constexpr int kChunk = 256;
 constexpr int kMaxE = 2048;
+constexpr int kScanRegs = 16;  // chunk counts a scan thread keeps in registers
 
 int route_num_chunks(int N) { return (N + kChunk - 1) / kChunk; }
 
@@ -123,44 +124,64 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
   __shared__ int32_t tmp[kMaxE];
   __shared__ int32_t wsum[16];
   __shared__ int32_t part[1024];
-  // tpe threads per expert split the chunks into contiguous ranges: sum each
-  // range (independent loads), scan the ranges in LDS, then rewrite every
-  // chunk count as its exclusive prefix within the expert
-  // (chunk counts are read 8 at a time so that the loads overlap)
+  // tpe threads per expert split the chunks into contiguous ranges of at
+  // most kScanRegs: each thread loads its range once into registers (all
+  // loads in flight together), the range sums are scanned in LDS, and every
+  // chunk count is rewritten as its exclusive prefix within the expert. Only
+  // if a range cannot fit (more than 1024 * kScanRegs / E chunks) are the
+  // counts read a second time.
   int tpe = 1;
   while (tpe * 2 * E <= (int)blockDim.x) tpe *= 2;
+  while (tpe < (int)blockDim.x && (nchunks + tpe - 1) / tpe > kScanRegs) tpe *= 2;
   const int per = (nchunks + tpe - 1) / tpe;
   for (int e0 = 0; e0 < E; e0 += blockDim.x / tpe) {
     const int e = e0 + (int)threadIdx.x / tpe, q = threadIdx.x % tpe;
     const bool act = e < E;
     const int c0 = q * per, c1 = min(nchunks, c0 + per);
     int sum = 0;
-    if (act)
+    int v[kScanRegs];
+    if (per <= kScanRegs) {
+#pragma unroll
+      for (int j = 0; j < kScanRegs; ++j)
+        v[j] = act && c0 + j < c1 ? cc[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanRegs; ++j) sum += v[j];
+    } else if (act) {
       for (int c = c0; c < c1; c += 8) {
-        int v[8];
+        int u[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          v[j] = c + j < c1 ? cc[(size_t)(c + j) * E + e] : 0;
+          u[j] = c + j < c1 ? cc[(size_t)(c + j) * E + e] : 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sum += v[j];
+        for (int j = 0; j < 8; ++j) sum += u[j];
       }
+    }
     part[threadIdx.x] = sum;
     __syncthreads();
     if (act) {
       int base = 0;
       for (int j = 0; j < q; ++j) base += part[threadIdx.x - q + j];
       if (q == tpe - 1) { cnt[e] = base + sum; off[e] = base + sum; counts[e] = base + sum; }
-      for (int c = c0; c < c1; c += 8) {
-        int v[8];
+      if (per <= kScanRegs) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          v[j] = c + j < c1 ? cc[(size_t)(c + j) * E + e] : 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (c + j < c1) {
-            cc[(size_t)(c + j) * E + e] = base;
+        for (int j = 0; j < kScanRegs; ++j)
+          if (c0 + j < c1) {
+            cc[(size_t)(c0 + j) * E + e] = base;
             base += v[j];
           }
+      } else {
+        for (int c = c0; c < c1; c += 8) {
+          int u[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            u[j] = c + j < c1 ? cc[(size_t)(c + j) * E + e] : 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (c + j < c1) {
+              cc[(size_t)(c + j) * E + e] = base;
+              base += u[j];
+            }
+        }
       }
     }
     __syncthreads();
@@ -354,23 +375,38 @@ __global__ __launch_bounds__(256) void route_gather_kernel(
   }
   uint8_t* dst = (uint8_t*)xp + (size_t)r * H;
   uint8_t* dsc = xs + (size_t)r * (H / 32);
-  for (int c = lane; c < H / 8; c += 64) {  // H % 32 == 0: 4-lane groups whole
-    uint4 v = src[c];
-    float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-    float amax = 0.f;
+  // eight 16-byte chunks per lane in flight before any encoding; a 32-value
+  // MX block is 4 consecutive chunks = 4 adjacent lanes (H % 32 == 0, so a
+  // block never straddles the end of the row)
+  for (int c0 = lane; c0 < H / 8; c0 += 512) {
+    uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const int s = mx_e4m3_scale_exp(amax);
-    uint32_t lo = 0, hi = 0;
+    for (int j = 0; j < 8; ++j) {
+      const int c = c0 + 64 * j;
+      v[j] = c < H / 8 ? src[c] : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= e4m3_encode_scaled(f[i], s) << (8 * i);
+    for (int j = 0; j < 8; ++j) {
+      const int c = c0 + 64 * j;
+      float f[8] = {bf16_lo(v[j].x), bf16_hi(v[j].x), bf16_lo(v[j].y),
+                    bf16_hi(v[j].y), bf16_lo(v[j].z), bf16_hi(v[j].z),
+                    bf16_lo(v[j].w), bf16_hi(v[j].w)};
+      float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= e4m3_encode_scaled(f[4 + i], s) << (8 * i);
-    *(uint2*)(dst + (size_t)c * 8) = make_uint2(lo, hi);
-    if ((c & 3) == 0) dsc[c >> 2] = (uint8_t)(s + 127);
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      const int s = mx_e4m3_scale_exp(amax);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo |= e4m3_encode_fast(f[i], s) << (8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hi |= e4m3_encode_fast(f[4 + i], s) << (8 * i);
+      if (c < H / 8) {
+        *(uint2*)(dst + (size_t)c * 8) = make_uint2(lo, hi);
+        if ((c & 3) == 0) dsc[c >> 2] = (uint8_t)(s + 127);
+      }
+    }
   }
 }
 

@@ -39,6 +39,11 @@ SMALL = {
     "prefill_skewed_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_bf16"),
                                    T=300, H=256, I=160, n_ffn=12, local_end=12,
                                    top_k=4),
+    # >= 192 rows per expert on average: the 256-row bf16 tiles; H = 384
+    # leaves a ragged GEMM2 slab, I = 160 a ragged GEMM1 slab
+    "prefill_wide_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_bf16"),
+                                 T=600, H=384, I=160, n_ffn=8, local_end=8,
+                                 top_k=4),
     "zero_experts_small": scaled(get_workload("longcat_flash_zero_experts_bf16"),
                                  T=64, H=512, I=256, n_ffn=24, n_zero=12,
                                  local_end=36, top_k=6),
@@ -47,6 +52,11 @@ SMALL = {
                             top_k=4),
     # enough rows per expert for the 128-row LDS-tiled scaled-MFMA kernel;
     # H = 384 leaves a ragged 256-column slab in GEMM2
+    # >= 192 rows per expert on average: the 256-row scaled-MFMA tiles with
+    # the 3-stage ring (GEMM1 K = 3 steps, GEMM2 K = 4 steps)
+    "ep_w4a8_wide_small": scaled(get_workload("qwen3_235b_a22b_ep_rank_w4a8"),
+                                 T=512, H=384, I=512, n_ffn=8, local_begin=2,
+                                 local_end=6, top_k=4),
     "ep_w4a8_prefill_small": scaled(get_workload("qwen3_235b_a22b_ep_rank_w4a8"),
                                     T=384, H=384, I=256, n_ffn=16, local_begin=4,
                                     local_end=12, top_k=4),
@@ -220,7 +230,8 @@ def test_layer_small(name, seed):
 def test_layer_split_calls_equal_fused():
     """The five calls in sequence give the same bits as moe_layer."""
     m = _m()
-    for name in ("prefill_skewed_small", "ep_w4a8_small", "ep_w4a8_prefill_small",
+    for name in ("prefill_skewed_small", "prefill_wide_small", "ep_w4a8_small",
+                 "ep_w4a8_prefill_small", "ep_w4a8_wide_small",
                  "tiny_fp32", "decode_bf16_small"):
         shape = SMALL[name]
         inp = generate(shape, seed=6, device=DEV)
@@ -323,6 +334,12 @@ def test_edge_hot_expert_many_tiles():
     b = SMALL["prefill_skewed_small"].replace(T=700)
     _layer_vs_oracle(b, logit_fn=lambda L: L + torch.nn.functional.one_hot(
         torch.full((L.shape[0],), 3, device=L.device), L.shape[1]).float() * 50)
+
+
+@pytest.mark.parametrize("I", [32, 64, 96])
+def test_edge_short_k_wide_tiles(I):
+    # GEMM2 with K = I of 1..3 steps of 32: shorter than the LDS ring
+    _layer_vs_oracle(SMALL["prefill_wide_small"].replace(I=I))
 
 
 def test_edge_range_drops_everything():
