@@ -49,13 +49,10 @@ size_t act_bytes(const Prob& q) { return q.act == MOE_F32 ? 4 : 2; }
 
 // Tile height of the grouped GEMM chosen for the problem, from the expected
 // rows per expert: weight-streaming tiles of 16 or 32 rows for decode-size
-// batches, 128-row LDS-tiled MFMA tiles for prefill-size batches and 256-row
-// scaled-MFMA tiles once experts average 192 rows or more.
-constexpr long long kWideRows = 1ll << 40;  // 256-row tiles: measured slower
+// batches, 128-row LDS-tiled MFMA tiles for prefill-size batches.
 int tile_rows(const Prob& q) {
   if (q.act == MOE_F32) return 32;
   const long long avg = q.E ? q.N / q.E : 0;  // expected rows per expert
-  if (q.mx && avg >= kWideRows) return 256;
   if (avg >= 64) return 128;
   return avg <= 12 ? 16 : 32;
 }
@@ -127,8 +124,8 @@ moe_status run_up(const Prob& q, int mt, const Tile* tiles,
     MOE_TRY(moe::launch_gemm_f32(true, tiles, tile_count, mtl, (const float*)xp,
                                  (const float*)w13, (float*)h, q.H, 2 * q.I,
                                  q.I, s));
-  else if (q.mx && mt >= 128)
-    MOE_TRY(moe::launch_gemm_mx_tiled(true, mt, tiles, tile_count, mtl,
+  else if (q.mx && mt == 128)
+    MOE_TRY(moe::launch_gemm_mx_tiled(true, tiles, tile_count, mtl,
                                       (const uint8_t*)xp, xs,
                                       (const uint8_t*)w13, w13s, h, hs, q.H,
                                       2 * q.I, q.I, gidx, gbase, q.k, s));
@@ -136,9 +133,9 @@ moe_status run_up(const Prob& q, int mt, const Tile* tiles,
     MOE_TRY(moe::launch_gemm_mx(true, mt / 16, tiles, tile_count, mtl,
                                 (const uint8_t*)xp, xs, (const uint8_t*)w13,
                                 w13s, h, hs, q.H, 2 * q.I, q.I, s));
-  else if (mt >= 128)
+  else if (mt == 128)
     MOE_TRY(moe::launch_gemm_bf16_tiled(
-        true, mt, tiles, tile_count, mtl, (const uint16_t*)xp,
+        true, tiles, tile_count, mtl, (const uint16_t*)xp,
         (const uint16_t*)w13, (uint16_t*)h, q.H, 2 * q.I, q.I, gidx, gbase,
         q.k, s));
   else
@@ -159,8 +156,8 @@ moe_status run_down(const Prob& q, int mt, const Tile* tiles,
     MOE_TRY(moe::launch_gemm_f32(false, tiles, tile_count, mtl,
                                  (const float*)h, (const float*)w2, (float*)y,
                                  q.I, q.H, q.H, s));
-  else if (q.mx && mt >= 128)
-    MOE_TRY(moe::launch_gemm_mx_tiled(false, mt, tiles, tile_count, mtl,
+  else if (q.mx && mt == 128)
+    MOE_TRY(moe::launch_gemm_mx_tiled(false, tiles, tile_count, mtl,
                                       (const uint8_t*)h, hs,
                                       (const uint8_t*)w2, w2s, y, nullptr,
                                       q.I, q.H, q.H, nullptr, nullptr, q.k,
@@ -169,9 +166,9 @@ moe_status run_down(const Prob& q, int mt, const Tile* tiles,
     MOE_TRY(moe::launch_gemm_mx(false, mt / 16, tiles, tile_count, mtl,
                                 (const uint8_t*)h, hs, (const uint8_t*)w2, w2s,
                                 y, nullptr, q.I, q.H, q.H, s));
-  else if (mt >= 128)
+  else if (mt == 128)
     MOE_TRY(moe::launch_gemm_bf16_tiled(
-        false, mt, tiles, tile_count, mtl, (const uint16_t*)h,
+        false, tiles, tile_count, mtl, (const uint16_t*)h,
         (const uint16_t*)w2, (uint16_t*)y, q.I, q.H, q.H, nullptr, nullptr,
         q.k, s));
   else
@@ -394,7 +391,7 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
   const bool gather = fused_gather(q);
   // MXFP8 with the tiled GEMM: x is quantised once per token and GEMM1 reads
   // the token rows of the codes
-  const bool mx_tok = q.mx && mt >= 128 && (int64_t)q.T * q.H < (int64_t(1) << 31);
+  const bool mx_tok = q.mx && mt == 128 && (int64_t)q.T * q.H < (int64_t(1) << 31);
   const size_t xrows = mx_tok ? (size_t)q.T : N;
   void* xp = c.take<char>(q.El && !gather ? xrows * q.H * ab : 0);
   uint8_t* xs = q.mx ? c.take<uint8_t>(q.El ? xrows * (q.H / 32) : 0) : nullptr;

@@ -7,18 +7,13 @@
 // (all experts in one grouped operator); prefill operators are compute-bound
 // (Prefill优化 / 并行策略选择).
 //
-// Block = 256 threads (2 x 2 waves) computing a (2*WR)-row x 256-weight-column
-// tile of one expert, K in steps of 32 through an LDS ring filled by direct
-// global->LDS loads (global_load_lds_dwordx4: lane l of a wave lands at the
-// wave's LDS base + 16*l, no VGPRs involved). Two shapes:
-//   * WR = 64: 128-row tiles, 3-stage ring (two steps in flight), two blocks
-//     per CU, 128 fp32 accumulators per lane;
-//   * WR = 128: 256-row tiles, 4-stage ring (three steps in flight), one
-//     block per CU, 256 accumulators per lane (in the accumulation registers)
-//     -- half the LDS operand reads and half the L2 -> LDS bytes per flop
-//     of the 128-row shape, which matters because MI355X's MFMA rate per CU
-//     outruns both (the LDS instruction issue of the transposing B reads
-//     most of all).
+// Block = 256 threads (2 x 2 waves) computing a 128-row x 256-weight-column
+// tile of one expert, K in steps of 32 through a 3-stage LDS ring filled by
+// direct global->LDS loads (global_load_lds_dwordx4: lane l of a wave lands
+// at the wave's LDS base + 16*l, no VGPRs involved), two steps in flight, two
+// blocks per CU. (The geometry is a template on the wave's row count WR;
+// 256-row tiles with one block per CU and a 4-stage ring were measured slower
+// on MI355X and are not launched.)
 //   * A (activation rows, K contiguous): LDS [row][4 x 16 B], the 16-byte
 //     piece index XOR-swizzled with (row/4)%4 so the MFMA reads of 8
 //     consecutive rows hit 8 different bank groups;
@@ -395,27 +390,23 @@ static hipError_t launch_tiled(bool glu, dim3 grid, const Tile* tiles,
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_bf16_tiled(bool glu, int mt, const Tile* tiles,
+hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
                                   const int32_t* tile_count, int max_tiles,
                                   const uint16_t* a, const uint16_t* w,
                                   uint16_t* out, int K, int Nw, int Nout,
                                   const int32_t* gidx, const int32_t* gbase,
                                   int gk, hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
-  if (mt != 128 && mt != 256) return hipErrorInvalidValue;
   const int slab = glu ? BNW / 2 : BNW;
   const int nslabs = (Nout + slab - 1) / slab;
-  // one resident block per slot, a multiple of 8 (the XCD count), never more
-  // blocks than items
+  // one resident block per slot (two per CU), a multiple of 8 (the XCD
+  // count), never more blocks than items
   const long long items = (long long)max_tiles * nslabs;
-  const long long slots = (long long)device_cus() * (mt == 256 ? 1 : 2);
+  const long long slots = (long long)device_cus() * 2;
   long long nblk = items < slots ? items : slots;
   nblk = ((nblk + 7) / 8) * 8;
-  dim3 grid((unsigned)nblk);
-  return mt == 256 ? launch_tiled<128>(glu, grid, tiles, tile_count, a, w, out,
-                                       K, Nw, Nout, nslabs, gidx, gbase, gk, s)
-                   : launch_tiled<64>(glu, grid, tiles, tile_count, a, w, out,
-                                      K, Nw, Nout, nslabs, gidx, gbase, gk, s);
+  return launch_tiled<64>(glu, dim3((unsigned)nblk), tiles, tile_count, a, w,
+                          out, K, Nw, Nout, nslabs, gidx, gbase, gk, s);
 }
 
 }  // namespace moe

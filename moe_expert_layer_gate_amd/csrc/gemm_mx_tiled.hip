@@ -7,23 +7,21 @@
 // the local experts (MoE EP优化 / AllGather方案(W4A8量化)) and the expert FFN
 // of MoE TP优化 / 计算分解 (down(SiLU(gate(x)) * up(x)), merged gate/up).
 //
-// Block = WMW x 2 waves, tile = 64*WMW rows x 256 weight columns of one
-// expert, K steps of 128 through an LDS ring filled by direct global -> LDS
-// copies (16 bytes per lane, no VGPRs involved):
-//   * WMW = 2: 128-row tiles, 256 threads, 2-stage ring (one step in
-//     flight), two blocks per CU;
-//   * WMW = 4: 256-row tiles, 512 threads, 3-stage ring (two steps in flight,
-//     150 KB of LDS), one block per CU: 1.5x the bytes in flight per CU and
-//     half the weight bytes per flop of the 128-row shape.
-// Both operands are K-contiguous in HBM and in LDS, so nothing is transposed:
+// Block = 256 threads (2 x 2 waves), tile = 128 rows x 256 weight columns of
+// one expert, K steps of 128 through a two-stage LDS ring filled by direct
+// global -> LDS copies (16 bytes per lane, no VGPRs involved). Both operands
+// are K-contiguous in HBM and in LDS, so nothing is transposed:
 //   * A (e4m3 codes): LDS [row][8 x 16 B], the 16-byte piece index XOR-ed
 //     with (row / 2) % 8: with 128-byte rows, the 16 rows one MFMA operand
 //     read touches then cover all 64 banks once (row parity picks the half);
 //   * B (e2m1 codes): LDS [column][4 x 16 B], piece index XOR-ed with
 //     (column / 4) % 4 for the same reason;
-//   * the e8m0 scales (one word = the step's four 32-K blocks per row or
-//     column) ride along in the same stage, 4 bytes per lane, and each lane
-//     reads back the byte of its K block.
+//   * the e8m0 scales have a two-slot ring of their own. When K/32 is a
+//     multiple of 16, one 16-byte copy per row (and per column) brings the
+//     scales of four K steps at once -- a copy per row or column costs an L2
+//     request however few bytes it moves, so batching cuts the requests of
+//     the scales fourfold (measured: without any scale copies GEMM1 runs
+//     16 % faster); otherwise one 4-byte word per row and step.
 // v_mfma_scale_f32_16x16x128_f8f6f4 operand layout (lane l, q = l/16; see the
 // streaming MX kernel): A row l%16 bytes from K [16q,+16) and [64+16q,+16); B
 // column l%16 bytes from K [32q,+32); scales of K block q. Each wave owns
@@ -42,22 +40,19 @@ namespace moe {
 
 namespace {
 
-constexpr int MBNW = 256, MBK = 128;
+constexpr int MBM = 128, MBNW = 256, MBK = 128;
+constexpr int MA_BYTES = MBM * MBK;           // 16 KB of e4m3
 constexpr int MB_BYTES = MBNW * MBK / 2;      // 16 KB of e2m1
+constexpr int MSTAGE = MA_BYTES + MB_BYTES;   // 32 KB per code stage
+constexpr int MCODES = 2 * MSTAGE;            // the two code stages
 
-// Tile geometry for WMW 64-row wave groups.
-template <int WMW>
-struct MxCfg {
-  static constexpr int NW = 2 * WMW;                 // waves
-  static constexpr int MBM = 64 * WMW;               // tile rows
-  static constexpr int MA_BYTES = MBM * MBK;         // 16 / 32 KB of e4m3
-  static constexpr int MSA = MA_BYTES + MB_BYTES;    // row scale words
-  static constexpr int MSB = MSA + MBM * 4;          // column scale words
-  static constexpr int MSTAGE = MSB + MBNW * 4;      // 33.5 / 50 KB
-  static constexpr int NSTAGE = WMW == 4 ? 3 : 2;
-  static constexpr int BLOCKS_PER_CU = WMW == 4 ? 1 : 2;
-  // copies per wave and step with WMW == 4: 4 (A) + 2 (B) + 1 (scales)
-  static constexpr int NI = 7;
+// Scale slot for SCB K steps per copy: [row][4*SCB bytes] then
+// [column][4*SCB bytes].
+template <int SCB>
+struct MxScales {
+  static constexpr int ROW = 4 * SCB;                 // bytes per row / column
+  static constexpr int SB = MBM * ROW;                // column scales offset
+  static constexpr int SLOT = (MBM + MBNW) * ROW;     // 1.5 / 6 KB
 };
 
 // 4 bytes per lane, global (base + lane offset) -> LDS at lds_wave_base +
@@ -79,20 +74,17 @@ MOE_DEV f32x4 mfma_mx(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
 
 }  // namespace
 
-template <bool GLU, int WMW>
-__global__ __launch_bounds__(128 * WMW, MxCfg<WMW>::BLOCKS_PER_CU) void gemm_mx_tiled_kernel(
+template <bool GLU, int SCB>
+// two blocks per CU: 2 waves per SIMD, 67 / 76 KB of LDS each
+__global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
     const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     const uint8_t* __restrict__ a, const uint8_t* __restrict__ as,
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws,
     void* __restrict__ out, uint8_t* __restrict__ os, int K, int Nw, int Nout,
     int nslabs, const int32_t* __restrict__ gidx,
     const int32_t* __restrict__ gbase, int gk) {
-  using C = MxCfg<WMW>;
-  constexpr int NW = C::NW, MBM = C::MBM, MA_BYTES = C::MA_BYTES;
-  constexpr int MSA = C::MSA, MSB = C::MSB, MSTAGE = C::MSTAGE;
-  constexpr int NSTAGE = C::NSTAGE, NI = C::NI;
-  static_assert(NSTAGE == 2 || NW == 8, "a 3-stage ring needs uniform copy counts");
-  __shared__ __align__(1024) uint8_t smem[NSTAGE * MSTAGE];
+  using S = MxScales<SCB>;
+  __shared__ __align__(1024) uint8_t smem[MCODES + 2 * S::SLOT];
   const int nb = tile_count[0] * nslabs;
   const int b = blockIdx.x;
   if (b >= nb) return;
@@ -133,24 +125,18 @@ __global__ __launch_bounds__(128 * WMW, MxCfg<WMW>::BLOCKS_PER_CU) void gemm_mx_
     return grow ? grow[rr] / gk : rr;
   };
 
-  // ---- copy assignment: each instruction of a wave moves 1 KB.
-  // A (4 per wave, j = 0..3): rows 8*(NW*j + wave) + lane/8, physical piece
-  //    lane%8 <- logical piece (lane%8) ^ ((row/2)%8); (row/2)%8 =
-  //    4*(wave%2) + lane/16 here.
-  // B (16/NW per wave): columns 16*(NW*j + wave) + lane/4, physical piece
-  //    lane%4 <- logical piece (lane%4) ^ ((column/4)%4); (column/4)%4 =
-  //    (lane/16)%4 here.
-  constexpr int NB = 16 / NW;
-  uint32_t a_off[4], b_off[NB];
+  // ---- copy assignment: instruction j (0..3) of a wave moves 1 KB.
+  // A: rows 8*(4j + wave) + lane/8, physical piece lane%8 <- logical piece
+  //    (lane%8) ^ ((row/2)%8); (row/2)%8 = 4*(wave%2) + lane/16 here.
+  // B: columns 16*(4j + wave) + lane/4, physical piece lane%4 <- logical
+  //    piece (lane%4) ^ ((column/4)%4); (column/4)%4 = (lane/16)%4 here.
+  uint32_t a_off[4], b_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int r = 8 * (NW * j + wave) + (lane >> 3);
+    const int r = 8 * (4 * j + wave) + (lane >> 3);
     a_off[j] = (uint32_t)arow(r) * K +
                16 * ((lane & 7) ^ (4 * (wave & 1) + (lane >> 4)));
-  }
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int t = 16 * (NW * j + wave) + (lane >> 2);
+    const int t = 16 * (4 * j + wave) + (lane >> 2);
     b_off[j] = (uint32_t)wcol(t) * (K / 2) + 16 * ((lane & 3) ^ (lane >> 4));
   }
   const uint32_t lds0 = lds_addr(smem);
@@ -158,30 +144,40 @@ __global__ __launch_bounds__(128 * WMW, MxCfg<WMW>::BLOCKS_PER_CU) void gemm_mx_
   const uint32_t b_dst =
       __builtin_amdgcn_readfirstlane(lds0 + MA_BYTES + 16 * wave * (MBK / 2));
 
-  // scale words: waves w < MBM/64 copy rows 64*w + lane; the last four waves
-  // copy tile columns 64*(w - NW + 4) + lane
-  const bool sa_wave = wave < MBM / 64;
-  const int sbw = wave - (NW - 4);
-  const bool sb_wave = sbw >= 0;
+  // scales: waves 0-1 copy rows 64*wave + lane, every wave copies tile
+  // columns 64*wave + lane; 4*SCB bytes each, lane l landing at 4*SCB*l
   const uint32_t sa_doff = (uint32_t)arow((64 * wave + lane) & (MBM - 1)) * KB;
-  const uint32_t sb_doff = (uint32_t)wcol((64 * sbw + lane) & (MBNW - 1)) * KB;
-  const uint32_t sa_dst = __builtin_amdgcn_readfirstlane(
-      lds0 + MSA + 64 * 4 * (wave & (MBM / 64 - 1)));
-  const uint32_t sb_dst = __builtin_amdgcn_readfirstlane(
-      lds0 + MSB + 64 * 4 * (sbw & 3));
+  const uint32_t sb_doff = (uint32_t)wcol(64 * wave + lane) * KB;
+  const uint32_t ss0 = lds0 + MCODES;
+  const uint32_t sa_dst =
+      __builtin_amdgcn_readfirstlane(ss0 + 64 * S::ROW * (wave & 1));
+  const uint32_t sb_dst =
+      __builtin_amdgcn_readfirstlane(ss0 + S::SB + 64 * S::ROW * wave);
 
-  // loads of K step s_ into stage st_
+  // codes of K step s_ into stage st_ (8 instructions per wave)
 #define MOE_MX_ISSUE(s_, st_)                                                 \
   do {                                                                        \
     const uint8_t* ab_ = a_tile + (size_t)(s_) * MBK;                         \
     const uint8_t* bb_ = we + (size_t)(s_) * (MBK / 2);                       \
     const uint32_t o_ = (st_) * MSTAGE;                                       \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
-      g2lds(ab_, a_off[j], a_dst + o_ + 8 * NW * j * MBK);                    \
-    _Pragma("unroll") for (int j = 0; j < NB; ++j)                            \
-      g2lds(bb_, b_off[j], b_dst + o_ + 16 * NW * j * (MBK / 2));             \
-    if (sa_wave) g2lds4(as_tile + 4 * (s_), sa_doff, sa_dst + o_);            \
-    if (sb_wave) g2lds4(wse + 4 * (s_), sb_doff, sb_dst + o_);                \
+      g2lds(ab_, a_off[j], a_dst + o_ + 32 * j * MBK);                        \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
+      g2lds(bb_, b_off[j], b_dst + o_ + 64 * j * (MBK / 2));                  \
+  } while (0)
+  // scales of K steps [SCB*g_, SCB*g_ + SCB) into slot g_ % 2 (1 or 2
+  // instructions per wave)
+#define MOE_MX_ISSUE_SCALES(g_)                                               \
+  do {                                                                        \
+    const uint32_t so_ = ((g_) & 1) * S::SLOT;                                \
+    const size_t go_ = (size_t)(g_) * S::ROW;                                 \
+    if (SCB == 4) {                                                           \
+      if (wave < 2) g2lds(as_tile + go_, sa_doff, sa_dst + so_);              \
+      g2lds(wse + go_, sb_doff, sb_dst + so_);                                \
+    } else {                                                                  \
+      if (wave < 2) g2lds4(as_tile + go_, sa_doff, sa_dst + so_);             \
+      g2lds4(wse + go_, sb_doff, sb_dst + so_);                               \
+    }                                                                         \
   } while (0)
 
   // ---- operand reads. A of 16-row block mb: row wm*64 + 16*mb + lane%16,
@@ -199,9 +195,9 @@ __global__ __launch_bounds__(128 * WMW, MxCfg<WMW>::BLOCKS_PER_CU) void gemm_mx_
       lds0 + MA_BYTES + bcol(0) * (MBK / 2) + 16 * (q ^ (lr >> 2));
 
   // scale bytes of this lane: row wm*64 + 16*mb + lane%16 and tile column
-  // bcol(g), byte q (K block 4s + q)
-  const uint32_t sa_rd = lds0 + MSA + (wm * 64 + lr) * 4 + q;
-  const uint32_t sb_rd = lds0 + MSB + bcol(0) * 4 + q;
+  // bcol(g), byte 4*(s % SCB) + q of the slot (K block 4s + q)
+  const uint32_t sa_rd = ss0 + (wm * 64 + lr) * S::ROW + q;
+  const uint32_t sb_rd = ss0 + S::SB + bcol(0) * S::ROW + q;
 #define MOE_MX_LDS_U8(a_) \
   ((int)*(const __attribute__((address_space(3))) uint8_t*)(uintptr_t)(a_))
 
@@ -215,7 +211,7 @@ __global__ __launch_bounds__(128 * WMW, MxCfg<WMW>::BLOCKS_PER_CU) void gemm_mx_
   // Two halves of four column groups each: the A fragments and the first
   // half's B fragments are read before its MFMAs, the second half's B while
   // they run.
-#define MOE_MX_HALF(st_, NMB_, G0_)                                 \
+#define MOE_MX_HALF(NMB_, G0_)                                                \
   do {                                                                        \
     u32x4_t fb[4];                                                            \
     _Pragma("unroll") for (int g = 0; g < 4; ++g)                             \
@@ -227,21 +223,22 @@ __global__ __launch_bounds__(128 * WMW, MxCfg<WMW>::BLOCKS_PER_CU) void gemm_mx_
     _Pragma("unroll") for (int g = 0; g < 4; ++g) {                           \
       const i32x8 b8 = i32x8{(int)fb[g].x, (int)fb[g].y, (int)fb[g].z,        \
                              (int)fb[g].w, 0, 0, 0, 0};                       \
-      const int sbv = MOE_MX_LDS_U8(sbr_ + (bcol((G0_) + g) - bcol(0)) * 4);  \
+      const int sbv =                                                         \
+          MOE_MX_LDS_U8(sbr_ + (bcol((G0_) + g) - bcol(0)) * S::ROW);         \
       _Pragma("unroll") for (int mb = 0; mb < (NMB_); ++mb)                   \
         acc[mb][(G0_) + g] = mfma_mx(fa[mb], b8, acc[mb][(G0_) + g],          \
                                      sa[mb], sbv);                            \
     }                                                                         \
   } while (0)
-#define MOE_MX_COMPUTE(st_, NMB_)                                             \
+#define MOE_MX_COMPUTE(t_, NMB_)                                              \
   do {                                                                        \
-    /* the stage's read bases, recomputed every step (an opaque offset keeps \
-       the compiler from holding one set of address registers per stage;     \
-       stage offsets past 64 KB do not fit the read's immediate) */          \
-    uint32_t so_ = (st_) * MSTAGE;                                            \
-    asm volatile("" : "+s"(so_));                                             \
+    /* read bases of step t_, recomputed every step (opaque offsets keep the \
+       compiler from holding a set of address registers per stage) */        \
+    uint32_t so_ = ((t_) & 1) * MSTAGE;                                       \
+    uint32_t sso_ = (((t_) / SCB) & 1) * S::SLOT + 4 * ((t_) % SCB);          \
+    asm volatile("" : "+s"(so_), "+s"(sso_));                                 \
     const uint32_t ar0_ = a_rd[0] + so_, ar1_ = a_rd[1] + so_;                \
-    const uint32_t br_ = b_rd + so_, sar_ = sa_rd + so_, sbr_ = sb_rd + so_;  \
+    const uint32_t br_ = b_rd + so_, sar_ = sa_rd + sso_, sbr_ = sb_rd + sso_; \
     i32x8 fa[4];                                                              \
     int sa[4];                                                                \
     _Pragma("unroll") for (int mb = 0; mb < (NMB_); ++mb) {                   \
@@ -249,35 +246,35 @@ __global__ __launch_bounds__(128 * WMW, MxCfg<WMW>::BLOCKS_PER_CU) void gemm_mx_
       const u32x4_t v1 = lds_read_b128(ar1_ + mb * 16 * MBK);                 \
       fa[mb] = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,              \
                      (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};             \
-      sa[mb] = MOE_MX_LDS_U8(sar_ + mb * 16 * 4);                             \
+      sa[mb] = MOE_MX_LDS_U8(sar_ + mb * 16 * S::ROW);                        \
     }                                                                         \
-    MOE_MX_HALF(st_, NMB_, 0);                                                \
-    MOE_MX_HALF(st_, NMB_, 4);                                                \
+    MOE_MX_HALF(NMB_, 0);                                                     \
+    MOE_MX_HALF(NMB_, 4);                                                     \
   } while (0)
 
-  // step t_ (stage st_ = t_ % NSTAGE): wait until its copies landed (the
-  // NI copies per wave of step t+1 may still be in flight in a 3-stage
-  // ring), then every wave is done with the stage of step t-1; refill it
-  // with step t + NSTAGE - 1 and multiply.
-#define MOE_MX_STEP(t_, st_, NMB_)                                            \
+  // step t_ (stage t_ % 2): its copies landed (issued one step earlier, with
+  // the scales of the next batch when t_ + 1 starts one) and every wave is
+  // done with the other stage and the other scale slot; refill them, multiply
+#define MOE_MX_STEP(t_, NMB_)                                                 \
   do {                                                                        \
-    if (NSTAGE == 3 && (t_) + 1 < nsteps) MOE_WAIT_VMCNT(NI);                 \
-    else MOE_WAIT_VMCNT(0);                                                   \
+    MOE_WAIT_VMCNT(0);                                                        \
     __syncthreads();                                                          \
-    if ((t_) + NSTAGE - 1 < nsteps)                                           \
-      MOE_MX_ISSUE((t_) + NSTAGE - 1, ((st_) + NSTAGE - 1) % NSTAGE);         \
-    MOE_MX_COMPUTE(st_, NMB_);                                                \
+    if ((t_) + 1 < nsteps) {                                                  \
+      MOE_MX_ISSUE((t_) + 1, ((t_) + 1) & 1);                                 \
+      if (((t_) + 1) % SCB == 0) MOE_MX_ISSUE_SCALES(((t_) + 1) / SCB);       \
+    }                                                                         \
+    MOE_MX_COMPUTE(t_, NMB_);                                                 \
   } while (0)
-// one step per iteration, the stage index at run time: unrolling over the
+// one step per iteration, stage offsets at run time: unrolling over the
 // ring's stages keeps a set of address registers per stage alive and spills
 #define MOE_MX_PIPE(NMB_)                                                     \
   do {                                                                        \
-    for (int t = 0; t < nsteps; ++t) MOE_MX_STEP(t, t % NSTAGE, NMB_);        \
+    for (int t = 0; t < nsteps; ++t) MOE_MX_STEP(t, NMB_);                    \
   } while (0)
 
   const int nsteps = K / MBK;
   MOE_MX_ISSUE(0, 0);
-  if (NSTAGE == 3 && nsteps > 1) MOE_MX_ISSUE(1, 1);
+  MOE_MX_ISSUE_SCALES(0);
   // 16-row blocks of this wave's 64 rows that hold tile rows, in pairs
   const int mrows = __builtin_amdgcn_readfirstlane(tl.rows - wm * 64);
   if (mrows > 32) MOE_MX_PIPE(4);
@@ -288,6 +285,7 @@ __global__ __launch_bounds__(128 * WMW, MxCfg<WMW>::BLOCKS_PER_CU) void gemm_mx_
 #undef MOE_MX_COMPUTE
 #undef MOE_MX_HALF
 #undef MOE_MX_LDS_U8
+#undef MOE_MX_ISSUE_SCALES
 #undef MOE_MX_ISSUE
   __syncthreads();
 
@@ -356,7 +354,7 @@ __global__ __launch_bounds__(128 * WMW, MxCfg<WMW>::BLOCKS_PER_CU) void gemm_mx_
   }
 }
 
-template <int WMW>
+template <int SCB>
 static hipError_t launch_mx(bool glu, dim3 grid, const Tile* tiles,
                             const int32_t* tile_count, const uint8_t* a,
                             const uint8_t* a_scale, const uint8_t* w,
@@ -365,19 +363,17 @@ static hipError_t launch_mx(bool glu, dim3 grid, const Tile* tiles,
                             int nslabs, const int32_t* gidx,
                             const int32_t* gbase, int gk, hipStream_t s) {
   if (glu)
-    hipLaunchKernelGGL((gemm_mx_tiled_kernel<true, WMW>), grid,
-                       dim3(128 * WMW), 0, s, tiles, tile_count, a, a_scale, w,
-                       w_scale, out, out_scale, K, Nw, Nout, nslabs, gidx,
-                       gbase, gk);
+    hipLaunchKernelGGL((gemm_mx_tiled_kernel<true, SCB>), grid, dim3(256), 0,
+                       s, tiles, tile_count, a, a_scale, w, w_scale, out,
+                       out_scale, K, Nw, Nout, nslabs, gidx, gbase, gk);
   else
-    hipLaunchKernelGGL((gemm_mx_tiled_kernel<false, WMW>), grid,
-                       dim3(128 * WMW), 0, s, tiles, tile_count, a, a_scale, w,
-                       w_scale, out, out_scale, K, Nw, Nout, nslabs, gidx,
-                       gbase, gk);
+    hipLaunchKernelGGL((gemm_mx_tiled_kernel<false, SCB>), grid, dim3(256), 0,
+                       s, tiles, tile_count, a, a_scale, w, w_scale, out,
+                       out_scale, K, Nw, Nout, nslabs, gidx, gbase, gk);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_mx_tiled(bool glu, int mt, const Tile* tiles,
+hipError_t launch_gemm_mx_tiled(bool glu, const Tile* tiles,
                                 const int32_t* tile_count, int max_tiles,
                                 const uint8_t* a, const uint8_t* a_scale,
                                 const uint8_t* w, const uint8_t* w_scale,
@@ -385,16 +381,18 @@ hipError_t launch_gemm_mx_tiled(bool glu, int mt, const Tile* tiles,
                                 int Nout, const int32_t* gidx,
                                 const int32_t* gbase, int gk, hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
-  if (mt != 128 && mt != 256) return hipErrorInvalidValue;
   const int slab = glu ? MBNW / 2 : MBNW;
   const int nslabs = (Nout + slab - 1) / slab;
   dim3 grid((unsigned)max_tiles * nslabs);
-  return mt == 256 ? launch_mx<4>(glu, grid, tiles, tile_count, a, a_scale, w,
-                                  w_scale, out, out_scale, K, Nw, Nout, nslabs,
-                                  gidx, gbase, gk, s)
-                   : launch_mx<2>(glu, grid, tiles, tile_count, a, a_scale, w,
-                                  w_scale, out, out_scale, K, Nw, Nout, nslabs,
-                                  gidx, gbase, gk, s);
+  // four steps of scales per copy when every row's scales split into whole
+  // 16-byte pieces (no copy reads past a row, so none past the array)
+  return (K / 32) % 16 == 0
+             ? launch_mx<4>(glu, grid, tiles, tile_count, a, a_scale, w,
+                            w_scale, out, out_scale, K, Nw, Nout, nslabs, gidx,
+                            gbase, gk, s)
+             : launch_mx<1>(glu, grid, tiles, tile_count, a, a_scale, w,
+                            w_scale, out, out_scale, K, Nw, Nout, nslabs, gidx,
+                            gbase, gk, s);
 }
 
 }  // namespace moe

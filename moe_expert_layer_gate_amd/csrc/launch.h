@@ -69,9 +69,9 @@ hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
                                    uint16_t* out, int K, int Nw, int Nout,
                                    const int32_t* gidx, const int32_t* gbase,
                                    int gk, hipStream_t s);
-// Same operands, LDS-tiled MFMA tiles of mt = 128 or 256 rows (the tile list
-// built with the same mt). With gidx, `a` must span less than 4 GB.
-hipError_t launch_gemm_bf16_tiled(bool glu, int mt, const Tile* tiles,
+// Same operands, 128-row LDS-tiled MFMA tiles (tile list built with mt=128).
+// With gidx, `a` must span less than 4 GB.
+hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
                                   const int32_t* tile_count, int max_tiles,
                                   const uint16_t* a, const uint16_t* w,
                                   uint16_t* out, int K, int Nw, int Nout,
@@ -92,11 +92,10 @@ hipError_t launch_gemm_mx(bool glu, int rg, const Tile* tiles,
                           uint8_t* out_scale, int K, int Nw, int Nout,
                           hipStream_t s);
 
-// Same operands, LDS-tiled scaled-MFMA tiles of mt = 128 or 256 rows (tile
-// list built with the same mt). With gidx non-NULL, A rows (and their scales)
-// are read from the per-token codes: row of sorted copy i =
-// gidx[gbase[0] + i] / gk (offsets < 2^31).
-hipError_t launch_gemm_mx_tiled(bool glu, int mt, const Tile* tiles,
+// Same operands, 128-row LDS-tiled scaled-MFMA tiles (tile list mt=128).
+// With gidx non-NULL, A rows (and their scales) are read from the per-token
+// codes: row of sorted copy i = gidx[gbase[0] + i] / gk (offsets < 2^31).
+hipError_t launch_gemm_mx_tiled(bool glu, const Tile* tiles,
                                 const int32_t* tile_count, int max_tiles,
                                 const uint8_t* a, const uint8_t* a_scale,
                                 const uint8_t* w, const uint8_t* w_scale,

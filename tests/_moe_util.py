@@ -48,9 +48,23 @@ def rel_l2(got, ref):
     return np.linalg.norm(got - ref) / (d if d > 0 else 1.0)
 
 
+def bf16_ulp(v):
+    """Unit in the last place of bf16 at |v| (8 significant bits)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, np.finfo(np.float64).tiny)))
+    return np.exp2(np.maximum(e, -126.0) - 7.0)
+
+
 def assert_close(got, ref, shape, what=""):
     """Tolerances of the layer: fp32 rel-L2 <= 1e-5; bf16 and quantised
-    rel-L2 <= 1e-2 and max-abs <= 5e-2 * RMS(ref)."""
+    rel-L2 <= 1e-2 and max-abs <= 5e-2 * RMS(ref).
+
+    A bf16 output is the rounding of an fp32 (GPU) or fp64 (oracle) sum; two
+    correct sums that straddle a rounding boundary land one bf16 ulp apart,
+    which for a rare large output (heavy-tailed MXFP4 weights give outputs
+    past 20x the RMS) exceeds 5e-2 * RMS by itself. The max-abs bound is
+    therefore applied to the part of each element's error beyond one bf16
+    ulp of the reference value; rel-L2 sees the whole error."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -60,9 +74,11 @@ def assert_close(got, ref, shape, what=""):
         assert r <= 1e-5, f"{what}: rel_l2 {r:.3e} > 1e-5"
         return r
     rms = np.sqrt(np.mean(ref ** 2)) if ref.size else 0.0
-    mx = np.max(np.abs(got - ref)) if ref.size else 0.0
+    excess = np.maximum(np.abs(got - ref) - bf16_ulp(ref), 0.0)
+    mx = np.max(excess) if ref.size else 0.0
     assert r <= 1e-2, f"{what}: rel_l2 {r:.3e} > 1e-2"
-    assert mx <= 5e-2 * rms + 1e-30, f"{what}: max_abs {mx:.3e} > 5e-2*rms {rms:.3e}"
+    assert mx <= 5e-2 * rms + 1e-30, (
+        f"{what}: max_abs beyond one bf16 ulp {mx:.3e} > 5e-2*rms {rms:.3e}")
     return r
 
 

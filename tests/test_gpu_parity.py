@@ -39,8 +39,8 @@ SMALL = {
     "prefill_skewed_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_bf16"),
                                    T=300, H=256, I=160, n_ffn=12, local_end=12,
                                    top_k=4),
-    # >= 192 rows per expert on average: the 256-row bf16 tiles; H = 384
-    # leaves a ragged GEMM2 slab, I = 160 a ragged GEMM1 slab
+    # many rows per expert: H = 384 leaves a ragged GEMM2 slab, I = 160 a
+    # ragged GEMM1 slab
     "prefill_wide_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_bf16"),
                                  T=600, H=384, I=160, n_ffn=8, local_end=8,
                                  top_k=4),
@@ -52,10 +52,10 @@ SMALL = {
                             top_k=4),
     # enough rows per expert for the 128-row LDS-tiled scaled-MFMA kernel;
     # H = 384 leaves a ragged 256-column slab in GEMM2
-    # >= 192 rows per expert on average: the 256-row scaled-MFMA tiles with
-    # the 3-stage ring (GEMM1 K = 3 steps, GEMM2 K = 4 steps)
+    # K/32 a multiple of 16: scales copied four K steps at a time (GEMM1:
+    # 8 steps = 2 batches, GEMM2: 4 steps = 1 batch)
     "ep_w4a8_wide_small": scaled(get_workload("qwen3_235b_a22b_ep_rank_w4a8"),
-                                 T=512, H=384, I=512, n_ffn=8, local_begin=2,
+                                 T=512, H=1024, I=512, n_ffn=8, local_begin=2,
                                  local_end=6, top_k=4),
     "ep_w4a8_prefill_small": scaled(get_workload("qwen3_235b_a22b_ep_rank_w4a8"),
                                     T=384, H=384, I=256, n_ffn=16, local_begin=4,
@@ -337,8 +337,8 @@ def test_edge_hot_expert_many_tiles():
 
 
 @pytest.mark.parametrize("I", [32, 64, 96])
-def test_edge_short_k_wide_tiles(I):
-    # GEMM2 with K = I of 1..3 steps of 32: shorter than the LDS ring
+def test_edge_short_k_tiled(I):
+    # GEMM2 with K = I of 1..3 steps of 32: no longer than the LDS ring
     _layer_vs_oracle(SMALL["prefill_wide_small"].replace(I=I))
 
 
