@@ -23,8 +23,8 @@
 //     fragment layout: row 16*rg + l%16, k0 + 8*(l/16) + 0..7. With a gather
 //     index the rows are read from x itself (row of sorted copy i = token
 //     sorted_copy[i] / k), so the permuted copy of x is never written.
-//   * KSPLIT waves of a block split K; partial sums meet in LDS 16 registers
-//     at a time; wave 0 applies SwiGLU / converts and stores 16 bytes per
+//   * KSPLIT waves of a block split K; partial sums meet in LDS in one or
+//     two rounds; wave 0 applies SwiGLU / converts and stores 16 bytes per
 //     row and lane.
 // Output D of each MFMA: lane l holds rows 4*(l/16) + 0..3 at column
 // col + 8*(l%16) + i, so a lane owns 8 consecutive columns of 4 rows.
@@ -57,8 +57,12 @@ MOE_DEV u32x4_t column_frag(const uint4 (&r)[8], int i) {
   return f;
 }
 
+// Two waves per SIMD: left to itself the compiler spends 288 registers per
+// lane (accumulators in AGPRs) and runs one wave per SIMD, so a decode launch
+// of two thousand waves would take two rounds.
 template <bool GLU, int RG, int KSPLIT>
-__global__ __launch_bounds__(64 * KSPLIT) void gemm_bf16_stream_kernel(
+__global__ __launch_bounds__(64 * KSPLIT)
+__attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
     const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ w,
     uint16_t* __restrict__ out, int K, int Nw, int Nout,
@@ -161,36 +165,39 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_bf16_stream_kernel(
     }
   }
 
-  // cross-wave reduction of the split-K partial sums, 16 registers a round
+  // cross-wave reduction of the split-K partial sums through LDS, up to 64
+  // registers a round (one round for 16-row tiles): every block ends here at
+  // about the same time, so the fewer barriers the shorter the exposed tail
   if (KSPLIT > 1) {
-    __shared__ float red[(KSPLIT > 1 ? KSPLIT - 1 : 1) * 16 * 64];
     constexpr int NREG = 2 * RG * 8 * 4;
+    constexpr int RR = NREG < 64 ? NREG : 64;
+    __shared__ float red[(KSPLIT > 1 ? KSPLIT - 1 : 1) * RR * 64];
 #pragma unroll
-    for (int q = 0; q < NREG / 16; ++q) {
+    for (int q = 0; q < NREG / RR; ++q) {
       if (wave > 0) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int rgi = q * 16 + j;
+        for (int j = 0; j < RR; ++j) {
+          const int rgi = q * RR + j;
           const int h = rgi / (RG * 32), rg = (rgi / 32) % RG;
           const int i = (rgi / 4) % 8, e = rgi % 4;
-          red[((wave - 1) * 16 + j) * 64 + lane] = acc[h][rg][i][e];
+          red[((wave - 1) * RR + j) * 64 + lane] = acc[h][rg][i][e];
         }
       }
       __syncthreads();
       if (wave == 0) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int rgi = q * 16 + j;
+        for (int j = 0; j < RR; ++j) {
+          const int rgi = q * RR + j;
           const int h = rgi / (RG * 32), rg = (rgi / 32) % RG;
           const int i = (rgi / 4) % 8, e = rgi % 4;
           float sum = acc[h][rg][i][e];
 #pragma unroll
           for (int ww = 0; ww < KSPLIT - 1; ++ww)
-            sum += red[(ww * 16 + j) * 64 + lane];
+            sum += red[(ww * RR + j) * 64 + lane];
           acc[h][rg][i][e] = sum;
         }
       }
-      __syncthreads();
+      if (q + 1 < NREG / RR) __syncthreads();
     }
     if (wave > 0) return;
   }
@@ -248,14 +255,9 @@ static hipError_t launch_stream(int ksplit, dim3 grid, const Tile* tiles,
                          dim3(128), 0, s, tiles, tile_count, a, w, out, K, Nw,
                          Nout, gidx, gbase, gk);
       break;
-    case 3:
+    default:
       hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 3>), grid,
                          dim3(192), 0, s, tiles, tile_count, a, w, out, K, Nw,
-                         Nout, gidx, gbase, gk);
-      break;
-    default:
-      hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 4>), grid,
-                         dim3(256), 0, s, tiles, tile_count, a, w, out, K, Nw,
                          Nout, gidx, gbase, gk);
       break;
   }
@@ -272,14 +274,16 @@ int device_cus() {
 }
 
 // Waves per block that split K. Decode launches have few (tile, slab) blocks;
-// splitting K across up to 4 waves fills the chip, but only as far as every
-// wave stays resident in one round (3 waves per SIMD for 16-row tiles, 2 for
-// 32-row tiles) and keeps at least 4 steps of 32.
+// splitting K across up to 3 waves fills the chip, but only as far as every
+// wave stays resident in one round (2 waves per SIMD) and keeps at least 4
+// steps of 32. The grid is sized for the host's upper bound on the tile
+// count; the tiles that exist on the device are typically 3/4 of it.
 int stream_ksplit(long long blocks, int steps, int rg) {
-  const long long slots = (long long)device_cus() * 4 * (rg == 1 ? 3 : 2);
+  (void)rg;
+  const long long slots = (long long)device_cus() * 4 * 2;
   int ks = 1;
-  for (int k = 2; k <= 4; ++k)
-    if (blocks * k <= slots && steps / k >= 4) ks = k;
+  for (int k = 2; k <= 3; ++k)
+    if (blocks * 3 / 4 * k <= slots && steps / k >= 4) ks = k;
   return ks;
 }
 
