@@ -55,13 +55,13 @@ TRAFFIC = {
     # workload: (kernel source set, sha256[:16] of its sources, FETCH KiB,
     #            WRITE KiB) per GEMM1 dispatch
     "qwen3_30b_a3b_decode_bf16":
-        ("gemm_bf16_stream", "dc15f36c5323b571", 342751.7, 384.0),
+        ("gemm_bf16_stream", "1cd977fa92316f22", 342876.0, 384.0),
     "qwen3_30b_a3b_prefill_skewed_bf16":
-        ("gemm_bf16_tiled", "a4d23f5ad3b14398", 586087.7, 49152.0),
+        ("gemm_bf16_tiled", "7bca9d494eefcb05", 596001.9, 49152.0),
     "longcat_flash_zero_experts_bf16":
-        ("gemm_bf16_stream", "dc15f36c5323b571", 13270927.4, 32528.0),
+        ("gemm_bf16_stream", "1cd977fa92316f22", 13561689.7, 32528.0),
     "qwen3_235b_a22b_ep_rank_w4a8":
-        ("gemm_mx_tiled", "f689ae886ad82391", 197958.9, 12932.8),
+        ("gemm_mx_tiled", "581eecb5dc46deea", 213261.0, 12829.2),
 }
 
 
