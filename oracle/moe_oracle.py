@@ -30,6 +30,14 @@ What each function follows:
                    hidden states before routing; [P1] "融合算子优化 / 融合RMSNorm MX
                    量化": round_mode "rint", dst float8_e4m3fn; OCP MX v1.0 for
                    block size 32, e8m0 scale = floor(log2(amax)) - emax_elem.
+  rms_norm, add_rms_norm_cast, add_rms_norm_mx_quant
+                   [P1] "融合算子优化": the residual add, RMSNorm and the output
+                   conversion fused into one operator -- dual output (fp32 for
+                   the router, bf16 for the experts, "融合RMSNorm Cast") or
+                   dynamic MXFP8 with round mode "rint" to float8_e4m3fn
+                   ("融合RMSNorm MX量化"; without a residual on the first layer);
+                   [P1] "RmsNorm算子优化": RMSNorm is LayerNorm without the mean
+                   subtraction, i.e. s / sqrt(mean(s^2) + eps) * weight.
   local expert range
                    [P1] "MoE EP优化 / AllGather方案": routing keeps only the copies
                    whose expert lies in this rank's range; finalize of a rank gives
@@ -42,6 +50,9 @@ Readings taken where the pages are silent (all listed in the design doc):
   * stable permutation key: (expert id, flat copy index t*k + j).
   * identity experts have ids [n_ffn, n_ffn + n_zero); a call's range
     [local_begin, local_end) is over all E_tot ids; copies outside it add 0.
+  * fused norm: the residual add is an fp32 add of the two bf16 inputs; the
+    RMSNorm is taken of that fp32 sum (not of its bf16 rounding), exactly; the
+    new residual is the sum rounded to bf16.
   * intermediates are stored in the activation dtype (bf16 or fp32) between
     the two GEMMs, or as MXFP8 when activations are quantised; y is stored in
     the activation dtype; finalize sums in high precision and rounds once.
@@ -61,6 +72,7 @@ __all__ = [
     "e8m0_decode", "mx_scale_code", "mx_quant", "mx_dequant",
     "mxfp4_unpack", "mxfp4_dequant_rows",
     "silu", "swiglu", "expert_ffn", "moe_layer", "moe_tokens", "moe_dense",
+    "rms_norm", "add_rms_norm", "add_rms_norm_cast", "add_rms_norm_mx_quant",
 ]
 
 # --------------------------------------------------------------------------
@@ -472,3 +484,51 @@ def moe_dense(*, logits, x, get_weights: WeightFn, T, H, I, n_ffn, n_zero,
             w13, w2 = get_weights(e)
             out += G[:, e:e + 1] * (swiglu(x @ w13) @ w2)
     return out
+
+
+# --------------------------------------------------------------------------
+# Upstream fused norm: residual add + RMSNorm + dual cast / dynamic MXFP8
+# --------------------------------------------------------------------------
+
+
+def rms_norm(s, weight, eps: float) -> np.ndarray:
+    """RMSNorm along the last axis in fp64: s / sqrt(mean(s^2) + eps) * weight
+    ([P1] "RmsNorm算子优化": LayerNorm without subtracting the mean)."""
+    s = np.asarray(s, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    ms = np.mean(s * s, axis=-1, keepdims=True)
+    return s / np.sqrt(ms + eps) * w
+
+
+def add_rms_norm(x, residual, weight, eps: float):
+    """Residual add then RMSNorm ([P1] "融合算子优化").
+
+    x, residual: bf16 values (as fp64) [T, H]; residual may be None (first
+    layer: the norm of x alone). The add is the fp32 sum of the two inputs;
+    the norm is exact (fp64) from that sum. Returns (y fp64 [T, H],
+    residual_out = the sum rounded to bf16)."""
+    x = np.asarray(x, dtype=np.float64)
+    if residual is None:
+        s = x
+    else:
+        s = round_f32(x + np.asarray(residual, dtype=np.float64))
+    return rms_norm(s, weight, eps), round_bf16(s)
+
+
+def add_rms_norm_cast(x, residual, weight, eps: float):
+    """[P1] "融合RMSNorm Cast": the normalised hidden states in fp32 (for the
+    router) and in bf16 (for the experts), plus the new residual.
+    Returns (y_f32, y_bf16, residual_out) as fp64 arrays of those values."""
+    y, r = add_rms_norm(x, residual, weight, eps)
+    return round_f32(y), round_bf16(y), r
+
+
+def add_rms_norm_mx_quant(x, residual, weight, eps: float):
+    """[P1] "融合RMSNorm MX量化": the normalised hidden states as MXFP8
+    (e4m3 codes rounded to nearest even, e8m0 scale per 32 along H), plus the
+    new residual. Returns (codes uint8 [T, H], scales uint8 [T, H/32],
+    residual_out fp64, y fp64 before quantisation)."""
+    y, r = add_rms_norm(x, residual, weight, eps)
+    codes, scales = mx_quant(y, "e4m3")
+    return codes, scales, r, y
+

@@ -344,3 +344,87 @@ def test_mxfp4_weights_dequant_exact():
     assert w.shape == (1, 64)
     assert w[0, :4].tolist() == [0.5 * 2**-7, 6.0 * 2**-7, -6.0 * 2**-7, -0.0]
     assert w[0, 32:36].tolist() == [0.5, 6.0, -6.0, -0.0]
+
+
+# ----------------------------------------------------------------- fused norm
+
+
+def _bf16_rows(rng, T, H, std=1.0):
+    return torch.from_numpy(rng.standard_normal((T, H)) * std).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 1e-2])
+def test_rms_norm_matches_torch(eps):
+    """torch's own rms_norm (float64) is an independent implementation."""
+    rng = np.random.default_rng(11)
+    s = rng.standard_normal((7, 96)) * rng.uniform(0.01, 10.0, (7, 1))
+    w = rng.standard_normal(96)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(s), (96,),
+                                       torch.from_numpy(w), eps).numpy()
+    np.testing.assert_allclose(O.rms_norm(s, w, eps), ref, rtol=1e-13, atol=0)
+
+
+def test_rms_norm_closed_forms():
+    w = np.array([0.5, -2.0, 3.0, 1.0])
+    # a constant row c normalises to sign(c) * weight when eps = 0
+    for c in (3.0, -0.25, 1e-20):
+        np.testing.assert_allclose(O.rms_norm(np.full((1, 4), c), w, 0.0)[0],
+                                   np.sign(c) * w, rtol=1e-15)
+    # [3, 4]: mean of squares 12.5
+    np.testing.assert_allclose(O.rms_norm(np.array([[3.0, 4.0]]), np.ones(2), 0.0),
+                               [[3 / math.sqrt(12.5), 4 / math.sqrt(12.5)]], rtol=1e-15)
+    # scale invariance without eps; with unit weight mean(y^2) = ms / (ms + eps)
+    rng = np.random.default_rng(3)
+    s = rng.standard_normal((5, 64))
+    np.testing.assert_allclose(O.rms_norm(37.0 * s, np.ones(64), 0.0),
+                               O.rms_norm(s, np.ones(64), 0.0), rtol=1e-13)
+    eps = 0.3
+    ms = np.mean(s * s, axis=1)
+    np.testing.assert_allclose(np.mean(O.rms_norm(s, np.ones(64), eps) ** 2, axis=1),
+                               ms / (ms + eps), rtol=1e-13)
+
+
+def test_add_rms_norm_residual_is_fp32_sum_rounded_to_bf16():
+    rng = np.random.default_rng(5)
+    x = _bf16_rows(rng, 9, 160)
+    r = _bf16_rows(rng, 9, 160, std=3.0)
+    r[0, :8] = torch.tensor([1e-6, -1e-6, 2.0 ** -20, 3e5, -3e5, 0.0, -0.0, 1.0]).to(torch.bfloat16)
+    # exponent gaps past fp32's 24 bits: the fp32 sum drops the small part
+    x[0, 3:5] = torch.tensor([1e-3, -1e-3]).to(torch.bfloat16)
+    w = _bf16_rows(rng, 1, 160)[0]
+    y, res = O.add_rms_norm(x.double().numpy(), r.double().numpy(),
+                            w.double().numpy(), 1e-6)
+    # torch's fp32 add and bf16 conversion as an independent path
+    ref = (x.float() + r.float()).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(res, ref)
+    s = (x.float() + r.float()).double().numpy()
+    np.testing.assert_allclose(y, O.rms_norm(s, w.double().numpy(), 1e-6), rtol=1e-15)
+    # no residual: the norm of x itself, residual out = x
+    y0, res0 = O.add_rms_norm(x.double().numpy(), None, w.double().numpy(), 1e-6)
+    assert np.array_equal(res0, x.double().numpy())
+    ref0 = torch.nn.functional.rms_norm(x.double(), (160,), w.double(), 1e-6).numpy()
+    np.testing.assert_allclose(y0, ref0, rtol=1e-13)
+
+
+def test_add_rms_norm_outputs():
+    rng = np.random.default_rng(8)
+    x = _bf16_rows(rng, 4, 128).double().numpy()
+    r = _bf16_rows(rng, 4, 128).double().numpy()
+    w = _bf16_rows(rng, 1, 128)[0].double().numpy()
+    y32, y16, res = O.add_rms_norm_cast(x, r, w, 1e-6)
+    y, res2 = O.add_rms_norm(x, r, w, 1e-6)
+    # torch's float32 / bfloat16 conversions of the exact value
+    assert np.array_equal(y32, torch.from_numpy(y).float().double().numpy())
+    assert np.array_equal(y16, torch.from_numpy(y).to(torch.bfloat16).double().numpy())
+    assert np.array_equal(res, res2)
+    codes, scales, res3, yq = O.add_rms_norm_mx_quant(x, r, w, 1e-6)
+    assert codes.shape == (4, 128) and scales.shape == (4, 4)
+    assert np.array_equal(res3, res)
+    # the MX pair reproduces y to within half an e4m3 step at the block scale
+    # (values past 448 at that scale saturate)
+    sc = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)
+    a = np.abs(yq) / sc
+    ulp = np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3)
+    bound = np.where(a > 448, a - 448, 0.5 * ulp) * sc
+    deq = O.mx_dequant(codes, scales, "e4m3")
+    assert np.all(np.abs(deq - yq) <= bound * (1 + 1e-12))
