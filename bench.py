@@ -16,7 +16,12 @@ Prints ONE JSON line: whole-step tokens/s plus
                same workload (a reported baseline, not the target).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--op layer|norm_cast|norm_mx]
+
+--op norm_cast / norm_mx time the fused residual add + RMSNorm in front of the
+MoE block instead (dual fp32/bf16 output, or MXFP8), on the workload's T x H
+rows; its JSON line has the same fields with the norm kernel as the roofline
+kernel (HBM bound).
 """
 from __future__ import annotations
 
@@ -111,6 +116,10 @@ def _parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the reference copy for counter scaling")
+    ap.add_argument("--op", default="layer",
+                    choices=["layer", "norm_cast", "norm_mx"],
+                    help="what one step is: the MoE layer (default) or the "
+                         "fused add + RMSNorm in front of it")
     ap.add_argument("--print-source-sha", action="store_true",
                     help="print the source hashes that key the traffic table")
     return ap.parse_args()
@@ -231,6 +240,8 @@ def main():
     from moe_inputs import generate, get_workload
 
     m.lib()
+    if args.op != "layer":
+        return _bench_norm(args, m)
     shape = get_workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -326,6 +337,95 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = _cpu_baseline(shape, inp, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+def _bench_norm(args, m):
+    """One step = one fused residual add + RMSNorm over the workload's T x H
+    hidden states (bf16 x and residual resident in HBM)."""
+    import numpy as np
+    import torch
+
+    from moe_inputs import NORM_EPS, generate_norm, get_workload
+
+    shape = get_workload(args.workload)
+    T, H = shape.T, shape.H
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = generate_norm(T, H, seed=args.seed, device=dev)
+    mx = args.op == "norm_mx"
+    y32 = torch.empty((T, H), dtype=torch.float32, device=dev)
+    y16 = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    codes = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    scales = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+    res = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    L = m.lib()
+    from moe_expert_layer_gate_amd import _ptr, _stream
+
+    def step():
+        if mx:
+            st = L.moe_add_rms_norm_mx_quant(T, H, _ptr(inp["x"]), _ptr(inp["residual"]),
+                                             _ptr(inp["weight"]), NORM_EPS, _ptr(codes),
+                                             _ptr(scales), _ptr(res), _stream())
+        else:
+            st = L.moe_add_rms_norm_cast(T, H, _ptr(inp["x"]), _ptr(inp["residual"]),
+                                         _ptr(inp["weight"]), NORM_EPS, _ptr(y32),
+                                         _ptr(y16), _ptr(res), _stream())
+        assert st == 0, st
+
+    for _ in range(args.warmup):
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    us = sum(a.elapsed_time(b) for a, b in ev) * 1e3 / args.steps
+    # algorithmic bytes: x and residual read, new residual and y written
+    # (fp32 + bf16, or e4m3 codes + e8m0 scales), the norm weight read once
+    per_tok = 2 * H + 2 * H + 2 * H + ((H + H // 32) if mx else (4 * H + 2 * H))
+    nbytes = T * per_tok + 2 * H
+    ach = nbytes / (us * 1e-6) / 1e9
+    rec = {
+        "metric": "fused residual add + RMSNorm tokens/s",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16->mxfp8" if mx else "bf16->f32+bf16", "data": "synthetic",
+        "config": {"workload": f"add_rms_norm_{'mx' if mx else 'cast'} of {shape.name}",
+                   "T": T, "H": H, "eps": NORM_EPS, "residual": True,
+                   "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "add_rms_norm_" + ("mx" if mx else "cast"),
+                     "avg_us": round(us, 2), "algorithmic_bytes": int(nbytes)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        x = inp["x"].double().cpu().numpy()
+        r = inp["residual"].double().cpu().numpy()
+        w = inp["weight"].double().cpu().numpy()
+        fn = O.add_rms_norm_mx_quant if mx else O.add_rms_norm_cast
+        done, t0 = 0, time.perf_counter()
+        while True:
+            fn(x, r, w, NORM_EPS)
+            done += T
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or done >= 20 * T:
+                break
+        rec["cpu_baseline"] = {"value": round(done / el, 1), "unit": "tokens/s",
+                               "cores": torch.get_num_threads(), "kind": "oracle",
+                               "sample": f"all {T} rows x{done // T}",
+                               "seconds": round(el, 1)}
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

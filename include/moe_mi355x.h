@@ -213,6 +213,48 @@ MOE_API moe_status moe_layer_traced(const moe_problem* p, const float* logits,
                                     size_t* workspace_bytes, void* stream,
                                     void* const* stage_events, int32_t n_events);
 
+/* ---------------------------------------------------------------------
+ * Upstream fused norm ([P1] "融合算子优化"): the residual add, the RMSNorm in
+ * front of the MoE block and the conversion of its output in one pass, so
+ * that neither the sum nor the normalised rows are written and read back
+ * between operators.
+ *
+ *   s[t]            = x[t] + residual[t]  (fp32 add of the bf16 inputs;
+ *                                           s = x when residual is NULL, the
+ *                                           first layer)
+ *   residual_out[t] = bf16(s[t])            (the new residual stream)
+ *   y[t]            = s[t] / sqrt(mean(s[t]^2) + epsilon) * norm_weight
+ *                     ([P1] "RmsNorm算子优化": LayerNorm without the mean)
+ *
+ * x, residual, residual_out: bf16 [T, H]; norm_weight: bf16 [H]. residual
+ * and residual_out may be NULL (residual_out is then not written). T >= 0
+ * (T == 0 launches nothing), H % 32 == 0 and H <= 8192 (else
+ * MOE_ERR_UNSUPPORTED), epsilon finite and >= 0 (else MOE_ERR_INVALID_ARG).
+ * The mean of squares is accumulated in fp32.
+ */
+
+/* "融合RMSNorm Cast": y in fp32 [T, H] (for the router) and in bf16 [T, H]
+ * (for the experts), each rounded to nearest even from the fp32 value. Either
+ * output may be NULL (not written), not both. */
+MOE_API moe_status moe_add_rms_norm_cast(int32_t T, int32_t H, const void* x,
+                                         const void* residual,
+                                         const void* norm_weight, float epsilon,
+                                         float* y_f32, void* y_bf16,
+                                         void* residual_out, void* stream);
+
+/* "融合RMSNorm MX量化": y as MXFP8 -- e4m3fn codes [T, H], rounded to nearest
+ * even ("rint") and saturating at 448, with one e8m0 scale per 32 consecutive
+ * columns [T, H/32] (OCP MX v1.0: floor(log2(amax)) - 8, clamped; an
+ * all-zero block gets code 0): the layout of moe_init_routing's MXFP8
+ * x_perm. */
+MOE_API moe_status moe_add_rms_norm_mx_quant(int32_t T, int32_t H,
+                                             const void* x,
+                                             const void* residual,
+                                             const void* norm_weight,
+                                             float epsilon, uint8_t* y_codes,
+                                             uint8_t* y_scales,
+                                             void* residual_out, void* stream);
+
 /* Static strings; never NULL. */
 MOE_API const char* moe_status_string(moe_status s);
 /* Library ABI version (major * 100 + minor). */

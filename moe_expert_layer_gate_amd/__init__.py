@@ -7,7 +7,8 @@ or ``python moe_expert_layer_gate_amd/build.py``); importing the binding
 without it raises, there is no fallback.
 
 Calls mirror the C ABI in include/moe_mi355x.h:
-  gate_topk, init_routing, ffn_up, ffn_down, grouped_ffn, finalize, layer.
+  gate_topk, init_routing, ffn_up, ffn_down, grouped_ffn, finalize, layer,
+  add_rms_norm_cast, add_rms_norm_mx_quant.
 """
 from __future__ import annotations
 
@@ -21,6 +22,7 @@ __all__ = [
     "LIB_PATH", "MoeProblem", "MoeError", "lib", "problem", "gate_topk",
     "init_routing", "ffn_up", "ffn_down", "grouped_ffn", "finalize", "layer",
     "layer_workspace_bytes", "layer_traced", "SYMBOLS", "STAGES",
+    "add_rms_norm_cast", "add_rms_norm_mx_quant",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -31,6 +33,7 @@ _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8_E4M3,
 
 SYMBOLS = ["moe_gate_topk", "moe_init_routing", "moe_grouped_ffn", "moe_ffn_up",
            "moe_ffn_down", "moe_finalize", "moe_layer", "moe_layer_traced",
+           "moe_add_rms_norm_cast", "moe_add_rms_norm_mx_quant",
            "moe_status_string", "moe_abi_version"]
 
 # stages of moe_layer_traced, in launch order
@@ -81,6 +84,11 @@ def lib() -> ctypes.CDLL:
                              _sz, _vp, ctypes.POINTER(ctypes.c_void_p),
                              ctypes.c_int32],
     }
+    _i32, _f32 = ctypes.c_int32, ctypes.c_float
+    sig["moe_add_rms_norm_cast"] = [_i32, _i32, _vp, _vp, _vp, _f32, _vp, _vp,
+                                    _vp, _vp]
+    sig["moe_add_rms_norm_mx_quant"] = [_i32, _i32, _vp, _vp, _vp, _f32, _vp,
+                                        _vp, _vp, _vp]
     for name, args in sig.items():
         f = getattr(L, name)
         f.argtypes = args
@@ -285,3 +293,45 @@ def layer(p: MoeProblem, logits, x, w13, w2, w13_scale=None, w2_scale=None,
                            _ptr(w2_scale), _ptr(out), _ptr(workspace),
                            ctypes.byref(n), _stream()))
     return out
+
+
+def _norm_args(x, residual, norm_weight):
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a [T, H] bfloat16 tensor")
+    T, H = x.shape
+    if residual is not None and (residual.shape != x.shape or residual.dtype != x.dtype):
+        raise ValueError("residual must match x")
+    if norm_weight.shape != (H,) or norm_weight.dtype != torch.bfloat16:
+        raise ValueError("norm_weight must be a [H] bfloat16 tensor")
+    return T, H
+
+
+def add_rms_norm_cast(x, residual, norm_weight, eps: float, want_f32=True,
+                      want_bf16=True, want_residual=True):
+    """Residual add + RMSNorm with fp32 and bf16 outputs.
+    Returns (y_f32 or None, y_bf16 or None, residual_out or None)."""
+    T, H = _norm_args(x, residual, norm_weight)
+    y32 = torch.empty((T, H), dtype=torch.float32, device=x.device) if want_f32 else None
+    y16 = torch.empty((T, H), dtype=torch.bfloat16, device=x.device) if want_bf16 else None
+    res = torch.empty_like(x) if want_residual else None
+    _check(lib().moe_add_rms_norm_cast(T, H, _ptr(x), _ptr(residual),
+                                       _ptr(norm_weight), float(eps), _ptr(y32),
+                                       _ptr(y16), _ptr(res), _stream()))
+    return y32, y16, res
+
+
+def add_rms_norm_mx_quant(x, residual, norm_weight, eps: float,
+                          want_residual=True):
+    """Residual add + RMSNorm with MXFP8 output.
+    Returns (codes uint8 [T, H], scales uint8 [T, H/32], residual_out or None)."""
+    T, H = _norm_args(x, residual, norm_weight)
+    codes = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((T, H // 32 if H % 32 == 0 else 1), dtype=torch.uint8,
+                         device=x.device)
+    res = torch.empty_like(x) if want_residual else None
+    _check(lib().moe_add_rms_norm_mx_quant(T, H, _ptr(x), _ptr(residual),
+                                           _ptr(norm_weight), float(eps),
+                                           _ptr(codes), _ptr(scales), _ptr(res),
+                                           _stream()))
+    return codes, scales, res
+

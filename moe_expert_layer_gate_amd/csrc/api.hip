@@ -9,6 +9,7 @@ using moe::Tile;
 
 constexpr int kMaxE = 2048;
 constexpr int kMaxK = 64;
+constexpr int kMaxNormH = 8192;  // fused norm: 16 chunks of 8 columns per lane
 
 struct Prob {
   int T, H, I, nffn, nzero, k, lb, le, act, wt, actq;
@@ -361,6 +362,37 @@ moe_status moe_finalize(const moe_problem* p, const int32_t* topk_ids,
       topk_ids, topk_weight, copy_pos, offsets, q.fb, q.nffn, q.lb, q.le, y, x,
       residual, out, q.act == MOE_F32 ? 0 : 1, q.T, q.H, q.k,
       (hipStream_t)stream));
+}
+
+moe_status moe_add_rms_norm_cast(int32_t T, int32_t H, const void* x,
+                                 const void* residual, const void* norm_weight,
+                                 float epsilon, float* y_f32, void* y_bf16,
+                                 void* residual_out, void* stream) {
+  if (T < 0 || H <= 0 || !(epsilon >= 0.f) || epsilon > 3.0e38f)
+    return MOE_ERR_INVALID_ARG;
+  if (H % 32 || H > kMaxNormH) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !norm_weight || (!y_f32 && !y_bf16)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_add_rms_norm(
+      0, (const uint16_t*)x, (const uint16_t*)residual,
+      (const uint16_t*)norm_weight, epsilon, T, H, y_f32, (uint16_t*)y_bf16,
+      nullptr, nullptr, (uint16_t*)residual_out, (hipStream_t)stream));
+}
+
+moe_status moe_add_rms_norm_mx_quant(int32_t T, int32_t H, const void* x,
+                                     const void* residual,
+                                     const void* norm_weight, float epsilon,
+                                     uint8_t* y_codes, uint8_t* y_scales,
+                                     void* residual_out, void* stream) {
+  if (T < 0 || H <= 0 || !(epsilon >= 0.f) || epsilon > 3.0e38f)
+    return MOE_ERR_INVALID_ARG;
+  if (H % 32 || H > kMaxNormH) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !norm_weight || !y_codes || !y_scales) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_add_rms_norm(
+      1, (const uint16_t*)x, (const uint16_t*)residual,
+      (const uint16_t*)norm_weight, epsilon, T, H, nullptr, nullptr, y_codes,
+      y_scales, (uint16_t*)residual_out, (hipStream_t)stream));
 }
 
 moe_status moe_layer_traced(const moe_problem* p, const float* logits,

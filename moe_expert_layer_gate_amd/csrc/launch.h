@@ -103,6 +103,14 @@ hipError_t launch_gemm_mx_tiled(bool glu, const Tile* tiles,
                                 int Nout, const int32_t* gidx,
                                 const int32_t* gbase, int gk, hipStream_t s);
 
+// Residual add + RMSNorm; mx = 0: fp32 and/or bf16 outputs, mx = 1: MXFP8
+// codes + e8m0 scales. H % 32 == 0, H <= 8192; residual / outputs may be null.
+hipError_t launch_add_rms_norm(int mx, const uint16_t* x, const uint16_t* r,
+                               const uint16_t* w, float eps, int T, int H,
+                               float* y32, uint16_t* y16, uint8_t* codes,
+                               uint8_t* scales, uint16_t* res_out,
+                               hipStream_t s);
+
 hipError_t launch_finalize(const int32_t* ids, const float* w,
                            const int32_t* copy_pos, const int32_t* offsets,
                            int fb, int n_ffn, int lb, int le, const void* y,

@@ -30,7 +30,7 @@ from typing import Dict, Optional
 import torch
 
 __all__ = ["MoEShape", "WORKLOADS", "get_workload", "generate", "seed_for",
-           "scaled"]
+           "scaled", "generate_norm", "NORM_EPS"]
 
 
 @dataclass(frozen=True)
@@ -132,6 +132,10 @@ _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 ROLE_LOGITS, ROLE_BIAS, ROLE_X, ROLE_RES, ROLE_W13, ROLE_W2 = range(6)
 ROLE_W13_SCALE, ROLE_W2_SCALE = 6, 7
+ROLE_NORM_X, ROLE_NORM_RES, ROLE_NORM_W = 8, 9, 10
+
+# RMSNorm epsilon of the Qwen3-MoE family's configs
+NORM_EPS = 1e-6
 
 
 def generate(shape: MoEShape, seed: int = 0, device="cpu",
@@ -206,3 +210,24 @@ def generate(shape: MoEShape, seed: int = 0, device="cpu",
     else:
         raise ValueError(shape.wt)
     return out
+
+
+def generate_norm(T: int, H: int, seed: int = 0, device="cpu",
+                  residual: bool = True, name: str = "fused_norm"
+                  ) -> Dict[str, Optional[torch.Tensor]]:
+    """Inputs of the fused residual add + RMSNorm in front of the MoE block:
+      x, residual  bf16 [T, H], N(0, 1) (the attention output and the residual
+                   stream);
+      weight       bf16 [H], 1 + N(0, 0.1) (a norm weight near one).
+    """
+    dev = torch.device(device)
+    key = MoEShape(name, T=T, H=H, I=32, n_ffn=1, n_zero=0, top_k=1,
+                   local_begin=0, local_end=1, act="bf16", wt="bf16",
+                   act_q="none")
+    x = _normal((T, H), 1.0, torch.bfloat16, dev, seed_for(key, seed, ROLE_NORM_X))
+    r = (_normal((T, H), 1.0, torch.bfloat16, dev, seed_for(key, seed, ROLE_NORM_RES))
+         if residual else None)
+    w = _normal((H,), 0.1, torch.float32, dev, seed_for(key, seed, ROLE_NORM_W))
+    w = (w + 1.0).to(torch.bfloat16)
+    return {"x": x, "residual": r, "weight": w}
+

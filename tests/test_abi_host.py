@@ -111,3 +111,28 @@ def test_missing_pointers_rejected(L):
 
 def test_null_problem(L):
     assert L.moe_gate_topk(None, None, None, None, None) == 1
+
+
+def test_fused_norm_host_checks(L):
+    """Argument checks of the fused-norm calls happen before any launch."""
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails a check
+    cast, mxq = L.moe_add_rms_norm_cast, L.moe_add_rms_norm_mx_quant
+    # H not a multiple of 32, or past 8192 columns: unsupported
+    assert cast(4, 100, fake, None, fake, 1e-6, fake, fake, None, None) == 2
+    assert cast(4, 8224, fake, None, fake, 1e-6, fake, fake, None, None) == 2
+    assert mxq(4, 48, fake, None, fake, 1e-6, fake, fake, None, None) == 2
+    # bad sizes / epsilon
+    assert cast(-1, 64, fake, None, fake, 1e-6, fake, fake, None, None) == 1
+    assert cast(4, 0, fake, None, fake, 1e-6, fake, fake, None, None) == 1
+    assert cast(4, 64, fake, None, fake, -1.0, fake, fake, None, None) == 1
+    assert cast(4, 64, fake, None, fake, float("nan"), fake, fake, None, None) == 1
+    assert mxq(4, 64, fake, None, fake, float("inf"), fake, fake, None, None) == 1
+    # missing inputs or outputs
+    assert cast(4, 64, None, None, fake, 1e-6, fake, fake, None, None) == 1
+    assert cast(4, 64, fake, None, None, 1e-6, fake, fake, None, None) == 1
+    assert cast(4, 64, fake, None, fake, 1e-6, None, None, fake, None) == 1
+    assert mxq(4, 64, fake, None, fake, 1e-6, None, fake, None, None) == 1
+    assert mxq(4, 64, fake, None, fake, 1e-6, fake, None, None, None) == 1
+    # no rows: nothing to do, nothing launched
+    assert cast(0, 64, None, None, None, 1e-6, None, None, None, None) == 0
+    assert mxq(0, 64, None, None, None, 1e-6, None, None, None, None) == 0
