@@ -60,9 +60,6 @@ int tile_rows(const Prob& q) {
 
 // moe_layer fuses the gather into GEMM1's activation loads for bf16 (the
 // tiled kernel addresses x with 32-bit offsets, so x must span < 4 GB).
-// Up to this many tokens the gate runs inside the single-block routing kernel
-// (16 waves, each scoring a token at a time).
-constexpr int64_t kSmallGateTokens = 64;
 
 bool fused_gather(const Prob& q) {
   return q.act == MOE_BF16 && !q.mx &&
@@ -243,11 +240,10 @@ moe_status moe_init_routing(const moe_problem* p, const int32_t* topk_ids,
     return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   if (moe::route_small_ok((int)q.N, q.E)) {
-    MOE_TRY(moe::launch_route_small(nullptr, q.T, q.k,
-                                    const_cast<int32_t*>(topk_ids), nullptr,
-                                    (int)q.N, q.E, tokens_per_expert, offsets,
-                                    sorted_copy, copy_pos, q.fb, q.fe, 0,
-                                    nullptr, 0, nullptr, s));
+    MOE_TRY(moe::launch_route_small(topk_ids, (int)q.N, q.E,
+                                    tokens_per_expert, offsets, sorted_copy,
+                                    copy_pos, q.fb, q.fe, 0, nullptr, 0,
+                                    nullptr, s));
   } else {
     if (q.N > 0) MOE_TRY(moe::launch_route_count(topk_ids, (int)q.N, q.E, cc, s));
     MOE_TRY(moe::launch_route_scan(cc, nch, q.E, tokens_per_expert, offsets,
@@ -442,17 +438,14 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
       return hipEventRecord((hipEvent_t)stage_events[i], s);
     return hipSuccess;
   };
-  // small problems route in one block; the tiniest also run the gate there
+  // small problems route in one block
   const bool small = moe::route_small_ok((int)q.N, q.E);
-  const bool small_gate = small && q.T <= kSmallGateTokens;
   const int mtl = (int)max_tiles(q, mt);
   MOE_TRY(mark(0));
-  if (!small_gate)
-    MOE_TRY(moe::launch_gate_topk(logits, q.T, q.E, q.k, ids, wts, s));
+  MOE_TRY(moe::launch_gate_topk(logits, q.T, q.E, q.k, ids, wts, s));
   MOE_TRY(mark(1));
   if (small) {
-    MOE_TRY(moe::launch_route_small(small_gate ? logits : nullptr, q.T, q.k,
-                                    ids, wts, (int)q.N, q.E, counts, offsets,
+    MOE_TRY(moe::launch_route_small(ids, (int)q.N, q.E, counts, offsets,
                                     sorted_copy, copy_pos, q.fb, q.fe, mt,
                                     mtl ? fw.tiles : nullptr, mtl,
                                     fw.tile_count, s));

@@ -35,18 +35,25 @@ MOE_DEV float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-// slot: this wave's 64 (key, id) pairs in LDS.
+// This lane's keys of one router row: expert e = lane + 64 * i.
 template <int VPL>
-MOE_DEV void topk_softmax_wave(const float* __restrict__ row, int E, int k,
-                               int32_t* __restrict__ ids,
-                               float* __restrict__ wout, uint2* slot) {
+MOE_DEV void load_row_keys(const float* __restrict__ row, int E,
+                           uint32_t (&key)[VPL]) {
   const int lane = threadIdx.x & 63;
-  uint32_t key[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
     key[i] = e < E ? order_key(row[e]) : 0u;
   }
+}
+
+// Top-k + softmax of a row whose keys are already in registers.
+// slot: this wave's 64 (key, id) pairs in LDS.
+template <int VPL>
+MOE_DEV void topk_softmax_keys(const uint32_t (&key)[VPL], int k,
+                               int32_t* __restrict__ ids,
+                               float* __restrict__ wout, uint2* slot) {
+  const int lane = threadIdx.x & 63;
   // the k-th largest key
   uint32_t thr = 0;
   for (int b = 31; b >= 0; --b) {
@@ -97,6 +104,16 @@ MOE_DEV void topk_softmax_wave(const float* __restrict__ row, int E, int k,
   // the slots are reused by this wave's next row
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// slot: this wave's 64 (key, id) pairs in LDS.
+template <int VPL>
+MOE_DEV void topk_softmax_wave(const float* __restrict__ row, int E, int k,
+                               int32_t* __restrict__ ids,
+                               float* __restrict__ wout, uint2* slot) {
+  uint32_t key[VPL];
+  load_row_keys<VPL>(row, E, key);
+  topk_softmax_keys<VPL>(key, k, ids, wout, slot);
 }
 
 }  // namespace moe

@@ -36,15 +36,14 @@ hipError_t launch_route_scatter(const int32_t* ids, int N, int E,
                                 const int32_t* chunk_base,
                                 const int32_t* offsets, int32_t* sorted_copy,
                                 int32_t* copy_pos, hipStream_t s);
-// Single-block routing (count + scan + tile list + scatter, optionally the
-// gate too when logits != NULL) for N <= 4096 copies and E <= 1024.
+// Single-block routing (count + scan + tile list + scatter) for N <= 4096
+// copies and E <= 1024.
 bool route_small_ok(int N, int E);
-hipError_t launch_route_small(const float* logits, int T, int k, int32_t* ids,
-                              float* wts, int N, int E, int32_t* counts,
-                              int32_t* offsets, int32_t* sorted_copy,
-                              int32_t* copy_pos, int fb, int fe, int mt,
-                              Tile* tiles, int max_tiles, int32_t* tile_count,
-                              hipStream_t s);
+hipError_t launch_route_small(const int32_t* ids, int N, int E,
+                              int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_copy, int32_t* copy_pos, int fb,
+                              int fe, int mt, Tile* tiles, int max_tiles,
+                              int32_t* tile_count, hipStream_t s);
 // act: 0 f32, 1 bf16. mx: quantise rows to MXFP8 (bf16 input only).
 // MXFP8 codes and e8m0 scales of the T rows of x (bf16), in token order.
 hipError_t launch_quantize_mx(const void* x, int T, int H, uint8_t* xq,
