@@ -16,6 +16,11 @@ Distributions ("N(0, s)" means standard deviation s):
   * MXFP4 expert weights: e2m1 codes drawn uniformly over all 16 codes and e8m0
     block scales drawn uniformly from {119, 120, 121} (2^-8..2^-6), which gives
     an element RMS of about 0.012..0.046, close to N(0, 0.02).
+  * int8 expert weights (W8A8): codes N(0, 32) rounded and clipped to
+    [-127, 127] (a per-channel amax near 127, as symmetric quantisation of a
+    Gaussian column gives) with one fp32 scale per output channel drawn
+    uniformly from [0.75, 1.25] * 0.02 / 32, so elements are again about
+    N(0, 0.02).
 
 Generation uses torch's seeded generator on the requested device, so the same
 (workload, seed, device) always gives the same tensors; the CPU oracle receives
@@ -45,8 +50,8 @@ class MoEShape:
     local_begin: int  # expert range [local_begin, local_end) handled by the call
     local_end: int
     act: str          # "f32" | "bf16"  (x, residual, y, out)
-    wt: str           # "f32" | "bf16" | "mxfp4"
-    act_q: str        # "none" | "mxfp8" (dynamic activation quantisation)
+    wt: str           # "f32" | "bf16" | "mxfp4" | "int8"
+    act_q: str        # "none" | "mxfp8" | "int8" (dynamic activation quantisation)
     w_std: float = 0.02
     logit_bias_std: float = 0.0
     residual: bool = False
@@ -90,6 +95,14 @@ WORKLOADS: Dict[str, MoEShape] = {
         MoEShape("qwen3_235b_a22b_ep_rank_w4a8", T=4096, H=4096, I=1536,
                  n_ffn=128, n_zero=0, top_k=8, local_begin=32, local_end=64,
                  act="bf16", wt="mxfp4", act_q="mxfp8"),
+        # W8A8 routed experts on the Qwen3-30B-A3B shapes
+        MoEShape("qwen3_30b_a3b_decode_w8a8", T=32, H=2048, I=768, n_ffn=128,
+                 n_zero=0, top_k=8, local_begin=0, local_end=128, act="bf16",
+                 wt="int8", act_q="int8"),
+        MoEShape("qwen3_30b_a3b_prefill_skewed_w8a8", T=4096, H=2048, I=768,
+                 n_ffn=128, n_zero=0, top_k=8, local_begin=0, local_end=128,
+                 act="bf16", wt="int8", act_q="int8", logit_bias_std=1.5,
+                 residual=True),
     ]
 }
 
@@ -129,6 +142,21 @@ def _normal(shape, std, dtype, device, s) -> torch.Tensor:
 
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+# spread of the int8 weight codes (a Gaussian column whose amax is near 127)
+INT8_CODE_STD = 32.0
+
+
+def _int8_codes(shape, device, s) -> torch.Tensor:
+    t = torch.randn(shape, generator=_gen(device, s), device=device,
+                    dtype=torch.float32)
+    return (t * INT8_CODE_STD).round_().clamp_(-127, 127).to(torch.int8)
+
+
+def _channel_scales(n, w_std, device, s) -> torch.Tensor:
+    u = torch.rand((n,), generator=_gen(device, s), device=device,
+                   dtype=torch.float32)
+    return (0.75 + 0.5 * u) * (w_std / INT8_CODE_STD)
 
 ROLE_LOGITS, ROLE_BIAS, ROLE_X, ROLE_RES, ROLE_W13, ROLE_W2 = range(6)
 ROLE_W13_SCALE, ROLE_W2_SCALE = 6, 7
@@ -206,6 +234,19 @@ def generate(shape: MoEShape, seed: int = 0, device="cpu",
                                   dtype=torch.int32,
                                   generator=_gen(dev, seed_for(shape, seed, ROLE_W2_SCALE, e))
                                   ).to(torch.uint8)
+        out["w13"], out["w2"], out["w13_scale"], out["w2_scale"] = w13, w2, s13, s2
+    elif shape.wt == "int8":
+        w13 = torch.empty((El, 2 * I, H), dtype=torch.int8, device=dev)
+        w2 = torch.empty((El, H, I), dtype=torch.int8, device=dev)
+        s13 = torch.empty((El, 2 * I), dtype=torch.float32, device=dev)
+        s2 = torch.empty((El, H), dtype=torch.float32, device=dev)
+        for i, e in enumerate(experts):
+            w13[i] = _int8_codes((2 * I, H), dev, seed_for(shape, seed, ROLE_W13, e))
+            w2[i] = _int8_codes((H, I), dev, seed_for(shape, seed, ROLE_W2, e))
+            s13[i] = _channel_scales(2 * I, shape.w_std, dev,
+                                     seed_for(shape, seed, ROLE_W13_SCALE, e))
+            s2[i] = _channel_scales(H, shape.w_std, dev,
+                                    seed_for(shape, seed, ROLE_W2_SCALE, e))
         out["w13"], out["w2"], out["w13_scale"], out["w2_scale"] = w13, w2, s13, s2
     else:
         raise ValueError(shape.wt)

@@ -9,6 +9,8 @@ Sources (web pages; cited by title and section):
   [P1] "Qwen3-MoE low-latency inference on Atlas A3 / 950 clusters"
        (cann-recipes-infer practice article)
   [P2] "LongCat-Flash inference on Atlas A3 clusters"
+  [P3] "NPU Qwen3-Next inference practice" (cann-recipes-infer practice
+       article; only its quantisation strategy section is used)
   OCP Microscaling Formats (MX) v1.0 specification for the MX element/scale
   encodings, which the pages use by name (MXFP8 / MXFP4) without defining.
 
@@ -30,6 +32,10 @@ What each function follows:
                    hidden states before routing; [P1] "融合算子优化 / 融合RMSNorm MX
                    量化": round_mode "rint", dst float8_e4m3fn; OCP MX v1.0 for
                    block size 32, e8m0 scale = floor(log2(amax)) - emax_elem.
+  int8_quant_rows, int8_dequant_rows
+                   [P3] "量化策略": routed experts in W8A8 -- weights int8 with a
+                   static scale per output channel, activations int8 with a
+                   dynamic scale per token (per row).
   rms_norm, add_rms_norm_cast, add_rms_norm_mx_quant
                    [P1] "融合算子优化": the residual add, RMSNorm and the output
                    conversion fused into one operator -- dual output (fp32 for
@@ -54,8 +60,14 @@ Readings taken where the pages are silent (all listed in the design doc):
     RMSNorm is taken of that fp32 sum (not of its bf16 rounding), exactly; the
     new residual is the sum rounded to bf16.
   * intermediates are stored in the activation dtype (bf16 or fp32) between
-    the two GEMMs, or as MXFP8 when activations are quantised; y is stored in
-    the activation dtype; finalize sums in high precision and rounds once.
+    the two GEMMs, or as MXFP8 / int8 when activations are quantised (the
+    fp32-rounded h is quantised); y is stored in the activation dtype;
+    finalize sums in high precision and rounds once.
+  * W8A8: symmetric int8 codes in [-127, 127]; a row's scale is its amax / 127
+    in fp32 and its codes are rint(v / scale) in fp32 (ties to even); an
+    all-zero row has scale 0 and codes 0. Weights arrive already quantised
+    (codes + one fp32 scale per output channel). x is quantised once per
+    token before routing and gathered; h per row (token copy).
 
 Parity status: every function here is pinned by tests/test_oracle_pins.py.
 """
@@ -71,6 +83,7 @@ __all__ = [
     "e4m3_decode", "e4m3_encode", "e2m1_decode", "e2m1_encode",
     "e8m0_decode", "mx_scale_code", "mx_quant", "mx_dequant",
     "mxfp4_unpack", "mxfp4_dequant_rows",
+    "int8_quant_rows", "int8_dequant_rows",
     "silu", "swiglu", "expert_ffn", "moe_layer", "moe_tokens", "moe_dense",
     "rms_norm", "add_rms_norm", "add_rms_norm_cast", "add_rms_norm_mx_quant",
 ]
@@ -290,6 +303,40 @@ def mxfp4_dequant_rows(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# W8A8: symmetric int8 with one fp32 scale per row ([P3] "量化策略")
+# --------------------------------------------------------------------------
+
+
+def int8_quant_rows(v):
+    """Dynamic per-row (per-token) int8 quantisation along the last axis.
+
+    The values must be fp32 numbers (bf16 x, or h after its fp32 rounding).
+    Per row: amax = max |v|; scale = amax / 127 rounded to fp32; code =
+    rint(v / scale) with the division rounded to fp32 and rint taking ties to
+    even, clipped to [-127, 127]. An all-zero row gets scale 0 and codes 0.
+    Returns (codes int8 [..., K], scales float32 [...])."""
+    v64 = np.asarray(v, dtype=np.float64)
+    v32 = v64.astype(np.float32)
+    if not np.array_equal(v32.astype(np.float64), v64):
+        raise ValueError("int8_quant_rows takes fp32 values")
+    amax = np.abs(v32).max(axis=-1)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    nz = scale > 0
+    div = np.where(nz, scale, np.float32(1.0)).astype(np.float32)
+    q = np.rint(v32 / div[..., None])            # fp32 quotient, half to even
+    q = np.clip(q, -127, 127)
+    q = np.where(nz[..., None], q, 0.0)
+    return q.astype(np.int8), scale
+
+
+def int8_dequant_rows(codes, scales) -> np.ndarray:
+    """codes [..., K] * scales[...] per row, exact in fp64. For weights the
+    rows are output channels ([N, K] codes, [N] scales)."""
+    return (np.asarray(codes, dtype=np.float64)
+            * np.asarray(scales, dtype=np.float64)[..., None])
+
+
+# --------------------------------------------------------------------------
 # Expert FFN: down(SiLU(gate(x)) * up(x)) with merged w13
 # --------------------------------------------------------------------------
 
@@ -313,6 +360,9 @@ def _act_rows(xrows: np.ndarray, act_q: str):
     if act_q == "mxfp8":
         codes, sc = mx_quant(xrows, "e4m3")
         return mx_dequant(codes, sc, "e4m3"), (codes, sc)
+    if act_q == "int8":
+        codes, sc = int8_quant_rows(xrows)
+        return int8_dequant_rows(codes, sc), (codes, sc)
     return np.asarray(xrows, dtype=np.float64), None
 
 
@@ -322,9 +372,10 @@ def expert_ffn(a: np.ndarray, w13: np.ndarray, w2: np.ndarray, *,
 
     w13: fp64 [H, 2I] (columns [0, I) gate, [I, 2I) up); w2: fp64 [I, H].
     Storage roundings (bf16 / fp32) between the steps follow the activation
-    format unless `exact`; MXFP8 quantisation of h (act_q == "mxfp8") is part
+    format unless `exact`; quantisation of h (act_q "mxfp8" or "int8") is part
     of the computed function and is applied either way, to the fp32-rounded h
-    unless `exact`. Returns (h, h_codes, y)."""
+    (int8 takes fp32 values, so it rounds even when `exact`).
+    Returns (h, h_codes, y)."""
     gu = a @ w13
     h = swiglu(gu)
     h_codes = None
@@ -332,6 +383,10 @@ def expert_ffn(a: np.ndarray, w13: np.ndarray, w2: np.ndarray, *,
         codes, sc = mx_quant(h if exact else round_f32(h), "e4m3")
         h_codes = (codes, sc)
         h = mx_dequant(codes, sc, "e4m3")
+    elif act_q == "int8":
+        codes, sc = int8_quant_rows(round_f32(h))
+        h_codes = (codes, sc)
+        h = int8_dequant_rows(codes, sc)
     elif not exact:
         h = round_to(h, act)
     y = h @ w2
@@ -380,7 +435,11 @@ def moe_layer(*, logits, x, get_weights: WeightFn, T, H, I, n_ffn, n_zero,
     a, a_codes = _act_rows(xrows, act_q)
     h = np.zeros((R, I))
     y = np.zeros((R, H))
-    h_codes = (np.zeros((R, I), np.uint8), np.zeros((R, I // 32 if I % 32 == 0 else 0), np.uint8))
+    if act_q == "int8":
+        h_codes = (np.zeros((R, I), np.int8), np.zeros(R, np.float32))
+    else:
+        h_codes = (np.zeros((R, I), np.uint8),
+                   np.zeros((R, I // 32 if I % 32 == 0 else 0), np.uint8))
     for e in range(fb, fe):
         lo, hi = int(offsets[e]) - r0, int(offsets[e + 1]) - r0
         if hi == lo:

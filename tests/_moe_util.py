@@ -24,6 +24,15 @@ def weight_getter(shape, inp):
             b = O.mxfp4_dequant_rows(w2[i].cpu().numpy(), s2[i].cpu().numpy())
             return a.T.copy(), b.T.copy()   # [H, 2I], [I, H]
         return get
+    if shape.wt == "int8":
+        w13, s13, w2, s2 = inp["w13"], inp["w13_scale"], inp["w2"], inp["w2_scale"]
+
+        def get(e):
+            i = e - fb
+            a = O.int8_dequant_rows(w13[i].cpu().numpy(), s13[i].cpu().numpy())
+            b = O.int8_dequant_rows(w2[i].cpu().numpy(), s2[i].cpu().numpy())
+            return a.T.copy(), b.T.copy()   # [H, 2I], [I, H]
+        return get
     w13, w2 = inp["w13"], inp["w2"]
 
     def get(e):

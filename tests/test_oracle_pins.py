@@ -428,3 +428,113 @@ def test_add_rms_norm_outputs():
     bound = np.where(a > 448, a - 448, 0.5 * ulp) * sc
     deq = O.mx_dequant(codes, scales, "e4m3")
     assert np.all(np.abs(deq - yq) <= bound * (1 + 1e-12))
+
+
+# ----------------------------------------------------------------- W8A8 int8
+
+
+def test_int8_quant_closed_forms():
+    # amax = 127 * 2^j gives the scale 2^j exactly; codes are then rint(v / 2^j)
+    # with ties to even (2.5 -> 2, -3.5 -> -4, 0.5 -> 0, 1.5 -> 2, 126.5 -> 126)
+    base = np.array([127.0, 2.5, -3.5, 0.5, -0.5, 1.5, 126.5, -127.0, 3.25, 0.0])
+    want = [127, 2, -4, 0, 0, 2, 126, -127, 3, 0]
+    for j in (-12, -3, 0, 5):
+        codes, sc = O.int8_quant_rows(base[None, :] * 2.0 ** j)
+        assert sc.dtype == np.float32 and sc[0] == np.float32(2.0 ** j)
+        assert codes.dtype == np.int8 and codes[0].tolist() == want
+
+
+def test_int8_quant_zero_row_and_sign():
+    codes, sc = O.int8_quant_rows(np.zeros((2, 8)))
+    assert sc.tolist() == [0.0, 0.0] and not codes.any()
+    # one nonzero element: it becomes +-127 and everything else 0
+    v = np.zeros((2, 8))
+    v[0, 3], v[1, 5] = -0.75, 2.0 ** -66
+    codes, sc = O.int8_quant_rows(v)
+    assert codes[0, 3] == -127 and codes[1, 5] == 127
+    assert np.count_nonzero(codes) == 2
+
+
+def test_int8_quant_invariants_and_error_bound():
+    # every nonzero row uses the full code range (amax / fl(amax/127) rounds to
+    # 127), codes keep the sign, and each code is the nearest integer to v/s
+    rng = np.random.default_rng(3)
+    v = O.round_bf16(rng.standard_normal((64, 256)) * rng.uniform(1e-3, 1e3, (64, 1)))
+    codes, sc = O.int8_quant_rows(v)
+    c = codes.astype(np.int64)
+    assert np.all(np.abs(c).max(axis=1) == 127)
+    assert np.all(np.abs(c) <= 127)
+    assert np.all((c == 0) | (np.sign(c) == np.sign(v)))
+    err = np.abs(v - c * sc.astype(np.float64)[:, None])
+    assert np.all(err <= 0.5 * sc[:, None] * (1 + 1e-5))
+    # homogeneity: scaling a row by a power of two scales s and keeps codes
+    codes2, sc2 = O.int8_quant_rows(v * 2.0 ** -7)
+    assert np.array_equal(codes2, codes)
+    assert np.array_equal(sc2, (sc.astype(np.float64) * 2.0 ** -7).astype(np.float32))
+
+
+def test_int8_quant_rejects_non_fp32_input():
+    with pytest.raises(ValueError):
+        O.int8_quant_rows(np.array([[1.0 + 2.0 ** -40, 1.0]]))
+
+
+def test_int8_dequant_is_per_output_channel():
+    codes = np.array([[1, -2, 3], [4, 5, -6]], dtype=np.int8)   # [N=2, K=3]
+    sc = np.array([0.5, 2.0 ** -10], dtype=np.float32)
+    w = O.int8_dequant_rows(codes, sc)
+    assert w.tolist() == [[0.5, -1.0, 1.5], [4 * 2.0 ** -10, 5 * 2.0 ** -10, -6 * 2.0 ** -10]]
+
+
+def test_w8a8_expert_is_integer_matmul_then_scales():
+    # one W8A8 expert computed another way: int64 products of the codes, the
+    # row scale of x and the channel scale of w applied after the sum, SwiGLU,
+    # then the row quantisation of h (pinned above) and the same for GEMM2
+    rng = np.random.default_rng(11)
+    n, H, I = 7, 96, 64
+    x = O.round_bf16(rng.standard_normal((n, H)))
+    q13 = rng.integers(-127, 128, (2 * I, H)).astype(np.int8)
+    s13 = rng.uniform(1e-4, 1e-3, 2 * I).astype(np.float32)
+    q2 = rng.integers(-127, 128, (H, I)).astype(np.int8)
+    s2 = rng.uniform(1e-4, 1e-3, H).astype(np.float32)
+    qx, sx = O.int8_quant_rows(x)
+    a = O.int8_dequant_rows(qx, sx)
+    w13 = O.int8_dequant_rows(q13, s13).T
+    w2 = O.int8_dequant_rows(q2, s2).T
+    h, (qh, sh), y = O.expert_ffn(a, w13, w2, act="bf16", act_q="int8", exact=True)
+
+    acc = qx.astype(np.int64) @ q13.astype(np.int64).T            # [n, 2I]
+    gu = acc * sx.astype(np.float64)[:, None] * s13.astype(np.float64)[None, :]
+    g, u = gu[:, :I], gu[:, I:]
+    h_ref = g / (1.0 + np.exp(-g)) * u
+    qh_ref, sh_ref = O.int8_quant_rows(h_ref.astype(np.float32))
+    assert np.array_equal(qh, qh_ref) and np.array_equal(sh, sh_ref)
+    acc2 = qh_ref.astype(np.int64) @ q2.astype(np.int64).T         # [n, H]
+    y_ref = acc2 * sh_ref.astype(np.float64)[:, None] * s2.astype(np.float64)[None, :]
+    np.testing.assert_allclose(y, y_ref, rtol=1e-12, atol=1e-15)
+
+
+def test_w8a8_routed_equals_pertoken():
+    rng = np.random.default_rng(5)
+    T, H, I, n_ffn, n_zero, k = 10, 64, 32, 6, 2, 3
+    logits = rng.standard_normal((T, n_ffn + n_zero)).astype(np.float32)
+    x = O.round_bf16(rng.standard_normal((T, H)))
+    res = O.round_bf16(rng.standard_normal((T, H)))
+    Q13 = rng.integers(-127, 128, (n_ffn, 2 * I, H)).astype(np.int8)
+    Q2 = rng.integers(-127, 128, (n_ffn, H, I)).astype(np.int8)
+    S13 = rng.uniform(1e-4, 1e-3, (n_ffn, 2 * I)).astype(np.float32)
+    S2 = rng.uniform(1e-4, 1e-3, (n_ffn, H)).astype(np.float32)
+
+    def get(e):
+        return (O.int8_dequant_rows(Q13[e], S13[e]).T.copy(),
+                O.int8_dequant_rows(Q2[e], S2[e]).T.copy())
+    kw = dict(logits=logits, x=x, get_weights=get, T=T, H=H, I=I, n_ffn=n_ffn,
+              n_zero=n_zero, top_k=k, local_begin=0, local_end=n_ffn + n_zero,
+              residual=res, act="bf16", act_q="int8")
+    r = O.moe_layer(**kw)
+    per_tok = O.moe_tokens(range(T), **kw)
+    assert np.array_equal(r["out"], per_tok)
+    # x is quantised per token: the gathered codes are the token's codes
+    qx, sx = O.int8_quant_rows(x)
+    tok = r["sorted_copy"][r["row0"]:r["row0"] + r["R"]] // k
+    assert np.array_equal(r["x_perm_codes"], qx[tok])
+    assert np.array_equal(r["x_perm_scale"], sx[tok])
