@@ -10,6 +10,7 @@
  * Sources (web pages, cited by title and section):
  *   [P1] "Qwen3-MoE low-latency inference on Atlas A3 / 950 clusters"
  *   [P2] "LongCat-Flash inference on Atlas A3 clusters"
+ *   [P3] "NPU Qwen3-Next inference practice" (quantisation strategy only)
  *
  * Conventions shared by every call
  *   - All tensor pointers are DEVICE pointers to memory the caller allocated
@@ -69,8 +70,11 @@ typedef enum moe_dtype {
   MOE_F32 = 0,
   MOE_BF16 = 1,
   MOE_MXFP8_E4M3 = 2, /* e4m3fn codes + one e8m0 scale per 32 along K      */
-  MOE_MXFP4_E2M1 = 3  /* e2m1 codes, 2 per byte (low nibble = even k),
+  MOE_MXFP4_E2M1 = 3, /* e2m1 codes, 2 per byte (low nibble = even k),
                          + one e8m0 scale per 32 along K                    */
+  MOE_INT8 = 4        /* symmetric int8 codes in [-127, 127] + one fp32
+                         scale per output channel (weights, static) or per
+                         row (activations, dynamic: amax / 127)             */
 } moe_dtype;
 
 typedef struct moe_problem {
@@ -83,12 +87,27 @@ typedef struct moe_problem {
   int32_t local_begin; /* expert-id range handled by the call              */
   int32_t local_end;
   int32_t act;   /* MOE_F32 | MOE_BF16: x, residual, y, out, h (unquantised) */
-  int32_t wt;    /* MOE_F32 | MOE_BF16 | MOE_MXFP4_E2M1                     */
-  int32_t act_q; /* == act (no quantisation) | MOE_MXFP8_E4M3 (dynamic)     */
+  int32_t wt;    /* MOE_F32 | MOE_BF16 | MOE_MXFP4_E2M1 | MOE_INT8          */
+  int32_t act_q; /* == act (no quantisation) | MOE_MXFP8_E4M3 | MOE_INT8
+                    (dynamic)                                               */
 } moe_problem;
 
 /* Supported combinations: (act, wt, act_q) = (F32, F32, F32),
- * (BF16, BF16, BF16), (BF16, MXFP4_E2M1, MXFP8_E4M3).
+ * (BF16, BF16, BF16), (BF16, MXFP4_E2M1, MXFP8_E4M3) and W8A8
+ * (BF16, INT8, INT8) -- [P3] "量化策略": routed experts with int8 weights
+ * (static per-channel scales) and int8 activations (dynamic per-token
+ * scales). MX and INT8 need H and I multiples of 128; INT8 also
+ * 2 * I * H < 2^31.
+ *
+ * Dynamic int8 quantisation of a row v (x per token before routing, h per
+ * row between the GEMMs, after h is formed in fp32): scale = amax|v| / 127
+ * rounded to fp32, code = rint(v / scale) with the quotient rounded to fp32
+ * and ties to even, clipped to [-127, 127]; an all-zero row has scale 0 and
+ * codes 0. int8 products are summed exactly in int32 and dequantised as
+ * acc * row scale * channel scale in fp32.
+ *
+ * Scale pointers (x_perm_scale, h_scale, w13_scale, w2_scale) point to
+ * uint8 e8m0 codes for MX and to fp32 values for INT8.
  *
  * Weight layouts (E_loc experts, weights of expert e at index e - fb):
  *   F32 / BF16:  w13 [E_loc, H, 2I]   columns [0, I) = gate, [I, 2I) = up
@@ -98,7 +117,11 @@ typedef struct moe_problem {
  *                column; rows [0, I) gate, [I, 2I) up
  *                w13_scale [E_loc, 2I, H/32] e8m0
  *                w2  [E_loc, H, I/2] bytes, w2_scale [E_loc, H, I/32] e8m0
- * Scale pointers must be NULL unless wt is MXFP4_E2M1.
+ *   INT8:        w13 [E_loc, 2I, H] int8, K (= H) contiguous per output
+ *                column; rows [0, I) gate, [I, 2I) up
+ *                w13_scale fp32 [E_loc, 2I] (one per output column)
+ *                w2  [E_loc, H, I] int8, w2_scale fp32 [E_loc, H]
+ * Scale pointers must be NULL unless wt is MXFP4_E2M1 or INT8.
  */
 
 /* Gating: [P1] "GMM使能和Routing优化 / 快速选择专家" (fused top-k + softmax
@@ -129,15 +152,18 @@ MOE_API moe_status moe_gate_topk(const moe_problem* p, const float* logits,
  *   x_perm            rows r = 0 .. R-1, R = offsets[fe] - offsets[fb]:
  *                     x_perm[r] = x[sorted_copy[offsets[fb] + r] / top_k];
  *                     act [T*top_k, H] or, when act_q is MXFP8_E4M3, e4m3
- *                     codes uint8 [T*top_k, H]. Rows >= R are not written.
+ *                     codes uint8 [T*top_k, H], or when act_q is INT8 the
+ *                     token's int8 codes [T*top_k, H]. Rows >= R are not
+ *                     written.
  *   x_perm_scale      e8m0 uint8 [T*top_k, H/32] when act_q is MXFP8_E4M3,
+ *                     the token's fp32 scale [T*top_k] when act_q is INT8,
  *                     else must be NULL.
  *   workspace         scratch (see conventions). */
 MOE_API moe_status moe_init_routing(const moe_problem* p, const int32_t* topk_ids,
                             const void* x, int32_t* tokens_per_expert,
                             int32_t* offsets, int32_t* sorted_copy,
                             int32_t* copy_pos, void* x_perm,
-                            uint8_t* x_perm_scale, void* workspace,
+                            void* x_perm_scale, void* workspace,
                             size_t* workspace_bytes, void* stream);
 
 /* Grouped expert FFN: [P1] "MoE TP优化 / 计算分解" (expert =
@@ -145,32 +171,36 @@ MOE_API moe_status moe_init_routing(const moe_problem* p, const int32_t* topk_id
  * SiLU(first) * second) and "高性能专家计算" (all experts' matmuls in one
  * grouped operator). For every FFN expert e in [fb, fe) with rows
  * [offsets[e] - offsets[fb], offsets[e+1] - offsets[fb]) of x_perm:
- *   h = SwiGLU(x_perm_rows @ w13[e])   fp32 accumulation; stored in act
- *                                      dtype, or MXFP8 (one e8m0 per 32
- *                                      along I) when act_q is MXFP8_E4M3
- *   y = h @ w2[e]                      fp32 accumulation, stored in act
+ *   h = SwiGLU(x_perm_rows @ w13[e])   fp32 accumulation (int32 for INT8);
+ *                                      stored in act dtype, or MXFP8 (one
+ *                                      e8m0 per 32 along I) when act_q is
+ *                                      MXFP8_E4M3, or int8 with one fp32
+ *                                      scale per row when act_q is INT8
+ *   y = h @ w2[e]                      fp32 (int32) accumulation, stored in act
  * Experts with no rows never read their weights.
  *   offsets  int32 [E_tot+1] as produced by moe_init_routing
  *   y        act [T*top_k, H]; rows >= R are not written
  * moe_ffn_up and moe_ffn_down are the two halves (h buffer explicit):
- *   h        act [T*top_k, I], or e4m3 codes uint8 [T*top_k, I]
- *   h_scale  e8m0 uint8 [T*top_k, I/32] when act_q is MXFP8_E4M3 else NULL */
+ *   h        act [T*top_k, I], or e4m3 codes uint8 [T*top_k, I], or int8
+ *            codes [T*top_k, I]
+ *   h_scale  e8m0 uint8 [T*top_k, I/32] when act_q is MXFP8_E4M3, fp32
+ *            [T*top_k] when act_q is INT8, else NULL */
 MOE_API moe_status moe_grouped_ffn(const moe_problem* p, const int32_t* offsets,
-                           const void* x_perm, const uint8_t* x_perm_scale,
-                           const void* w13, const uint8_t* w13_scale,
-                           const void* w2, const uint8_t* w2_scale, void* y,
+                           const void* x_perm, const void* x_perm_scale,
+                           const void* w13, const void* w13_scale,
+                           const void* w2, const void* w2_scale, void* y,
                            void* workspace, size_t* workspace_bytes,
                            void* stream);
 
 MOE_API moe_status moe_ffn_up(const moe_problem* p, const int32_t* offsets,
-                      const void* x_perm, const uint8_t* x_perm_scale,
-                      const void* w13, const uint8_t* w13_scale, void* h,
-                      uint8_t* h_scale, void* workspace,
+                      const void* x_perm, const void* x_perm_scale,
+                      const void* w13, const void* w13_scale, void* h,
+                      void* h_scale, void* workspace,
                       size_t* workspace_bytes, void* stream);
 
 MOE_API moe_status moe_ffn_down(const moe_problem* p, const int32_t* offsets,
-                        const void* h, const uint8_t* h_scale, const void* w2,
-                        const uint8_t* w2_scale, void* y, void* workspace,
+                        const void* h, const void* h_scale, const void* w2,
+                        const void* w2_scale, void* y, void* workspace,
                         size_t* workspace_bytes, void* stream);
 
 /* Finalize: [P1] "高效排序和token路由" (finalize_routing restores token order
@@ -193,22 +223,23 @@ MOE_API moe_status moe_finalize(const moe_problem* p, const int32_t* topk_ids,
  * sequence. */
 MOE_API moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
                      const void* residual, const void* w13,
-                     const uint8_t* w13_scale, const void* w2,
-                     const uint8_t* w2_scale, void* out, void* workspace,
+                     const void* w13_scale, const void* w2,
+                     const void* w2_scale, void* out, void* workspace,
                      size_t* workspace_bytes, void* stream);
 
 /* moe_layer with stage timing: when stage_events is non-NULL, entry i (a
  * hipEvent_t or NULL) is recorded on `stream` right before stage i is
  * enqueued, for i < n_events, with stages 0 gate, 1 expert histogram,
- * 2 scan (+ GEMM tile list), 3 permutation, 4 gather (+ MXFP8), 5 GEMM1 +
- * SwiGLU, 6 GEMM2, 7 finalize, and entry 8 after the last. Each of stages
- * 0-7 is exactly one kernel launch (a stage with nothing to do launches
- * nothing), so events i and i+1 bracket one kernel. For performance tooling;
- * results are identical to moe_layer. */
+ * 2 scan (+ GEMM tile list), 3 permutation, 4 gather (+ MXFP8 or int8
+ * quantisation of x), 5 GEMM1 + SwiGLU, 6 GEMM2, 7 finalize, and entry 8
+ * after the last. Each of stages 0-7 is at most one kernel launch (a stage
+ * with nothing to do launches nothing), except stage 6 for INT8, which
+ * quantises h and then runs GEMM2. For performance tooling; results are
+ * identical to moe_layer. */
 MOE_API moe_status moe_layer_traced(const moe_problem* p, const float* logits,
                                     const void* x, const void* residual,
-                                    const void* w13, const uint8_t* w13_scale,
-                                    const void* w2, const uint8_t* w2_scale,
+                                    const void* w13, const void* w13_scale,
+                                    const void* w2, const void* w2_scale,
                                     void* out, void* workspace,
                                     size_t* workspace_bytes, void* stream,
                                     void* const* stage_events, int32_t n_events);

@@ -27,9 +27,9 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
-MOE_F32, MOE_BF16, MOE_MXFP8_E4M3, MOE_MXFP4_E2M1 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_MXFP8_E4M3, MOE_MXFP4_E2M1, MOE_INT8 = 0, 1, 2, 3, 4
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8_E4M3,
-       "mxfp4": MOE_MXFP4_E2M1}
+       "mxfp4": MOE_MXFP4_E2M1, "int8": MOE_INT8}
 
 SYMBOLS = ["moe_gate_topk", "moe_init_routing", "moe_grouped_ffn", "moe_ffn_up",
            "moe_ffn_down", "moe_finalize", "moe_layer", "moe_layer_traced",
@@ -104,7 +104,8 @@ def lib() -> ctypes.CDLL:
 def problem(shape=None, **kw) -> MoeProblem:
     """Build a MoeProblem from an object with the shape attributes (T, H, I,
     n_ffn, n_zero, top_k, local_begin, local_end, act, wt, act_q with dtype
-    names "f32" / "bf16" / "mxfp4" / "mxfp8" / "none") and/or keywords."""
+    names "f32" / "bf16" / "mxfp4" / "mxfp8" / "int8" / "none") and/or
+    keywords."""
     vals = {}
     for n in ("T", "H", "I", "n_ffn", "n_zero", "top_k", "local_begin",
               "local_end", "act", "wt", "act_q"):
@@ -172,6 +173,9 @@ def init_routing(p: MoeProblem, topk_ids, x):
     if mx:
         x_perm = torch.empty((N, p.H), dtype=torch.uint8, device=dev)
         x_scale = torch.empty((N, p.H // 32), dtype=torch.uint8, device=dev)
+    elif p.act_q == MOE_INT8:
+        x_perm = torch.empty((N, p.H), dtype=torch.int8, device=dev)
+        x_scale = torch.empty(N, dtype=torch.float32, device=dev)
     else:
         x_perm = torch.empty((N, p.H), dtype=_act_dtype(p), device=dev)
         x_scale = None
@@ -193,6 +197,9 @@ def _h_buffers(p: MoeProblem, dev):
     if p.act_q == MOE_MXFP8_E4M3:
         return (torch.empty((N, p.I), dtype=torch.uint8, device=dev),
                 torch.empty((N, p.I // 32), dtype=torch.uint8, device=dev))
+    if p.act_q == MOE_INT8:
+        return (torch.empty((N, p.I), dtype=torch.int8, device=dev),
+                torch.empty(N, dtype=torch.float32, device=dev))
     return torch.empty((N, p.I), dtype=_act_dtype(p), device=dev), None
 
 

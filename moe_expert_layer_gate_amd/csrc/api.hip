@@ -15,7 +15,8 @@ struct Prob {
   int T, H, I, nffn, nzero, k, lb, le, act, wt, actq;
   int E, fb, fe, El;
   long long N;  // T * k copies
-  bool mx;
+  bool mx;      // MXFP8 activations x MXFP4 weights
+  bool i8;      // W8A8: int8 activations and weights, fp32 scales
 };
 
 moe_status check(const moe_problem* p, Prob* q) {
@@ -37,8 +38,13 @@ moe_status check(const moe_problem* p, Prob* q) {
   const bool f32 = r.act == MOE_F32 && r.wt == MOE_F32 && r.actq == MOE_F32;
   const bool bf16 = r.act == MOE_BF16 && r.wt == MOE_BF16 && r.actq == MOE_BF16;
   r.mx = r.act == MOE_BF16 && r.wt == MOE_MXFP4_E2M1 && r.actq == MOE_MXFP8_E4M3;
-  if (!f32 && !bf16 && !r.mx) return MOE_ERR_UNSUPPORTED;
+  r.i8 = r.act == MOE_BF16 && r.wt == MOE_INT8 && r.actq == MOE_INT8;
+  if (!f32 && !bf16 && !r.mx && !r.i8) return MOE_ERR_UNSUPPORTED;
   if (r.mx && (r.H % 128 || r.I % 128)) return MOE_ERR_UNSUPPORTED;
+  // int8: K steps of 128; int32 sums of 127 * 127 * K products stay exact;
+  // weight offsets (2I * H bytes per expert) fit 32 bits
+  if (r.i8 && (r.H % 128 || r.I % 128 || 2LL * r.I * r.H >= (1LL << 31)))
+    return MOE_ERR_UNSUPPORTED;
   r.fb = r.lb < r.nffn ? r.lb : r.nffn;
   r.fe = r.le < r.nffn ? r.le : r.nffn;
   r.El = r.fe - r.fb;
@@ -62,7 +68,7 @@ int tile_rows(const Prob& q) {
 // tiled kernel addresses x with 32-bit offsets, so x must span < 4 GB).
 
 bool fused_gather(const Prob& q) {
-  return q.act == MOE_BF16 && !q.mx &&
+  return q.act == MOE_BF16 && !q.mx && !q.i8 &&
          (unsigned long long)q.T * q.H * 2 < (1ull << 32);
 }
 
@@ -111,26 +117,41 @@ FfnWs carve_ffn_ws(Carve& c, const Prob& q, int mt) {
 
 // gidx/gbase: fused gather (bf16 only) -- activation row of sorted copy i is
 // row gidx[gbase[0] + i] / top_k of xp (= x); NULL: xp holds permuted rows.
+// W8A8: GEMM1 writes h in fp32 (h), quantised by run_quant_h afterwards.
 moe_status run_up(const Prob& q, int mt, const Tile* tiles,
-                  const int32_t* tile_count, const void* xp, const uint8_t* xs,
-                  const void* w13, const uint8_t* w13s, void* h, uint8_t* hs,
+                  const int32_t* tile_count, const void* xp, const void* xs,
+                  const void* w13, const void* w13s, void* h, void* hs,
                   hipStream_t s, const int32_t* gidx = nullptr,
                   const int32_t* gbase = nullptr) {
   const int mtl = (int)max_tiles(q, mt);
   if (mtl == 0) return MOE_OK;
-  if (q.act == MOE_F32)
+  if (q.i8 && mt == 128)
+    MOE_TRY(moe::launch_gemm_i8_tiled(true, tiles, tile_count, mtl,
+                                      (const int8_t*)xp, (const float*)xs,
+                                      (const int8_t*)w13, (const float*)w13s,
+                                      h, q.H, 2 * q.I, q.I, gidx, gbase, q.k,
+                                      s));
+  else if (q.i8)
+    MOE_TRY(moe::launch_gemm_i8_stream(true, mt / 16, tiles, tile_count, mtl,
+                                       (const int8_t*)xp, (const float*)xs,
+                                       (const int8_t*)w13, (const float*)w13s,
+                                       h, q.H, 2 * q.I, q.I, gidx, gbase, q.k,
+                                       s));
+  else if (q.act == MOE_F32)
     MOE_TRY(moe::launch_gemm_f32(true, tiles, tile_count, mtl, (const float*)xp,
                                  (const float*)w13, (float*)h, q.H, 2 * q.I,
                                  q.I, s));
   else if (q.mx && mt == 128)
     MOE_TRY(moe::launch_gemm_mx_tiled(true, tiles, tile_count, mtl,
-                                      (const uint8_t*)xp, xs,
-                                      (const uint8_t*)w13, w13s, h, hs, q.H,
-                                      2 * q.I, q.I, gidx, gbase, q.k, s));
+                                      (const uint8_t*)xp, (const uint8_t*)xs,
+                                      (const uint8_t*)w13,
+                                      (const uint8_t*)w13s, h, (uint8_t*)hs,
+                                      q.H, 2 * q.I, q.I, gidx, gbase, q.k, s));
   else if (q.mx)
     MOE_TRY(moe::launch_gemm_mx(true, mt / 16, tiles, tile_count, mtl,
-                                (const uint8_t*)xp, xs, (const uint8_t*)w13,
-                                w13s, h, hs, q.H, 2 * q.I, q.I, s));
+                                (const uint8_t*)xp, (const uint8_t*)xs,
+                                (const uint8_t*)w13, (const uint8_t*)w13s, h,
+                                (uint8_t*)hs, q.H, 2 * q.I, q.I, s));
   else if (mt == 128)
     MOE_TRY(moe::launch_gemm_bf16_tiled(
         true, tiles, tile_count, mtl, (const uint16_t*)xp,
@@ -144,26 +165,46 @@ moe_status run_up(const Prob& q, int mt, const Tile* tiles,
   return MOE_OK;
 }
 
+// W8A8: the R rows of GEMM1's fp32 h -> int8 codes hq + fp32 row scales hs.
+moe_status run_quant_h(const Prob& q, const float* h32, const int32_t* offsets,
+                       void* hq, void* hs, hipStream_t s) {
+  MOE_TRY(moe::launch_quant_i8_rows(true, h32, q.I, (int)q.N, nullptr, offsets,
+                                    q.fb, q.fe, 1, (int8_t*)hq, (float*)hs, s));
+  return MOE_OK;
+}
+
 moe_status run_down(const Prob& q, int mt, const Tile* tiles,
                     const int32_t* tile_count, const void* h,
-                    const uint8_t* hs, const void* w2, const uint8_t* w2s,
+                    const void* hs, const void* w2, const void* w2s,
                     void* y, hipStream_t s) {
   const int mtl = (int)max_tiles(q, mt);
   if (mtl == 0) return MOE_OK;
-  if (q.act == MOE_F32)
+  if (q.i8 && mt == 128)
+    MOE_TRY(moe::launch_gemm_i8_tiled(false, tiles, tile_count, mtl,
+                                      (const int8_t*)h, (const float*)hs,
+                                      (const int8_t*)w2, (const float*)w2s, y,
+                                      q.I, q.H, q.H, nullptr, nullptr, q.k, s));
+  else if (q.i8)
+    MOE_TRY(moe::launch_gemm_i8_stream(false, mt / 16, tiles, tile_count, mtl,
+                                       (const int8_t*)h, (const float*)hs,
+                                       (const int8_t*)w2, (const float*)w2s, y,
+                                       q.I, q.H, q.H, nullptr, nullptr, q.k,
+                                       s));
+  else if (q.act == MOE_F32)
     MOE_TRY(moe::launch_gemm_f32(false, tiles, tile_count, mtl,
                                  (const float*)h, (const float*)w2, (float*)y,
                                  q.I, q.H, q.H, s));
   else if (q.mx && mt == 128)
     MOE_TRY(moe::launch_gemm_mx_tiled(false, tiles, tile_count, mtl,
-                                      (const uint8_t*)h, hs,
-                                      (const uint8_t*)w2, w2s, y, nullptr,
-                                      q.I, q.H, q.H, nullptr, nullptr, q.k,
-                                      s));
+                                      (const uint8_t*)h, (const uint8_t*)hs,
+                                      (const uint8_t*)w2, (const uint8_t*)w2s,
+                                      y, nullptr, q.I, q.H, q.H, nullptr,
+                                      nullptr, q.k, s));
   else if (q.mx)
     MOE_TRY(moe::launch_gemm_mx(false, mt / 16, tiles, tile_count, mtl,
-                                (const uint8_t*)h, hs, (const uint8_t*)w2, w2s,
-                                y, nullptr, q.I, q.H, q.H, s));
+                                (const uint8_t*)h, (const uint8_t*)hs,
+                                (const uint8_t*)w2, (const uint8_t*)w2s, y,
+                                nullptr, q.I, q.H, q.H, s));
   else if (mt == 128)
     MOE_TRY(moe::launch_gemm_bf16_tiled(
         false, tiles, tile_count, mtl, (const uint16_t*)h,
@@ -177,12 +218,12 @@ moe_status run_down(const Prob& q, int mt, const Tile* tiles,
   return MOE_OK;
 }
 
-moe_status check_weights(const Prob& q, const void* w13, const uint8_t* w13s,
-                         const void* w2, const uint8_t* w2s, bool need13,
+moe_status check_weights(const Prob& q, const void* w13, const void* w13s,
+                         const void* w2, const void* w2s, bool need13,
                          bool need2) {
   if (q.El == 0) return MOE_OK;  // no FFN expert in range: weights unused
   if ((need13 && !w13) || (need2 && !w2)) return MOE_ERR_INVALID_ARG;
-  if (q.mx) {
+  if (q.mx || q.i8) {
     if ((need13 && !w13s) || (need2 && !w2s)) return MOE_ERR_INVALID_ARG;
   } else if (w13s || w2s) {
     return MOE_ERR_INVALID_ARG;
@@ -222,7 +263,7 @@ moe_status moe_init_routing(const moe_problem* p, const int32_t* topk_ids,
                             const void* x, int32_t* tokens_per_expert,
                             int32_t* offsets, int32_t* sorted_copy,
                             int32_t* copy_pos, void* x_perm,
-                            uint8_t* x_perm_scale, void* workspace,
+                            void* x_perm_scale, void* workspace,
                             size_t* workspace_bytes, void* stream) {
   Prob q;
   moe_status st = check(p, &q);
@@ -236,7 +277,8 @@ moe_status moe_init_routing(const moe_problem* p, const int32_t* topk_ids,
   if (!tokens_per_expert || !offsets) return MOE_ERR_INVALID_ARG;
   if (q.N > 0 && (!topk_ids || !sorted_copy || !copy_pos)) return MOE_ERR_INVALID_ARG;
   if (q.El > 0 && q.N > 0 && (!x || !x_perm)) return MOE_ERR_INVALID_ARG;
-  if (q.mx ? (q.El > 0 && q.N > 0 && !x_perm_scale) : (x_perm_scale != nullptr))
+  if ((q.mx || q.i8) ? (q.El > 0 && q.N > 0 && !x_perm_scale)
+                     : (x_perm_scale != nullptr))
     return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   if (moe::route_small_ok((int)q.N, q.E)) {
@@ -252,18 +294,24 @@ moe_status moe_init_routing(const moe_problem* p, const int32_t* topk_ids,
       MOE_TRY(moe::launch_route_scatter(topk_ids, (int)q.N, q.E, cc, offsets,
                                         sorted_copy, copy_pos, s));
   }
-  if (q.N > 0) {
+  if (q.N > 0 && q.i8) {
+    MOE_TRY(moe::launch_quant_i8_rows(false, x, q.H, (int)q.N, sorted_copy,
+                                      offsets, q.fb, q.fe, q.k,
+                                      (int8_t*)x_perm, (float*)x_perm_scale,
+                                      s));
+  } else if (q.N > 0) {
     MOE_TRY(moe::launch_route_gather(x, q.act == MOE_F32 ? 0 : 1, q.mx ? 1 : 0,
                                      q.H, q.k, sorted_copy, offsets, q.fb,
-                                     q.fe, (int)q.N, x_perm, x_perm_scale, s));
+                                     q.fe, (int)q.N, x_perm,
+                                     (uint8_t*)x_perm_scale, s));
   }
   return MOE_OK;
 }
 
 moe_status moe_ffn_up(const moe_problem* p, const int32_t* offsets,
-                      const void* x_perm, const uint8_t* x_perm_scale,
-                      const void* w13, const uint8_t* w13_scale, void* h,
-                      uint8_t* h_scale, void* workspace,
+                      const void* x_perm, const void* x_perm_scale,
+                      const void* w13, const void* w13_scale, void* h,
+                      void* h_scale, void* workspace,
                       size_t* workspace_bytes, void* stream) {
   Prob q;
   moe_status st = check(p, &q);
@@ -272,24 +320,31 @@ moe_status moe_ffn_up(const moe_problem* p, const int32_t* offsets,
   const int mt = tile_rows(q);
   Carve c(workspace);
   FfnWs fw = carve_ffn_ws(c, q, mt);
+  float* h32 = q.i8 ? c.take<float>((size_t)q.N * q.I) : nullptr;
   if (!workspace) { *workspace_bytes = c.off; return MOE_OK; }
   if (*workspace_bytes < c.off) return MOE_ERR_WORKSPACE;
   if ((st = check_weights(q, w13, w13_scale, nullptr, nullptr, true, false)) != MOE_OK)
     return st;
   if (q.El == 0 || q.N == 0) return MOE_OK;
   if (!offsets || !x_perm || !h) return MOE_ERR_INVALID_ARG;
-  if (q.mx ? (!x_perm_scale || !h_scale) : (x_perm_scale || h_scale))
+  if ((q.mx || q.i8) ? (!x_perm_scale || !h_scale) : (x_perm_scale || h_scale))
     return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   MOE_TRY(moe::launch_build_tiles(offsets, q.fb, q.fe, mt, fw.tiles,
                                   (int)max_tiles(q, mt), fw.tile_count, s));
+  if (q.i8) {
+    st = run_up(q, mt, fw.tiles, fw.tile_count, x_perm, x_perm_scale, w13,
+                w13_scale, h32, nullptr, s);
+    if (st != MOE_OK) return st;
+    return run_quant_h(q, h32, offsets, h, h_scale, s);
+  }
   return run_up(q, mt, fw.tiles, fw.tile_count, x_perm, x_perm_scale, w13,
                 w13_scale, h, h_scale, s);
 }
 
 moe_status moe_ffn_down(const moe_problem* p, const int32_t* offsets,
-                        const void* h, const uint8_t* h_scale, const void* w2,
-                        const uint8_t* w2_scale, void* y, void* workspace,
+                        const void* h, const void* h_scale, const void* w2,
+                        const void* w2_scale, void* y, void* workspace,
                         size_t* workspace_bytes, void* stream) {
   Prob q;
   moe_status st = check(p, &q);
@@ -304,7 +359,7 @@ moe_status moe_ffn_down(const moe_problem* p, const int32_t* offsets,
     return st;
   if (q.El == 0 || q.N == 0) return MOE_OK;
   if (!offsets || !h || !y) return MOE_ERR_INVALID_ARG;
-  if (q.mx ? !h_scale : (h_scale != nullptr)) return MOE_ERR_INVALID_ARG;
+  if ((q.mx || q.i8) ? !h_scale : (h_scale != nullptr)) return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   MOE_TRY(moe::launch_build_tiles(offsets, q.fb, q.fe, mt, fw.tiles,
                                   (int)max_tiles(q, mt), fw.tile_count, s));
@@ -313,9 +368,9 @@ moe_status moe_ffn_down(const moe_problem* p, const int32_t* offsets,
 }
 
 moe_status moe_grouped_ffn(const moe_problem* p, const int32_t* offsets,
-                           const void* x_perm, const uint8_t* x_perm_scale,
-                           const void* w13, const uint8_t* w13_scale,
-                           const void* w2, const uint8_t* w2_scale, void* y,
+                           const void* x_perm, const void* x_perm_scale,
+                           const void* w13, const void* w13_scale,
+                           const void* w2, const void* w2_scale, void* y,
                            void* workspace, size_t* workspace_bytes,
                            void* stream) {
   Prob q;
@@ -325,21 +380,26 @@ moe_status moe_grouped_ffn(const moe_problem* p, const int32_t* offsets,
   const int mt = tile_rows(q);
   Carve c(workspace);
   FfnWs fw = carve_ffn_ws(c, q, mt);
-  void* h = c.take<char>((size_t)q.N * q.I * (q.mx ? 1 : act_bytes(q)));
-  uint8_t* hs = q.mx ? c.take<uint8_t>((size_t)q.N * (q.I / 32)) : nullptr;
+  void* h = c.take<char>((size_t)q.N * q.I * ((q.mx || q.i8) ? 1 : act_bytes(q)));
+  void* hs = q.mx ? (void*)c.take<uint8_t>((size_t)q.N * (q.I / 32))
+             : q.i8 ? (void*)c.take<float>((size_t)q.N) : nullptr;
+  float* h32 = q.i8 ? c.take<float>((size_t)q.N * q.I) : nullptr;
   if (!workspace) { *workspace_bytes = c.off; return MOE_OK; }
   if (*workspace_bytes < c.off) return MOE_ERR_WORKSPACE;
   if ((st = check_weights(q, w13, w13_scale, w2, w2_scale, true, true)) != MOE_OK)
     return st;
   if (q.El == 0 || q.N == 0) return MOE_OK;
   if (!offsets || !x_perm || !y) return MOE_ERR_INVALID_ARG;
-  if (q.mx ? !x_perm_scale : (x_perm_scale != nullptr)) return MOE_ERR_INVALID_ARG;
+  if ((q.mx || q.i8) ? !x_perm_scale : (x_perm_scale != nullptr))
+    return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   MOE_TRY(moe::launch_build_tiles(offsets, q.fb, q.fe, mt, fw.tiles,
                                   (int)max_tiles(q, mt), fw.tile_count, s));
   st = run_up(q, mt, fw.tiles, fw.tile_count, x_perm, x_perm_scale, w13,
-              w13_scale, h, hs, s);
+              w13_scale, q.i8 ? (void*)h32 : h, hs, s);
   if (st != MOE_OK) return st;
+  if (q.i8 && (st = run_quant_h(q, h32, offsets, h, hs, s)) != MOE_OK)
+    return st;
   return run_down(q, mt, fw.tiles, fw.tile_count, h, hs, w2, w2_scale, y, s);
 }
 
@@ -393,8 +453,8 @@ moe_status moe_add_rms_norm_mx_quant(int32_t T, int32_t H, const void* x,
 
 moe_status moe_layer_traced(const moe_problem* p, const float* logits,
                             const void* x, const void* residual,
-                            const void* w13, const uint8_t* w13_scale,
-                            const void* w2, const uint8_t* w2_scale, void* out,
+                            const void* w13, const void* w13_scale,
+                            const void* w2, const void* w2_scale, void* out,
                             void* workspace, size_t* workspace_bytes,
                             void* stream, void* const* stage_events,
                             int32_t n_events) {
@@ -414,17 +474,22 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
   int32_t* sorted_copy = c.take<int32_t>(N);
   int32_t* copy_pos = c.take<int32_t>(N);
   FfnWs fw = carve_ffn_ws(c, q, mt);
-  const size_t ab = q.mx ? 1 : act_bytes(q);
+  const size_t ab = (q.mx || q.i8) ? 1 : act_bytes(q);
   // bf16: GEMM1 reads its rows straight from x (no permuted copy)
   const bool gather = fused_gather(q);
-  // MXFP8 with the tiled GEMM: x is quantised once per token and GEMM1 reads
-  // the token rows of the codes
-  const bool mx_tok = q.mx && mt == 128 && (int64_t)q.T * q.H < (int64_t(1) << 31);
-  const size_t xrows = mx_tok ? (size_t)q.T : N;
+  // MXFP8 with the tiled GEMM, and int8: x is quantised once per token and
+  // GEMM1 reads the token rows of the codes (32-bit offsets)
+  const bool small_x = (int64_t)q.T * q.H < (int64_t(1) << 31);
+  const bool mx_tok = q.mx && mt == 128 && small_x;
+  const bool i8_tok = q.i8 && small_x;
+  const size_t xrows = (mx_tok || i8_tok) ? (size_t)q.T : N;
   void* xp = c.take<char>(q.El && !gather ? xrows * q.H * ab : 0);
-  uint8_t* xs = q.mx ? c.take<uint8_t>(q.El ? xrows * (q.H / 32) : 0) : nullptr;
+  void* xs = q.mx ? (void*)c.take<uint8_t>(q.El ? xrows * (q.H / 32) : 0)
+             : q.i8 ? (void*)c.take<float>(q.El ? xrows : 0) : nullptr;
   void* h = c.take<char>(q.El ? N * q.I * ab : 0);
-  uint8_t* hs = q.mx ? c.take<uint8_t>(q.El ? N * (q.I / 32) : 0) : nullptr;
+  void* hs = q.mx ? (void*)c.take<uint8_t>(q.El ? N * (q.I / 32) : 0)
+             : q.i8 ? (void*)c.take<float>(q.El ? N : 0) : nullptr;
+  float* h32 = q.i8 ? c.take<float>(q.El ? N * q.I : 0) : nullptr;
   void* y = c.take<char>(q.El ? N * q.H * act_bytes(q) : 0);
   if (!workspace) { *workspace_bytes = c.off; return MOE_OK; }
   if (*workspace_bytes < c.off) return MOE_ERR_WORKSPACE;
@@ -463,26 +528,38 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
                                       sorted_copy, copy_pos, s));
   MOE_TRY(mark(4));
   if (q.El > 0 && mx_tok)
-    MOE_TRY(moe::launch_quantize_mx(x, (int)q.T, q.H, (uint8_t*)xp, xs, s));
+    MOE_TRY(moe::launch_quantize_mx(x, (int)q.T, q.H, (uint8_t*)xp,
+                                    (uint8_t*)xs, s));
+  else if (q.El > 0 && i8_tok)
+    MOE_TRY(moe::launch_quant_i8_rows(false, x, q.H, (int)q.T, nullptr,
+                                      nullptr, 0, 0, 1, (int8_t*)xp,
+                                      (float*)xs, s));
+  else if (q.El > 0 && q.i8)
+    MOE_TRY(moe::launch_quant_i8_rows(false, x, q.H, (int)q.N, sorted_copy,
+                                      offsets, q.fb, q.fe, q.k, (int8_t*)xp,
+                                      (float*)xs, s));
   else if (q.El > 0 && !gather)
     MOE_TRY(moe::launch_route_gather(x, q.act == MOE_F32 ? 0 : 1, q.mx ? 1 : 0,
                                      q.H, q.k, sorted_copy, offsets, q.fb,
-                                     q.fe, (int)q.N, xp, xs, s));
+                                     q.fe, (int)q.N, xp, (uint8_t*)xs, s));
   MOE_TRY(mark(5));
+  void* h_up = q.i8 ? (void*)h32 : h;  // W8A8: fp32 h, quantised below
   if (q.El > 0) {
     if (gather)
       st = run_up(q, mt, fw.tiles, fw.tile_count, x, nullptr, w13, w13_scale,
-                  h, hs, s, sorted_copy, offsets + q.fb);
-    else if (mx_tok)
-      st = run_up(q, mt, fw.tiles, fw.tile_count, xp, xs, w13, w13_scale, h,
-                  hs, s, sorted_copy, offsets + q.fb);
+                  h_up, hs, s, sorted_copy, offsets + q.fb);
+    else if (mx_tok || i8_tok)
+      st = run_up(q, mt, fw.tiles, fw.tile_count, xp, xs, w13, w13_scale,
+                  h_up, hs, s, sorted_copy, offsets + q.fb);
     else
-      st = run_up(q, mt, fw.tiles, fw.tile_count, xp, xs, w13, w13_scale, h,
-                  hs, s);
+      st = run_up(q, mt, fw.tiles, fw.tile_count, xp, xs, w13, w13_scale,
+                  h_up, hs, s);
     if (st != MOE_OK) return st;
   }
   MOE_TRY(mark(6));
   if (q.El > 0) {
+    if (q.i8 && (st = run_quant_h(q, h32, offsets, h, hs, s)) != MOE_OK)
+      return st;
     st = run_down(q, mt, fw.tiles, fw.tile_count, h, hs, w2, w2_scale, y, s);
     if (st != MOE_OK) return st;
   }
@@ -496,8 +573,8 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
 
 moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
                      const void* residual, const void* w13,
-                     const uint8_t* w13_scale, const void* w2,
-                     const uint8_t* w2_scale, void* out, void* workspace,
+                     const void* w13_scale, const void* w2,
+                     const void* w2_scale, void* out, void* workspace,
                      size_t* workspace_bytes, void* stream) {
   return moe_layer_traced(p, logits, x, residual, w13, w13_scale, w2, w2_scale,
                           out, workspace, workspace_bytes, stream, nullptr, 0);

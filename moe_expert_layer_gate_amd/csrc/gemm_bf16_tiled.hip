@@ -32,6 +32,19 @@
 //   * blocks are remapped so each XCD works on a contiguous range of
 //     (tile, slab) pairs: the m-tiles of one expert and one weight slab run on
 //     the same XCD and share its L2.
+//
+// The same schedule runs the W8A8 experts ([P3] "NPU Qwen3-Next inference
+// practice", 量化策略: int8 weights with static per-channel scales, int8
+// activations with dynamic per-token scales): a step is 64 bytes of every row
+// either way (32 bf16 or 64 int8 K), so the LDS ring, the copies of A and
+// the fragment reads are byte for byte those of bf16. The int8 weights are
+// [N, K] (K contiguous) and are staged like A, [column][4 x 16 B] with the
+// same swizzle, and read with plain 16-byte reads; v_mfma_i32_32x32x32_i8
+// takes the place of the bf16 MFMA (same operand bytes, same issue cycles,
+// twice the K); the int32 sums are dequantised in the epilogue with the row
+// scales (staged in LDS per tile) and the weight column scales.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "lds_dma.h"
@@ -42,6 +55,8 @@ namespace {
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int BNW = 256, BK = 32;
 constexpr int B_BYTES = BK * BNW * 2;           // 16 KB
@@ -66,6 +81,15 @@ MOE_DEV f32x16 mfma32(u32x4_t a, u32x4_t b, f32x16 c) {
       0, 0);
 }
 
+// int8 x int8 -> int32: 32 K per instruction, the same 16 bytes per lane and
+// operand as the bf16 form; A and B lanes hold the same K offsets, so the sum
+// over K is exact whatever order the hardware takes them in.
+MOE_DEV i32x16 mfma32(u32x4_t a, u32x4_t b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4_t, a),
+                                               __builtin_bit_cast(i32x4_t, b),
+                                               c, 0, 0, 0);
+}
+
 MOE_DEV v4i16_t lds_read_tr(uint32_t a) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) v4i16_t*)(uintptr_t)a);
@@ -77,16 +101,26 @@ MOE_DEV int swz_b(int k) { return 4 * (k & 3); }
 }  // namespace
 
 // One (tile, slab) work item L of the grid's list: tile L / nslabs, weight
-// slab L % nslabs. smem is the block's LDS ring; the item starts and ends
-// with every wave past its LDS accesses of the previous item.
-template <bool GLU, int WR>
+// slab L % nslabs. smem is the block's LDS ring (plus, for int8, 128 row
+// scales after it); the item starts and ends with every wave past its LDS
+// accesses of the previous item.
+// I8: W8A8 -- A int8 codes [rows, K] with one fp32 scale per row (a_scale,
+// indexed like the rows), weights int8 [E_loc, N, K] (K contiguous) with one
+// fp32 scale per output channel (w_scale [E_loc, N]); int32 accumulation,
+// dequantised in the epilogue; GEMM1 stores h in fp32, GEMM2 y in bf16.
+template <bool GLU, int WR, bool I8>
 MOE_DEV void tiled_item(
     uint8_t* smem, int L, const Tile* __restrict__ tiles,
-    const uint16_t* __restrict__ a, const uint16_t* __restrict__ w,
-    uint16_t* __restrict__ out, int K, int Nw, int Nout, int nslabs,
+    const void* __restrict__ a, const void* __restrict__ w,
+    void* __restrict__ out, int K, int Nw, int Nout, int nslabs,
     const int32_t* __restrict__ gidx, const int32_t* __restrict__ gbase,
-    int gk) {
+    int gk, const float* __restrict__ a_scale,
+    const float* __restrict__ w_scale) {
   using C = TiledCfg<WR>;
+  using Acc = typename std::conditional<I8, i32x16, f32x16>::type;
+  constexpr int EB = I8 ? 1 : 2;      // bytes per element
+  constexpr int KS = 64 / EB;         // K per step (64 bytes of every row)
+  constexpr int NBR = I8 ? 4 : 8;     // LDS reads of B per half step
   constexpr int BM = C::BM, NMB = C::NMB, NSTAGE = C::NSTAGE;
   constexpr int A_BYTES = C::A_BYTES, STAGE_BYTES = C::STAGE_BYTES;
   constexpr int NA = C::NA, NI = C::NI;
@@ -98,7 +132,7 @@ MOE_DEV void tiled_item(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 1, wn = wave & 1;
-  const uint16_t* we = w + (size_t)tl.expert * K * Nw;
+  const char* we = (const char*)w + (size_t)tl.expert * K * Nw * EB;
 
   // ---- global -> LDS assignment (per wave instruction: 1 KB contiguous)
   // A, instruction j (0..NA-1): tile rows 16*(wave + 4j) + lane/4, physical
@@ -106,62 +140,89 @@ MOE_DEV void tiled_item(
   // With a gather index the rows come straight from x (row of sorted copy
   // i = token sorted_copy[i] / k; the host keeps x under 4 GB so 32-bit
   // offsets hold), otherwise from the permuted rows of this tile.
-  const uint16_t* a_tile = gidx ? a : a + (size_t)tl.row0 * K;  // uniform
+  const char* a_tile =
+      (const char*)a + (gidx ? 0 : (size_t)tl.row0 * K * EB);  // uniform
   uint32_t a_off[NA];
 #pragma unroll
   for (int j = 0; j < NA; ++j) {
     const int r = 16 * (wave + 4 * j) + (lane >> 2);
     int src = r < tl.rows ? r : 0;
     if (gidx) src = gidx[gbase[0] + tl.row0 + src] / gk;
-    a_off[j] = ((uint32_t)src * K + 8 * ((lane & 3) ^ swz_a(r))) * 2u;
+    a_off[j] = (uint32_t)src * K * EB + 16 * ((lane & 3) ^ swz_a(r));
   }
-  // B, instruction j (0..3): k-row 2*(wave + 4j) + lane/32 of the step,
-  // physical piece lane%32 holds logical piece (lane%32) ^ swz_b(k); the
-  // swizzle only depends on k%4 = 2*(wave&1) + lane/32, the same for all j
-  uint32_t b_off;
-  {
-    const int kr = 2 * wave + (lane >> 5);
-    const int cl = (lane & 31) ^ swz_b(kr);
-    const int j = 8 * cl;  // tile column
-    int col, oc;
+  // int8: the row scales of the tile, in LDS after the ring (0 past its rows)
+  float* rs_lds = (float*)(smem + NSTAGE * STAGE_BYTES);
+  if (I8 && tid < BM) {
+    float sc = 0.f;
+    if (tid < tl.rows)
+      sc = a_scale[gidx ? gidx[gbase[0] + tl.row0 + tid] / gk : tl.row0 + tid];
+    rs_lds[tid] = sc;
+  }
+  // weight column of tile column t (0..255); columns past Nout read column 0
+  auto wcol = [&](int t) -> int {
+    int oc, col;
     if (GLU) {
-      oc = c0 + (j & (BNW / 2 - 1));
-      col = j < BNW / 2 ? oc : Nout + oc;
+      oc = c0 + (t & (BNW / 2 - 1));
+      col = t < BNW / 2 ? oc : Nout + oc;
     } else {
-      oc = c0 + j;
+      oc = c0 + t;
       col = oc;
     }
-    if (oc >= Nout) col = 0;  // unused columns read column 0
-    b_off = (uint32_t)(kr * Nw + col) * 2;
+    return oc < Nout ? col : 0;
+  };
+  // B (bf16 [K, N]), instruction j (0..3): k-row 2*(wave + 4j) + lane/32 of
+  // the step, physical piece lane%32 holds logical piece (lane%32) ^
+  // swz_b(k); the swizzle only depends on k%4 = 2*(wave&1) + lane/32, the
+  // same for all j.
+  // B (int8 [N, K]), instruction j (0..3): like A, tile columns
+  // 16*(wave + 4j) + lane/4 of 64 bytes each, LDS [column][4 x 16 B], piece
+  // lane%4 <- logical piece (lane%4) ^ swz_a(column).
+  uint32_t b_off[I8 ? 4 : 1];
+  if constexpr (I8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 16 * (wave + 4 * j) + (lane >> 2);
+      b_off[j] = (uint32_t)wcol(t) * K + 16 * ((lane & 3) ^ swz_a(t));
+    }
+  } else {
+    const int kr = 2 * wave + (lane >> 5);
+    const int cl = (lane & 31) ^ swz_b(kr);
+    b_off[0] = (uint32_t)(kr * Nw + wcol(8 * cl)) * 2;
   }
   const uint32_t a_dst = __builtin_amdgcn_readfirstlane(
       lds_addr(smem + (16 * wave) * (BK * 2)));
-  const uint32_t b_dst = __builtin_amdgcn_readfirstlane(
-      lds_addr(smem + A_BYTES + (2 * wave) * B_ROW));
+  const uint32_t b_dst = __builtin_amdgcn_readfirstlane(lds_addr(
+      smem + A_BYTES + (I8 ? 16 * wave * 64 : (2 * wave) * B_ROW)));
   const size_t b_step = (size_t)BK * Nw * 2;     // bytes per K step of B
   const uint32_t b_row8 = 8u * Nw * 2;          // 8 k-rows of B
 
   // loads of K step s_ into stage st_ (NI instructions per wave)
 #define MOE_TILED_ISSUE(s_, st_)                                              \
   do {                                                                        \
-    const char* ab_ = (const char*)a_tile + (size_t)(s_) * (BK * 2);         \
-    const char* bb_ = (const char*)we + (size_t)(s_) * b_step;               \
+    const char* ab_ = a_tile + (size_t)(s_) * 64;                             \
     const uint32_t o_ = (st_) * STAGE_BYTES;                                  \
     _Pragma("unroll") for (int j = 0; j < NA; ++j)                            \
       g2lds(ab_, a_off[j], a_dst + o_ + 64 * j * (BK * 2));                   \
-    g2lds(bb_, b_off, b_dst + o_);                                            \
-    g2lds(bb_, b_off + b_row8, b_dst + o_ + 8 * B_ROW);                       \
-    g2lds(bb_, b_off + 2 * b_row8, b_dst + o_ + 16 * B_ROW);                  \
-    g2lds(bb_, b_off + 3 * b_row8, b_dst + o_ + 24 * B_ROW);                  \
+    if constexpr (I8) {                                                       \
+      const char* bb_ = we + (size_t)(s_) * 64;                               \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j)                           \
+        g2lds(bb_, b_off[j], b_dst + o_ + 64 * j * 64);                       \
+    } else {                                                                  \
+      const char* bb_ = we + (size_t)(s_) * b_step;                           \
+      g2lds(bb_, b_off[0], b_dst + o_);                                       \
+      g2lds(bb_, b_off[0] + b_row8, b_dst + o_ + 8 * B_ROW);                  \
+      g2lds(bb_, b_off[0] + 2 * b_row8, b_dst + o_ + 16 * B_ROW);             \
+      g2lds(bb_, b_off[0] + 3 * b_row8, b_dst + o_ + 24 * B_ROW);             \
+    }                                                                         \
   } while (0)
 
-  f32x16 acc[NMB][4];
+  Acc acc[NMB][4];
 #pragma unroll
   for (int i = 0; i < NMB; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
   // LDS read offsets, loop invariant (stage offsets are immediates below)
   const int lr = lane & 31, lh = lane >> 5;
@@ -173,19 +234,27 @@ MOE_DEV void tiled_item(
       const int m = wm * WR + mb * 32 + lr;
       a_rd[kk][mb] = lds_addr(smem) + m * (BK * 2) + 16 * ((kk * 2 + lh) ^ swz_a(m));
     }
-  // transpose reads: group g = lane/16, source lane s = lane%16 supplies row
-  // kk*16 + 8*(g/2) + s/4 and columns cb + 16*(g%2) + 4*(s%4) .. +3
+  // bf16 transpose reads: group g = lane/16, source lane s = lane%16
+  // supplies row kk*16 + 8*(g/2) + s/4 and columns cb + 16*(g%2) + 4*(s%4)
+  // .. +3. int8: lane l reads tile column cb + l%32, logical piece
+  // 2*kk + l/32 (the same K bytes as its A read).
   uint32_t b_rd[2][4];  // [kk][nbk]
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int nbk = 0; nbk < 4; ++nbk) {
-      const int kr = kk * 16 + 8 * lh + ((lane & 15) >> 2);
       const int cb = GLU ? (nbk < 2 ? 0 : BNW / 2) + wn * 64 + (nbk & 1) * 32
                          : wn * 128 + nbk * 32;
-      const int col = cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      b_rd[kk][nbk] = lds_addr(smem) + A_BYTES + kr * B_ROW +
-                      16 * ((col >> 3) ^ swz_b(kr)) + 2 * (col & 7);
+      if constexpr (I8) {
+        const int col = cb + lr;
+        b_rd[kk][nbk] = lds_addr(smem) + A_BYTES + col * 64 +
+                        16 * ((kk * 2 + lh) ^ swz_a(col));
+      } else {
+        const int kr = kk * 16 + 8 * lh + ((lane & 15) >> 2);
+        const int col = cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        b_rd[kk][nbk] = lds_addr(smem) + A_BYTES + kr * B_ROW +
+                        16 * ((col >> 3) ^ swz_b(kr)) + 2 * (col & 7);
+      }
     }
 
   // fragments of one half step (16 K): A for the wave's 32-row blocks,
@@ -197,10 +266,14 @@ MOE_DEV void tiled_item(
       fa_[mb] = lds_read_b128(a_rd[kk_][mb] + (st_) * STAGE_BYTES);           \
     _Pragma("unroll") for (int nbk = 0; nbk < 4; ++nbk) {                     \
       const uint32_t p_ = b_rd[kk_][nbk] + (st_) * STAGE_BYTES;               \
-      const v4i16_t lo = lds_read_tr(p_);                                     \
-      const v4i16_t hi = lds_read_tr(p_ + 4 * B_ROW);                         \
-      fb_[nbk] = __builtin_bit_cast(                                          \
-          u32x4_t, v8i16_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}); \
+      if constexpr (I8) {                                                     \
+        fb_[nbk] = lds_read_b128(p_);                                         \
+      } else {                                                                \
+        const v4i16_t lo = lds_read_tr(p_);                                   \
+        const v4i16_t hi = lds_read_tr(p_ + 4 * B_ROW);                       \
+        fb_[nbk] = __builtin_bit_cast(                                        \
+            u32x4_t, v8i16_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}); \
+      }                                                                       \
     }                                                                         \
   } while (0)
   // NMB_: 32-row blocks of this wave that hold tile rows (blocks past the
@@ -239,7 +312,7 @@ MOE_DEV void tiled_item(
 #define MOE_TILED_ORDER(NMB_)                                                 \
   do {                                                                        \
     if ((NMB_) > 0) {                                                         \
-      __builtin_amdgcn_sched_group_barrier(0x100, (NMB_) + 8, 0);             \
+      __builtin_amdgcn_sched_group_barrier(0x100, (NMB_) + NBR, 0);           \
       __builtin_amdgcn_sched_group_barrier(0x008, 4 * (NMB_), 0);             \
     }                                                                         \
   } while (0)
@@ -278,7 +351,7 @@ MOE_DEV void tiled_item(
       MOE_TILED_STEP(s + i, i % NSTAGE, NMB_);                                \
   } while (0)
 
-  const int nsteps = K / BK;
+  const int nsteps = K / KS;
   // rows of this wave's WR-row part of the tile (wave-uniform)
   const int mrows = __builtin_amdgcn_readfirstlane(tl.rows - wm * WR);
   u32x4_t f0a[NMB], f0b[4], f1a[NMB], f1b[4];
@@ -308,27 +381,66 @@ MOE_DEV void tiled_item(
   __syncthreads();
 
   // epilogue through LDS: each wave stages 32 rows at a time
-  uint16_t* stage = (uint16_t*)smem + wave * (32 * 128);
   const int ncols = GLU ? 64 : 128;  // output columns of this wave
   const int oc0 = c0 + wn * ncols;   // first output column of this wave
+  // int8: value = acc * scale of its row * scale of its weight column
+  float cs[4];
+#pragma unroll
+  for (int nbk = 0; nbk < 4; ++nbk) {
+    cs[nbk] = 1.f;
+    if constexpr (I8) {
+      const int t = (GLU ? (nbk < 2 ? 0 : BNW / 2) + wn * 64 + (nbk & 1) * 32
+                         : wn * 128 + nbk * 32) + lr;
+      cs[nbk] = w_scale[(size_t)tl.expert * Nw + wcol(t)];
+    }
+  }
+  auto val = [&](int mb, int nbk, int e, int r) -> float {
+    if constexpr (I8)
+      return (float)acc[mb][nbk][e] * rs_lds[wm * WR + mb * 32 + r] * cs[nbk];
+    else
+      return acc[mb][nbk][e];
+  };
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
     // acc element e of a 32x32 block: row 8*(e/4) + 4*(lane/32) + e%4,
     // column lane%32
+    if (GLU && I8) {
+      // h in fp32: 32 rows x 64 columns per wave (8 KB)
+      float* st = (float*)smem + wave * (32 * 64);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = 8 * (e >> 2) + 4 * lh + (e & 3);
+#pragma unroll
+        for (int gb = 0; gb < 2; ++gb)
+          st[r * 64 + gb * 32 + lr] = silu(val(mb, gb, e, r)) * val(mb, gb + 2, e, r);
+      }
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int q = it * 64 + lane;
+        const int r = q >> 4, c = q & 15;
+        const int row = wm * WR + mb * 32 + r;
+        const int col = oc0 + 4 * c;
+        if (row < tl.rows && col < Nout)
+          *(uint4*)((float*)out + (size_t)(tl.row0 + row) * Nout + col) =
+              *(const uint4*)&st[r * 64 + 4 * c];
+      }
+      continue;
+    }
+    uint16_t* stage = (uint16_t*)smem + wave * (32 * 128);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int r = 8 * (e >> 2) + 4 * lh + (e & 3);
       if (GLU) {
 #pragma unroll
         for (int gb = 0; gb < 2; ++gb) {
-          const float hv = silu(acc[mb][gb][e]) * acc[mb][gb + 2][e];
+          const float hv = silu(val(mb, gb, e, r)) * val(mb, gb + 2, e, r);
           stage[r * 128 + gb * 32 + lr] = (uint16_t)f32_to_bf16_bits(hv);
         }
       } else {
 #pragma unroll
         for (int nbk = 0; nbk < 4; ++nbk)
           stage[r * 128 + nbk * 32 + lr] =
-              (uint16_t)f32_to_bf16_bits(acc[mb][nbk][e]);
+              (uint16_t)f32_to_bf16_bits(val(mb, nbk, e, r));
       }
     }
     // each lane writes 16-byte pieces of the staged rows
@@ -340,7 +452,7 @@ MOE_DEV void tiled_item(
       const int row = wm * WR + mb * 32 + r;
       const int col = oc0 + 8 * c;
       if (row < tl.rows && col < Nout)
-        *(uint4*)(out + (size_t)(tl.row0 + row) * Nout + col) =
+        *(uint4*)((uint16_t*)out + (size_t)(tl.row0 + row) * Nout + col) =
             *(const uint4*)&stage[r * 128 + 8 * c];
     }
   }
@@ -352,50 +464,37 @@ MOE_DEV void tiled_item(
 // (nj blocks per XCD). The items running at once on an XCD are therefore
 // consecutive: the slabs of a few tiles and the tiles of one expert, whose A
 // rows and weight slabs that XCD's L2 serves to all of them.
-template <bool GLU, int WR>
+template <bool GLU, int WR, bool I8>
 __global__ __launch_bounds__(256, TiledCfg<WR>::BLOCKS_PER_CU) void gemm_bf16_tiled_kernel(
     const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
-    const uint16_t* __restrict__ a, const uint16_t* __restrict__ w,
-    uint16_t* __restrict__ out, int K, int Nw, int Nout, int nslabs,
+    const void* __restrict__ a, const void* __restrict__ w,
+    void* __restrict__ out, int K, int Nw, int Nout, int nslabs,
     const int32_t* __restrict__ gidx, const int32_t* __restrict__ gbase,
-    int gk) {
+    int gk, const float* __restrict__ a_scale,
+    const float* __restrict__ w_scale) {
   using C = TiledCfg<WR>;
-  __shared__ __align__(1024) uint8_t smem[C::NSTAGE * C::STAGE_BYTES];
+  __shared__ __align__(1024) uint8_t
+      smem[C::NSTAGE * C::STAGE_BYTES + (I8 ? 4 * C::BM : 0)];
   const int nb = tile_count[0] * nslabs;
   const int xcd = blockIdx.x % 8, j = blockIdx.x / 8, nj = gridDim.x / 8;
   const int per = nb / 8, rem = nb % 8;
   const int lo = xcd * per + min(xcd, rem);
   const int hi = lo + per + (xcd < rem ? 1 : 0);
   for (int L = lo + j; L < hi; L += nj) {
-    tiled_item<GLU, WR>(smem, L, tiles, a, w, out, K, Nw, Nout, nslabs, gidx,
-                        gbase, gk);
+    tiled_item<GLU, WR, I8>(smem, L, tiles, a, w, out, K, Nw, Nout, nslabs,
+                            gidx, gbase, gk, a_scale, w_scale);
     __syncthreads();  // LDS staging of this item read before the next fills
   }
 }
 
-template <int WR>
-static hipError_t launch_tiled(bool glu, dim3 grid, const Tile* tiles,
-                               const int32_t* tile_count, const uint16_t* a,
-                               const uint16_t* w, uint16_t* out, int K, int Nw,
-                               int Nout, int nslabs, const int32_t* gidx,
-                               const int32_t* gbase, int gk, hipStream_t s) {
-  if (glu)
-    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<true, WR>), grid, dim3(256), 0,
-                       s, tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
-                       gidx, gbase, gk);
-  else
-    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<false, WR>), grid, dim3(256), 0,
-                       s, tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
-                       gidx, gbase, gk);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
-                                  const int32_t* tile_count, int max_tiles,
-                                  const uint16_t* a, const uint16_t* w,
-                                  uint16_t* out, int K, int Nw, int Nout,
-                                  const int32_t* gidx, const int32_t* gbase,
-                                  int gk, hipStream_t s) {
+template <int WR, bool I8>
+static hipError_t launch_tiled(bool glu, const Tile* tiles,
+                               const int32_t* tile_count, int max_tiles,
+                               const void* a, const void* w, void* out, int K,
+                               int Nw, int Nout, const int32_t* gidx,
+                               const int32_t* gbase, int gk,
+                               const float* a_scale, const float* w_scale,
+                               hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
   const int slab = glu ? BNW / 2 : BNW;
   const int nslabs = (Nout + slab - 1) / slab;
@@ -405,8 +504,39 @@ hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
   const long long slots = (long long)device_cus() * 2;
   long long nblk = items < slots ? items : slots;
   nblk = ((nblk + 7) / 8) * 8;
-  return launch_tiled<64>(glu, dim3((unsigned)nblk), tiles, tile_count, a, w,
-                          out, K, Nw, Nout, nslabs, gidx, gbase, gk, s);
+  const dim3 grid((unsigned)nblk);
+  if (glu)
+    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<true, WR, I8>), grid, dim3(256),
+                       0, s, tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
+                       gidx, gbase, gk, a_scale, w_scale);
+  else
+    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<false, WR, I8>), grid,
+                       dim3(256), 0, s, tiles, tile_count, a, w, out, K, Nw,
+                       Nout, nslabs, gidx, gbase, gk, a_scale, w_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
+                                  const int32_t* tile_count, int max_tiles,
+                                  const uint16_t* a, const uint16_t* w,
+                                  uint16_t* out, int K, int Nw, int Nout,
+                                  const int32_t* gidx, const int32_t* gbase,
+                                  int gk, hipStream_t s) {
+  return launch_tiled<64, false>(glu, tiles, tile_count, max_tiles, a, w, out,
+                                 K, Nw, Nout, gidx, gbase, gk, nullptr,
+                                 nullptr, s);
+}
+
+hipError_t launch_gemm_i8_tiled(bool glu, const Tile* tiles,
+                                const int32_t* tile_count, int max_tiles,
+                                const int8_t* a, const float* a_scale,
+                                const int8_t* w, const float* w_scale,
+                                void* out, int K, int Nw, int Nout,
+                                const int32_t* gidx, const int32_t* gbase,
+                                int gk, hipStream_t s) {
+  return launch_tiled<64, true>(glu, tiles, tile_count, max_tiles, a, w, out,
+                                K, Nw, Nout, gidx, gbase, gk, a_scale, w_scale,
+                                s);
 }
 
 }  // namespace moe

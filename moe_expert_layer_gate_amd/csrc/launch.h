@@ -56,6 +56,9 @@ hipError_t launch_route_gather(const void* x, int act, int mx, int H, int k,
 
 // Compute units of the current device (256 on MI355X if the query fails).
 int device_cus();
+// Waves per block that split K in the weight-streaming kernels, for a grid
+// of `blocks` blocks and `steps` K steps of 16 KB of weights per wave.
+int stream_ksplit(long long blocks, int steps, int rg);
 
 // Grouped GEMMs. glu: GEMM1 with SwiGLU epilogue (N = 2*I weight columns,
 // I outputs), else GEMM2 (N outputs). Tiles come from the tile list.
@@ -76,6 +79,37 @@ hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
                                   uint16_t* out, int K, int Nw, int Nout,
                                   const int32_t* gidx, const int32_t* gbase,
                                   int gk, hipStream_t s);
+// W8A8: int8 activations [rows, K] with one fp32 scale per row (a_scale,
+// indexed like the rows of a, through gidx when it is non-NULL), int8
+// weights [E_loc, N, K] with one fp32 scale per output channel
+// (w_scale [E_loc, N]); int32 accumulation. glu: fp32 h, else bf16 y.
+// 128-row LDS-tiled tiles (mt = 128), K % 64 == 0.
+hipError_t launch_gemm_i8_tiled(bool glu, const Tile* tiles,
+                                const int32_t* tile_count, int max_tiles,
+                                const int8_t* a, const float* a_scale,
+                                const int8_t* w, const float* w_scale,
+                                void* out, int K, int Nw, int Nout,
+                                const int32_t* gidx, const int32_t* gbase,
+                                int gk, hipStream_t s);
+// Same operands, weight-streaming tiles of 16 * rg rows (mt = 16 or 32),
+// K % 128 == 0.
+hipError_t launch_gemm_i8_stream(bool glu, int rg, const Tile* tiles,
+                                 const int32_t* tile_count, int max_tiles,
+                                 const int8_t* a, const float* a_scale,
+                                 const int8_t* w, const float* w_scale,
+                                 void* out, int K, int Nw, int Nout,
+                                 const int32_t* gidx, const int32_t* gbase,
+                                 int gk, hipStream_t s);
+// Dynamic per-row int8 quantisation (bf16 or fp32 rows of K, K % 8 == 0):
+// codes [rows, K] and fp32 scales [rows]. offs == NULL: nrows rows, row r
+// from source row r. Else the R = offs[fe] - offs[fb] (<= nrows) rows of the
+// copies of experts [fb, fe), row r from source row gidx[offs[fb] + r] / gk
+// (gidx != NULL) or r.
+hipError_t launch_quant_i8_rows(bool f32, const void* src, int K, int nrows,
+                                const int32_t* gidx, const int32_t* offs,
+                                int fb, int fe, int gk, int8_t* codes,
+                                float* scales, hipStream_t s);
+
 // fp32 activations / fp32 weights [E_loc, K, N], VALU.
 hipError_t launch_gemm_f32(bool glu, const Tile* tiles,
                            const int32_t* tile_count, int max_tiles,

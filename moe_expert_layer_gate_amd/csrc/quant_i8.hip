@@ -1,0 +1,105 @@
+// Dynamic per-row int8 quantisation of activations for the W8A8 experts.
+//
+// [P3] "NPU Qwen3-Next inference practice", section 量化策略: the routed
+// experts run W8A8 -- int8 weights with a static scale per output channel and
+// int8 activations with a dynamic scale per token. Applied here to the tokens
+// of x (once, before routing; GEMM1 gathers the token rows of the codes) and
+// to the rows of h between the two GEMMs.
+//
+// Row r: amax = max |v|; scale = amax / 127 rounded to nearest fp32; code =
+// rint(v / scale) with the quotient rounded to nearest fp32 and rint taking
+// ties to even, clipped to [-127, 127]. An all-zero row gets scale 0 and codes
+// 0. Divisions are the correctly rounded fp32 division (__fdiv_rn), so codes
+// and scales are bit-identical to any other IEEE evaluation of that rule.
+//
+// One wave per row, 8 elements (16 or 32 bytes) per lane and chunk. The row is
+// read twice (amax, then codes); the second pass is served by the caches.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+template <bool F32>
+MOE_DEV void load8(const void* src, size_t off, float (&v)[8]) {
+  if (F32) {
+    const float4 a = *(const float4*)((const float*)src + off);
+    const float4 b = *(const float4*)((const float*)src + off + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 a = *(const uint4*)((const uint16_t*)src + off);
+    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
+    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
+  }
+}
+
+MOE_DEV uint32_t code_byte(float v, float scale) {
+  float q = rintf(__fdiv_rn(v, scale));
+  q = fminf(fmaxf(q, -127.f), 127.f);
+  return (uint32_t)(int)q & 0xFFu;
+}
+
+// rows: offs == NULL: nrows rows, row r reads source row r. Otherwise the
+// R = offs[fe] - offs[fb] rows of the sorted copies of experts [fb, fe); row r
+// reads source row gidx[offs[fb] + r] / gk (gidx != NULL) or r.
+template <bool F32>
+__global__ __launch_bounds__(256) void quant_i8_rows_kernel(
+    const void* __restrict__ src, int K, int nrows,
+    const int32_t* __restrict__ gidx, const int32_t* __restrict__ offs, int fb,
+    int fe, int gk, int8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int R = nrows, base = 0;
+  if (offs) {
+    base = offs[fb];
+    R = offs[fe] - base;
+  }
+  if (r >= R) return;
+  const int srow = gidx ? gidx[base + r] / gk : r;
+  const size_t so = (size_t)srow * K;
+  float amax = 0.f;
+  for (int c = 8 * lane; c < K; c += 512) {
+    float v[8];
+    load8<F32>(src, so + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float scale = __fdiv_rn(amax, 127.f);
+  if (lane == 0) scales[r] = scale;
+  int8_t* orow = codes + (size_t)r * K;
+  for (int c = 8 * lane; c < K; c += 512) {
+    uint2 o = {0u, 0u};
+    if (scale > 0.f) {
+      float v[8];
+      load8<F32>(src, so + c, v);
+      o.x = code_byte(v[0], scale) | code_byte(v[1], scale) << 8 |
+            code_byte(v[2], scale) << 16 | code_byte(v[3], scale) << 24;
+      o.y = code_byte(v[4], scale) | code_byte(v[5], scale) << 8 |
+            code_byte(v[6], scale) << 16 | code_byte(v[7], scale) << 24;
+    }
+    *(uint2*)(orow + c) = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_i8_rows(bool f32, const void* src, int K, int nrows,
+                                const int32_t* gidx, const int32_t* offs,
+                                int fb, int fe, int gk, int8_t* codes,
+                                float* scales, hipStream_t s) {
+  if (nrows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((nrows + 3) / 4));
+  if (f32)
+    hipLaunchKernelGGL(quant_i8_rows_kernel<true>, grid, dim3(256), 0, s, src,
+                       K, nrows, gidx, offs, fb, fe, gk, codes, scales);
+  else
+    hipLaunchKernelGGL(quant_i8_rows_kernel<false>, grid, dim3(256), 0, s, src,
+                       K, nrows, gidx, offs, fb, fe, gk, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -68,6 +68,13 @@ def _query(L, p):
     (dict(n_ffn=4096, local_end=4096), 2), (dict(top_k=65, n_ffn=128), 2),
     (dict(act="f32"), 2), (dict(wt="mxfp4"), 2),
     (dict(wt="mxfp4", act_q="mxfp8", H=2048 + 32), 2),
+    # W8A8 needs int8 on both sides, H and I multiples of 128 and
+    # 2 * I * H < 2^31
+    (dict(wt="int8"), 2), (dict(act_q="int8"), 2),
+    (dict(wt="int8", act_q="mxfp8"), 2),
+    (dict(wt="int8", act_q="int8", H=2048 + 64), 2),
+    (dict(wt="int8", act_q="int8", I=768 + 32), 2),
+    (dict(wt="int8", act_q="int8", H=32768, I=32768), 2),
 ])
 def test_invalid_problems_rejected_on_host(L, kw, status):
     st, _ = _query(L, _p(**kw))
@@ -84,6 +91,9 @@ def test_workspace_query_and_too_small(L):
     st, _ = _query(L, _p(wt="mxfp4", act_q="mxfp8", H=4096, I=1536,
                          local_begin=32, local_end=64))
     assert st == 0
+    # W8A8 adds the int8 codes of x, fp32 h and its int8 codes
+    st, need8 = _query(L, _p(wt="int8", act_q="int8"))
+    assert st == 0 and need8 > need
     # a buffer smaller than required is refused before any launch
     n = ctypes.c_size_t(need - 1)
     st = L.moe_layer(ctypes.byref(p), None, None, None, None, None, None, None,
@@ -103,6 +113,13 @@ def test_missing_pointers_rejected(L):
                      fake, fake, ctypes.byref(n), None)
     assert st == 1  # scale given for bf16 weights
     st = L.moe_gate_topk(ctypes.byref(p), None, fake, fake, None)
+    assert st == 1
+    # W8A8 weights without their channel scales
+    p8 = _p(wt="int8", act_q="int8")
+    _, need8 = _query(L, p8)
+    n8 = ctypes.c_size_t(need8)
+    st = L.moe_layer(ctypes.byref(p8), fake, fake, None, fake, None, fake, None,
+                     fake, fake, ctypes.byref(n8), None)
     assert st == 1
     st = L.moe_finalize(ctypes.byref(p), fake, fake, None, fake, fake, fake,
                         None, fake, None)

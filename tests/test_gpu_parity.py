@@ -60,6 +60,18 @@ SMALL = {
     "ep_w4a8_prefill_small": scaled(get_workload("qwen3_235b_a22b_ep_rank_w4a8"),
                                     T=384, H=384, I=256, n_ffn=16, local_begin=4,
                                     local_end=12, top_k=4),
+    # W8A8: decode-size (weight-streaming kernel, 16-row tiles)
+    "decode_w8a8_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"), T=32,
+                                H=512, I=384, n_ffn=16, local_end=16, top_k=4),
+    # W8A8 prefill-size (128-row tiles): I = 384 gives three GEMM1 slabs,
+    # H = 384 a ragged GEMM2 slab
+    "prefill_w8a8_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_w8a8"),
+                                 T=600, H=384, I=384, n_ffn=8, local_end=8,
+                                 top_k=4),
+    # W8A8 on an expert range with 32-row streaming tiles
+    "range_w8a8_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"), T=96,
+                               H=256, I=256, n_ffn=16, local_begin=4,
+                               local_end=10, top_k=4),
 }
 
 
@@ -126,6 +138,10 @@ def _routing_case(shape, seed):
         codes, scl = O.mx_quant(x.double().numpy()[tok], "e4m3")
         assert np.array_equal(r["x_perm"][: r1 - r0].cpu().numpy(), codes)
         assert np.array_equal(r["x_perm_scale"][: r1 - r0].cpu().numpy(), scl)
+    elif shape.act_q == "int8":
+        codes, scl = O.int8_quant_rows(x.double().numpy()[tok])
+        assert np.array_equal(r["x_perm"][: r1 - r0].cpu().numpy(), codes)
+        assert np.array_equal(bits(r["x_perm_scale"][: r1 - r0]), scl.view(np.int32))
     else:
         assert np.array_equal(bits(r["x_perm"][: r1 - r0]), bits(x[torch.from_numpy(tok)]))
 
@@ -172,9 +188,11 @@ def test_grouped_ffn_on_oracle_routing(name):
     p = m.problem(shape)
     offsets = torch.from_numpy(ref["offsets"].astype(np.int32)).to(DEV)
     N = shape.T * shape.top_k
-    if shape.act_q == "mxfp8":
-        xp = torch.zeros((N, shape.H), dtype=torch.uint8)
-        xs = torch.zeros((N, shape.H // 32), dtype=torch.uint8)
+    if shape.act_q in ("mxfp8", "int8"):
+        i8 = shape.act_q == "int8"
+        xp = torch.zeros((N, shape.H), dtype=torch.int8 if i8 else torch.uint8)
+        xs = (torch.zeros(N, dtype=torch.float32) if i8 else
+              torch.zeros((N, shape.H // 32), dtype=torch.uint8))
         xp[:R] = torch.from_numpy(ref["x_perm_codes"])
         xs[:R] = torch.from_numpy(ref["x_perm_scale"])
         xp, xs = xp.to(DEV), xs.to(DEV)
@@ -187,6 +205,17 @@ def test_grouped_ffn_on_oracle_routing(name):
                       inp["w13_scale"], inp["w2_scale"])
     torch.cuda.synchronize()
     assert_close(to64(y[:R]), ref["y"], shape, "y")
+    if shape.act_q == "int8":
+        # h's int8 row quantisation: the GPU's fp32 h differs from the
+        # oracle's by rounding only, so row scales agree to a few ulps and
+        # codes by at most one step
+        h, hs = m.ffn_up(p, offsets, xp, xs, inp["w13"], inp["w13_scale"])
+        torch.cuda.synchronize()
+        hc = h[:R].cpu().numpy().astype(np.int64)
+        rc = ref["h_codes"].astype(np.int64)
+        assert np.max(np.abs(hc - rc)) <= 1
+        assert np.mean(hc != rc) < 0.01
+        np.testing.assert_allclose(hs[:R].cpu().numpy(), ref["h_scale"], rtol=1e-5)
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -232,7 +261,8 @@ def test_layer_split_calls_equal_fused():
     m = _m()
     for name in ("prefill_skewed_small", "prefill_wide_small", "ep_w4a8_small",
                  "ep_w4a8_prefill_small", "ep_w4a8_wide_small",
-                 "tiny_fp32", "decode_bf16_small"):
+                 "tiny_fp32", "decode_bf16_small", "decode_w8a8_small",
+                 "prefill_w8a8_small", "range_w8a8_small"):
         shape = SMALL[name]
         inp = generate(shape, seed=6, device=DEV)
         p = m.problem(shape)
@@ -342,6 +372,30 @@ def test_edge_short_k_tiled(I):
     _layer_vs_oracle(SMALL["prefill_wide_small"].replace(I=I))
 
 
+@pytest.mark.parametrize("name", ["prefill_w8a8_small", "decode_w8a8_small"])
+def test_edge_short_k_w8a8(name):
+    # GEMM2 with K = I = 128: two int8 steps of the tiled kernel, one of the
+    # streaming kernel
+    _layer_vs_oracle(SMALL[name].replace(I=128))
+
+
+def test_edge_w8a8_zero_rows_of_x():
+    # all-zero tokens quantise to scale 0 and codes 0: their expert outputs
+    # are exactly 0 and the layer returns the residual for them
+    def zero_some(inp):
+        inp["x"][::3] = 0
+        return inp
+    b = SMALL["prefill_w8a8_small"]
+    m = _m()
+    inp = zero_some(generate(b, seed=1, device=DEV))
+    out = m.layer(m.problem(b), inp["logits"], inp["x"], inp["w13"], inp["w2"],
+                  inp["w13_scale"], inp["w2_scale"], residual=inp["residual"])
+    torch.cuda.synchronize()
+    ref = _oracle_layer(b, inp)["out"]
+    assert_close(to64(out), ref, b, "zero rows")
+    assert np.array_equal(bits(out[::3]), bits(inp["residual"][::3]))
+
+
 def test_edge_range_drops_everything():
     b = SMALL["ep_w4a8_small"]
     # logits steer every token away from the local range: partial sum is 0
@@ -362,7 +416,9 @@ def _sample_tokens(T, n, seed=0):
 FULL_SAMPLES = {"tiny_fp32": 16, "qwen3_30b_a3b_decode_bf16": 32,
                 "qwen3_30b_a3b_prefill_skewed_bf16": 48,
                 "longcat_flash_zero_experts_bf16": 6,
-                "qwen3_235b_a22b_ep_rank_w4a8": 48}
+                "qwen3_235b_a22b_ep_rank_w4a8": 48,
+                "qwen3_30b_a3b_decode_w8a8": 32,
+                "qwen3_30b_a3b_prefill_skewed_w8a8": 48}
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
