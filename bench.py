@@ -10,10 +10,14 @@ Prints ONE JSON line: whole-step tokens/s plus
                around it inside the timed steps, against the MI355X peak of
                the bound it hits (HBM 8 TB/s for decode-size batches, dense
                MFMA for prefill-size batches);
-  stages_us    every stage from a second, untimed pass with an event at each
-               stage boundary (each event adds a few microseconds);
+  stages_us    every stage from an untimed pass after the timed steps, with
+               an event at each stage boundary (each event adds a few
+               microseconds);
   cpu_baseline the CPU oracle timed on the host on a bounded sample of the
                same workload (a reported baseline, not the target).
+
+Before the W warm-up steps, untimed steps run for 0.1 s of wall time so that
+the GPU has left its idle clocks when the (short) timed region starts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--op layer|norm_cast|norm_mx]
@@ -40,7 +44,8 @@ METRIC = ("MoE layer tokens/s; grouped-GEMM % of MFMA peak (prefill) / "
 DEFAULT_WORKLOAD = "qwen3_30b_a3b_decode_bf16"
 
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {"bf16": 2500.0, "mx": 5000.0, "f32": 157.3}
+# dense MFMA peaks (int8: 5.0 POP/s, reported in the same unit as tera-ops)
+PEAK_TFLOPS = {"bf16": 2500.0, "mx": 5000.0, "i8": 5000.0, "f32": 157.3}
 
 
 # HBM bytes of one launch of the dominant kernel, from two rocprofv3 --pmc
@@ -55,6 +60,7 @@ KERNEL_SOURCES = {
     "gemm_bf16_stream": ["gemm_bf16_stream.hip", "common.h", "launch.h"],
     "gemm_bf16_tiled": ["gemm_bf16_tiled.hip", "lds_dma.h", "common.h", "launch.h"],
     "gemm_mx_tiled": ["gemm_mx_tiled.hip", "lds_dma.h", "common.h", "launch.h"],
+    "gemm_i8_stream": ["gemm_i8_stream.hip", "common.h", "launch.h"],
 }
 TRAFFIC = {
     # workload: (kernel source set, sha256[:16] of its sources, FETCH KiB,
@@ -104,6 +110,18 @@ def _copy_calibration():
     print(json.dumps({"copy_bytes": n, "dispatches": 5}), flush=True)
 
 
+def _settle(step, seconds=0.1):
+    """Untimed steps for `seconds` of wall time before the warm-up: the GPU
+    leaves its idle clocks only after some milliseconds of work, and a short
+    timed region would otherwise be measured on a ramping clock."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+
+
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +161,11 @@ def _gemm1_units(shape, touched, R):
     if shape.wt == "mxfp4":
         wbytes = touched * (2 * I * H // 2 + 2 * I * H // 32)
         abytes = R * (H + H // 32) + R * (I + I // 32)
+    elif shape.wt == "int8":
+        # int8 codes + fp32 channel scales; int8 rows of x + fp32 row scales
+        # in, h out in fp32 (quantised to int8 by the next launch)
+        wbytes = touched * (2 * I * H + 2 * I * 4)
+        abytes = R * (H + 4) + R * I * 4
     else:
         eb = 4 if shape.wt == "f32" else 2
         wbytes = touched * H * 2 * I * eb
@@ -156,7 +179,7 @@ def _bound(shape, R, touched):
     are MFMA bound. Chosen by arithmetic intensity of GEMM1 against the
     ridge point of the format's peak."""
     nbytes, flops = _gemm1_units(shape, touched, R)
-    kind = "mx" if shape.wt == "mxfp4" else ("f32" if shape.wt == "f32" else "bf16")
+    kind = {"mxfp4": "mx", "int8": "i8", "f32": "f32"}.get(shape.wt, "bf16")
     ridge = PEAK_TFLOPS[kind] * 1e12 / (PEAK_HBM_GBS * 1e9)
     return ("mfma" if flops / nbytes > ridge else "hbm"), kind
 
@@ -180,6 +203,12 @@ def _cpu_baseline(shape, inp, target_s):
             i = e - fb
             a = O.mxfp4_dequant_rows(host["w13"][i].numpy(), host["w13_scale"][i].numpy())
             b = O.mxfp4_dequant_rows(host["w2"][i].numpy(), host["w2_scale"][i].numpy())
+            return a.T.copy(), b.T.copy()
+    elif shape.wt == "int8":
+        def get(e):
+            i = e - fb
+            a = O.int8_dequant_rows(host["w13"][i].numpy(), host["w13_scale"][i].numpy())
+            b = O.int8_dequant_rows(host["w2"][i].numpy(), host["w2_scale"][i].numpy())
             return a.T.copy(), b.T.copy()
     else:
         def get(e):
@@ -258,8 +287,6 @@ def main():
                        residual=inp["residual"], out=out, workspace=ws)
 
     none = [None] * nst
-    for _ in range(args.warmup):
-        step(none)
     g1 = m.STAGES.index("gemm1_swiglu")
 
     def events(n):
@@ -270,9 +297,27 @@ def main():
                 e.record()
         return ev
 
-    # Timed region: the only events inside it bracket the GEMM1 launch (each
-    # event record costs a few microseconds of stream time, so the per-stage
-    # breakdown is taken in a separate pass below).
+    def stage_pass():
+        """Untimed pass with an event at every stage boundary (each event
+        record costs a few microseconds of stream time, so these events stay
+        out of the timed steps)."""
+        ev = events(nst)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(ev[i])
+        torch.cuda.synchronize()
+        st = {}
+        for s, name in enumerate(m.STAGES):
+            d = [ev[i][s].elapsed_time(ev[i][s + 1]) * 1e3 for i in range(args.steps)]
+            st[name] = round(sum(d) / len(d), 2)
+        tot = sum(ev[i][0].elapsed_time(ev[i][nst - 1]) * 1e3
+                  for i in range(args.steps)) / args.steps
+        return st, tot
+
+    _settle(lambda: step(none))
+    for _ in range(args.warmup):
+        step(none)
+    # Timed region: the only events inside it bracket the GEMM1 launch.
     ev = events(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -285,18 +330,8 @@ def main():
     ms = (t1 - t0) * 1e3 / args.steps
     gemm1_us = sum(ev[i][0].elapsed_time(ev[i][1]) * 1e3
                    for i in range(args.steps)) / args.steps
-    # Untimed pass with an event at every stage boundary.
-    ev = events(nst)
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(ev[i])
-    torch.cuda.synchronize()
-    stage_us = {}
-    for s, name in enumerate(m.STAGES):
-        d = [ev[i][s].elapsed_time(ev[i][s + 1]) * 1e3 for i in range(args.steps)]
-        stage_us[name] = round(sum(d) / len(d), 2)
-    traced_step_us = sum(ev[i][0].elapsed_time(ev[i][nst - 1]) * 1e3
-                         for i in range(args.steps)) / args.steps
+    # per-stage breakdown, reported from a pass after the timed region
+    stage_us, traced_step_us = stage_pass()
 
     touched, R = _routing_stats(m, p, shape, inp)
     bound, kind = _bound(shape, R, touched)
@@ -323,7 +358,8 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "mxfp4": "mxfp8xmxfp4"}[shape.wt],
+        "dtype": {"f32": "f32", "bf16": "bf16", "mxfp4": "mxfp8xmxfp4",
+                  "int8": "int8xint8"}[shape.wt],
         "data": "synthetic",
         "config": {"workload": shape.name, "T": shape.T, "H": shape.H,
                    "I": shape.I, "n_ffn": shape.n_ffn, "n_zero": shape.n_zero,
@@ -375,6 +411,7 @@ def _bench_norm(args, m):
                                          _ptr(y16), _ptr(res), _stream())
         assert st == 0, st
 
+    _settle(step)
     for _ in range(args.warmup):
         step()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
