@@ -66,13 +66,17 @@ TRAFFIC = {
     # workload: (kernel source set, sha256[:16] of its sources, FETCH KiB,
     #            WRITE KiB) per GEMM1 dispatch
     "qwen3_30b_a3b_decode_bf16":
-        ("gemm_bf16_stream", "1cd977fa92316f22", 342876.0, 384.0),
+        ("gemm_bf16_stream", "9d7dc2a9b87298f4", 342877.0, 384.0),
     "qwen3_30b_a3b_prefill_skewed_bf16":
-        ("gemm_bf16_tiled", "7bca9d494eefcb05", 596001.9, 49152.0),
+        ("gemm_bf16_tiled", "2445794285fc5e27", 594841.2, 49152.0),
     "longcat_flash_zero_experts_bf16":
-        ("gemm_bf16_stream", "1cd977fa92316f22", 13561689.7, 32528.0),
+        ("gemm_bf16_stream", "9d7dc2a9b87298f4", 13561475.4, 32528.0),
     "qwen3_235b_a22b_ep_rank_w4a8":
-        ("gemm_mx_tiled", "581eecb5dc46deea", 213261.0, 12829.2),
+        ("gemm_mx_tiled", "cf3928170e5fbde2", 213060.9, 12827.9),
+    "qwen3_30b_a3b_decode_w8a8":
+        ("gemm_i8_stream", "651a4ace5b559916", 171468.6, 773.5),
+    "qwen3_30b_a3b_prefill_skewed_w8a8":
+        ("gemm_bf16_tiled", "2445794285fc5e27", 249729.0, 98304.0),
 }
 
 

@@ -12,8 +12,9 @@
 // 0. Divisions are the correctly rounded fp32 division (__fdiv_rn), so codes
 // and scales are bit-identical to any other IEEE evaluation of that rule.
 //
-// One wave per row, 8 elements (16 or 32 bytes) per lane and chunk. The row is
-// read twice (amax, then codes); the second pass is served by the caches.
+// One wave per row, 8 elements (16 or 32 bytes) per lane and chunk of 512.
+// Rows up to 8192 elements stay in registers between the amax and the codes
+// (one read); longer rows are read twice.
 #include "common.h"
 #include "launch.h"
 
@@ -44,7 +45,9 @@ MOE_DEV uint32_t code_byte(float v, float scale) {
 // rows: offs == NULL: nrows rows, row r reads source row r. Otherwise the
 // R = offs[fe] - offs[fb] rows of the sorted copies of experts [fb, fe); row r
 // reads source row gidx[offs[fb] + r] / gk (gidx != NULL) or r.
-template <bool F32>
+// CPL > 0: the row (at most 512 * CPL elements) is held in registers and read
+// once; CPL == 0: any length, read twice (amax, then codes).
+template <bool F32, int CPL>
 __global__ __launch_bounds__(256) void quant_i8_rows_kernel(
     const void* __restrict__ src, int K, int nrows,
     const int32_t* __restrict__ gidx, const int32_t* __restrict__ offs, int fb,
@@ -59,7 +62,41 @@ __global__ __launch_bounds__(256) void quant_i8_rows_kernel(
   if (r >= R) return;
   const int srow = gidx ? gidx[base + r] / gk : r;
   const size_t so = (size_t)srow * K;
+  int8_t* orow = codes + (size_t)r * K;
   float amax = 0.f;
+  if constexpr (CPL > 0) {
+    float v[CPL][8];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = 512 * i + 8 * lane;
+      if (c < K) {
+        load8<F32>(src, so + c, v[i]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[i][j] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float scale = __fdiv_rn(amax, 127.f);
+    if (lane == 0) scales[r] = scale;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = 512 * i + 8 * lane;
+      if (c >= K) break;
+      uint2 o = {0u, 0u};
+      if (scale > 0.f) {
+        o.x = code_byte(v[i][0], scale) | code_byte(v[i][1], scale) << 8 |
+              code_byte(v[i][2], scale) << 16 | code_byte(v[i][3], scale) << 24;
+        o.y = code_byte(v[i][4], scale) | code_byte(v[i][5], scale) << 8 |
+              code_byte(v[i][6], scale) << 16 | code_byte(v[i][7], scale) << 24;
+      }
+      *(uint2*)(orow + c) = o;
+    }
+    return;
+  }
   for (int c = 8 * lane; c < K; c += 512) {
     float v[8];
     load8<F32>(src, so + c, v);
@@ -70,7 +107,6 @@ __global__ __launch_bounds__(256) void quant_i8_rows_kernel(
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   const float scale = __fdiv_rn(amax, 127.f);
   if (lane == 0) scales[r] = scale;
-  int8_t* orow = codes + (size_t)r * K;
   for (int c = 8 * lane; c < K; c += 512) {
     uint2 o = {0u, 0u};
     if (scale > 0.f) {
@@ -85,6 +121,29 @@ __global__ __launch_bounds__(256) void quant_i8_rows_kernel(
   }
 }
 
+template <bool F32>
+hipError_t launch_rows(int cpl, dim3 grid, hipStream_t s, const void* src,
+                       int K, int nrows, const int32_t* gidx,
+                       const int32_t* offs, int fb, int fe, int gk,
+                       int8_t* codes, float* scales) {
+#define MOE_Q(C)                                                              \
+  hipLaunchKernelGGL((quant_i8_rows_kernel<F32, C>), grid, dim3(256), 0, s,   \
+                     src, K, nrows, gidx, offs, fb, fe, gk, codes, scales)
+  switch (cpl) {
+    case 1: MOE_Q(1); break;
+    case 2: MOE_Q(2); break;
+    case 3: MOE_Q(3); break;
+    case 4: MOE_Q(4); break;
+    case 6: MOE_Q(6); break;
+    case 8: MOE_Q(8); break;
+    case 12: MOE_Q(12); break;
+    case 16: MOE_Q(16); break;
+    default: MOE_Q(0); break;
+  }
+#undef MOE_Q
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quant_i8_rows(bool f32, const void* src, int K, int nrows,
@@ -93,13 +152,15 @@ hipError_t launch_quant_i8_rows(bool f32, const void* src, int K, int nrows,
                                 float* scales, hipStream_t s) {
   if (nrows <= 0) return hipSuccess;
   const dim3 grid((unsigned)((nrows + 3) / 4));
-  if (f32)
-    hipLaunchKernelGGL(quant_i8_rows_kernel<true>, grid, dim3(256), 0, s, src,
-                       K, nrows, gidx, offs, fb, fe, gk, codes, scales);
-  else
-    hipLaunchKernelGGL(quant_i8_rows_kernel<false>, grid, dim3(256), 0, s, src,
-                       K, nrows, gidx, offs, fb, fe, gk, codes, scales);
-  return hipGetLastError();
+  // chunks of 512 elements per row, rounded up to an instantiated count
+  int cpl = (K + 511) / 512;
+  for (int c : {1, 2, 3, 4, 6, 8, 12, 16})
+    if (cpl <= c) { cpl = c; break; }
+  if (cpl > 16) cpl = 0;
+  return f32 ? launch_rows<true>(cpl, grid, s, src, K, nrows, gidx, offs, fb,
+                                 fe, gk, codes, scales)
+             : launch_rows<false>(cpl, grid, s, src, K, nrows, gidx, offs, fb,
+                                  fe, gk, codes, scales);
 }
 
 }  // namespace moe
