@@ -72,7 +72,7 @@ TRAFFIC = {
     "longcat_flash_zero_experts_bf16":
         ("gemm_bf16_stream", "9d7dc2a9b87298f4", 13561475.4, 32528.0),
     "qwen3_235b_a22b_ep_rank_w4a8":
-        ("gemm_mx_tiled", "cf3928170e5fbde2", 213060.9, 12827.9),
+        ("gemm_mx_tiled", "cdb8242d03e3f9a3", 213173.0, 12824.5),
     "qwen3_30b_a3b_decode_w8a8":
         ("gemm_i8_stream", "651a4ace5b559916", 171468.6, 773.5),
     "qwen3_30b_a3b_prefill_skewed_w8a8":

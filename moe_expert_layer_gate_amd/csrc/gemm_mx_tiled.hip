@@ -76,7 +76,8 @@ MOE_DEV f32x4 mfma_mx(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
 
 }  // namespace
 
-template <bool GLU, int SCB>
+// GEMM1 + SwiGLU + MXFP8 quantisation of h.
+template <int SCB>
 // two blocks per CU: 2 waves per SIMD, 67 / 76 KB of LDS each
 __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
     const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   const int L = xcd * per + min(xcd, rem) + b / 8;
   const Tile tl = tiles[L / nslabs];
   const int slab = L % nslabs;
-  const int c0 = slab * (GLU ? MBNW / 2 : MBNW);
+  const int c0 = slab * (MBNW / 2);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -109,16 +110,12 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   const uint8_t* as_tile = gidx ? as : as + (size_t)tl.row0 * KB;
   const int32_t* grow = gidx ? gidx + gbase[0] + tl.row0 : nullptr;
 
-  // weight column of tile column t (0..255); columns past Nout read column 0
+  // weight column of tile column t (0..255): gate columns c0 + t for
+  // t < 128, the matching up columns at +Nout; columns past Nout read
+  // column 0
   auto wcol = [&](int t) -> int {
-    int oc, col;
-    if (GLU) {
-      oc = c0 + (t & (MBNW / 2 - 1));
-      col = t < MBNW / 2 ? oc : Nout + oc;
-    } else {
-      oc = c0 + t;
-      col = oc;
-    }
+    const int oc = c0 + (t & (MBNW / 2 - 1));
+    const int col = t < MBNW / 2 ? oc : Nout + oc;
     return oc < Nout ? col : 0;
   };
   // tile rows past the tile read its row 0 (their outputs are never stored)
@@ -190,8 +187,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   for (int h = 0; h < 2; ++h)
     a_rd[h] = lds0 + (wm * 64 + lr) * MBK + 16 * ((4 * h + q) ^ (lr >> 1));
   auto bcol = [&](int g) -> int {
-    if (GLU) return (g < 4 ? 0 : MBNW / 2) + wn * 64 + (g & 3) * 16 + lr;
-    return wn * 128 + g * 16 + lr;
+    return (g < 4 ? 0 : MBNW / 2) + wn * 64 + (g & 3) * 16 + lr;
   };
   const uint32_t b_rd =
       lds0 + MA_BYTES + bcol(0) * (MBK / 2) + 16 * (q ^ (lr >> 2));
@@ -292,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   __syncthreads();
 
   // epilogue, staged per wave in the (free) operand buffers
-  if (GLU) {
+  {
     // h: 64 rows x 64 columns of e4m3 codes per wave + 2 scales per row
     uint8_t* st = smem + wave * (64 * 64);
 #pragma unroll
@@ -327,31 +323,6 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
       if (row < tl.rows && colo < Nout)
         *(uint4*)((uint8_t*)out + (size_t)(tl.row0 + row) * Nout + colo) =
             *(const uint4*)&st[r * 64 + 16 * c];
-    }
-  } else {
-    // y: 64 rows x 128 bf16 columns per wave (16 KB), staged 32 rows at a time
-    uint16_t* st = (uint16_t*)smem + wave * (32 * 128);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int mb2 = 0; mb2 < 2; ++mb2) {
-        const int mb = 2 * h + mb2;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = mb2 * 16 + 4 * q + e;
-#pragma unroll
-          for (int g = 0; g < 8; ++g)
-            st[r * 128 + g * 16 + lr] = (uint16_t)f32_to_bf16_bits(acc[mb][g][e]);
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int p = it * 64 + lane, r = p >> 4, c = p & 15;
-        const int row = wm * 64 + 32 * h + r, colo = c0 + wn * 128 + 8 * c;
-        if (row < tl.rows && colo < Nout)
-          *(uint4*)((uint16_t*)out + (size_t)(tl.row0 + row) * Nout + colo) =
-              *(const uint4*)&st[r * 128 + 8 * c];
-      }
     }
   }
 }
@@ -647,8 +618,8 @@ static hipError_t launch_mx(bool glu, dim3 grid, const Tile* tiles,
                             int nslabs, const int32_t* gidx,
                             const int32_t* gbase, int gk, hipStream_t s) {
   if (glu)
-    hipLaunchKernelGGL((gemm_mx_tiled_kernel<true, SCB>), grid, dim3(256), 0,
-                       s, tiles, tile_count, a, a_scale, w, w_scale, out,
+    hipLaunchKernelGGL((gemm_mx_tiled_kernel<SCB>), grid, dim3(256), 0, s,
+                       tiles, tile_count, a, a_scale, w, w_scale, out,
                        out_scale, K, Nw, Nout, nslabs, gidx, gbase, gk);
   else
     hipLaunchKernelGGL((gemm_mx32_tiled_kernel<SCB>), grid, dim3(256), 0, s,
