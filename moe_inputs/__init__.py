@@ -35,7 +35,7 @@ from typing import Dict, Optional
 import torch
 
 __all__ = ["MoEShape", "WORKLOADS", "get_workload", "generate", "seed_for",
-           "scaled", "generate_norm", "NORM_EPS"]
+           "scaled", "generate_norm", "generate_router", "NORM_EPS"]
 
 
 @dataclass(frozen=True)
@@ -161,6 +161,7 @@ def _channel_scales(n, w_std, device, s) -> torch.Tensor:
 ROLE_LOGITS, ROLE_BIAS, ROLE_X, ROLE_RES, ROLE_W13, ROLE_W2 = range(6)
 ROLE_W13_SCALE, ROLE_W2_SCALE = 6, 7
 ROLE_NORM_X, ROLE_NORM_RES, ROLE_NORM_W = 8, 9, 10
+ROLE_ROUTER_Y, ROLE_ROUTER_W = 11, 12
 
 # RMSNorm epsilon of the Qwen3-MoE family's configs
 NORM_EPS = 1e-6
@@ -272,3 +273,18 @@ def generate_norm(T: int, H: int, seed: int = 0, device="cpu",
     w = (w + 1.0).to(torch.bfloat16)
     return {"x": x, "residual": r, "weight": w}
 
+
+def generate_router(T: int, H: int, E: int, seed: int = 0, device="cpu",
+                    name: str = "router") -> Dict[str, torch.Tensor]:
+    """Inputs of the fp32 router linear in front of the gate:
+      y  fp32 [T, H], N(0, 1) (the normalised hidden states, RMS about one);
+      w  fp32 [E, H], N(0, 1/sqrt(H)) (so the logits are about N(0, 1)).
+    """
+    dev = torch.device(device)
+    key = MoEShape(name, T=T, H=H, I=32, n_ffn=E, n_zero=0, top_k=1,
+                   local_begin=0, local_end=E, act="f32", wt="f32",
+                   act_q="none")
+    y = _normal((T, H), 1.0, torch.float32, dev, seed_for(key, seed, ROLE_ROUTER_Y))
+    w = _normal((E, H), H ** -0.5, torch.float32, dev,
+                seed_for(key, seed, ROLE_ROUTER_W))
+    return {"y": y, "w": w}

@@ -32,6 +32,9 @@ What each function follows:
                    hidden states before routing; [P1] "融合算子优化 / 融合RMSNorm MX
                    量化": round_mode "rint", dst float8_e4m3fn; OCP MX v1.0 for
                    block size 32, e8m0 scale = floor(log2(amax)) - emax_elem.
+  router_logits    [P1] "融合算子优化 / 融合RMSNorm Cast": the fp32 output of the
+                   norm feeds the gate (router) computation; the router is a
+                   linear map without bias to one logit per expert.
   int8_quant_rows, int8_dequant_rows
                    [P3] "量化策略": routed experts in W8A8 -- weights int8 with a
                    static scale per output channel, activations int8 with a
@@ -86,6 +89,7 @@ __all__ = [
     "int8_quant_rows", "int8_dequant_rows",
     "silu", "swiglu", "expert_ffn", "moe_layer", "moe_tokens", "moe_dense",
     "rms_norm", "add_rms_norm", "add_rms_norm_cast", "add_rms_norm_mx_quant",
+    "router_logits",
 ]
 
 # --------------------------------------------------------------------------
@@ -591,3 +595,16 @@ def add_rms_norm_mx_quant(x, residual, weight, eps: float):
     codes, scales = mx_quant(y, "e4m3")
     return codes, scales, r, y
 
+
+def router_logits(y, w_router) -> np.ndarray:
+    """Router logits of the normalised hidden states, exact in fp64:
+    logits[t, e] = sum_h y[t, h] * w_router[e, h].
+
+    y: fp32 values [T, H] (the fp32 output of the fused norm); w_router: fp32
+    values [E, H] (one row per expert, the layout of a linear layer's weight,
+    no bias)."""
+    y = np.asarray(y, dtype=np.float64)
+    w = np.asarray(w_router, dtype=np.float64)
+    if y.ndim != 2 or w.ndim != 2 or y.shape[1] != w.shape[1]:
+        raise ValueError("y [T, H] and w_router [E, H] expected")
+    return y @ w.T

@@ -538,3 +538,23 @@ def test_w8a8_routed_equals_pertoken():
     tok = r["sorted_copy"][r["row0"]:r["row0"] + r["R"]] // k
     assert np.array_equal(r["x_perm_codes"], qx[tok])
     assert np.array_equal(r["x_perm_scale"], sx[tok])
+
+
+# ----------------------------------------------------------------- router linear
+
+
+def test_router_logits_bruteforce_and_closed_forms():
+    rng = np.random.default_rng(21)
+    y = rng.standard_normal((5, 12)).astype(np.float32)
+    w = rng.standard_normal((7, 12)).astype(np.float32)
+    got = O.router_logits(y, w)
+    want = np.array([[sum(float(y[t, h]) * float(w[e, h]) for h in range(12))
+                      for e in range(7)] for t in range(5)])
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13)
+    # one-hot weight rows pick single columns of y exactly
+    eye = np.zeros((3, 12), np.float32)
+    eye[0, 4], eye[1, 0], eye[2, 11] = 1.0, 1.0, -2.0
+    sel = O.router_logits(y, eye)
+    assert np.array_equal(sel, np.stack([y[:, 4], y[:, 0], -2.0 * y[:, 11]], 1).astype(np.float64))
+    with pytest.raises(ValueError):
+        O.router_logits(y, w[:, :11])
