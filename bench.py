@@ -25,7 +25,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 --op norm_cast / norm_mx time the fused residual add + RMSNorm in front of the
 MoE block instead (dual fp32/bf16 output, or MXFP8), on the workload's T x H
 rows; its JSON line has the same fields with the norm kernel as the roofline
-kernel (HBM bound).
+kernel (HBM bound). --op router times the fp32 router linear (T x H hidden
+states times the E_tot x H router weight; fp32 MFMA bound).
 """
 from __future__ import annotations
 
@@ -139,7 +140,7 @@ def _parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the reference copy for counter scaling")
     ap.add_argument("--op", default="layer",
-                    choices=["layer", "norm_cast", "norm_mx"],
+                    choices=["layer", "norm_cast", "norm_mx", "router"],
                     help="what one step is: the MoE layer (default) or the "
                          "fused add + RMSNorm in front of it")
     ap.add_argument("--print-source-sha", action="store_true",
@@ -273,6 +274,8 @@ def main():
     from moe_inputs import generate, get_workload
 
     m.lib()
+    if args.op == "router":
+        return _bench_router(args, m)
     if args.op != "layer":
         return _bench_norm(args, m)
     shape = get_workload(args.workload)
@@ -466,6 +469,76 @@ def _bench_norm(args, m):
         rec["cpu_baseline"] = {"value": round(done / el, 1), "unit": "tokens/s",
                                "cores": torch.get_num_threads(), "kind": "oracle",
                                "sample": f"all {T} rows x{done // T}",
+                               "seconds": round(el, 1)}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+def _bench_router(args, m):
+    """One step = one fp32 router linear over the workload's T tokens: logits
+    [T, E_tot] = y [T, H] @ w_router [E_tot, H]^T (inputs resident in HBM)."""
+    import torch
+
+    from moe_inputs import generate_router, get_workload
+
+    shape = get_workload(args.workload)
+    T, H, E = shape.T, shape.H, shape.E_tot
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = generate_router(T, H, E, seed=args.seed, device=dev)
+    out = torch.empty((T, E), dtype=torch.float32, device=dev)
+
+    def step():
+        m.router_logits(inp["y"], inp["w"], out=out)
+
+    _settle(step)
+    for _ in range(args.warmup):
+        step()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    us = sum(a.elapsed_time(b) for a, b in ev) * 1e3 / args.steps
+    flops = 2.0 * T * H * E
+    nbytes = 4 * (T * H + E * H + T * E)
+    ach = flops / (us * 1e-6) / 1e12
+    peak = PEAK_TFLOPS["f32"]
+    rec = {
+        "metric": "fp32 router linear tokens/s",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"router_logits of {shape.name}", "T": T,
+                   "H": H, "E": E, "seed": args.seed},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                     "traffic": None, "kernel": "router_logits",
+                     "avg_us": round(us, 2), "algorithmic_flops": flops,
+                     "algorithmic_bytes": int(nbytes)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        y = inp["y"].double().cpu().numpy()
+        w = inp["w"].double().cpu().numpy()
+        done, t0 = 0, time.perf_counter()
+        while True:
+            O.router_logits(y, w)
+            done += T
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or done >= 20 * T:
+                break
+        rec["cpu_baseline"] = {"value": round(done / el, 1), "unit": "tokens/s",
+                               "cores": torch.get_num_threads(), "kind": "oracle",
+                               "sample": f"all {T} tokens x{done // T}",
                                "seconds": round(el, 1)}
     else:
         rec["cpu_baseline"] = None

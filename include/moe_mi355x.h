@@ -286,6 +286,19 @@ MOE_API moe_status moe_add_rms_norm_mx_quant(int32_t T, int32_t H,
                                              uint8_t* y_scales,
                                              void* residual_out, void* stream);
 
+/* Router linear ([P1] "融合算子优化 / 融合RMSNorm Cast": the fp32 output of
+ * the norm is the input of the gate computation): the logits of
+ * moe_gate_topk,
+ *   logits[t, e] = sum_h y[t, h] * w_router[e, h]   (fp32 accumulation)
+ * y: fp32 [T, H] (the y_f32 output of moe_add_rms_norm_cast); w_router: fp32
+ * [E, H] (one row per expert, the layout of a linear layer's weight, no
+ * bias); logits: fp32 [T, E]. T >= 0 (T == 0 launches nothing), H > 0,
+ * E > 0 (else MOE_ERR_INVALID_ARG); H % 16 == 0, E % 32 == 0, E <= 2048
+ * (else MOE_ERR_UNSUPPORTED). */
+MOE_API moe_status moe_router_logits(int32_t T, int32_t H, int32_t E,
+                                     const float* y, const float* w_router,
+                                     float* logits, void* stream);
+
 /* Static strings; never NULL. */
 MOE_API const char* moe_status_string(moe_status s);
 /* Library ABI version (major * 100 + minor). */

@@ -8,7 +8,7 @@ without it raises, there is no fallback.
 
 Calls mirror the C ABI in include/moe_mi355x.h:
   gate_topk, init_routing, ffn_up, ffn_down, grouped_ffn, finalize, layer,
-  add_rms_norm_cast, add_rms_norm_mx_quant.
+  add_rms_norm_cast, add_rms_norm_mx_quant, router_logits.
 """
 from __future__ import annotations
 
@@ -22,7 +22,7 @@ __all__ = [
     "LIB_PATH", "MoeProblem", "MoeError", "lib", "problem", "gate_topk",
     "init_routing", "ffn_up", "ffn_down", "grouped_ffn", "finalize", "layer",
     "layer_workspace_bytes", "layer_traced", "SYMBOLS", "STAGES",
-    "add_rms_norm_cast", "add_rms_norm_mx_quant",
+    "add_rms_norm_cast", "add_rms_norm_mx_quant", "router_logits",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -34,7 +34,7 @@ _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8_E4M3,
 SYMBOLS = ["moe_gate_topk", "moe_init_routing", "moe_grouped_ffn", "moe_ffn_up",
            "moe_ffn_down", "moe_finalize", "moe_layer", "moe_layer_traced",
            "moe_add_rms_norm_cast", "moe_add_rms_norm_mx_quant",
-           "moe_status_string", "moe_abi_version"]
+           "moe_router_logits", "moe_status_string", "moe_abi_version"]
 
 # stages of moe_layer_traced, in launch order
 STAGES = ["gate_topk", "route_count", "route_scan", "route_scatter",
@@ -89,6 +89,7 @@ def lib() -> ctypes.CDLL:
                                     _vp, _vp]
     sig["moe_add_rms_norm_mx_quant"] = [_i32, _i32, _vp, _vp, _vp, _f32, _vp,
                                         _vp, _vp, _vp]
+    sig["moe_router_logits"] = [_i32, _i32, _i32, _vp, _vp, _vp, _vp]
     for name, args in sig.items():
         f = getattr(L, name)
         f.argtypes = args
@@ -342,3 +343,17 @@ def add_rms_norm_mx_quant(x, residual, norm_weight, eps: float,
                                            _stream()))
     return codes, scales, res
 
+
+def router_logits(y, w_router, out=None):
+    """fp32 router logits [T, E] = y [T, H] @ w_router [E, H]^T."""
+    if y.dim() != 2 or y.dtype != torch.float32:
+        raise ValueError("y must be a [T, H] float32 tensor")
+    T, H = y.shape
+    if w_router.dim() != 2 or w_router.dtype != torch.float32 or w_router.shape[1] != H:
+        raise ValueError("w_router must be an [E, H] float32 tensor")
+    E = w_router.shape[0]
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=y.device)
+    _check(lib().moe_router_logits(T, H, E, _ptr(y), _ptr(w_router), _ptr(out),
+                                   _stream()))
+    return out

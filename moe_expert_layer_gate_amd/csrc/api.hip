@@ -451,6 +451,17 @@ moe_status moe_add_rms_norm_mx_quant(int32_t T, int32_t H, const void* x,
       y_scales, (uint16_t*)residual_out, (hipStream_t)stream));
 }
 
+moe_status moe_router_logits(int32_t T, int32_t H, int32_t E, const float* y,
+                             const float* w_router, float* logits,
+                             void* stream) {
+  if (T < 0 || H <= 0 || E <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 16 || E % 32 || E > kMaxE) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y || !w_router || !logits) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_router_logits(y, w_router, logits, T, H, E,
+                                              (hipStream_t)stream));
+}
+
 moe_status moe_layer_traced(const moe_problem* p, const float* logits,
                             const void* x, const void* residual,
                             const void* w13, const void* w13_scale,

@@ -144,6 +144,11 @@ hipError_t launch_add_rms_norm(int mx, const uint16_t* x, const uint16_t* r,
                                uint8_t* scales, uint16_t* res_out,
                                hipStream_t s);
 
+// fp32 router logits [T, E] = y [T, H] @ w [E, H]^T; H % 16 == 0,
+// E % 32 == 0.
+hipError_t launch_router_logits(const float* y, const float* w, float* out,
+                                int T, int H, int E, hipStream_t s);
+
 hipError_t launch_finalize(const int32_t* ids, const float* w,
                            const int32_t* copy_pos, const int32_t* offsets,
                            int fb, int n_ffn, int lb, int le, const void* y,

@@ -153,3 +153,18 @@ def test_fused_norm_host_checks(L):
     # no rows: nothing to do, nothing launched
     assert cast(0, 64, None, None, None, 1e-6, None, None, None, None) == 0
     assert mxq(0, 64, None, None, None, 1e-6, None, None, None, None) == 0
+
+
+def test_router_host_checks(L):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails a check
+    r = L.moe_router_logits
+    assert r(-1, 64, 32, fake, fake, fake, None) == 1
+    assert r(4, 0, 32, fake, fake, fake, None) == 1
+    assert r(4, 64, 0, fake, fake, fake, None) == 1
+    assert r(4, 40, 32, fake, fake, fake, None) == 2     # H % 16
+    assert r(4, 64, 48, fake, fake, fake, None) == 2     # E % 32
+    assert r(4, 64, 4096, fake, fake, fake, None) == 2   # E > 2048
+    assert r(4, 64, 32, None, fake, fake, None) == 1
+    assert r(4, 64, 32, fake, None, fake, None) == 1
+    assert r(4, 64, 32, fake, fake, None, None) == 1
+    assert r(0, 64, 32, None, None, None, None) == 0
