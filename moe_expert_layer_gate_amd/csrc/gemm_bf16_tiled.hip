@@ -7,13 +7,22 @@
 // (all experts in one grouped operator); prefill operators are compute-bound
 // (Prefill优化 / 并行策略选择).
 //
-// Block = 256 threads (2 x 2 waves) computing a 128-row x 256-weight-column
-// tile of one expert, K in steps of 32 through a 3-stage LDS ring filled by
-// direct global->LDS loads (global_load_lds_dwordx4: lane l of a wave lands
-// at the wave's LDS base + 16*l, no VGPRs involved), two steps in flight, two
-// blocks per CU. (The geometry is a template on the wave's row count WR;
-// 256-row tiles with one block per CU and a 4-stage ring were measured slower
-// on MI355X and are not launched.)
+// Two tile geometries, both 256 weight columns wide with K in steps of 32
+// through an LDS ring filled by direct global->LDS loads
+// (global_load_lds_dwordx4: lane l of a wave lands at the wave's LDS base +
+// 16*l, no VGPRs involved):
+//   * 128 rows: 4 waves (2 x 2), each 64 rows x 128 columns, 3-stage ring,
+//     two blocks per CU -- for batches of 64 to 127 rows per expert;
+//   * 256 rows: 8 waves (2 x 4), each 128 rows x 64 columns, 3-stage ring,
+//     one block per CU -- for larger batches. Per K step a CU then issues
+//     160 LDS instructions (copies in, fragment reads out) for 32 MFMAs per
+//     SIMD, against 208 for the same work in 128-row tiles: on gfx950 an LDS
+//     instruction occupies the CU's LDS for about 6.5 clocks whether it moves
+//     16 bytes per lane (ds_read_b128) or 8 (the transposing reads of B), and
+//     a 32x32x16 MFMA takes about 36, so the 128-row tile is bound by LDS
+//     instruction issue and the 256-row tile by the MFMAs. Its L2 traffic per
+//     flop is a quarter lower as well.
+// In both, each SIMD holds two waves, and the tile's layout in LDS is:
 //   * A (activation rows, K contiguous): LDS [row][4 x 16 B], the 16-byte
 //     piece index XOR-swizzled with (row/4)%4 so the MFMA reads of 8
 //     consecutive rows hit 8 different bank groups;
@@ -23,10 +32,10 @@
 //     columns n0 + 4*(s%4) .. +3, and lane j receives column n0 + j at rows
 //     kb .. kb+3 (transpose semantics measured with an in-bounds probe); two
 //     such reads form the 8 consecutive K of an MFMA B fragment;
-//   * v_mfma_f32_32x32x16_bf16: each wave owns WR rows x 128 weight columns
-//     (WR/32 x 4 blocks of 32 x 32);
+//   * v_mfma_f32_32x32x16_bf16: each wave owns WR rows x WC weight columns
+//     (WR/32 x WC/32 blocks of 32 x 32);
 //   * GEMM1 tiles hold 128 gate columns and the 128 matching up columns; a
-//     wave takes 64 of each, so SwiGLU is lane-local in the epilogue;
+//     wave takes WC/2 of each, so SwiGLU is lane-local in the epilogue;
 //   * the epilogue stages each wave's 32-row slice through LDS and writes
 //     16-byte rows to HBM;
 //   * blocks are remapped so each XCD works on a contiguous range of
@@ -62,18 +71,30 @@ constexpr int BNW = 256, BK = 32;
 constexpr int B_BYTES = BK * BNW * 2;           // 16 KB
 constexpr int B_ROW = BNW * 2;                  // 512 B
 
-// Tile geometry for wave-row count WR (64 or 128).
-template <int WR>
+// Tile geometry: WAVES_M x WAVES_N waves of WR rows x WC = 256 / WAVES_N
+// weight columns each.
+template <int WR_, int WAVES_M_, int WAVES_N_, int NSTAGE_, int BPC_>
 struct TiledCfg {
-  static constexpr int BM = 2 * WR;                      // tile rows
+  static constexpr int WR = WR_;                         // rows per wave
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NWAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * NWAVES;
+  static constexpr int WC = BNW / WAVES_N;               // columns per wave
+  static constexpr int BM = WAVES_M * WR;                // tile rows
   static constexpr int NMB = WR / 32;                    // 32-row blocks per wave
-  static constexpr int NSTAGE = WR == 128 ? 4 : 3;       // LDS ring depth
+  static constexpr int NNB = WC / 32;                    // 32-column blocks per wave
+  static constexpr int NSTAGE = NSTAGE_;                 // LDS ring depth
   static constexpr int A_BYTES = BM * BK * 2;            // 8 / 16 KB
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;  // 24 / 32 KB
-  static constexpr int NA = BM / 64;                     // A copies per wave
-  static constexpr int NI = NA + 4;                      // copies per wave and step
-  static constexpr int BLOCKS_PER_CU = WR == 128 ? 1 : 2;
+  static constexpr int NA = BM / 16 / NWAVES;            // A copies per wave and step
+  static constexpr int NB = 16 / NWAVES;                 // B copies per wave and step
+  static constexpr int NI = NA + NB;                     // copies per wave and step
+  static constexpr int BLOCKS_PER_CU = BPC_;
+  static_assert(NA * 16 * NWAVES == BM && NB * NWAVES == 16, "copy split");
+  static_assert(NNB % 2 == 0, "GLU splits a wave's columns in halves");
 };
+using Tiles128 = TiledCfg<64, 2, 2, 3, 2>;
+using Tiles256 = TiledCfg<128, 2, 4, 3, 1>;
 
 MOE_DEV f32x16 mfma32(u32x4_t a, u32x4_t b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -108,7 +129,7 @@ MOE_DEV int swz_b(int k) { return 4 * (k & 3); }
 // indexed like the rows), weights int8 [E_loc, N, K] (K contiguous) with one
 // fp32 scale per output channel (w_scale [E_loc, N]); int32 accumulation,
 // dequantised in the epilogue; GEMM1 stores h in fp32, GEMM2 y in bf16.
-template <bool GLU, int WR, bool I8>
+template <bool GLU, class C, bool I8>
 MOE_DEV void tiled_item(
     uint8_t* smem, int L, const Tile* __restrict__ tiles,
     const void* __restrict__ a, const void* __restrict__ w,
@@ -116,14 +137,14 @@ MOE_DEV void tiled_item(
     const int32_t* __restrict__ gidx, const int32_t* __restrict__ gbase,
     int gk, const float* __restrict__ a_scale,
     const float* __restrict__ w_scale) {
-  using C = TiledCfg<WR>;
   using Acc = typename std::conditional<I8, i32x16, f32x16>::type;
   constexpr int EB = I8 ? 1 : 2;      // bytes per element
   constexpr int KS = 64 / EB;         // K per step (64 bytes of every row)
-  constexpr int NBR = I8 ? 4 : 8;     // LDS reads of B per half step
-  constexpr int BM = C::BM, NMB = C::NMB, NSTAGE = C::NSTAGE;
+  constexpr int WR = C::WR, WC = C::WC, NW = C::NWAVES;
+  constexpr int BM = C::BM, NMB = C::NMB, NNB = C::NNB, NSTAGE = C::NSTAGE;
+  constexpr int NBR = I8 ? NNB : 2 * NNB;  // LDS reads of B per half step
   constexpr int A_BYTES = C::A_BYTES, STAGE_BYTES = C::STAGE_BYTES;
-  constexpr int NA = C::NA, NI = C::NI;
+  constexpr int NA = C::NA, NB = C::NB, NI = C::NI;
   (void)BM;
   const Tile tl = tiles[L / nslabs];
   const int slab = L % nslabs;
@@ -131,11 +152,11 @@ MOE_DEV void tiled_item(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const char* we = (const char*)w + (size_t)tl.expert * K * Nw * EB;
 
   // ---- global -> LDS assignment (per wave instruction: 1 KB contiguous)
-  // A, instruction j (0..NA-1): tile rows 16*(wave + 4j) + lane/4, physical
+  // A, instruction j (0..NA-1): tile rows 16*(wave + NW*j) + lane/4, physical
   // piece lane%4 holds logical piece (lane%4) ^ swz_a(row)
   // With a gather index the rows come straight from x (row of sorted copy
   // i = token sorted_copy[i] / k; the host keeps x under 4 GB so 32-bit
@@ -145,7 +166,7 @@ MOE_DEV void tiled_item(
   uint32_t a_off[NA];
 #pragma unroll
   for (int j = 0; j < NA; ++j) {
-    const int r = 16 * (wave + 4 * j) + (lane >> 2);
+    const int r = 16 * (wave + NW * j) + (lane >> 2);
     int src = r < tl.rows ? r : 0;
     if (gidx) src = gidx[gbase[0] + tl.row0 + src] / gk;
     a_off[j] = (uint32_t)src * K * EB + 16 * ((lane & 3) ^ swz_a(r));
@@ -170,18 +191,18 @@ MOE_DEV void tiled_item(
     }
     return oc < Nout ? col : 0;
   };
-  // B (bf16 [K, N]), instruction j (0..3): k-row 2*(wave + 4j) + lane/32 of
-  // the step, physical piece lane%32 holds logical piece (lane%32) ^
-  // swz_b(k); the swizzle only depends on k%4 = 2*(wave&1) + lane/32, the
-  // same for all j.
-  // B (int8 [N, K]), instruction j (0..3): like A, tile columns
-  // 16*(wave + 4j) + lane/4 of 64 bytes each, LDS [column][4 x 16 B], piece
+  // B (bf16 [K, N]), instruction j (0..NB-1): k-row 2*(wave + NW*j) +
+  // lane/32 of the step, physical piece lane%32 holds logical piece
+  // (lane%32) ^ swz_b(k); the swizzle only depends on k%4 = 2*(wave&1) +
+  // lane/32 (NW is even), the same for all j.
+  // B (int8 [N, K]), instruction j (0..NB-1): like A, tile columns
+  // 16*(wave + NW*j) + lane/4 of 64 bytes each, LDS [column][4 x 16 B], piece
   // lane%4 <- logical piece (lane%4) ^ swz_a(column).
-  uint32_t b_off[I8 ? 4 : 1];
+  uint32_t b_off[I8 ? NB : 1];
   if constexpr (I8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 16 * (wave + 4 * j) + (lane >> 2);
+    for (int j = 0; j < NB; ++j) {
+      const int t = 16 * (wave + NW * j) + (lane >> 2);
       b_off[j] = (uint32_t)wcol(t) * K + 16 * ((lane & 3) ^ swz_a(t));
     }
   } else {
@@ -194,7 +215,7 @@ MOE_DEV void tiled_item(
   const uint32_t b_dst = __builtin_amdgcn_readfirstlane(lds_addr(
       smem + A_BYTES + (I8 ? 16 * wave * 64 : (2 * wave) * B_ROW)));
   const size_t b_step = (size_t)BK * Nw * 2;     // bytes per K step of B
-  const uint32_t b_row8 = 8u * Nw * 2;          // 8 k-rows of B
+  const uint32_t b_rowj = 2u * NW * Nw * 2;     // 2*NW k-rows of B
 
   // loads of K step s_ into stage st_ (NI instructions per wave)
 #define MOE_TILED_ISSUE(s_, st_)                                              \
@@ -202,49 +223,58 @@ MOE_DEV void tiled_item(
     const char* ab_ = a_tile + (size_t)(s_) * 64;                             \
     const uint32_t o_ = (st_) * STAGE_BYTES;                                  \
     _Pragma("unroll") for (int j = 0; j < NA; ++j)                            \
-      g2lds(ab_, a_off[j], a_dst + o_ + 64 * j * (BK * 2));                   \
+      g2lds(ab_, a_off[j], a_dst + o_ + 16 * NW * j * (BK * 2));              \
     if constexpr (I8) {                                                       \
       const char* bb_ = we + (size_t)(s_) * 64;                               \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                           \
-        g2lds(bb_, b_off[j], b_dst + o_ + 64 * j * 64);                       \
+      _Pragma("unroll") for (int j = 0; j < NB; ++j)                          \
+        g2lds(bb_, b_off[j], b_dst + o_ + 16 * NW * j * 64);                  \
     } else {                                                                  \
       const char* bb_ = we + (size_t)(s_) * b_step;                           \
-      g2lds(bb_, b_off[0], b_dst + o_);                                       \
-      g2lds(bb_, b_off[0] + b_row8, b_dst + o_ + 8 * B_ROW);                  \
-      g2lds(bb_, b_off[0] + 2 * b_row8, b_dst + o_ + 16 * B_ROW);             \
-      g2lds(bb_, b_off[0] + 3 * b_row8, b_dst + o_ + 24 * B_ROW);             \
+      _Pragma("unroll") for (int j = 0; j < NB; ++j)                          \
+        g2lds(bb_, b_off[0] + j * b_rowj, b_dst + o_ + 2 * NW * j * B_ROW);   \
     }                                                                         \
   } while (0)
 
-  Acc acc[NMB][4];
+  Acc acc[NMB][NNB];
 #pragma unroll
   for (int i = 0; i < NMB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NNB; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
   // LDS read offsets, loop invariant (stage offsets are immediates below)
   const int lr = lane & 31, lh = lane >> 5;
-  uint32_t a_rd[2][NMB];  // [kk][mb]
+  // A: row m = wm*WR + 32*mb + lr; its swizzle (m/4)%4 = (lr/4)%4 is the
+  // same for every mb, so block mb sits a constant 32 rows further on
+  uint32_t a_rd[2];  // [kk]
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) {
-      const int m = wm * WR + mb * 32 + lr;
-      a_rd[kk][mb] = lds_addr(smem) + m * (BK * 2) + 16 * ((kk * 2 + lh) ^ swz_a(m));
-    }
+  for (int kk = 0; kk < 2; ++kk) {
+    const int m = wm * WR + lr;
+    a_rd[kk] = lds_addr(smem) + m * (BK * 2) + 16 * ((kk * 2 + lh) ^ swz_a(m));
+  }
   // bf16 transpose reads: group g = lane/16, source lane s = lane%16
   // supplies row kk*16 + 8*(g/2) + s/4 and columns cb + 16*(g%2) + 4*(s%4)
   // .. +3. int8: lane l reads tile column cb + l%32, logical piece
   // 2*kk + l/32 (the same K bytes as its A read).
-  uint32_t b_rd[2][4];  // [kk][nbk]
+  // Column block nbk of the wave: GLU -- gate blocks first (nbk < NNB/2),
+  // then the matching up blocks, WC/2 columns of each half of the tile.
+  // (a part that depends on the wave, and a constant per nbk)
+  auto cdelta = [](int nbk) -> int {
+    return GLU ? (nbk < NNB / 2 ? 0 : BNW / 2) + (nbk % (NNB / 2)) * 32
+               : nbk * 32;
+  };
+  const int cwave = wn * (GLU ? WC / 2 : WC);
+  auto colblk = [&](int nbk) -> int { return cwave + cdelta(nbk); };
+  // int8: the swizzle (col/4)%4 = (lr/4)%4 is the same for every nbk, so
+  // only the nbk = 0 offsets are kept (b_rd[kk][0]) and the others are
+  // constant distances from them
+  uint32_t b_rd[2][I8 ? 1 : NNB];  // [kk][nbk]
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int nbk = 0; nbk < 4; ++nbk) {
-      const int cb = GLU ? (nbk < 2 ? 0 : BNW / 2) + wn * 64 + (nbk & 1) * 32
-                         : wn * 128 + nbk * 32;
+    for (int nbk = 0; nbk < (I8 ? 1 : NNB); ++nbk) {
+      const int cb = colblk(nbk);
       if constexpr (I8) {
         const int col = cb + lr;
         b_rd[kk][nbk] = lds_addr(smem) + A_BYTES + col * 64 +
@@ -258,14 +288,16 @@ MOE_DEV void tiled_item(
     }
 
   // fragments of one half step (16 K): A for the wave's 32-row blocks,
-  // B for its four 32-column blocks; two register sets so that the LDS reads
+  // B for its 32-column blocks; two register sets so that the LDS reads
   // of the next half step overlap the MFMAs of the current one
 #define MOE_TILED_READ(fa_, fb_, st_, kk_)                                    \
   do {                                                                        \
     _Pragma("unroll") for (int mb = 0; mb < NMB; ++mb)                        \
-      fa_[mb] = lds_read_b128(a_rd[kk_][mb] + (st_) * STAGE_BYTES);           \
-    _Pragma("unroll") for (int nbk = 0; nbk < 4; ++nbk) {                     \
-      const uint32_t p_ = b_rd[kk_][nbk] + (st_) * STAGE_BYTES;               \
+      fa_[mb] = lds_read_b128(a_rd[kk_] + mb * 32 * (BK * 2) + (st_) * STAGE_BYTES); \
+    _Pragma("unroll") for (int nbk = 0; nbk < NNB; ++nbk) {                   \
+      const uint32_t p_ = (I8 ? b_rd[kk_][0] + cdelta(nbk) * 64               \
+                              : b_rd[kk_][I8 ? 0 : nbk]) +                    \
+                          (st_) * STAGE_BYTES;                                \
       if constexpr (I8) {                                                     \
         fb_[nbk] = lds_read_b128(p_);                                         \
       } else {                                                                \
@@ -281,7 +313,7 @@ MOE_DEV void tiled_item(
 #define MOE_TILED_MMA(fa_, fb_, NMB_)                                         \
   do {                                                                        \
     _Pragma("unroll") for (int mb = 0; mb < (NMB_); ++mb)                     \
-      _Pragma("unroll") for (int nbk = 0; nbk < 4; ++nbk)                     \
+      _Pragma("unroll") for (int nbk = 0; nbk < NNB; ++nbk)                   \
         acc[mb][nbk] = mfma32(fa_[mb], fb_[nbk], acc[mb][nbk]);               \
   } while (0)
 
@@ -313,7 +345,7 @@ MOE_DEV void tiled_item(
   do {                                                                        \
     if ((NMB_) > 0) {                                                         \
       __builtin_amdgcn_sched_group_barrier(0x100, (NMB_) + NBR, 0);           \
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * (NMB_), 0);             \
+      __builtin_amdgcn_sched_group_barrier(0x008, NNB * (NMB_), 0);           \
     }                                                                         \
   } while (0)
   // wait until step t+1 has landed: the copies of steps t+2 .. up to
@@ -354,7 +386,7 @@ MOE_DEV void tiled_item(
   const int nsteps = K / KS;
   // rows of this wave's WR-row part of the tile (wave-uniform)
   const int mrows = __builtin_amdgcn_readfirstlane(tl.rows - wm * WR);
-  u32x4_t f0a[NMB], f0b[4], f1a[NMB], f1b[4];
+  u32x4_t f0a[NMB], f0b[NNB], f1a[NMB], f1b[NNB];
   // prologue: steps 0 .. NSTAGE-2 in flight, wait for step 0, then the last
   // stage gets step NSTAGE-1
   MOE_TILED_ISSUE(0, 0);
@@ -381,18 +413,15 @@ MOE_DEV void tiled_item(
   __syncthreads();
 
   // epilogue through LDS: each wave stages 32 rows at a time
-  const int ncols = GLU ? 64 : 128;  // output columns of this wave
-  const int oc0 = c0 + wn * ncols;   // first output column of this wave
+  constexpr int OCOLS = GLU ? WC / 2 : WC;  // output columns of this wave
+  const int oc0 = c0 + wn * OCOLS;          // first output column of this wave
   // int8: value = acc * scale of its row * scale of its weight column
-  float cs[4];
+  float cs[NNB];
 #pragma unroll
-  for (int nbk = 0; nbk < 4; ++nbk) {
+  for (int nbk = 0; nbk < NNB; ++nbk) {
     cs[nbk] = 1.f;
-    if constexpr (I8) {
-      const int t = (GLU ? (nbk < 2 ? 0 : BNW / 2) + wn * 64 + (nbk & 1) * 32
-                         : wn * 128 + nbk * 32) + lr;
-      cs[nbk] = w_scale[(size_t)tl.expert * Nw + wcol(t)];
-    }
+    if constexpr (I8)
+      cs[nbk] = w_scale[(size_t)tl.expert * Nw + wcol(colblk(nbk) + lr)];
   }
   auto val = [&](int mb, int nbk, int e, int r) -> float {
     if constexpr (I8)
@@ -402,22 +431,28 @@ MOE_DEV void tiled_item(
   };
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
+    // one 32-row block at a time: the scale reads and staging of block mb
+    // stay after those of block mb-1 (fewer live registers)
+    __builtin_amdgcn_sched_barrier(0);
     // acc element e of a 32x32 block: row 8*(e/4) + 4*(lane/32) + e%4,
     // column lane%32
     if (GLU && I8) {
-      // h in fp32: 32 rows x 64 columns per wave (8 KB)
+      // h in fp32: 32 rows x OCOLS (<= 64) columns per wave, rows 64 apart
       float* st = (float*)smem + wave * (32 * 64);
+      float* st_lane = st + 4 * lh * 64 + lr;  // constant offsets below
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = 8 * (e >> 2) + 4 * lh + (e & 3);
 #pragma unroll
-        for (int gb = 0; gb < 2; ++gb)
-          st[r * 64 + gb * 32 + lr] = silu(val(mb, gb, e, r)) * val(mb, gb + 2, e, r);
+        for (int gb = 0; gb < NNB / 2; ++gb)
+          st_lane[(8 * (e >> 2) + (e & 3)) * 64 + gb * 32] =
+              silu(val(mb, gb, e, r)) * val(mb, gb + NNB / 2, e, r);
       }
+      constexpr int CH = OCOLS / 4;  // 16-byte pieces per row
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
+      for (int it = 0; it < 32 * CH / 64; ++it) {
         const int q = it * 64 + lane;
-        const int r = q >> 4, c = q & 15;
+        const int r = q / CH, c = q % CH;
         const int row = wm * WR + mb * 32 + r;
         const int col = oc0 + 4 * c;
         if (row < tl.rows && col < Nout)
@@ -426,29 +461,31 @@ MOE_DEV void tiled_item(
       }
       continue;
     }
+    // bf16: 32 rows x OCOLS (<= 128) columns per wave, rows 128 apart
     uint16_t* stage = (uint16_t*)smem + wave * (32 * 128);
+    uint16_t* stage_lane = stage + 4 * lh * 128 + lr;  // constant offsets below
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int r = 8 * (e >> 2) + 4 * lh + (e & 3);
+      const int ro = (8 * (e >> 2) + (e & 3)) * 128;
       if (GLU) {
 #pragma unroll
-        for (int gb = 0; gb < 2; ++gb) {
-          const float hv = silu(val(mb, gb, e, r)) * val(mb, gb + 2, e, r);
-          stage[r * 128 + gb * 32 + lr] = (uint16_t)f32_to_bf16_bits(hv);
+        for (int gb = 0; gb < NNB / 2; ++gb) {
+          const float hv = silu(val(mb, gb, e, r)) * val(mb, gb + NNB / 2, e, r);
+          stage_lane[ro + gb * 32] = (uint16_t)f32_to_bf16_bits(hv);
         }
       } else {
 #pragma unroll
-        for (int nbk = 0; nbk < 4; ++nbk)
-          stage[r * 128 + nbk * 32 + lr] =
-              (uint16_t)f32_to_bf16_bits(val(mb, nbk, e, r));
+        for (int nbk = 0; nbk < NNB; ++nbk)
+          stage_lane[ro + nbk * 32] = (uint16_t)f32_to_bf16_bits(val(mb, nbk, e, r));
       }
     }
     // each lane writes 16-byte pieces of the staged rows
-    const int chunks = ncols / 8;  // 16-byte pieces per row
+    constexpr int CH = OCOLS / 8;  // 16-byte pieces per row
 #pragma unroll
-    for (int it = 0; it < 32 * (GLU ? 8 : 16) / 64; ++it) {
+    for (int it = 0; it < 32 * CH / 64; ++it) {
       const int q = it * 64 + lane;
-      const int r = q / chunks, c = q % chunks;
+      const int r = q / CH, c = q % CH;
       const int row = wm * WR + mb * 32 + r;
       const int col = oc0 + 8 * c;
       if (row < tl.rows && col < Nout)
@@ -464,15 +501,16 @@ MOE_DEV void tiled_item(
 // (nj blocks per XCD). The items running at once on an XCD are therefore
 // consecutive: the slabs of a few tiles and the tiles of one expert, whose A
 // rows and weight slabs that XCD's L2 serves to all of them.
-template <bool GLU, int WR, bool I8>
-__global__ __launch_bounds__(256, TiledCfg<WR>::BLOCKS_PER_CU) void gemm_bf16_tiled_kernel(
+template <bool GLU, class C, bool I8>
+__global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_bf16_tiled_kernel(
     const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     const void* __restrict__ a, const void* __restrict__ w,
     void* __restrict__ out, int K, int Nw, int Nout, int nslabs,
     const int32_t* __restrict__ gidx, const int32_t* __restrict__ gbase,
     int gk, const float* __restrict__ a_scale,
     const float* __restrict__ w_scale) {
-  using C = TiledCfg<WR>;
+  static_assert(C::NSTAGE * C::STAGE_BYTES >= C::NWAVES * 8192,
+                "epilogue staging fits the ring");
   __shared__ __align__(1024) uint8_t
       smem[C::NSTAGE * C::STAGE_BYTES + (I8 ? 4 * C::BM : 0)];
   const int nb = tile_count[0] * nslabs;
@@ -481,13 +519,13 @@ __global__ __launch_bounds__(256, TiledCfg<WR>::BLOCKS_PER_CU) void gemm_bf16_ti
   const int lo = xcd * per + min(xcd, rem);
   const int hi = lo + per + (xcd < rem ? 1 : 0);
   for (int L = lo + j; L < hi; L += nj) {
-    tiled_item<GLU, WR, I8>(smem, L, tiles, a, w, out, K, Nw, Nout, nslabs,
+    tiled_item<GLU, C, I8>(smem, L, tiles, a, w, out, K, Nw, Nout, nslabs,
                             gidx, gbase, gk, a_scale, w_scale);
     __syncthreads();  // LDS staging of this item read before the next fills
   }
 }
 
-template <int WR, bool I8>
+template <class C, bool I8>
 static hipError_t launch_tiled(bool glu, const Tile* tiles,
                                const int32_t* tile_count, int max_tiles,
                                const void* a, const void* w, void* out, int K,
@@ -498,45 +536,53 @@ static hipError_t launch_tiled(bool glu, const Tile* tiles,
   if (max_tiles == 0) return hipSuccess;
   const int slab = glu ? BNW / 2 : BNW;
   const int nslabs = (Nout + slab - 1) / slab;
-  // one resident block per slot (two per CU), a multiple of 8 (the XCD
-  // count), never more blocks than items
+  // one resident block per slot, a multiple of 8 (the XCD count), never
+  // more blocks than items
   const long long items = (long long)max_tiles * nslabs;
-  const long long slots = (long long)device_cus() * 2;
+  const long long slots = (long long)device_cus() * C::BLOCKS_PER_CU;
   long long nblk = items < slots ? items : slots;
   nblk = ((nblk + 7) / 8) * 8;
-  const dim3 grid((unsigned)nblk);
+  const dim3 grid((unsigned)nblk), block(C::THREADS);
   if (glu)
-    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<true, WR, I8>), grid, dim3(256),
-                       0, s, tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
+    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<true, C, I8>), grid, block, 0,
+                       s, tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
                        gidx, gbase, gk, a_scale, w_scale);
   else
-    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<false, WR, I8>), grid,
-                       dim3(256), 0, s, tiles, tile_count, a, w, out, K, Nw,
-                       Nout, nslabs, gidx, gbase, gk, a_scale, w_scale);
+    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<false, C, I8>), grid, block, 0,
+                       s, tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
+                       gidx, gbase, gk, a_scale, w_scale);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
+hipError_t launch_gemm_bf16_tiled(bool glu, int mt, const Tile* tiles,
                                   const int32_t* tile_count, int max_tiles,
                                   const uint16_t* a, const uint16_t* w,
                                   uint16_t* out, int K, int Nw, int Nout,
                                   const int32_t* gidx, const int32_t* gbase,
                                   int gk, hipStream_t s) {
-  return launch_tiled<64, false>(glu, tiles, tile_count, max_tiles, a, w, out,
-                                 K, Nw, Nout, gidx, gbase, gk, nullptr,
-                                 nullptr, s);
+  if (mt == 256)
+    return launch_tiled<Tiles256, false>(glu, tiles, tile_count, max_tiles, a,
+                                         w, out, K, Nw, Nout, gidx, gbase, gk,
+                                         nullptr, nullptr, s);
+  return launch_tiled<Tiles128, false>(glu, tiles, tile_count, max_tiles, a, w,
+                                       out, K, Nw, Nout, gidx, gbase, gk,
+                                       nullptr, nullptr, s);
 }
 
-hipError_t launch_gemm_i8_tiled(bool glu, const Tile* tiles,
+hipError_t launch_gemm_i8_tiled(bool glu, int mt, const Tile* tiles,
                                 const int32_t* tile_count, int max_tiles,
                                 const int8_t* a, const float* a_scale,
                                 const int8_t* w, const float* w_scale,
                                 void* out, int K, int Nw, int Nout,
                                 const int32_t* gidx, const int32_t* gbase,
                                 int gk, hipStream_t s) {
-  return launch_tiled<64, true>(glu, tiles, tile_count, max_tiles, a, w, out,
-                                K, Nw, Nout, gidx, gbase, gk, a_scale, w_scale,
-                                s);
+  if (mt == 256)
+    return launch_tiled<Tiles256, true>(glu, tiles, tile_count, max_tiles, a,
+                                        w, out, K, Nw, Nout, gidx, gbase, gk,
+                                        a_scale, w_scale, s);
+  return launch_tiled<Tiles128, true>(glu, tiles, tile_count, max_tiles, a, w,
+                                      out, K, Nw, Nout, gidx, gbase, gk,
+                                      a_scale, w_scale, s);
 }
 
 }  // namespace moe

@@ -71,9 +71,9 @@ hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
                                    uint16_t* out, int K, int Nw, int Nout,
                                    const int32_t* gidx, const int32_t* gbase,
                                    int gk, hipStream_t s);
-// Same operands, 128-row LDS-tiled MFMA tiles (tile list built with mt=128).
-// With gidx, `a` must span less than 4 GB.
-hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
+// Same operands, LDS-tiled MFMA tiles of mt = 128 or 256 rows (the tile
+// list's height). With gidx, `a` must span less than 4 GB.
+hipError_t launch_gemm_bf16_tiled(bool glu, int mt, const Tile* tiles,
                                   const int32_t* tile_count, int max_tiles,
                                   const uint16_t* a, const uint16_t* w,
                                   uint16_t* out, int K, int Nw, int Nout,
@@ -83,8 +83,8 @@ hipError_t launch_gemm_bf16_tiled(bool glu, const Tile* tiles,
 // indexed like the rows of a, through gidx when it is non-NULL), int8
 // weights [E_loc, N, K] with one fp32 scale per output channel
 // (w_scale [E_loc, N]); int32 accumulation. glu: fp32 h, else bf16 y.
-// 128-row LDS-tiled tiles (mt = 128), K % 64 == 0.
-hipError_t launch_gemm_i8_tiled(bool glu, const Tile* tiles,
+// LDS-tiled tiles of mt = 128 or 256 rows, K % 64 == 0.
+hipError_t launch_gemm_i8_tiled(bool glu, int mt, const Tile* tiles,
                                 const int32_t* tile_count, int max_tiles,
                                 const int8_t* a, const float* a_scale,
                                 const int8_t* w, const float* w_scale,

@@ -68,6 +68,18 @@ SMALL = {
     "prefill_w8a8_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_w8a8"),
                                  T=600, H=384, I=384, n_ffn=8, local_end=8,
                                  top_k=4),
+    # W8A8 with about 100 rows per expert
+    "prefill_w8a8_mid_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_w8a8"),
+                                     T=300, H=256, I=256, n_ffn=12,
+                                     local_end=12, top_k=4),
+    # about 600 rows per expert: 256-row tiles, ragged last tiles, ragged
+    # GEMM1 (I = 160) and GEMM2 (H = 384) slabs
+    "prefill_long_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_bf16"),
+                                 T=1200, H=384, I=160, n_ffn=8, local_end=8,
+                                 top_k=4),
+    "prefill_w8a8_long_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_w8a8"),
+                                      T=1200, H=384, I=384, n_ffn=8,
+                                      local_end=8, top_k=4),
     # W8A8 on an expert range with 32-row streaming tiles
     "range_w8a8_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"), T=96,
                                H=256, I=256, n_ffn=16, local_begin=4,
@@ -262,7 +274,9 @@ def test_layer_split_calls_equal_fused():
     for name in ("prefill_skewed_small", "prefill_wide_small", "ep_w4a8_small",
                  "ep_w4a8_prefill_small", "ep_w4a8_wide_small",
                  "tiny_fp32", "decode_bf16_small", "decode_w8a8_small",
-                 "prefill_w8a8_small", "range_w8a8_small"):
+                 "prefill_w8a8_small", "prefill_w8a8_mid_small",
+                 "prefill_long_small", "prefill_w8a8_long_small",
+                 "range_w8a8_small"):
         shape = SMALL[name]
         inp = generate(shape, seed=6, device=DEV)
         p = m.problem(shape)
@@ -419,6 +433,25 @@ FULL_SAMPLES = {"tiny_fp32": 16, "qwen3_30b_a3b_decode_bf16": 32,
                 "qwen3_235b_a22b_ep_rank_w4a8": 48,
                 "qwen3_30b_a3b_decode_w8a8": 32,
                 "qwen3_30b_a3b_prefill_skewed_w8a8": 48}
+
+
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b_prefill_skewed_bf16",
+                                  "qwen3_30b_a3b_prefill_skewed_w8a8"])
+def test_layer_long_prefill_sampled(name):
+    """The skewed prefill workloads at T = 16384 (1024 rows per expert on
+    average: the 256-row LDS tiles); sampled tokens against the oracle."""
+    m = _m()
+    shape = get_workload(name).replace(T=16384)
+    _say("long prefill", name)
+    inp = generate(shape, seed=1, device=DEV)
+    out = m.layer(m.problem(shape), inp["logits"], inp["x"], inp["w13"],
+                  inp["w2"], inp["w13_scale"], inp["w2_scale"],
+                  residual=inp["residual"])
+    torch.cuda.synchronize()
+    toks = _sample_tokens(shape.T, 32, seed=1)
+    ref = O.moe_tokens(toks, cache_weights=True, **oracle_kwargs(shape, inp))
+    assert_close(to64(out)[toks], ref, shape, name)
+    assert torch.isfinite(out.float()).all()
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
