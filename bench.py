@@ -71,7 +71,7 @@ TRAFFIC = {
     "qwen3_30b_a3b_decode_bf16":
         ("gemm_bf16_stream", "3a57a47a3cc406f8", 342877.0, 384.0),
     "qwen3_30b_a3b_prefill_skewed_bf16":
-        ("gemm_bf16_tiled", "97722ffe6fad9e0e", 594841.2, 49152.0),
+        ("gemm_bf16_tiled", "846bd2c047cb6c5f", 595552.9, 49152.0),
     "longcat_flash_zero_experts_bf16":
         ("gemm_bf16_stream", "3a57a47a3cc406f8", 13561475.4, 32528.0),
     "qwen3_235b_a22b_ep_rank_w4a8":
@@ -79,7 +79,7 @@ TRAFFIC = {
     "qwen3_30b_a3b_decode_w8a8":
         ("gemm_i8_stream", "94d4417b4227aabd", 171468.6, 773.5),
     "qwen3_30b_a3b_prefill_skewed_w8a8":
-        ("gemm_bf16_tiled", "97722ffe6fad9e0e", 249729.0, 98304.0),
+        ("gemm_bf16_tiled", "846bd2c047cb6c5f", 249931.7, 98304.0),
 }
 
 
