@@ -323,6 +323,33 @@ def main():
                   for i in range(args.steps)) / args.steps
         return st, tot
 
+    def bracket_pass(cold):
+        """Steps timed one by one with an event pair, the first pass around
+        the layer, the second around GEMM1; returns the two medians in
+        microseconds. cold: a 512 MB buffer (twice the 256 MB MALL, far more
+        than the 8 x 4 MB of L2) is read before every step, outside the
+        events, as the rest of a model's layers would between two calls of
+        one layer. (It is read, not written: a write would leave the caches
+        full of dirty lines whose write-back then competes with the next
+        step's reads, which a model's other layers need not cause.)"""
+        scrub = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+        res = []
+        for a, b in ((0, nst - 1), (g1, g1 + 1)):
+            ev = events(2)
+            torch.cuda.synchronize()
+            for i in range(args.steps):
+                if cold:
+                    scrub.amax()
+                row = list(none)
+                row[a], row[b] = ev[i]
+                step(row)
+            torch.cuda.synchronize()
+            d = sorted(ev[i][0].elapsed_time(ev[i][1]) * 1e3
+                       for i in range(args.steps))
+            res.append(d[len(d) // 2])
+        del scrub
+        return res
+
     _settle(lambda: step(none))
     for _ in range(args.warmup):
         step(none)
@@ -347,6 +374,8 @@ def main():
                    for i in sampled) / len(sampled)
     # per-stage breakdown, reported from a pass after the timed region
     stage_us, traced_step_us = stage_pass()
+    cold_layer_us, cold_gemm1_us = bracket_pass(True)
+    warm_layer_us, warm_gemm1_us = bracket_pass(False)
 
     touched, R = _routing_stats(m, p, shape, inp)
     bound, kind = _bound(shape, R, touched)
@@ -363,6 +392,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                 "traffic": _traffic(shape.name)}
+    cold_frac = roof["frac"] * gemm1_us / cold_gemm1_us
     roof.update({"kernel": "gemm1_swiglu", "avg_us": round(gemm1_us, 2),
                  "algorithmic_bytes": int(nbytes), "algorithmic_flops": flops,
                  "touched_experts": touched, "routed_rows": R})
@@ -385,6 +415,14 @@ def main():
         "traced_step_us": round(traced_step_us, 2),
         "stages_us": stage_us,
         "roofline": roof,
+        # medians of per-step event pairs with the caches cleared before
+        # every step, and of the same pairs on back-to-back steps
+        "cold": {"layer_us": round(cold_layer_us, 2),
+                 "tokens_per_s": round(shape.T / (cold_layer_us * 1e-6), 1),
+                 "gemm1_us": round(cold_gemm1_us, 2),
+                 "gemm1_roofline_frac": round(cold_frac, 4),
+                 "warm_layer_us": round(warm_layer_us, 2),
+                 "warm_gemm1_us": round(warm_gemm1_us, 2)},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = _cpu_baseline(shape, inp, args.cpu_seconds)
