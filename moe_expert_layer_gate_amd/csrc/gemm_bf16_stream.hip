@@ -68,8 +68,14 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
     uint16_t* __restrict__ out, int K, int Nw, int Nout,
     const int32_t* __restrict__ gidx, const int32_t* __restrict__ gbase,
     int gk) {
-  if ((int)blockIdx.x >= tile_count[0]) return;
+  // The tile entry is read alongside the tile count (entries past the count
+  // are in bounds, merely stale): the empty asm keeps both loads ahead of the
+  // exit test, so the weight loads start one scalar-load latency after the
+  // kernel does.
   const Tile tl = tiles[blockIdx.x];
+  const int ntiles = tile_count[0];
+  asm volatile("" ::"s"(ntiles), "s"(tl.expert), "s"(tl.row0), "s"(tl.rows));
+  if ((int)blockIdx.x >= ntiles) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane & 15, kq = lane >> 4;
   // two column groups per lane
@@ -90,17 +96,19 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
   const int s_begin = wave * nsteps / KSPLIT;
   const int s_end = (wave + 1) * nsteps / KSPLIT;
 
+  // A rows are resolved after the first step's weight loads are issued
+  // (the gather index is two dependent loads away)
   const uint16_t* arow[RG];
-  bool aok[RG];
+  auto resolve_rows = [&]() {
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    int r = 16 * rg + g;
-    aok[rg] = r < tl.rows;
-    int src = tl.row0 + (aok[rg] ? r : 0);
-    // fused gather: the row of the sorted copy is its token's row of x
-    if (gidx) src = gidx[gbase[0] + src] / gk;
-    arow[rg] = a + (size_t)src * K + 8 * kq;
-  }
+    for (int rg = 0; rg < RG; ++rg) {
+      const int r = 16 * rg + g;
+      int src = tl.row0 + (r < tl.rows ? r : 0);
+      // fused gather: the row of the sorted copy is its token's row of x
+      if (gidx) src = gidx[gbase[0] + src] / gk;
+      arow[rg] = a + (size_t)src * K + 8 * kq;
+    }
+  };
 
   f32x4 acc[2][RG][8];
 #pragma unroll
@@ -115,7 +123,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
     uint4 bA[8], bB[8];
     u32x4_t af[RG];
   };
-  auto load = [&](Stage& st, int s) {
+  auto load_w = [&](Stage& st, int s) {
     const int k0 = s * 32;
     const uint16_t* pA = we + (size_t)(k0 + 8 * kq) * Nw + ldA;
     const uint16_t* pB = we + (size_t)(k0 + 8 * kq) * Nw + ldB;
@@ -124,11 +132,17 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
       st.bA[r] = *(const uint4*)(pA + (size_t)r * Nw);
       st.bB[r] = *(const uint4*)(pB + (size_t)r * Nw);
     }
+  };
+  auto load_a = [&](Stage& st, int s) {
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      uint4 v = *(const uint4*)(arow[rg] + k0);
+      uint4 v = *(const uint4*)(arow[rg] + s * 32);
       st.af[rg] = u32x4_t{v.x, v.y, v.z, v.w};
     }
+  };
+  auto load = [&](Stage& st, int s) {
+    load_w(st, s);
+    load_a(st, s);
   };
   auto compute = [&](const Stage& st) {
 #pragma unroll
@@ -146,7 +160,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
     // two register stages: the loads of step s+1 are in flight while step s
     // is transposed and multiplied
     Stage st0, st1;
-    if (s_begin < s_end) load(st0, s_begin);
+    if (s_begin < s_end) load_w(st0, s_begin);
+    resolve_rows();
+    if (s_begin < s_end) load_a(st0, s_begin);
     for (int s = s_begin; s < s_end; s += 2) {
       if (s + 1 < s_end) load(st1, s + 1);
       compute(st0);
@@ -158,6 +174,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
   } else {
     // 32-row tiles carry twice the accumulators: one stage, loads of a step
     // still issued together before its MFMAs
+    resolve_rows();
     for (int s = s_begin; s < s_end; ++s) {
       Stage st;
       load(st, s);

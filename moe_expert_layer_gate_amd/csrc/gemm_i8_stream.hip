@@ -52,8 +52,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_stream_kernel(
     int gk) {
   constexpr int NG = 8;                 // 16-column groups per lane
   constexpr int SLAB = GLU ? 64 : 128;  // output columns per block
-  if ((int)blockIdx.x >= tile_count[0]) return;
+  // tile entry and count read together (entries past the count are in
+  // bounds, merely stale); the empty asm keeps both ahead of the exit test
   const Tile tl = tiles[blockIdx.x];
+  const int ntiles = tile_count[0];
+  asm volatile("" ::"s"(ntiles), "s"(tl.expert), "s"(tl.row0), "s"(tl.rows));
+  if ((int)blockIdx.x >= ntiles) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane & 15, q = lane >> 4;
   const int c0 = blockIdx.y * SLAB;
@@ -69,14 +73,18 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_stream_kernel(
     cok[gi] = c < Nout;
     col[gi] = cok[gi] ? ((GLU && gi >= 4) ? Nout + c : c) : 0;
   }
+  // A rows are resolved after the first step's weight loads are issued
+  // (the gather index is two dependent loads away)
   const int8_t* arow[RG];
+  auto resolve_rows = [&]() {
 #pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    const int r = 16 * rg + g;
-    int src = tl.row0 + (r < tl.rows ? r : 0);
-    if (gidx) src = gidx[gbase[0] + src] / gk;  // fused gather of token rows
-    arow[rg] = a + (size_t)src * K + 16 * q;
-  }
+    for (int rg = 0; rg < RG; ++rg) {
+      const int r = 16 * rg + g;
+      int src = tl.row0 + (r < tl.rows ? r : 0);
+      if (gidx) src = gidx[gbase[0] + src] / gk;  // fused gather of token rows
+      arow[rg] = a + (size_t)src * K + 16 * q;
+    }
+  };
 
   i32x4_t acc[NG][RG];
 #pragma unroll
@@ -88,7 +96,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_stream_kernel(
     uint4 b[NG][2];
     uint4 a[RG][2];
   };
-  auto load = [&](Stage& st, int s) {
+  auto load_w = [&](Stage& st, int s) {
     const size_t k0 = (size_t)s * 128 + 16 * q;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
@@ -96,11 +104,17 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_stream_kernel(
       st.b[gi][0] = *(const uint4*)p;
       st.b[gi][1] = *(const uint4*)(p + 64);
     }
+  };
+  auto load_a = [&](Stage& st, int s) {
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
       st.a[rg][0] = *(const uint4*)(arow[rg] + (size_t)s * 128);
       st.a[rg][1] = *(const uint4*)(arow[rg] + (size_t)s * 128 + 64);
     }
+  };
+  auto load = [&](Stage& st, int s) {
+    load_w(st, s);
+    load_a(st, s);
   };
   auto compute = [&](const Stage& st) {
 #pragma unroll
@@ -117,7 +131,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_stream_kernel(
   if (RG == 1) {
     // two register stages: step s+1's loads are in flight during step s
     Stage st0, st1;
-    if (s_begin < s_end) load(st0, s_begin);
+    if (s_begin < s_end) load_w(st0, s_begin);
+    resolve_rows();
+    if (s_begin < s_end) load_a(st0, s_begin);
     for (int s = s_begin; s < s_end; s += 2) {
       if (s + 1 < s_end) load(st1, s + 1);
       compute(st0);
@@ -127,6 +143,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_stream_kernel(
       }
     }
   } else {
+    resolve_rows();
     for (int s = s_begin; s < s_end; ++s) {
       Stage st;
       load(st, s);
