@@ -170,6 +170,31 @@ def test_init_routing_small(name):
     _routing_case(SMALL[name], seed=3)
 
 
+@pytest.mark.parametrize("T,E,k", [(50, 2048, 2), (600, 2048, 64), (64, 1024, 64),
+                                   (65, 1024, 64), (4096, 1, 1)])
+def test_init_routing_max_sizes(T, E, k):
+    """The largest expert count and top-k the library takes (2048 experts
+    route through the multi-block kernels), and both sides of the
+    single-block routing limit of 4096 copies and 1024 experts (64 x 64
+    copies is the last on the single-block side, 65 x 64 the first past it)."""
+    m = _m()
+    g = torch.Generator().manual_seed(T * 31 + E + k)
+    L = torch.randn(T, E, generator=g)
+    rid, _ = O.gate_topk(L.numpy(), k)
+    x = torch.randn(T, 64, generator=g).to(torch.bfloat16)
+    p = m.problem(T=T, H=64, I=32, n_ffn=E, n_zero=0, top_k=k, local_begin=0,
+                  local_end=E, act="bf16", wt="bf16", act_q="none")
+    r = m.init_routing(p, torch.from_numpy(rid).to(DEV), x.to(DEV))
+    torch.cuda.synchronize()
+    counts, offsets, sc, cp = O.init_routing(rid, E)
+    assert np.array_equal(r["counts"].cpu().numpy(), counts)
+    assert np.array_equal(r["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(r["sorted_copy"].cpu().numpy(), sc)
+    assert np.array_equal(r["copy_pos"].cpu().numpy(), cp)
+    assert np.array_equal(bits(r["x_perm"][: T * k]),
+                          bits(x[torch.from_numpy(sc // k)]))
+
+
 def test_init_routing_invalid_ids_are_ignored():
     m = _m()
     shape = SMALL["decode_bf16_small"]
@@ -353,6 +378,14 @@ def test_edge_single_token_and_k_equals_E():
     _layer_vs_oracle(b.replace(T=1))
     _layer_vs_oracle(b.replace(T=5, top_k=b.n_ffn))
     _layer_vs_oracle(SMALL["tiny_fp32"].replace(top_k=1))
+
+
+def test_edge_max_experts_and_top_k():
+    """2048 experts with top-64 routing (the library's limits): about two
+    rows per expert through the streaming GEMMs, checked on the whole layer."""
+    b = SMALL["decode_bf16_small"].replace(T=64, H=64, I=32, n_ffn=2048,
+                                            local_end=2048, top_k=64)
+    _layer_vs_oracle(b)
 
 
 def test_edge_zero_tokens():
