@@ -69,15 +69,15 @@ TRAFFIC = {
     # workload: (kernel source set, sha256[:16] of its sources, FETCH KiB,
     #            WRITE KiB) per GEMM1 dispatch
     "qwen3_30b_a3b_decode_bf16":
-        ("gemm_bf16_stream", "3a57a47a3cc406f8", 342877.0, 384.0),
+        ("gemm_bf16_stream", "c2d6d095ac0bf990", 342578.3, 384.0),
     "qwen3_30b_a3b_prefill_skewed_bf16":
         ("gemm_bf16_tiled", "846bd2c047cb6c5f", 595552.9, 49152.0),
     "longcat_flash_zero_experts_bf16":
-        ("gemm_bf16_stream", "3a57a47a3cc406f8", 13561475.4, 32528.0),
+        ("gemm_bf16_stream", "c2d6d095ac0bf990", 13560901.9, 32528.0),
     "qwen3_235b_a22b_ep_rank_w4a8":
         ("gemm_mx_tiled", "498bd15b909f0051", 213173.0, 12824.5),
     "qwen3_30b_a3b_decode_w8a8":
-        ("gemm_i8_stream", "94d4417b4227aabd", 171468.6, 773.5),
+        ("gemm_i8_stream", "f05e741ff09c9a4d", 171459.6, 773.6),
     "qwen3_30b_a3b_prefill_skewed_w8a8":
         ("gemm_bf16_tiled", "846bd2c047cb6c5f", 249931.7, 98304.0),
 }

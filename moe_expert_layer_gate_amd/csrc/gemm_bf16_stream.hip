@@ -292,15 +292,19 @@ int device_cus() {
 
 // Waves per block that split K. Decode launches have few (tile, slab) blocks;
 // splitting K across up to 3 waves fills the chip, but only as far as every
-// wave stays resident in one round (2 waves per SIMD) and keeps at least 4
-// steps of 32. The grid is sized for the host's upper bound on the tile
+// block stays resident in one round and each wave keeps at least 4 steps.
+// At two waves per SIMD a CU holds 8 waves, i.e. floor(8 / k) blocks of k
+// waves: 2 blocks of 3 waves leave two slots empty, so a 3-way split holds
+// 512 blocks per round on 256 CUs, not 2048 / 3 (counting wave slots let
+// the decode GEMM1's 666 blocks spill into a partial second round, which
+// cost it 3-4 %). The grid is sized for the host's upper bound on the tile
 // count; the tiles that exist on the device are typically 3/4 of it.
 int stream_ksplit(long long blocks, int steps, int rg) {
   (void)rg;
-  const long long slots = (long long)device_cus() * 4 * 2;
   int ks = 1;
   for (int k = 2; k <= 3; ++k)
-    if (blocks * 3 / 4 * k <= slots && steps / k >= 4) ks = k;
+    if (blocks * 3 / 4 <= (long long)device_cus() * (8 / k) && steps / k >= 4)
+      ks = k;
   return ks;
 }
 
