@@ -27,7 +27,10 @@
  *   - Workspace (hipcub style): when `workspace` is NULL the call stores the
  *     bytes it needs in *workspace_bytes, returns MOE_OK and launches nothing.
  *     Otherwise *workspace_bytes is the size of `workspace`; a buffer that is
- *     too small gives MOE_ERR_WORKSPACE. Workspace must be 256-byte aligned.
+ *     too small gives MOE_ERR_WORKSPACE.
+ *   - Alignment: every array pointer must be 16-byte aligned and the
+ *     workspace 256-byte aligned (allocations from hipMalloc or the torch
+ *     allocator are); a misaligned one gives MOE_ERR_INVALID_ARG.
  *
  * Expert ids: FFN experts are [0, n_ffn); identity ("zero-compute") experts
  * are [n_ffn, n_ffn + n_zero) and return their input, MoE(x) = x ([P2]

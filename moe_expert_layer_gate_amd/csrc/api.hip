@@ -96,6 +96,15 @@ struct Carve {
   }
 };
 
+// Every tensor pointer must be 16-byte aligned (the kernels move 16 bytes
+// per lane and copy straight into LDS); NULL passes.
+bool aligned16() { return true; }
+template <class P, class... R>
+bool aligned16(P p, R... rest) {
+  return ((uintptr_t)(const void*)p & 15u) == 0 && aligned16(rest...);
+}
+bool ws_aligned(const void* w) { return ((uintptr_t)w & 255u) == 0; }
+
 moe_status hip_status(hipError_t e) {
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -260,6 +269,7 @@ moe_status moe_gate_topk(const moe_problem* p, const float* logits,
   if (st != MOE_OK) return st;
   if (q.T == 0) return MOE_OK;
   if (!logits || !topk_ids || !topk_weight) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(logits, topk_ids, topk_weight)) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_gate_topk(logits, q.T, q.E, q.k, topk_ids,
                                           topk_weight, (hipStream_t)stream));
 }
@@ -284,6 +294,10 @@ moe_status moe_init_routing(const moe_problem* p, const int32_t* topk_ids,
   if (q.El > 0 && q.N > 0 && (!x || !x_perm)) return MOE_ERR_INVALID_ARG;
   if ((q.mx || q.i8) ? (q.El > 0 && q.N > 0 && !x_perm_scale)
                      : (x_perm_scale != nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if (!ws_aligned(workspace) ||
+      !aligned16(topk_ids, x, tokens_per_expert, offsets, sorted_copy,
+                 copy_pos, x_perm, x_perm_scale))
     return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   if (moe::route_small_ok((int)q.N, q.E)) {
@@ -334,6 +348,9 @@ moe_status moe_ffn_up(const moe_problem* p, const int32_t* offsets,
   if (!offsets || !x_perm || !h) return MOE_ERR_INVALID_ARG;
   if ((q.mx || q.i8) ? (!x_perm_scale || !h_scale) : (x_perm_scale || h_scale))
     return MOE_ERR_INVALID_ARG;
+  if (!ws_aligned(workspace) ||
+      !aligned16(offsets, x_perm, x_perm_scale, w13, w13_scale, h, h_scale))
+    return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   MOE_TRY(moe::launch_build_tiles(offsets, q.fb, q.fe, mt, fw.tiles,
                                   (int)max_tiles(q, mt), fw.tile_count, s));
@@ -365,6 +382,8 @@ moe_status moe_ffn_down(const moe_problem* p, const int32_t* offsets,
   if (q.El == 0 || q.N == 0) return MOE_OK;
   if (!offsets || !h || !y) return MOE_ERR_INVALID_ARG;
   if ((q.mx || q.i8) ? !h_scale : (h_scale != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!ws_aligned(workspace) || !aligned16(offsets, h, h_scale, w2, w2_scale, y))
+    return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   MOE_TRY(moe::launch_build_tiles(offsets, q.fb, q.fe, mt, fw.tiles,
                                   (int)max_tiles(q, mt), fw.tile_count, s));
@@ -397,6 +416,9 @@ moe_status moe_grouped_ffn(const moe_problem* p, const int32_t* offsets,
   if (!offsets || !x_perm || !y) return MOE_ERR_INVALID_ARG;
   if ((q.mx || q.i8) ? !x_perm_scale : (x_perm_scale != nullptr))
     return MOE_ERR_INVALID_ARG;
+  if (!ws_aligned(workspace) ||
+      !aligned16(offsets, x_perm, x_perm_scale, w13, w13_scale, w2, w2_scale, y))
+    return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   MOE_TRY(moe::launch_build_tiles(offsets, q.fb, q.fe, mt, fw.tiles,
                                   (int)max_tiles(q, mt), fw.tile_count, s));
@@ -419,6 +441,8 @@ moe_status moe_finalize(const moe_problem* p, const int32_t* topk_ids,
   if (!topk_ids || !topk_weight || !copy_pos || !offsets || !x || !out)
     return MOE_ERR_INVALID_ARG;
   if (q.El > 0 && !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(topk_ids, topk_weight, copy_pos, offsets, y, x, residual, out))
+    return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_finalize(
       topk_ids, topk_weight, copy_pos, offsets, q.fb, q.nffn, q.lb, q.le, y, x,
       residual, out, q.act == MOE_F32 ? 0 : 1, q.T, q.H, q.k,
@@ -434,6 +458,8 @@ moe_status moe_add_rms_norm_cast(int32_t T, int32_t H, const void* x,
   if (H % 32 || H > kMaxNormH) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !norm_weight || (!y_f32 && !y_bf16)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x, residual, norm_weight, y_f32, y_bf16, residual_out))
+    return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_add_rms_norm(
       0, (const uint16_t*)x, (const uint16_t*)residual,
       (const uint16_t*)norm_weight, epsilon, T, H, y_f32, (uint16_t*)y_bf16,
@@ -450,6 +476,8 @@ moe_status moe_add_rms_norm_mx_quant(int32_t T, int32_t H, const void* x,
   if (H % 32 || H > kMaxNormH) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !norm_weight || !y_codes || !y_scales) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x, residual, norm_weight, y_codes, y_scales, residual_out))
+    return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_add_rms_norm(
       1, (const uint16_t*)x, (const uint16_t*)residual,
       (const uint16_t*)norm_weight, epsilon, T, H, nullptr, nullptr, y_codes,
@@ -463,6 +491,7 @@ moe_status moe_router_logits(int32_t T, int32_t H, int32_t E, const float* y,
   if (H % 16 || E % 32 || E > kMaxE) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!y || !w_router || !logits) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y, w_router, logits)) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_router_logits(y, w_router, logits, T, H, E,
                                               (hipStream_t)stream));
 }
@@ -513,6 +542,9 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
     return st;
   if (q.T == 0) return MOE_OK;
   if (!logits || !x || !out) return MOE_ERR_INVALID_ARG;
+  if (!ws_aligned(workspace) ||
+      !aligned16(logits, x, residual, w13, w13_scale, w2, w2_scale, out))
+    return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   auto mark = [&](int i) -> hipError_t {
     if (stage_events && i < n_events && stage_events[i])

@@ -168,3 +168,57 @@ def test_router_host_checks(L):
     assert r(4, 64, 32, fake, None, fake, None) == 1
     assert r(4, 64, 32, fake, fake, None, None) == 1
     assert r(0, 64, 32, None, None, None, None) == 0
+
+
+def test_misaligned_pointers_rejected(L):
+    """Array pointers must be 16-byte aligned and the workspace 256-byte
+    aligned; a misaligned one is refused on the host (never dereferenced)."""
+    ok = ctypes.c_void_p(1 << 20)
+    bad = ctypes.c_void_p((1 << 20) + 2)      # not 16-byte aligned
+    ws_bad = ctypes.c_void_p((1 << 20) + 16)  # 16- but not 256-byte aligned
+    p = _p()
+    _, need = _query(L, p)
+    n = ctypes.c_size_t(need)
+    lay = L.moe_layer
+    # logits, x, residual, w13, w13_scale, w2, w2_scale, out, workspace
+    assert lay(ctypes.byref(p), bad, ok, None, ok, None, ok, None, ok, ok,
+               ctypes.byref(n), None) == 1
+    assert lay(ctypes.byref(p), ok, bad, None, ok, None, ok, None, ok, ok,
+               ctypes.byref(n), None) == 1
+    assert lay(ctypes.byref(p), ok, ok, bad, ok, None, ok, None, ok, ok,
+               ctypes.byref(n), None) == 1
+    assert lay(ctypes.byref(p), ok, ok, None, ok, None, bad, None, ok, ok,
+               ctypes.byref(n), None) == 1
+    assert lay(ctypes.byref(p), ok, ok, None, ok, None, ok, None, bad, ok,
+               ctypes.byref(n), None) == 1
+    assert lay(ctypes.byref(p), ok, ok, None, ok, None, ok, None, ok, ws_bad,
+               ctypes.byref(n), None) == 1
+    assert L.moe_gate_topk(ctypes.byref(p), bad, ok, ok, None) == 1
+    assert L.moe_gate_topk(ctypes.byref(p), ok, ok, bad, None) == 1
+    # finalize: topk_ids, topk_weight, copy_pos, offsets, y, x, residual, out
+    assert L.moe_finalize(ctypes.byref(p), ok, ok, ok, ok, bad, ok, None, ok,
+                          None) == 1
+    assert L.moe_finalize(ctypes.byref(p), ok, ok, ok, ok, ok, ok, None, bad,
+                          None) == 1
+    # grouped FFN: offsets, x_perm, x_perm_scale, w13, w13_scale, w2,
+    # w2_scale, y, workspace
+    ng = ctypes.c_size_t(0)
+    assert L.moe_grouped_ffn(ctypes.byref(p), None, None, None, None, None,
+                             None, None, None, None, ctypes.byref(ng), None) == 0
+    assert L.moe_grouped_ffn(ctypes.byref(p), ok, ok, None, bad, None, ok,
+                             None, ok, ok, ctypes.byref(ng), None) == 1
+    assert L.moe_grouped_ffn(ctypes.byref(p), ok, ok, None, ok, None, ok,
+                             None, ok, ws_bad, ctypes.byref(ng), None) == 1
+    # routing: topk_ids, x, tokens_per_expert, offsets, sorted_copy,
+    # copy_pos, x_perm, x_perm_scale, workspace
+    nr = ctypes.c_size_t(0)
+    assert L.moe_init_routing(ctypes.byref(p), None, None, None, None, None,
+                              None, None, None, None, ctypes.byref(nr),
+                              None) == 0
+    assert L.moe_init_routing(ctypes.byref(p), ok, ok, ok, ok, ok, ok, bad,
+                              None, ok, ctypes.byref(nr), None) == 1
+    assert L.moe_router_logits(4, 64, 32, ok, bad, ok, None) == 1
+    assert L.moe_add_rms_norm_cast(4, 64, bad, None, ok, 1e-6, ok, ok, None,
+                                   None) == 1
+    assert L.moe_add_rms_norm_mx_quant(4, 64, ok, None, ok, 1e-6, ok, bad,
+                                       None, None) == 1
