@@ -46,9 +46,11 @@
 // practice", 量化策略: int8 weights with static per-channel scales, int8
 // activations with dynamic per-token scales): a step is 64 bytes of every row
 // either way (32 bf16 or 64 int8 K), so the LDS ring, the copies of A and
-// the fragment reads are byte for byte those of bf16. The int8 weights are
-// [N, K] (K contiguous) and are staged like A, [column][4 x 16 B] with the
-// same swizzle, and read with plain 16-byte reads; v_mfma_i32_32x32x32_i8
+// the fragment reads are byte for byte those of bf16. The int8 weights come
+// packed in 1 KB fragments (16 columns x 64 K bytes each); they are staged
+// like A, [column][4 x 16 B] with the same swizzle, each copy instruction
+// reading one whole fragment, and read with plain 16-byte reads;
+// v_mfma_i32_32x32x32_i8
 // takes the place of the bf16 MFMA (same operand bytes, same issue cycles,
 // twice the K); the int32 sums are dequantised in the epilogue with the row
 // scales (staged in LDS per tile) and the weight column scales.
@@ -195,16 +197,19 @@ MOE_DEV void tiled_item(
   // lane/32 of the step, physical piece lane%32 holds logical piece
   // (lane%32) ^ swz_b(k); the swizzle only depends on k%4 = 2*(wave&1) +
   // lane/32 (NW is even), the same for all j.
-  // B (int8 [N, K]), instruction j (0..NB-1): like A, tile columns
-  // 16*(wave + NW*j) + lane/4 of 64 bytes each, LDS [column][4 x 16 B], piece
-  // lane%4 <- logical piece (lane%4) ^ swz_a(column).
+  // B (int8, packed: 1 KB fragments per K block of 128, 16 columns and
+  // half m, 16 bytes of column c, K piece p at 16 * (c + 16 p)), instruction j
+  // (0..NB-1): the fragment of tile columns 16*(wave + NW*j) .. +15 for this
+  // step, copied as it is (lane l takes bytes 16 l, one contiguous 1 KB), so
+  // LDS holds [16-column group][piece][column] -- the MFMA reads (32 lanes
+  // on 32 consecutive columns, one piece) are conflict-free without a
+  // swizzle. (N % 16 == 0: a 16-column group is in or past N whole, and
+  // wcol sends it to group 0 in the latter case.)
   uint32_t b_off[I8 ? NB : 1];
   if constexpr (I8) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int t = 16 * (wave + NW * j) + (lane >> 2);
-      b_off[j] = (uint32_t)wcol(t) * K + 16 * ((lane & 3) ^ swz_a(t));
-    }
+    for (int j = 0; j < NB; ++j)
+      b_off[j] = (uint32_t)wcol(16 * (wave + NW * j)) / 16 * 2048u + 16u * lane;
   } else {
     const int kr = 2 * wave + (lane >> 5);
     const int cl = (lane & 31) ^ swz_b(kr);
@@ -225,7 +230,8 @@ MOE_DEV void tiled_item(
     _Pragma("unroll") for (int j = 0; j < NA; ++j)                            \
       g2lds(ab_, a_off[j], a_dst + o_ + 16 * NW * j * (BK * 2));              \
     if constexpr (I8) {                                                       \
-      const char* bb_ = we + (size_t)(s_) * 64;                               \
+      /* K block s/2 (N/16 groups of 2 KB), half s%2 */                      \
+      const char* bb_ = we + (size_t)((s_) >> 1) * Nw * 128 + ((s_) & 1) * 1024; \
       _Pragma("unroll") for (int j = 0; j < NB; ++j)                          \
         g2lds(bb_, b_off[j], b_dst + o_ + 16 * NW * j * 64);                  \
     } else {                                                                  \
@@ -266,7 +272,8 @@ MOE_DEV void tiled_item(
   };
   const int cwave = wn * (GLU ? WC / 2 : WC);
   auto colblk = [&](int nbk) -> int { return cwave + cdelta(nbk); };
-  // int8: the swizzle (col/4)%4 = (lr/4)%4 is the same for every nbk, so
+  // int8: column col, piece p sits at (col/16) KB + 16 (16 p + col%16);
+  // the 32-column blocks of the wave are whole 16-column groups apart, so
   // only the nbk = 0 offsets are kept (b_rd[kk][0]) and the others are
   // constant distances from them
   uint32_t b_rd[2][I8 ? 1 : NNB];  // [kk][nbk]
@@ -277,8 +284,8 @@ MOE_DEV void tiled_item(
       const int cb = colblk(nbk);
       if constexpr (I8) {
         const int col = cb + lr;
-        b_rd[kk][nbk] = lds_addr(smem) + A_BYTES + col * 64 +
-                        16 * ((kk * 2 + lh) ^ swz_a(col));
+        b_rd[kk][nbk] = lds_addr(smem) + A_BYTES + (col >> 4) * 1024 +
+                        16 * (16 * (kk * 2 + lh) + (col & 15));
       } else {
         const int kr = kk * 16 + 8 * lh + ((lane & 15) >> 2);
         const int col = cb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);

@@ -11,12 +11,14 @@
 // straight into registers.
 //
 // v_mfma_i32_16x16x64_i8: lane l holds 16 bytes of row (A) / column (B) l%16.
-// Both operands are K-contiguous in memory. Per K step of 128 a lane with
-// q = l/16 loads bytes [16q, 16q+16) and [64+16q, 64+16q+16) of its row and of
-// each of its weight columns -- four lanes cover one 64-byte half of a 128-byte
-// line per load -- and feeds the first pair to one MFMA and the second pair to
-// another. A and B lanes hold the same K offsets, so the two MFMAs sum every K
-// of the step exactly, whatever order the hardware takes them in.
+// Per K step of 128, MFMA m (0, 1) takes from lane l (q = l/16) bytes
+// [64m + 16q, +16) of its activation row and of its weight column. A and B
+// lanes hold the same K offsets, so the two MFMAs sum every K of the step
+// exactly, whatever order the hardware takes them in. Activation rows are
+// K-contiguous and read in place; the weights come packed (one 1 KB
+// fragment per K block of 128, 16 columns and m, in exactly this lane
+// order, column groups of a K block adjacent), so every weight load of a
+// wave reads 1 KB contiguous.
 //
 // Each lane carries 8 groups of 16 weight columns: for GEMM1 4 gate groups and
 // the 4 matching up groups (64 h columns per block, SwiGLU lane-local), for
@@ -64,14 +66,18 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_stream_kernel(
   const int8_t* we = w + (size_t)tl.expert * Nw * K;
 
   // Columns past N and rows past the tile only feed outputs that are never
-  // stored; their loads read column / row 0, so every load is unconditional.
+  // stored; their loads read column group / row 0, so every load is
+  // unconditional. (N is a multiple of 16: a group is in or out whole.)
   int col[NG];
   bool cok[NG];
+  uint32_t frag[NG];  // byte offset of the group's K-block-0 fragment + lane
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     const int c = GLU ? c0 + 16 * (gi & 3) + g : c0 + 16 * gi + g;
     cok[gi] = c < Nout;
     col[gi] = cok[gi] ? ((GLU && gi >= 4) ? Nout + c : c) : 0;
+    const int n16 = cok[gi] ? (col[gi] - g) / 16 : 0;  // group's column / 16
+    frag[gi] = (uint32_t)n16 * 2048u + 16u * lane;
   }
   // A rows are resolved after the first step's weight loads are issued
   // (the gather index is two dependent loads away)
@@ -97,12 +103,12 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_stream_kernel(
     uint4 a[RG][2];
   };
   auto load_w = [&](Stage& st, int s) {
-    const size_t k0 = (size_t)s * 128 + 16 * q;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      const int8_t* p = we + (size_t)col[gi] * K + k0;
+      // K block s: the N/16 column groups of 2 KB each
+      const int8_t* p = we + frag[gi] + (size_t)s * Nw * 128;
       st.b[gi][0] = *(const uint4*)p;
-      st.b[gi][1] = *(const uint4*)(p + 64);
+      st.b[gi][1] = *(const uint4*)(p + 1024);
     }
   };
   auto load_a = [&](Stage& st, int s) {

@@ -5,7 +5,23 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+import moe_inputs
 import oracle as O
+
+
+def generate(shape, *args, **kwargs):
+    """The seeded inputs of moe_inputs.generate; int8 expert weights on a GPU
+    are handed to the library packed (the form its int8 GEMMs take, made by
+    the library's own pack call), and the row-major originals stay under
+    "w13_rowmajor" / "w2_rowmajor" for the oracle."""
+    inp = moe_inputs.generate(shape, *args, **kwargs)
+    w13 = inp.get("w13")
+    if shape.wt == "int8" and w13 is not None and w13.is_cuda:
+        import moe_expert_layer_gate_amd as m
+        for k in ("w13", "w2"):
+            inp[k + "_rowmajor"] = inp[k]
+            inp[k] = m.pack_int8_weights(inp[k])
+    return inp
 
 
 def to64(t):
@@ -25,7 +41,8 @@ def weight_getter(shape, inp):
             return a.T.copy(), b.T.copy()   # [H, 2I], [I, H]
         return get
     if shape.wt == "int8":
-        w13, s13, w2, s2 = inp["w13"], inp["w13_scale"], inp["w2"], inp["w2_scale"]
+        w13, w2 = inp.get("w13_rowmajor", inp["w13"]), inp.get("w2_rowmajor", inp["w2"])
+        s13, s2 = inp["w13_scale"], inp["w2_scale"]
 
         def get(e):
             i = e - fb

@@ -222,3 +222,18 @@ def test_misaligned_pointers_rejected(L):
                                    None) == 1
     assert L.moe_add_rms_norm_mx_quant(4, 64, ok, None, ok, 1e-6, ok, bad,
                                        None, None) == 1
+
+
+def test_pack_int8_host_checks(L):
+    ok = ctypes.c_void_p(1 << 20)
+    far = ctypes.c_void_p(1 << 30)
+    pk = L.moe_pack_int8_weights
+    assert pk(-1, 32, 128, ok, far, None) == 1
+    assert pk(2, 0, 128, ok, far, None) == 1
+    assert pk(2, 24, 128, ok, far, None) == 2         # N % 16
+    assert pk(2, 32, 192, ok, far, None) == 2         # K % 128
+    assert pk(2, 1 << 16, 1 << 15, ok, far, None) == 2  # N * K >= 2^31
+    assert pk(2, 32, 128, None, far, None) == 1
+    assert pk(2, 32, 128, ok, ctypes.c_void_p((1 << 30) + 8), None) == 1  # misaligned
+    assert pk(2, 32, 128, ok, ctypes.c_void_p((1 << 20) + 4096), None) == 1  # overlap
+    assert pk(0, 32, 128, None, None, None) == 0     # nothing to do

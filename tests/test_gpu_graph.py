@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 import torch
 
-from moe_inputs import generate, get_workload, scaled
+from moe_inputs import get_workload, scaled
+from _moe_util import generate
 from _moe_util import bits
 
 pytestmark = pytest.mark.gpu

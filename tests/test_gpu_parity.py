@@ -11,8 +11,9 @@ import pytest
 import torch
 
 import oracle as O
-from moe_inputs import WORKLOADS, generate, get_workload, scaled
-from _moe_util import (assert_close, bits, np_to_act_bits, oracle_kwargs, to64)
+from moe_inputs import WORKLOADS, get_workload, scaled
+from _moe_util import (assert_close, bits, generate, np_to_act_bits, oracle_kwargs,
+                       to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -506,3 +507,19 @@ def test_layer_full_size_sampled(name):
     assert_close(got, ref, shape, name)
     # every output row is finite
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("E,N,K", [(3, 48, 256), (1, 16, 128), (2, 1536, 2048)])
+def test_pack_int8_weights(E, N, K):
+    """The packed int8 weight order, byte for byte: fragments in the order
+    [e][kb][n16][m]; lane l of fragment (e, kb, n16, m) holds
+    W[e, 16 n16 + l % 16, 128 kb + 64 m + 16 (l / 16) .. + 15]."""
+    m = _m()
+    g = torch.Generator().manual_seed(E * 1000 + N + K)
+    w = torch.randint(-127, 128, (E, N, K), generator=g, dtype=torch.int8)
+    got = m.pack_int8_weights(w.to(DEV))
+    torch.cuda.synchronize()
+    W = w.numpy().reshape(E, N // 16, 16, K // 128, 2, 4, 16)
+    # -> [e][kb][n16][m][q][col][16 bytes]; lane l = 16 q + col
+    want = W.transpose(0, 3, 1, 4, 5, 2, 6).reshape(E, N, K)
+    assert np.array_equal(got.cpu().numpy(), want)
