@@ -250,8 +250,11 @@ MOE_API moe_status moe_layer(const moe_problem* p, const float* logits, const vo
  * quantisation of x), 5 GEMM1 + SwiGLU, 6 GEMM2, 7 finalize, and entry 8
  * after the last. Each of stages 0-7 is at most one kernel launch (a stage
  * with nothing to do launches nothing), except stage 6 for INT8, which
- * quantises h and then runs GEMM2. For performance tooling; results are
- * identical to moe_layer. */
+ * quantises h and then runs GEMM2. Where x is quantised once per token
+ * (INT8, and MXFP8 with 128-row GEMM tiles) and E_tot <= 256, the gate
+ * kernel of stage 0 quantises it as well and stage 4 is empty (int8: only
+ * for H = 2048 or 4096). For performance tooling; results are identical to
+ * moe_layer. */
 MOE_API moe_status moe_layer_traced(const moe_problem* p, const float* logits,
                                     const void* x, const void* residual,
                                     const void* w13, const void* w13_scale,

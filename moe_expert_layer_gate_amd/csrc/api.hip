@@ -568,8 +568,17 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
   // small problems route in one block
   const bool small = moe::route_small_ok((int)q.N, q.E);
   const int mtl = (int)max_tiles(q, mt);
+  // the per-token quantisation of x (W4A8 tiled, W8A8) rides along with the
+  // gate when the fused kernel covers the shape
+  const bool tok_q = q.El > 0 && (mx_tok || i8_tok);
+  const bool fused_q = tok_q && moe::gate_quant_ok(q.E, q.H, q.mx);
   MOE_TRY(mark(0));
-  MOE_TRY(moe::launch_gate_topk(logits, q.T, q.E, q.k, ids, wts, s));
+  if (fused_q)
+    MOE_TRY(moe::launch_gate_topk_quant(logits, q.T, q.E, q.k, ids, wts,
+                                        (const uint16_t*)x, q.H, q.mx, xp, xs,
+                                        s));
+  else
+    MOE_TRY(moe::launch_gate_topk(logits, q.T, q.E, q.k, ids, wts, s));
   MOE_TRY(mark(1));
   if (small) {
     MOE_TRY(moe::launch_route_small(ids, (int)q.N, q.E, counts, offsets,
@@ -589,7 +598,9 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
     MOE_TRY(moe::launch_route_scatter(ids, (int)q.N, q.E, cc, offsets,
                                       sorted_copy, copy_pos, s));
   MOE_TRY(mark(4));
-  if (q.El > 0 && mx_tok)
+  if (fused_q)
+    ;  // x was quantised with the gate
+  else if (q.El > 0 && mx_tok)
     MOE_TRY(moe::launch_quantize_mx(x, (int)q.T, q.H, (uint8_t*)xp,
                                     (uint8_t*)xs, s));
   else if (q.El > 0 && i8_tok)

@@ -6,6 +6,7 @@
 #include "common.h"
 #include "gate_wave.h"
 #include "launch.h"
+#include "quant_row.h"
 
 namespace moe {
 
@@ -40,6 +41,63 @@ hipError_t launch_gate_topk(const float* logits, int T, int E, int k,
   MOE_GATE_CASE(32)
 #undef MOE_GATE_CASE
   return hipErrorInvalidValue;
+}
+
+// The gate fused with the per-token quantisation of x that the W4A8 (MXFP8)
+// and W8A8 (int8) layers apply before routing: the wave that gates token t
+// also quantises row t of x, so the two per-token passes share one launch
+// and their memory latencies overlap. Q = 1: MXFP8 (codes [T, H], e8m0
+// [T, H/32]); Q = 2: int8 with CPL chunks of 512 per lane (codes [T, H],
+// fp32 scales [T]). The codes equal those of the separate kernels bit for
+// bit (same row routines).
+template <int VPL, int Q, int CPL>
+__global__ __launch_bounds__(256) void gate_quant_kernel(
+    const float* __restrict__ logits, int T, int E, int k,
+    int32_t* __restrict__ ids, float* __restrict__ wout,
+    const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ xq,
+    void* __restrict__ xs) {
+  __shared__ uint2 slots[4][64];
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave exits together
+  const int lane = threadIdx.x & 63;
+  if (Q == 1)
+    quant_mx_row_bf16((const uint4*)(x + (size_t)t * H), H,
+                      xq + (size_t)t * H, (uint8_t*)xs + (size_t)t * (H / 32),
+                      lane);
+  else
+    quant_i8_row<false, CPL>(x, H, (size_t)t * H, (int8_t*)xq + (size_t)t * H,
+                             (float*)xs + t, lane);
+  topk_softmax_wave<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
+                         wout + (size_t)t * k, slots[threadIdx.x >> 6]);
+}
+
+bool gate_quant_ok(int E, int H, bool mx) {
+  return E <= 256 && H % 32 == 0 && (mx || H == 2048 || H == 4096);
+}
+
+hipError_t launch_gate_topk_quant(const float* logits, int T, int E, int k,
+                                  int32_t* ids, float* w, const uint16_t* x,
+                                  int H, bool mx, void* xq, void* xs,
+                                  hipStream_t s) {
+  if (!gate_quant_ok(E, H, mx)) return hipErrorInvalidValue;
+  if (T == 0) return hipSuccess;
+  dim3 grid((T + 3) / 4), block(256);
+  const int vpl = (E + 63) / 64;
+#define MOE_GQ(V, Q_, C)                                                      \
+  hipLaunchKernelGGL((gate_quant_kernel<V, Q_, C>), grid, block, 0, s, logits, \
+                     T, E, k, ids, w, x, H, (uint8_t*)xq, xs)
+#define MOE_GQ_V(Q_, C)                                                       \
+  do {                                                                        \
+    if (vpl <= 1) MOE_GQ(1, Q_, C);                                           \
+    else if (vpl <= 2) MOE_GQ(2, Q_, C);                                      \
+    else MOE_GQ(4, Q_, C);                                                    \
+  } while (0)
+  if (mx) MOE_GQ_V(1, 0);
+  else if (H == 2048) MOE_GQ_V(2, 4);
+  else MOE_GQ_V(2, 8);
+#undef MOE_GQ_V
+#undef MOE_GQ
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -17,6 +17,14 @@ struct Tile {
 
 hipError_t launch_gate_topk(const float* logits, int T, int E, int k,
                             int32_t* ids, float* w, hipStream_t s);
+// The gate fused with the per-token quantisation of x [T, H] bf16 (mx:
+// MXFP8 codes + e8m0 scales; else int8 codes + fp32 scales), for E <= 256
+// and (MX) H % 32 == 0 or (int8) H = 2048 or 4096 (gate_quant_ok).
+bool gate_quant_ok(int E, int H, bool mx);
+hipError_t launch_gate_topk_quant(const float* logits, int T, int E, int k,
+                                  int32_t* ids, float* w, const uint16_t* x,
+                                  int H, bool mx, void* xq, void* xs,
+                                  hipStream_t s);
 
 // Routing. chunk_counts has route_num_chunks(N) * E ints.
 int route_num_chunks(int N);

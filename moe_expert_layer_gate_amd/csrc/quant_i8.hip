@@ -17,36 +17,15 @@
 // (one read); longer rows are read twice.
 #include "common.h"
 #include "launch.h"
+#include "quant_row.h"
 
 namespace moe {
 
 namespace {
 
-template <bool F32>
-MOE_DEV void load8(const void* src, size_t off, float (&v)[8]) {
-  if (F32) {
-    const float4 a = *(const float4*)((const float*)src + off);
-    const float4 b = *(const float4*)((const float*)src + off + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    const uint4 a = *(const uint4*)((const uint16_t*)src + off);
-    v[0] = bf16_lo(a.x); v[1] = bf16_hi(a.x); v[2] = bf16_lo(a.y); v[3] = bf16_hi(a.y);
-    v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
-  }
-}
-
-MOE_DEV uint32_t code_byte(float v, float scale) {
-  float q = rintf(__fdiv_rn(v, scale));
-  q = fminf(fmaxf(q, -127.f), 127.f);
-  return (uint32_t)(int)q & 0xFFu;
-}
-
 // rows: offs == NULL: nrows rows, row r reads source row r. Otherwise the
 // R = offs[fe] - offs[fb] rows of the sorted copies of experts [fb, fe); row r
 // reads source row gidx[offs[fb] + r] / gk (gidx != NULL) or r.
-// CPL > 0: the row (at most 512 * CPL elements) is held in registers and read
-// once; CPL == 0: any length, read twice (amax, then codes).
 template <bool F32, int CPL>
 __global__ __launch_bounds__(256) void quant_i8_rows_kernel(
     const void* __restrict__ src, int K, int nrows,
@@ -61,64 +40,8 @@ __global__ __launch_bounds__(256) void quant_i8_rows_kernel(
   }
   if (r >= R) return;
   const int srow = gidx ? gidx[base + r] / gk : r;
-  const size_t so = (size_t)srow * K;
-  int8_t* orow = codes + (size_t)r * K;
-  float amax = 0.f;
-  if constexpr (CPL > 0) {
-    float v[CPL][8];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = 512 * i + 8 * lane;
-      if (c < K) {
-        load8<F32>(src, so + c, v[i]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[i][j] = 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    const float scale = __fdiv_rn(amax, 127.f);
-    if (lane == 0) scales[r] = scale;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = 512 * i + 8 * lane;
-      if (c >= K) break;
-      uint2 o = {0u, 0u};
-      if (scale > 0.f) {
-        o.x = code_byte(v[i][0], scale) | code_byte(v[i][1], scale) << 8 |
-              code_byte(v[i][2], scale) << 16 | code_byte(v[i][3], scale) << 24;
-        o.y = code_byte(v[i][4], scale) | code_byte(v[i][5], scale) << 8 |
-              code_byte(v[i][6], scale) << 16 | code_byte(v[i][7], scale) << 24;
-      }
-      *(uint2*)(orow + c) = o;
-    }
-    return;
-  }
-  for (int c = 8 * lane; c < K; c += 512) {
-    float v[8];
-    load8<F32>(src, so + c, v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const float scale = __fdiv_rn(amax, 127.f);
-  if (lane == 0) scales[r] = scale;
-  for (int c = 8 * lane; c < K; c += 512) {
-    uint2 o = {0u, 0u};
-    if (scale > 0.f) {
-      float v[8];
-      load8<F32>(src, so + c, v);
-      o.x = code_byte(v[0], scale) | code_byte(v[1], scale) << 8 |
-            code_byte(v[2], scale) << 16 | code_byte(v[3], scale) << 24;
-      o.y = code_byte(v[4], scale) | code_byte(v[5], scale) << 8 |
-            code_byte(v[6], scale) << 16 | code_byte(v[7], scale) << 24;
-    }
-    *(uint2*)(orow + c) = o;
-  }
+  quant_i8_row<F32, CPL>(src, K, (size_t)srow * K, codes + (size_t)r * K,
+                         scales + r, lane);
 }
 
 template <bool F32>

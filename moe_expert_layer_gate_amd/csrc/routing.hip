@@ -20,6 +20,7 @@
 //   gather  : one wave per routed row copies (or MXFP8-quantises) x[t]
 #include "common.h"
 #include "launch.h"
+#include "quant_row.h"
 
 namespace moe {
 
@@ -365,41 +366,8 @@ __global__ __launch_bounds__(256) void route_gather_kernel(
     for (int c = lane; c < H / 8; c += 64) dst[c] = src[c];
     return;
   }
-  uint8_t* dst = (uint8_t*)xp + (size_t)r * H;
-  uint8_t* dsc = xs + (size_t)r * (H / 32);
-  // eight 16-byte chunks per lane in flight before any encoding; a 32-value
-  // MX block is 4 consecutive chunks = 4 adjacent lanes (H % 32 == 0, so a
-  // block never straddles the end of the row)
-  for (int c0 = lane; c0 < H / 8; c0 += 512) {
-    uint4 v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = c0 + 64 * j;
-      v[j] = c < H / 8 ? src[c] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = c0 + 64 * j;
-      float f[8] = {bf16_lo(v[j].x), bf16_hi(v[j].x), bf16_lo(v[j].y),
-                    bf16_hi(v[j].y), bf16_lo(v[j].z), bf16_hi(v[j].z),
-                    bf16_lo(v[j].w), bf16_hi(v[j].w)};
-      float amax = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 1));
-      amax = fmaxf(amax, __shfl_xor(amax, 2));
-      const int s = mx_e4m3_scale_exp(amax);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= e4m3_encode_fast(f[i], s) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= e4m3_encode_fast(f[4 + i], s) << (8 * i);
-      if (c < H / 8) {
-        *(uint2*)(dst + (size_t)c * 8) = make_uint2(lo, hi);
-        if ((c & 3) == 0) dsc[c >> 2] = (uint8_t)(s + 127);
-      }
-    }
-  }
+  quant_mx_row_bf16(src, H, (uint8_t*)xp + (size_t)r * H,
+                    xs + (size_t)r * (H / 32), lane);
 }
 
 hipError_t launch_route_count(const int32_t* ids, int N, int E,

@@ -81,6 +81,10 @@ SMALL = {
     "prefill_w8a8_long_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_w8a8"),
                                       T=1200, H=384, I=384, n_ffn=8,
                                       local_end=8, top_k=4),
+    # W8A8 with H = 2048: x quantised per token inside the gate kernel
+    "decode_w8a8_h2048_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"),
+                                      T=40, H=2048, I=256, n_ffn=16,
+                                      local_end=16, top_k=4),
     # W8A8 on an expert range with 32-row streaming tiles
     "range_w8a8_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"), T=96,
                                H=256, I=256, n_ffn=16, local_begin=4,
@@ -302,7 +306,7 @@ def test_layer_split_calls_equal_fused():
                  "tiny_fp32", "decode_bf16_small", "decode_w8a8_small",
                  "prefill_w8a8_small", "prefill_w8a8_mid_small",
                  "prefill_long_small", "prefill_w8a8_long_small",
-                 "range_w8a8_small"):
+                 "decode_w8a8_h2048_small", "range_w8a8_small"):
         shape = SMALL[name]
         inp = generate(shape, seed=6, device=DEV)
         p = m.problem(shape)
