@@ -116,10 +116,12 @@ typedef struct moe_problem {
  *   F32 / BF16:  w13 [E_loc, H, 2I]   columns [0, I) = gate, [I, 2I) = up
  *                w2  [E_loc, I, H]
  *                (the merged gate/up matrix of [P1] "MoE TP优化 / 计算分解")
- *   MXFP4_E2M1:  w13 [E_loc, 2I, H/2] bytes, K (= H) contiguous per output
- *                column; rows [0, I) gate, [I, 2I) up
- *                w13_scale [E_loc, 2I, H/32] e8m0
- *                w2  [E_loc, H, I/2] bytes, w2_scale [E_loc, H, I/32] e8m0
+ *   MXFP4_E2M1:  w13 = W13 [E_loc, 2I, H/2] bytes (K = H per output
+ *                column, two codes per byte; columns [0, I) gate, [I, 2I)
+ *                up) and w2 = W2 [E_loc, H, I/2] bytes, each in the packed
+ *                order below (same byte count);
+ *                w13_scale [E_loc, 2I, H/32] e8m0 (not packed)
+ *                w2_scale [E_loc, H, I/32] e8m0 (not packed)
  *   INT8:        w13 = W13 [E_loc, 2I, H] int8 (K = H per output column;
  *                columns [0, I) gate, [I, 2I) up) and w2 = W2 [E_loc, H, I]
  *                int8, each in the packed order below (same byte count);
@@ -127,17 +129,18 @@ typedef struct moe_problem {
  *                w2_scale fp32 [E_loc, H]
  * Scale pointers must be NULL unless wt is MXFP4_E2M1 or INT8.
  *
- * Packed int8 weights: a static weight matrix W [E, N, K] (K contiguous per
- * output column n) is stored as fragments of 1 KB in the order
- * [E][K/128][N/16][2]; fragment (e, kb, n16, m) holds, at byte 16 * l
- * (l = 0..63), the 16 bytes
- * W[e, 16 * n16 + l % 16, 128 * kb + 64 * m + 16 * (l / 16) .. + 15]:
- * exactly what lane l of a wave feeds as the B operand of a
- * v_mfma_i32_16x16x64_i8 over K [128 kb + 64 m, + 64). Every weight load of
- * the int8 GEMMs then reads 1 KB contiguous (K-contiguous rows read 64
- * bytes per column per load otherwise, ~30 % below the streaming rate), and
- * the column groups of one K block sit next to each other.
- * moe_pack_int8_weights converts once, e.g. when the weights are loaded.
+ * Packed weights (MXFP4_E2M1 and INT8): a static weight matrix W [E, N, Kb]
+ * of bytes (Kb = K for int8, K/2 for e2m1; K contiguous per output column
+ * n) is stored as fragments of 1 KB in the order [E][Kb/64][N/16];
+ * fragment (e, c, n16) holds, at byte 16 * l (l = 0..63), the 16 bytes
+ * W[e, 16 * n16 + l % 16, 64 * c + 16 * (l / 16) .. + 15]: exactly what
+ * lane l of a wave feeds as the B operand of a v_mfma_i32_16x16x64_i8 (K
+ * bytes [64 c, + 64)) or of a scaled v_mfma_*_16x16x128_f8f6f4 (e2m1, K
+ * [128 c, + 128)), and one LDS copy instruction's worth for the tiled
+ * kernels. Every weight load of the quantised GEMMs then reads 1 KB
+ * contiguous (K-contiguous rows read 64 bytes per column per load
+ * otherwise, ~30 % below the streaming rate). moe_pack_weights converts
+ * once, e.g. when the weights are loaded.
  */
 
 /* Gating: [P1] "GMM使能和Routing优化 / 快速选择专家" (fused top-k + softmax
@@ -305,16 +308,17 @@ MOE_API moe_status moe_add_rms_norm_mx_quant(int32_t T, int32_t H,
                                              uint8_t* y_scales,
                                              void* residual_out, void* stream);
 
-/* Packs static int8 expert weights (the W8A8 routed experts of [P3]
- * "量化策略": int8 weights with fixed per-channel scales, prepared once)
- * into the packed order described above: src = W [E, N, K] int8 row-major,
- * dst = the same E * N * K bytes packed; dst must not overlap src. E >= 0
- * (E == 0 launches nothing), N > 0, K > 0 (else MOE_ERR_INVALID_ARG);
- * N % 16 == 0, K % 128 == 0, N * K < 2^31 (else MOE_ERR_UNSUPPORTED);
- * pointers 16-byte aligned. Stream-ordered; the caller owns both buffers. */
-MOE_API moe_status moe_pack_int8_weights(int32_t E, int32_t N, int32_t K,
-                                         const void* src, void* dst,
-                                         void* stream);
+/* Packs static quantised expert weights -- the W8A8 int8 experts ([P3]
+ * "量化策略": int8 weights with fixed per-channel scales) and the MXFP4
+ * experts of W4A8 ([P1] "MoE EP优化 / AllGather方案(W4A8量化)"), both prepared
+ * once -- into the packed order described above: src = W [E, N, K_bytes]
+ * row-major bytes, dst = the same E * N * K_bytes bytes packed; dst must not
+ * overlap src. E >= 0 (E == 0 launches nothing), N > 0, K_bytes > 0 (else
+ * MOE_ERR_INVALID_ARG); N % 16 == 0, K_bytes % 64 == 0,
+ * N * K_bytes < 2^31 (else MOE_ERR_UNSUPPORTED); pointers 16-byte aligned.
+ * Stream-ordered; the caller owns both buffers. */
+MOE_API moe_status moe_pack_weights(int32_t E, int32_t N, int32_t K_bytes,
+                                    const void* src, void* dst, void* stream);
 
 /* Router linear ([P1] "融合算子优化 / 融合RMSNorm Cast": the fp32 output of
  * the norm is the input of the gate computation): the logits of

@@ -23,7 +23,7 @@ __all__ = [
     "init_routing", "ffn_up", "ffn_down", "grouped_ffn", "finalize", "layer",
     "layer_workspace_bytes", "layer_traced", "SYMBOLS", "STAGES",
     "add_rms_norm_cast", "add_rms_norm_mx_quant", "router_logits",
-    "pack_int8_weights",
+    "pack_weights",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -35,7 +35,7 @@ _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8_E4M3,
 SYMBOLS = ["moe_gate_topk", "moe_init_routing", "moe_grouped_ffn", "moe_ffn_up",
            "moe_ffn_down", "moe_finalize", "moe_layer", "moe_layer_traced",
            "moe_add_rms_norm_cast", "moe_add_rms_norm_mx_quant",
-           "moe_router_logits", "moe_pack_int8_weights", "moe_status_string",
+           "moe_router_logits", "moe_pack_weights", "moe_status_string",
            "moe_abi_version"]
 
 # stages of moe_layer_traced, in launch order
@@ -92,7 +92,7 @@ def lib() -> ctypes.CDLL:
     sig["moe_add_rms_norm_mx_quant"] = [_i32, _i32, _vp, _vp, _vp, _f32, _vp,
                                         _vp, _vp, _vp]
     sig["moe_router_logits"] = [_i32, _i32, _i32, _vp, _vp, _vp, _vp]
-    sig["moe_pack_int8_weights"] = [_i32, _i32, _i32, _vp, _vp, _vp]
+    sig["moe_pack_weights"] = [_i32, _i32, _i32, _vp, _vp, _vp]
     for name, args in sig.items():
         f = getattr(L, name)
         f.argtypes = args
@@ -362,13 +362,14 @@ def router_logits(y, w_router, out=None):
     return out
 
 
-def pack_int8_weights(w, out=None):
-    """int8 expert weights [E, N, K] (K contiguous) -> the packed order the
-    int8 GEMMs read (same shape and bytes; see moe_pack_int8_weights)."""
-    if w.dim() != 3 or w.dtype != torch.int8:
-        raise ValueError("w must be an [E, N, K] int8 tensor")
-    E, N, K = w.shape
+def pack_weights(w, out=None):
+    """Quantised expert weights -- int8 [E, N, K] or MXFP4 codes uint8
+    [E, N, K/2], K contiguous -> the packed order the int8 and MX GEMMs read
+    (same shape and bytes; see moe_pack_weights)."""
+    if w.dim() != 3 or w.dtype not in (torch.int8, torch.uint8):
+        raise ValueError("w must be an [E, N, K_bytes] int8 or uint8 tensor")
+    E, N, Kb = w.shape
     if out is None:
         out = torch.empty_like(w)
-    _check(lib().moe_pack_int8_weights(E, N, K, _ptr(w), _ptr(out), _stream()))
+    _check(lib().moe_pack_weights(E, N, Kb, _ptr(w), _ptr(out), _stream()))
     return out

@@ -484,18 +484,20 @@ moe_status moe_add_rms_norm_mx_quant(int32_t T, int32_t H, const void* x,
       y_scales, (uint16_t*)residual_out, (hipStream_t)stream));
 }
 
-moe_status moe_pack_int8_weights(int32_t E, int32_t N, int32_t K,
-                                 const void* src, void* dst, void* stream) {
-  if (E < 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
-  if (N % 16 || K % 128 || (long long)N * K >= (1LL << 31))
+moe_status moe_pack_weights(int32_t E, int32_t N, int32_t K_bytes,
+                            const void* src, void* dst, void* stream) {
+  if (E < 0 || N <= 0 || K_bytes <= 0) return MOE_ERR_INVALID_ARG;
+  if (N % 16 || K_bytes % 64 || (long long)N * K_bytes >= (1LL << 31))
     return MOE_ERR_UNSUPPORTED;
   if (E == 0) return MOE_OK;
   if (!src || !dst || !aligned16(src, dst)) return MOE_ERR_INVALID_ARG;
   const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
-  const uintptr_t n = (uintptr_t)E * N * K;
+  const uintptr_t n = (uintptr_t)E * N * K_bytes;
   if (a < b + n && b < a + n) return MOE_ERR_INVALID_ARG;  // overlap
-  return hip_status(moe::launch_pack_int8(E, N, K, (const int8_t*)src,
-                                          (int8_t*)dst, (hipStream_t)stream));
+  return hip_status(moe::launch_pack_weights(E, N, K_bytes,
+                                             (const uint8_t*)src,
+                                             (uint8_t*)dst,
+                                             (hipStream_t)stream));
 }
 
 moe_status moe_router_logits(int32_t T, int32_t H, int32_t E, const float* y,

@@ -197,8 +197,8 @@ MOE_DEV void tiled_item(
   // lane/32 of the step, physical piece lane%32 holds logical piece
   // (lane%32) ^ swz_b(k); the swizzle only depends on k%4 = 2*(wave&1) +
   // lane/32 (NW is even), the same for all j.
-  // B (int8, packed: 1 KB fragments per K block of 128, 16 columns and
-  // half m, 16 bytes of column c, K piece p at 16 * (c + 16 p)), instruction j
+  // B (int8, packed: 1 KB fragments per 64-byte K chunk and 16 columns,
+  // 16 bytes of column c, K piece p at 16 * (c + 16 p)), instruction j
   // (0..NB-1): the fragment of tile columns 16*(wave + NW*j) .. +15 for this
   // step, copied as it is (lane l takes bytes 16 l, one contiguous 1 KB), so
   // LDS holds [16-column group][piece][column] -- the MFMA reads (32 lanes
@@ -209,7 +209,7 @@ MOE_DEV void tiled_item(
   if constexpr (I8) {
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      b_off[j] = (uint32_t)wcol(16 * (wave + NW * j)) / 16 * 2048u + 16u * lane;
+      b_off[j] = (uint32_t)wcol(16 * (wave + NW * j)) / 16 * 1024u + 16u * lane;
   } else {
     const int kr = 2 * wave + (lane >> 5);
     const int cl = (lane & 31) ^ swz_b(kr);
@@ -219,7 +219,10 @@ MOE_DEV void tiled_item(
       lds_addr(smem + (16 * wave) * (BK * 2)));
   const uint32_t b_dst = __builtin_amdgcn_readfirstlane(lds_addr(
       smem + A_BYTES + (I8 ? 16 * wave * 64 : (2 * wave) * B_ROW)));
-  const size_t b_step = (size_t)BK * Nw * 2;     // bytes per K step of B
+  // bytes per K step of B: 32 rows of bf16 [K, N]; for int8 one packed
+  // 64-byte K chunk of all N / 16 column groups (32-bit: N * K < 2^31)
+  const size_t b_step = (size_t)BK * Nw * 2;
+  const uint32_t b_step_i8 = (uint32_t)Nw * 64u;
   const uint32_t b_rowj = 2u * NW * Nw * 2;     // 2*NW k-rows of B
 
   // loads of K step s_ into stage st_ (NI instructions per wave)
@@ -230,8 +233,7 @@ MOE_DEV void tiled_item(
     _Pragma("unroll") for (int j = 0; j < NA; ++j)                            \
       g2lds(ab_, a_off[j], a_dst + o_ + 16 * NW * j * (BK * 2));              \
     if constexpr (I8) {                                                       \
-      /* K block s/2 (N/16 groups of 2 KB), half s%2 */                      \
-      const char* bb_ = we + (size_t)((s_) >> 1) * Nw * 128 + ((s_) & 1) * 1024; \
+      const char* bb_ = we + (uint32_t)(s_) * b_step_i8;                      \
       _Pragma("unroll") for (int j = 0; j < NB; ++j)                          \
         g2lds(bb_, b_off[j], b_dst + o_ + 16 * NW * j * 64);                  \
     } else {                                                                  \

@@ -16,9 +16,10 @@
 // lanes hold the same K offsets, so the two MFMAs sum every K of the step
 // exactly, whatever order the hardware takes them in. Activation rows are
 // K-contiguous and read in place; the weights come packed (one 1 KB
-// fragment per K block of 128, 16 columns and m, in exactly this lane
-// order, column groups of a K block adjacent), so every weight load of a
-// wave reads 1 KB contiguous.
+// fragment per 64-byte K chunk and 16 columns, in exactly this lane order,
+// the column groups of a chunk adjacent: chunk c of group n16 at
+// c * N * 64 + n16 * 1024), so every weight load of a wave reads 1 KB
+// contiguous; MFMA m of step s takes chunk 2s + m.
 //
 // Each lane carries 8 groups of 16 weight columns: for GEMM1 4 gate groups and
 // the 4 matching up groups (64 h columns per block, SwiGLU lane-local), for
@@ -77,7 +78,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_stream_kernel(
     cok[gi] = c < Nout;
     col[gi] = cok[gi] ? ((GLU && gi >= 4) ? Nout + c : c) : 0;
     const int n16 = cok[gi] ? (col[gi] - g) / 16 : 0;  // group's column / 16
-    frag[gi] = (uint32_t)n16 * 2048u + 16u * lane;
+    frag[gi] = (uint32_t)n16 * 1024u + 16u * lane;
   }
   // A rows are resolved after the first step's weight loads are issued
   // (the gather index is two dependent loads away)
@@ -105,10 +106,9 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_stream_kernel(
   auto load_w = [&](Stage& st, int s) {
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      // K block s: the N/16 column groups of 2 KB each
-      const int8_t* p = we + frag[gi] + (size_t)s * Nw * 128;
+      const int8_t* p = we + frag[gi] + (size_t)(2 * s) * Nw * 64;
       st.b[gi][0] = *(const uint4*)p;
-      st.b[gi][1] = *(const uint4*)(p + 1024);
+      st.b[gi][1] = *(const uint4*)(p + (size_t)Nw * 64);
     }
   };
   auto load_a = [&](Stage& st, int s) {

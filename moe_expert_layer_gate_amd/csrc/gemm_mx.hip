@@ -52,12 +52,15 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_mx_kernel(
 
   int col[NG];
   bool cok[NG];
+  uint32_t frag[NG];
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
     int c = GLU ? c0 + 16 * (gi & 3) + g : c0 + 16 * gi + g;
     cok[gi] = c < Nout;
     col[gi] = (GLU && gi >= 4) ? Nout + c : c;  // up columns at +I
     if (!cok[gi]) col[gi] = 0;
+    // packed codes: chunk c of 16-column group n16 at c * Nw * 64 + n16 KB
+    frag[gi] = (uint32_t)(cok[gi] ? (col[gi] - g) / 16 : 0) * 1024u + 16u * lane;
   }
   int arow[RG];
   bool aok[RG];
@@ -94,7 +97,8 @@ __global__ __launch_bounds__(64 * KSPLIT) void gemm_mx_kernel(
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       // columns past N read column 0: their outputs are never stored
-      uint4 v = *(const uint4*)(we + (size_t)col[gi] * (K / 2) + kblk * 16);
+      // lane l: column l%16, K block 4s + l/16 of its 64-byte step chunk
+      uint4 v = *(const uint4*)(we + (size_t)s * Nw * 64 + frag[gi]);
       int bsc = wse[(size_t)col[gi] * KB + kblk];
       i32x8 bf = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
 #pragma unroll

@@ -14,8 +14,11 @@
 //   * A (e4m3 codes): LDS [row][8 x 16 B], the 16-byte piece index XOR-ed
 //     with (row / 2) % 8: with 128-byte rows, the 16 rows one MFMA operand
 //     read touches then cover all 64 banks once (row parity picks the half);
-//   * B (e2m1 codes): LDS [column][4 x 16 B], piece index XOR-ed with
-//     (column / 4) % 4 for the same reason;
+//   * B (e2m1 codes, packed: 1 KB fragments of 16 columns x one 64-byte K
+//     step, 16 bytes of column c, K piece p at 16 (16 p + c)): each copy
+//     instruction moves one fragment as it is (one contiguous 1 KB), so LDS
+//     holds [16-column group][piece][column]; 16 consecutive lanes reading
+//     16 consecutive columns of one piece touch 256 contiguous bytes;
 //   * the e8m0 scales have a two-slot ring of their own. When K/32 is a
 //     multiple of 16, one 16-byte copy per row (and per column) brings the
 //     scales of four K steps at once -- a copy per row or column costs an L2
@@ -127,16 +130,15 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   // ---- copy assignment: instruction j (0..3) of a wave moves 1 KB.
   // A: rows 8*(4j + wave) + lane/8, physical piece lane%8 <- logical piece
   //    (lane%8) ^ ((row/2)%8); (row/2)%8 = 4*(wave%2) + lane/16 here.
-  // B: columns 16*(4j + wave) + lane/4, physical piece lane%4 <- logical
-  //    piece (lane%4) ^ ((column/4)%4); (column/4)%4 = (lane/16)%4 here.
+  // B: the packed fragment of tile columns 16*(4j + wave) .. +15, lane l
+  //    taking bytes 16 l.
   uint32_t a_off[4], b_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 8 * (4 * j + wave) + (lane >> 3);
     a_off[j] = (uint32_t)arow(r) * K +
                16 * ((lane & 7) ^ (4 * (wave & 1) + (lane >> 4)));
-    const int t = 16 * (4 * j + wave) + (lane >> 2);
-    b_off[j] = (uint32_t)wcol(t) * (K / 2) + 16 * ((lane & 3) ^ (lane >> 4));
+    b_off[j] = (uint32_t)wcol(16 * (4 * j + wave)) / 16 * 1024u + 16u * lane;
   }
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds0 + 8 * wave * MBK);
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
 #define MOE_MX_ISSUE(s_, st_)                                                 \
   do {                                                                        \
     const uint8_t* ab_ = a_tile + (size_t)(s_) * MBK;                         \
-    const uint8_t* bb_ = we + (size_t)(s_) * (MBK / 2);                       \
+    const uint8_t* bb_ = we + (size_t)(s_) * Nw * (MBK / 2);                  \
     const uint32_t o_ = (st_) * MSTAGE;                                       \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
       g2lds(ab_, a_off[j], a_dst + o_ + 32 * j * MBK);                        \
@@ -189,8 +191,9 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   auto bcol = [&](int g) -> int {
     return (g < 4 ? 0 : MBNW / 2) + wn * 64 + (g & 3) * 16 + lr;
   };
+  // packed B in LDS: [16-column group][piece][column], 16 B each
   const uint32_t b_rd =
-      lds0 + MA_BYTES + bcol(0) * (MBK / 2) + 16 * (q ^ (lr >> 2));
+      lds0 + MA_BYTES + (bcol(0) - lr) * (MBK / 2) + 16 * (16 * q + lr);
 
   // scale bytes of this lane: row wm*64 + 16*mb + lane%16 and tile column
   // bcol(g), byte 4*(s % SCB) + q of the slot (K block 4s + q)
@@ -386,8 +389,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx32_tiled_kernel(
     const int r = 8 * (4 * j + wave) + (lane >> 3);
     a_off[j] = (uint32_t)arow(r) * K +
                16 * ((lane & 7) ^ (4 * (wave & 1) + (lane >> 4)));
-    const int t = 16 * (4 * j + wave) + (lane >> 2);
-    b_off[j] = (uint32_t)wcol(t) * (K / 2) + 16 * ((lane & 3) ^ (lane >> 4));
+    b_off[j] = (uint32_t)wcol(16 * (4 * j + wave)) / 16 * 1024u + 16u * lane;
   }
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds0 + 8 * wave * MBK);
@@ -404,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx32_tiled_kernel(
 #define MOE_MX_ISSUE(s_, st_)                                                 \
   do {                                                                        \
     const uint8_t* ab_ = a_tile + (size_t)(s_) * MBK;                         \
-    const uint8_t* bb_ = we + (size_t)(s_) * (MBK / 2);                       \
+    const uint8_t* bb_ = we + (size_t)(s_) * Nw * (MBK / 2);                  \
     const uint32_t o_ = (st_) * MSTAGE;                                       \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
       g2lds(ab_, a_off[j], a_dst + o_ + 32 * j * MBK);                        \
@@ -427,18 +429,20 @@ __global__ __launch_bounds__(256, 2) void gemm_mx32_tiled_kernel(
   // ---- operand reads. Lane l: r32 = l%32, q = l/32.
   // A block mb: row wm*64 + 32*mb + r32 (its (row/2)%8 = (r32/2)%8), logical
   // pieces 4s + q and 4s + 2 + q of the 128-byte step row.
-  // B block nb: tile column bcol(nb) (its (col/4)%4 = (r32/4)%4), logical
-  // piece 2s + q of the 64-byte step row.
-  // Physical piece of logical piece c (bit 0 = q): c ^ swizzle = (c - q) ^
-  // (q ^ swizzle); the row / column base is 128- / 64-byte aligned, so the
-  // lane's base ORed with 16 * (q ^ swizzle) only needs the compile-time
+  // B block nb: tile column bcol(nb), piece 2s + q of the 64-byte step
+  // chunk (packed LDS layout, no swizzle).
+  // A: physical piece of logical piece c (bit 0 = q): c ^ swizzle =
+  // (c - q) ^ (q ^ swizzle); the row base is 128-byte aligned, so the lane's
+  // base ORed with 16 * (q ^ swizzle) only needs the compile-time
   // 16 * (c - q) XORed in per read.
   const int r32 = lane & 31, q = lane >> 5;
   const uint32_t a_rd =
       (lds0 + (wm * 64 + r32) * MBK) | (16 * (q ^ ((r32 >> 1) & 7)));
   auto bcol = [&](int n) -> int { return wn * 128 + n * 32 + r32; };
-  const uint32_t b_rd = (lds0 + MA_BYTES + bcol(0) * (MBK / 2)) |
-                        (16 * (q ^ ((r32 >> 2) & 3)));
+  // packed B in LDS: [16-column group][piece][column]; piece 2s + q of
+  // column bcol(n) at group (bcol/16) KB + 16 (16 (2s + q) + bcol % 16)
+  const uint32_t b_rd = lds0 + MA_BYTES + (bcol(0) & ~15) * (MBK / 2) +
+                        16 * (16 * q + (bcol(0) & 15));
   // scale words: row / column, bytes 4*(t % SCB) .. +3 of the slot
   const uint32_t sa_rd = ss0 + (wm * 64 + r32) * S::ROW;
   const uint32_t sb_rd = ss0 + S::SB + bcol(0) * S::ROW;
@@ -483,7 +487,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx32_tiled_kernel(
     }                                                                         \
     _Pragma("unroll") for (int n = 0; n < 4; ++n) {                           \
       const u32x4_t v_ = lds_read_b128(                                       \
-          (b_rd + so_ + (bcol(n) - bcol(0)) * (MBK / 2)) ^ (32 * (ss_)));     \
+          b_rd + so_ + (bcol(n) - bcol(0)) * (MBK / 2) + 512 * (ss_));        \
       fb_[n] = i32x8{(int)v_.x, (int)v_.y, (int)v_.z, (int)v_.w, 0, 0, 0, 0}; \
     }                                                                         \
   } while (0)

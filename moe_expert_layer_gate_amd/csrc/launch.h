@@ -113,9 +113,10 @@ hipError_t launch_gemm_i8_stream(bool glu, int rg, const Tile* tiles,
 // from source row r. Else the R = offs[fe] - offs[fb] (<= nrows) rows of the
 // copies of experts [fb, fe), row r from source row gidx[offs[fb] + r] / gk
 // (gidx != NULL) or r.
-// Packed int8 weights (fragment order of the int8 GEMMs) from [E, N, K].
-hipError_t launch_pack_int8(int E, int N, int K, const int8_t* src,
-                            int8_t* dst, hipStream_t s);
+// Packed weights (fragments of 16 columns x 64 bytes, [E][Kb/64][N/16]) from
+// byte matrices [E, N, Kb] (int8 codes, or two e2m1 codes per byte).
+hipError_t launch_pack_weights(int E, int N, int Kb, const uint8_t* src,
+                               uint8_t* dst, hipStream_t s);
 hipError_t launch_quant_i8_rows(bool f32, const void* src, int K, int nrows,
                                 const int32_t* gidx, const int32_t* offs,
                                 int fb, int fe, int gk, int8_t* codes,

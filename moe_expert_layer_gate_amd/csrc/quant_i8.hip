@@ -69,36 +69,35 @@ hipError_t launch_rows(int cpl, dim3 grid, hipStream_t s, const void* src,
 
 }  // namespace
 
-// Packed int8 weights: thread i moves 16-byte fragment piece i. Piece i of
-// the packed buffer is lane l = i % 64 of fragment f = i / 64, fragment
-// f = ((e * K/128 + kb) * N/16 + n16) * 2 + m; it holds row 16 * n16 + l % 16,
-// bytes [128 kb + 64 m + 16 (l / 16), + 16) of expert e's [N, K] matrix.
-// Writes are contiguous; reads gather 16 bytes per lane (a one-time step).
-__global__ __launch_bounds__(256) void pack_int8_kernel(
-    const int8_t* __restrict__ src, int8_t* __restrict__ dst, long long npieces,
-    int N, int K) {
+// Packed weights: thread i moves 16-byte fragment piece i. Piece i of the
+// packed buffer is lane l = i % 64 of fragment f = i / 64,
+// f = (e * Kb/64 + c) * N/16 + n16; it holds row 16 * n16 + l % 16, bytes
+// [64 c + 16 (l / 16), + 16) of expert e's [N, Kb] byte matrix. Writes are
+// contiguous; reads gather 16 bytes per lane (a one-time step).
+__global__ __launch_bounds__(256) void pack_weights_kernel(
+    const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+    long long npieces, int N, int Kb) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= npieces) return;
   const int l = (int)(i & 63);
   long long f = i >> 6;
-  const int m = (int)(f & 1);
-  f >>= 1;
   const int n16 = (int)(f % (N / 16));
   f /= N / 16;
-  const int kbn = K / 128;
-  const int kb = (int)(f % kbn);
-  const long long e = f / kbn;
-  const long long so = (e * N + 16 * n16 + (l & 15)) * (long long)K + 128 * kb +
-                       64 * m + 16 * (l >> 4);
+  const int nc = Kb / 64;
+  const int c = (int)(f % nc);
+  const long long e = f / nc;
+  const long long so = (e * N + 16 * n16 + (l & 15)) * (long long)Kb + 64 * c +
+                       16 * (l >> 4);
   *(uint4*)(dst + 16 * i) = *(const uint4*)(src + so);
 }
 
-hipError_t launch_pack_int8(int E, int N, int K, const int8_t* src,
-                            int8_t* dst, hipStream_t s) {
-  const long long npieces = (long long)E * N * K / 16;
+hipError_t launch_pack_weights(int E, int N, int Kb, const uint8_t* src,
+                               uint8_t* dst, hipStream_t s) {
+  const long long npieces = (long long)E * N * Kb / 16;
   if (npieces == 0) return hipSuccess;
-  hipLaunchKernelGGL(pack_int8_kernel, dim3((unsigned)((npieces + 255) / 256)),
-                     dim3(256), 0, s, src, dst, npieces, N, K);
+  hipLaunchKernelGGL(pack_weights_kernel,
+                     dim3((unsigned)((npieces + 255) / 256)), dim3(256), 0, s,
+                     src, dst, npieces, N, Kb);
   return hipGetLastError();
 }
 

@@ -10,17 +10,18 @@ import oracle as O
 
 
 def generate(shape, *args, **kwargs):
-    """The seeded inputs of moe_inputs.generate; int8 expert weights on a GPU
-    are handed to the library packed (the form its int8 GEMMs take, made by
-    the library's own pack call), and the row-major originals stay under
-    "w13_rowmajor" / "w2_rowmajor" for the oracle."""
+    """The seeded inputs of moe_inputs.generate; quantised (int8, MXFP4)
+    expert weights on a GPU are handed to the library packed (the form its
+    int8 and MX GEMMs take, made by the library's own pack call), and the
+    row-major originals stay under "w13_rowmajor" / "w2_rowmajor" for the
+    oracle."""
     inp = moe_inputs.generate(shape, *args, **kwargs)
     w13 = inp.get("w13")
-    if shape.wt == "int8" and w13 is not None and w13.is_cuda:
+    if shape.wt in ("int8", "mxfp4") and w13 is not None and w13.is_cuda:
         import moe_expert_layer_gate_amd as m
         for k in ("w13", "w2"):
             inp[k + "_rowmajor"] = inp[k]
-            inp[k] = m.pack_int8_weights(inp[k])
+            inp[k] = m.pack_weights(inp[k])
     return inp
 
 
@@ -32,7 +33,8 @@ def weight_getter(shape, inp):
     """Lazy per-expert fp64 weights from (possibly device-resident) tensors."""
     fb = shape.ffn_begin
     if shape.wt == "mxfp4":
-        w13, s13, w2, s2 = inp["w13"], inp["w13_scale"], inp["w2"], inp["w2_scale"]
+        w13, w2 = inp.get("w13_rowmajor", inp["w13"]), inp.get("w2_rowmajor", inp["w2"])
+        s13, s2 = inp["w13_scale"], inp["w2_scale"]
 
         def get(e):
             i = e - fb

@@ -224,14 +224,14 @@ def test_misaligned_pointers_rejected(L):
                                        None, None) == 1
 
 
-def test_pack_int8_host_checks(L):
+def test_pack_weights_host_checks(L):
     ok = ctypes.c_void_p(1 << 20)
     far = ctypes.c_void_p(1 << 30)
-    pk = L.moe_pack_int8_weights
+    pk = L.moe_pack_weights
     assert pk(-1, 32, 128, ok, far, None) == 1
     assert pk(2, 0, 128, ok, far, None) == 1
     assert pk(2, 24, 128, ok, far, None) == 2         # N % 16
-    assert pk(2, 32, 192, ok, far, None) == 2         # K % 128
+    assert pk(2, 32, 96, ok, far, None) == 2          # K_bytes % 64
     assert pk(2, 1 << 16, 1 << 15, ok, far, None) == 2  # N * K >= 2^31
     assert pk(2, 32, 128, None, far, None) == 1
     assert pk(2, 32, 128, ok, ctypes.c_void_p((1 << 30) + 8), None) == 1  # misaligned

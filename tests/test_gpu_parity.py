@@ -513,17 +513,20 @@ def test_layer_full_size_sampled(name):
     assert torch.isfinite(out.float()).all()
 
 
-@pytest.mark.parametrize("E,N,K", [(3, 48, 256), (1, 16, 128), (2, 1536, 2048)])
-def test_pack_int8_weights(E, N, K):
-    """The packed int8 weight order, byte for byte: fragments in the order
-    [e][kb][n16][m]; lane l of fragment (e, kb, n16, m) holds
-    W[e, 16 n16 + l % 16, 128 kb + 64 m + 16 (l / 16) .. + 15]."""
+@pytest.mark.parametrize("E,N,Kb,dt", [(3, 48, 256, torch.int8),
+                                       (1, 16, 64, torch.uint8),
+                                       (2, 1536, 2048, torch.int8),
+                                       (2, 3072, 2048, torch.uint8)])
+def test_pack_weights(E, N, Kb, dt):
+    """The packed weight order, byte for byte: fragments in the order
+    [e][c][n16]; lane l of fragment (e, c, n16) holds
+    W[e, 16 n16 + l % 16, 64 c + 16 (l / 16) .. + 15]."""
     m = _m()
-    g = torch.Generator().manual_seed(E * 1000 + N + K)
-    w = torch.randint(-127, 128, (E, N, K), generator=g, dtype=torch.int8)
-    got = m.pack_int8_weights(w.to(DEV))
+    g = torch.Generator().manual_seed(E * 1000 + N + Kb)
+    w = torch.randint(-128, 128, (E, N, Kb), generator=g, dtype=torch.int16).to(dt)
+    got = m.pack_weights(w.to(DEV))
     torch.cuda.synchronize()
-    W = w.numpy().reshape(E, N // 16, 16, K // 128, 2, 4, 16)
-    # -> [e][kb][n16][m][q][col][16 bytes]; lane l = 16 q + col
-    want = W.transpose(0, 3, 1, 4, 5, 2, 6).reshape(E, N, K)
+    W = w.numpy().reshape(E, N // 16, 16, Kb // 64, 4, 16)
+    # [e][n16][col][c][q][16 bytes] -> [e][c][n16][q][col][16]; lane = 16 q + col
+    want = W.transpose(0, 3, 1, 4, 2, 5).reshape(E, N, Kb)
     assert np.array_equal(got.cpu().numpy(), want)
