@@ -57,13 +57,14 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_stream_kernel(
   constexpr int SLAB = GLU ? 64 : 128;  // output columns per block
   // tile entry and count read together (entries past the count are in
   // bounds, merely stale); the empty asm keeps both ahead of the exit test
-  const Tile tl = tiles[blockIdx.x];
+  // grid: x = column slab, y = tile (consecutive blocks: one expert's slabs)
+  const Tile tl = tiles[blockIdx.y];
   const int ntiles = tile_count[0];
   asm volatile("" ::"s"(ntiles), "s"(tl.expert), "s"(tl.row0), "s"(tl.rows));
-  if ((int)blockIdx.x >= ntiles) return;
+  if ((int)blockIdx.y >= ntiles) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane & 15, q = lane >> 4;
-  const int c0 = blockIdx.y * SLAB;
+  const int c0 = blockIdx.x * SLAB;
   const int8_t* we = w + (size_t)tl.expert * Nw * K;
 
   // Columns past N and rows past the tile only feed outputs that are never
@@ -248,7 +249,8 @@ hipError_t launch_gemm_i8_stream(bool glu, int rg, const Tile* tiles,
                                  int gk, hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
   const int slab = glu ? 64 : 128;
-  dim3 grid(max_tiles, (Nout + slab - 1) / slab);
+  // (max_tiles < 65536: this schedule serves fewer than 64 rows per expert)
+  dim3 grid((Nout + slab - 1) / slab, max_tiles);
   // a step of 128 K moves as many weight bytes per wave (16 KB) as a bf16
   // step of 32, so the bf16 kernel's split rule applies in these steps
   const int ksplit = stream_ksplit((long long)grid.x * grid.y, K / 128, rg);
