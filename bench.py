@@ -69,15 +69,15 @@ TRAFFIC = {
     # workload: (kernel source set, sha256[:16] of its sources, FETCH KiB,
     #            WRITE KiB) per GEMM1 dispatch
     "qwen3_30b_a3b_decode_bf16":
-        ("gemm_bf16_stream", "c2d6d095ac0bf990", 342578.3, 384.0),
+        ("gemm_bf16_stream", "eb5dc45129abba45", 342332.7, 384.0),
     "qwen3_30b_a3b_prefill_skewed_bf16":
         ("gemm_bf16_tiled", "ec4346a119d21336", 594356.3, 49152.0),
     "longcat_flash_zero_experts_bf16":
-        ("gemm_bf16_stream", "c2d6d095ac0bf990", 13560901.9, 32528.0),
+        ("gemm_bf16_stream", "eb5dc45129abba45", 13281945.9, 32528.0),
     "qwen3_235b_a22b_ep_rank_w4a8":
         ("gemm_mx_tiled", "f992f0c5fedf635a", 200173.3, 12804.4),
     "qwen3_30b_a3b_decode_w8a8":
-        ("gemm_i8_stream", "3680b9e5f214f356", 171398.5, 772.7),
+        ("gemm_i8_stream", "85089ab032197951", 171374.9, 768.4),
     "qwen3_30b_a3b_prefill_skewed_w8a8":
         ("gemm_bf16_tiled", "ec4346a119d21336", 248924.8, 98304.0),
 }
