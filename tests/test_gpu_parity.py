@@ -176,12 +176,15 @@ def test_init_routing_small(name):
 
 
 @pytest.mark.parametrize("T,E,k", [(50, 2048, 2), (600, 2048, 64), (64, 1024, 64),
-                                   (65, 1024, 64), (4096, 1, 1)])
+                                   (65, 1024, 64), (4096, 1, 1), (1000, 300, 7),
+                                   (4096, 512, 32), (5000, 96, 1)])
 def test_init_routing_max_sizes(T, E, k):
     """The largest expert count and top-k the library takes (2048 experts
-    route through the multi-block kernels), and both sides of the
+    route through the count / scan / scatter kernels), both sides of the
     single-block routing limit of 4096 copies and 1024 experts (64 x 64
-    copies is the last on the single-block side, 65 x 64 the first past it)."""
+    copies is the last on the single-block side, 65 x 64 the first past it),
+    and multi-block routing with a ragged last chunk and 300 experts, 512
+    chunks with 512 experts, and one copy per token."""
     m = _m()
     g = torch.Generator().manual_seed(T * 31 + E + k)
     L = torch.randn(T, E, generator=g)
