@@ -56,16 +56,22 @@ size_t act_bytes(const Prob& q) { return q.act == MOE_F32 ? 4 : 2; }
 
 // Tile height of the grouped GEMM chosen for the problem, from the expected
 // rows per expert: weight-streaming tiles of 16 or 32 rows for decode-size
-// batches, LDS-tiled MFMA tiles of 128 rows for prefill-size batches and of
-// 256 rows (bf16 and int8) once experts average 512 rows or more. (256-row
-// tiles are 6-11 % faster when most rows sit in full tiles, but slower than
-// 128-row ones at 256 rows per expert under skewed routing, where the many
-// partial tiles leave half of their waves without rows.)
+// batches, LDS-tiled MFMA tiles of 128 rows beyond them and of 256 rows
+// (bf16 and int8) once experts average 512 rows or more. (256-row tiles are
+// 6-11 % faster when most rows sit in full tiles, but slower than 128-row
+// ones at 256 rows per expert under skewed routing, where the many partial
+// tiles leave half of their waves without rows.) The streaming kernels read
+// an expert's weights once per tile they run, the tiled ones once per 128
+// rows, so the tiled kernels take over from a few rows per expert on: from
+// 8 for MXFP4 weights, 12 for int8 and 20 for bf16 (the measured crossovers
+// on the 2048 x 768 and 4096 x 1536 expert shapes; with 6144 x 2048 bf16
+// experts streaming 32-row tiles was still 4.6 % faster at 16 rows).
 int tile_rows(const Prob& q) {
   if (q.act == MOE_F32) return 32;
   const long long avg = q.E ? q.N / q.E : 0;  // expected rows per expert
   if (avg >= 512 && !q.mx) return 256;
-  if (avg >= 64) return 128;
+  const long long tiled_from = q.mx ? 8 : q.i8 ? 12 : 20;
+  if (avg >= tiled_from) return 128;
   return avg <= 12 ? 16 : 32;
 }
 

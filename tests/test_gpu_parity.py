@@ -85,10 +85,23 @@ SMALL = {
     "decode_w8a8_h2048_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"),
                                       T=40, H=2048, I=256, n_ffn=16,
                                       local_end=16, top_k=4),
-    # W8A8 on an expert range with 32-row streaming tiles
+    # W8A8 on an expert range, about 24 rows per expert: 128-row tiles
     "range_w8a8_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"), T=96,
                                H=256, I=256, n_ffn=16, local_begin=4,
                                local_end=10, top_k=4),
+    # W8A8 on an expert range, 10 rows per expert: 16-row streaming tiles
+    "range_w8a8_stream_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"),
+                                      T=40, H=256, I=256, n_ffn=16,
+                                      local_begin=4, local_end=10, top_k=4),
+    # bf16 with 16 rows per expert: 32-row streaming tiles
+    "decode_bf16_32row_small": scaled(get_workload("qwen3_30b_a3b_decode_bf16"),
+                                      T=64, H=512, I=384, n_ffn=16,
+                                      local_end=16, top_k=4),
+    # W4A8 decode-size on an expert range, 6 rows per expert: the
+    # weight-streaming scaled-MFMA kernel
+    "ep_w4a8_decode_small": scaled(get_workload("qwen3_235b_a22b_ep_rank_w4a8"),
+                                   T=24, H=512, I=256, n_ffn=16, local_begin=4,
+                                   local_end=8, top_k=4),
 }
 
 
