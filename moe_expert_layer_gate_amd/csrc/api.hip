@@ -63,15 +63,17 @@ size_t act_bytes(const Prob& q) { return q.act == MOE_F32 ? 4 : 2; }
 // tiles leave half of their waves without rows.) The streaming kernels read
 // an expert's weights once per tile they run, the tiled ones once per 128
 // rows, so the tiled kernels take over from a few rows per expert on: from
-// 8 for MXFP4 weights, 12 for int8 and 20 for bf16 (the measured crossovers
-// on the 2048 x 768 and 4096 x 1536 expert shapes; with 6144 x 2048 bf16
-// experts streaming 32-row tiles was still 4.6 % faster at 16 rows).
+// 12 for int8 and 20 for bf16 (the measured crossovers on the 2048 x 768
+// expert shape; with 6144 x 2048 bf16 experts streaming 32-row tiles was
+// still 4.6 % faster at 16 rows). W4A8 always runs the tiled scaled-MFMA
+// kernels, which beat weight streaming on 4096 x 1536 experts from a single
+// token on (1 to 128 tokens of a 32-expert share: 15-26 % faster).
 int tile_rows(const Prob& q) {
   if (q.act == MOE_F32) return 32;
+  if (q.mx) return 128;
   const long long avg = q.E ? q.N / q.E : 0;  // expected rows per expert
-  if (avg >= 512 && !q.mx) return 256;
-  const long long tiled_from = q.mx ? 8 : q.i8 ? 12 : 20;
-  if (avg >= tiled_from) return 128;
+  if (avg >= 512) return 256;
+  if (avg >= (q.i8 ? 12 : 20)) return 128;
   return avg <= 12 ? 16 : 32;
 }
 
@@ -161,17 +163,12 @@ moe_status run_up(const Prob& q, int mt, const Tile* tiles,
     MOE_TRY(moe::launch_gemm_f32(true, tiles, tile_count, mtl, (const float*)xp,
                                  (const float*)w13, (float*)h, q.H, 2 * q.I,
                                  q.I, s));
-  else if (q.mx && mt == 128)
+  else if (q.mx)
     MOE_TRY(moe::launch_gemm_mx_tiled(true, tiles, tile_count, mtl,
                                       (const uint8_t*)xp, (const uint8_t*)xs,
                                       (const uint8_t*)w13,
                                       (const uint8_t*)w13s, h, (uint8_t*)hs,
                                       q.H, 2 * q.I, q.I, gidx, gbase, q.k, s));
-  else if (q.mx)
-    MOE_TRY(moe::launch_gemm_mx(true, mt / 16, tiles, tile_count, mtl,
-                                (const uint8_t*)xp, (const uint8_t*)xs,
-                                (const uint8_t*)w13, (const uint8_t*)w13s, h,
-                                (uint8_t*)hs, q.H, 2 * q.I, q.I, s));
   else if (mt >= 128)
     MOE_TRY(moe::launch_gemm_bf16_tiled(
         true, mt, tiles, tile_count, mtl, (const uint16_t*)xp,
@@ -214,17 +211,12 @@ moe_status run_down(const Prob& q, int mt, const Tile* tiles,
     MOE_TRY(moe::launch_gemm_f32(false, tiles, tile_count, mtl,
                                  (const float*)h, (const float*)w2, (float*)y,
                                  q.I, q.H, q.H, s));
-  else if (q.mx && mt == 128)
+  else if (q.mx)
     MOE_TRY(moe::launch_gemm_mx_tiled(false, tiles, tile_count, mtl,
                                       (const uint8_t*)h, (const uint8_t*)hs,
                                       (const uint8_t*)w2, (const uint8_t*)w2s,
                                       y, nullptr, q.I, q.H, q.H, nullptr,
                                       nullptr, q.k, s));
-  else if (q.mx)
-    MOE_TRY(moe::launch_gemm_mx(false, mt / 16, tiles, tile_count, mtl,
-                                (const uint8_t*)h, (const uint8_t*)hs,
-                                (const uint8_t*)w2, (const uint8_t*)w2s, y,
-                                nullptr, q.I, q.H, q.H, s));
   else if (mt >= 128)
     MOE_TRY(moe::launch_gemm_bf16_tiled(
         false, mt, tiles, tile_count, mtl, (const uint16_t*)h,
@@ -547,7 +539,7 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
   // MXFP8 with the tiled GEMM, and int8: x is quantised once per token and
   // GEMM1 reads the token rows of the codes (32-bit offsets)
   const bool small_x = (int64_t)q.T * q.H < (int64_t(1) << 31);
-  const bool mx_tok = q.mx && mt == 128 && small_x;
+  const bool mx_tok = q.mx && small_x;
   const bool i8_tok = q.i8 && small_x;
   const size_t xrows = (mx_tok || i8_tok) ? (size_t)q.T : N;
   void* xp = c.take<char>(q.El && !gather ? xrows * q.H * ab : 0);

@@ -129,15 +129,7 @@ hipError_t launch_gemm_f32(bool glu, const Tile* tiles,
                            int Nw, int Nout, hipStream_t s);
 // MXFP8 activations [rows, K] + e8m0 [rows, K/32]; MXFP4 weights
 // [E_loc, N, K/2] + e8m0 [E_loc, N, K/32]. glu: output MXFP8 h (+ scales);
-// else bf16 y.
-hipError_t launch_gemm_mx(bool glu, int rg, const Tile* tiles,
-                          const int32_t* tile_count, int max_tiles,
-                          const uint8_t* a, const uint8_t* a_scale,
-                          const uint8_t* w, const uint8_t* w_scale, void* out,
-                          uint8_t* out_scale, int K, int Nw, int Nout,
-                          hipStream_t s);
-
-// Same operands, 128-row LDS-tiled scaled-MFMA tiles (tile list mt=128).
+// else bf16 y. 128-row LDS-tiled scaled-MFMA tiles (tile list mt=128).
 // With gidx non-NULL, A rows (and their scales) are read from the per-token
 // codes: row of sorted copy i = gidx[gbase[0] + i] / gk (offsets < 2^31).
 hipError_t launch_gemm_mx_tiled(bool glu, const Tile* tiles,

@@ -97,8 +97,8 @@ SMALL = {
     "decode_bf16_32row_small": scaled(get_workload("qwen3_30b_a3b_decode_bf16"),
                                       T=64, H=512, I=384, n_ffn=16,
                                       local_end=16, top_k=4),
-    # W4A8 decode-size on an expert range, 6 rows per expert: the
-    # weight-streaming scaled-MFMA kernel
+    # W4A8 decode-size on an expert range, 6 rows per expert: mostly empty
+    # 128-row scaled-MFMA tiles
     "ep_w4a8_decode_small": scaled(get_workload("qwen3_235b_a22b_ep_rank_w4a8"),
                                    T=24, H=512, I=256, n_ffn=16, local_begin=4,
                                    local_end=8, top_k=4),
