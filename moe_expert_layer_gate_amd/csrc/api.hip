@@ -67,14 +67,17 @@ size_t act_bytes(const Prob& q) { return q.act == MOE_F32 ? 4 : 2; }
 // expert shape; with 6144 x 2048 bf16 experts streaming 32-row tiles was
 // still 4.6 % faster at 16 rows). W4A8 always runs the tiled scaled-MFMA
 // kernels, which beat weight streaming on 4096 x 1536 experts from a single
-// token on (1 to 128 tokens of a 32-expert share: 15-26 % faster).
+// token on (1 to 128 tokens of a 32-expert share: 15-26 % faster). Below
+// the switch bf16 streams 32-row tiles from 8 rows per expert (3-6 % faster
+// than 16-row ones at 8-12 rows), int8 16-row tiles throughout (32-row ones
+// were 8-12 % slower at 8-10 rows).
 int tile_rows(const Prob& q) {
   if (q.act == MOE_F32) return 32;
   if (q.mx) return 128;
   const long long avg = q.E ? q.N / q.E : 0;  // expected rows per expert
   if (avg >= 512) return 256;
   if (avg >= (q.i8 ? 12 : 20)) return 128;
-  return avg <= 12 ? 16 : 32;
+  return q.i8 || avg < 8 ? 16 : 32;
 }
 
 // moe_layer fuses the gather into GEMM1's activation loads for bf16 (the
