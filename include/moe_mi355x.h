@@ -80,6 +80,12 @@ typedef enum moe_dtype {
                          row (activations, dynamic: amax / 127)             */
 } moe_dtype;
 
+/* Layout of the expert weights handed to a call (moe_problem.wt_layout). */
+typedef enum moe_layout {
+  MOE_LAYOUT_ROWMAJOR = 0, /* as in "Weight layouts" below, unpacked        */
+  MOE_LAYOUT_PACKED = 1    /* the packed order of moe_pack_weights           */
+} moe_layout;
+
 typedef struct moe_problem {
   int32_t T;           /* tokens                                            */
   int32_t H;           /* hidden size                                       */
@@ -93,6 +99,13 @@ typedef struct moe_problem {
   int32_t wt;    /* MOE_F32 | MOE_BF16 | MOE_MXFP4_E2M1 | MOE_INT8          */
   int32_t act_q; /* == act (no quantisation) | MOE_MXFP8_E4M3 | MOE_INT8
                     (dynamic)                                               */
+  int32_t wt_layout; /* moe_layout of w13 / w2: MOE_LAYOUT_PACKED for
+                        MXFP4_E2M1 and INT8 weights, MOE_LAYOUT_ROWMAJOR for
+                        F32 and BF16; any other pairing is refused with
+                        MOE_ERR_UNSUPPORTED before anything is launched (the
+                        quantised GEMMs read only the packed order: pack
+                        row-major MXFP4 / int8 weights once with
+                        moe_pack_weights)                                    */
 } moe_problem;
 
 /* Supported combinations: (act, wt, act_q) = (F32, F32, F32),
@@ -128,6 +141,11 @@ typedef struct moe_problem {
  *                w13_scale fp32 [E_loc, 2I] (one per output column),
  *                w2_scale fp32 [E_loc, H]
  * Scale pointers must be NULL unless wt is MXFP4_E2M1 or INT8.
+ * The quantised byte matrices W13 / W2 arrive row-major (K contiguous, as
+ * moe_quant_mxfp4_weights writes them) from a checkpoint; the calls below
+ * take them only in the packed order, made once by moe_pack_weights, and the
+ * problem states which it holds (wt_layout): a row-major quantised buffer is
+ * refused with MOE_ERR_UNSUPPORTED, never misread.
  *
  * Packed weights (MXFP4_E2M1 and INT8): a static weight matrix W [E, N, Kb]
  * of bytes (Kb = K for int8, K/2 for e2m1; K contiguous per output column
@@ -319,6 +337,27 @@ MOE_API moe_status moe_add_rms_norm_mx_quant(int32_t T, int32_t H,
  * Stream-ordered; the caller owns both buffers. */
 MOE_API moe_status moe_pack_weights(int32_t E, int32_t N, int32_t K_bytes,
                                     const void* src, void* dst, void* stream);
+
+/* MXFP4 quantisation of bf16 expert weights, the form the W4A8 experts hold
+ * ([P1] "MoE EP优化 / AllGather方案(W4A8量化)": MXFP4 weights), for a caller
+ * that has bf16 weights; done once, e.g. when the weights are loaded. The
+ * encoding is OCP MX v1.0 (the pages name MXFP4 without defining it): each
+ * block of 32 consecutive K of one output column shares an e8m0 scale 2^s,
+ * s = floor(log2(amax of the block)) - 2 clamped to [-127, 127] (an all-zero
+ * block gets scale code 0); each element is the e2m1 code of v / 2^s rounded
+ * to nearest, ties to even, saturating at 6, sign kept.
+ *   w      bf16 [E, K, N], N contiguous (w13 [E, H, 2I] with K = H, N = 2I;
+ *          w2 [E, I, H] with K = I, N = H)
+ *   codes  uint8 [E, N, K/2]: K contiguous per output column, two codes per
+ *          byte, the low nibble holds the even k -- the row-major MXFP4
+ *          layout; moe_pack_weights turns it into the packed order
+ *   scales uint8 [E, N, K/32] e8m0 (the w13_scale / w2_scale of moe_layer)
+ * E >= 0 (E == 0 launches nothing), K > 0, N > 0 (else MOE_ERR_INVALID_ARG);
+ * K % 32 == 0 and E * N * K < 2^40 (else MOE_ERR_UNSUPPORTED); pointers
+ * 16-byte aligned. Stream-ordered; the caller owns all buffers. */
+MOE_API moe_status moe_quant_mxfp4_weights(int32_t E, int32_t K, int32_t N,
+                                           const void* w, uint8_t* codes,
+                                           uint8_t* scales, void* stream);
 
 /* Router linear ([P1] "融合算子优化 / 融合RMSNorm Cast": the fp32 output of
  * the norm is the input of the gate computation): the logits of

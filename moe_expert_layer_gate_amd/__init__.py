@@ -23,19 +23,22 @@ __all__ = [
     "init_routing", "ffn_up", "ffn_down", "grouped_ffn", "finalize", "layer",
     "layer_workspace_bytes", "layer_traced", "SYMBOLS", "STAGES",
     "add_rms_norm_cast", "add_rms_norm_mx_quant", "router_logits",
-    "pack_weights",
+    "pack_weights", "quant_mxfp4_weights",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16, MOE_MXFP8_E4M3, MOE_MXFP4_E2M1, MOE_INT8 = 0, 1, 2, 3, 4
+MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED = 0, 1
+_LAYOUT = {"rowmajor": MOE_LAYOUT_ROWMAJOR, "packed": MOE_LAYOUT_PACKED}
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8_E4M3,
        "mxfp4": MOE_MXFP4_E2M1, "int8": MOE_INT8}
 
 SYMBOLS = ["moe_gate_topk", "moe_init_routing", "moe_grouped_ffn", "moe_ffn_up",
            "moe_ffn_down", "moe_finalize", "moe_layer", "moe_layer_traced",
            "moe_add_rms_norm_cast", "moe_add_rms_norm_mx_quant",
-           "moe_router_logits", "moe_pack_weights", "moe_status_string",
+           "moe_router_logits", "moe_pack_weights", "moe_quant_mxfp4_weights",
+           "moe_status_string",
            "moe_abi_version"]
 
 # stages of moe_layer_traced, in launch order
@@ -52,7 +55,7 @@ class MoeError(RuntimeError):
 class MoeProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "H", "I", "n_ffn", "n_zero", "top_k", "local_begin", "local_end",
-        "act", "wt", "act_q")]
+        "act", "wt", "act_q", "wt_layout")]
 
 
 _lib = None
@@ -93,6 +96,7 @@ def lib() -> ctypes.CDLL:
                                         _vp, _vp, _vp]
     sig["moe_router_logits"] = [_i32, _i32, _i32, _vp, _vp, _vp, _vp]
     sig["moe_pack_weights"] = [_i32, _i32, _i32, _vp, _vp, _vp]
+    sig["moe_quant_mxfp4_weights"] = [_i32, _i32, _i32, _vp, _vp, _vp, _vp]
     for name, args in sig.items():
         f = getattr(L, name)
         f.argtypes = args
@@ -109,19 +113,27 @@ def problem(shape=None, **kw) -> MoeProblem:
     """Build a MoeProblem from an object with the shape attributes (T, H, I,
     n_ffn, n_zero, top_k, local_begin, local_end, act, wt, act_q with dtype
     names "f32" / "bf16" / "mxfp4" / "mxfp8" / "int8" / "none") and/or
-    keywords."""
+    keywords. wt_layout ("rowmajor" / "packed") defaults to "packed" for
+    MXFP4 and int8 weights (the form pack_weights makes) and "rowmajor"
+    otherwise; the library refuses any other pairing."""
     vals = {}
     for n in ("T", "H", "I", "n_ffn", "n_zero", "top_k", "local_begin",
-              "local_end", "act", "wt", "act_q"):
+              "local_end", "act", "wt", "act_q", "wt_layout"):
         if n in kw:
             vals[n] = kw[n]
-        elif shape is not None:
+        elif shape is not None and hasattr(shape, n):
             vals[n] = getattr(shape, n)
     if vals.get("act_q") in (None, "none"):
         vals["act_q"] = vals["act"]
+    if vals.get("wt_layout") is None:
+        vals["wt_layout"] = ("packed" if vals["wt"] in ("mxfp4", "int8",
+                                                         MOE_MXFP4_E2M1, MOE_INT8)
+                             else "rowmajor")
     for n in ("act", "wt", "act_q"):
         if isinstance(vals[n], str):
             vals[n] = _DT[vals[n]]
+    if isinstance(vals["wt_layout"], str):
+        vals["wt_layout"] = _LAYOUT[vals["wt_layout"]]
     return MoeProblem(**vals)
 
 
@@ -373,3 +385,20 @@ def pack_weights(w, out=None):
         out = torch.empty_like(w)
     _check(lib().moe_pack_weights(E, N, Kb, _ptr(w), _ptr(out), _stream()))
     return out
+
+
+def quant_mxfp4_weights(w, codes=None, scales=None):
+    """bf16 expert weights [E, K, N] (N contiguous) -> MXFP4 codes uint8
+    [E, N, K/2] (low nibble = even k) and e8m0 scales uint8 [E, N, K/32]
+    (see moe_quant_mxfp4_weights). The codes are row-major; pack_weights
+    turns them into the order the GEMMs read."""
+    if w.dim() != 3 or w.dtype != torch.bfloat16:
+        raise ValueError("w must be an [E, K, N] bfloat16 tensor")
+    E, K, N = w.shape
+    if codes is None:
+        codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device=w.device)
+    _check(lib().moe_quant_mxfp4_weights(E, K, N, _ptr(w), _ptr(codes),
+                                         _ptr(scales), _stream()))
+    return codes, scales

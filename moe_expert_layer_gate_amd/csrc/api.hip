@@ -25,6 +25,7 @@ moe_status check(const moe_problem* p, Prob* q) {
   r.T = p->T; r.H = p->H; r.I = p->I; r.nffn = p->n_ffn; r.nzero = p->n_zero;
   r.k = p->top_k; r.lb = p->local_begin; r.le = p->local_end;
   r.act = p->act; r.wt = p->wt; r.actq = p->act_q;
+  const int layout = p->wt_layout;
   if (r.T < 0 || r.H <= 0 || r.I <= 0 || r.nffn < 0 || r.nzero < 0)
     return MOE_ERR_INVALID_ARG;
   r.E = r.nffn + r.nzero;
@@ -40,6 +41,9 @@ moe_status check(const moe_problem* p, Prob* q) {
   r.mx = r.act == MOE_BF16 && r.wt == MOE_MXFP4_E2M1 && r.actq == MOE_MXFP8_E4M3;
   r.i8 = r.act == MOE_BF16 && r.wt == MOE_INT8 && r.actq == MOE_INT8;
   if (!f32 && !bf16 && !r.mx && !r.i8) return MOE_ERR_UNSUPPORTED;
+  // the quantised GEMMs read packed weights only, the others row-major ones
+  if (layout != ((r.mx || r.i8) ? MOE_LAYOUT_PACKED : MOE_LAYOUT_ROWMAJOR))
+    return MOE_ERR_UNSUPPORTED;
   if (r.mx && (r.H % 128 || r.I % 128)) return MOE_ERR_UNSUPPORTED;
   // int8: K steps of 128; int32 sums of 127 * 127 * K products stay exact;
   // weight offsets (2I * H bytes per expert) fit 32 bits
@@ -261,7 +265,7 @@ const char* moe_status_string(moe_status s) {
   return "unknown moe_status";
 }
 
-int32_t moe_abi_version(void) { return 100; }
+int32_t moe_abi_version(void) { return 200; }
 
 moe_status moe_gate_topk(const moe_problem* p, const float* logits,
                          int32_t* topk_ids, float* topk_weight, void* stream) {
@@ -499,6 +503,18 @@ moe_status moe_pack_weights(int32_t E, int32_t N, int32_t K_bytes,
                                              (const uint8_t*)src,
                                              (uint8_t*)dst,
                                              (hipStream_t)stream));
+}
+
+moe_status moe_quant_mxfp4_weights(int32_t E, int32_t K, int32_t N,
+                                   const void* w, uint8_t* codes,
+                                   uint8_t* scales, void* stream) {
+  if (E < 0 || K <= 0 || N <= 0) return MOE_ERR_INVALID_ARG;
+  if (K % 32 || (long long)E * N * K >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  if (E == 0) return MOE_OK;
+  if (!w || !codes || !scales || !aligned16(w, codes, scales))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_quant_mxfp4_weights(
+      E, K, N, (const uint16_t*)w, codes, scales, (hipStream_t)stream));
 }
 
 moe_status moe_router_logits(int32_t T, int32_t H, int32_t E, const float* y,

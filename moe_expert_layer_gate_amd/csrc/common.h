@@ -95,6 +95,38 @@ MOE_DEV uint32_t e4m3_encode_scaled(float v, int s) {
   return sign | n;
 }
 
+// e8m0 shared exponent of an MXFP4 block: floor(log2(amax)) - 2 (emax of
+// e2m1), clamped to [-127, 127]; an all-zero block gives -127 (code 0).
+MOE_DEV int mx_e2m1_scale_exp(float amax) {
+  if (!(amax > 0.f)) return -127;
+  int s = floor_log2_f32(amax) - 2;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// e2m1 code (OCP MX v1.0: 1 sign, 2 exponent bits with bias 1, 1 mantissa
+// bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6) of v * 2^-s, rounded to nearest
+// with ties to even, saturating at 6, sign kept (values that round to zero
+// give +0 or -0). Exact integer arithmetic on the fp32 bits of v.
+MOE_DEV uint32_t e2m1_encode_scaled(float v, int s) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 28) & 0x8u;
+  int ex = (int)((u >> 23) & 0xFF);
+  uint32_t M = u & 0x7FFFFFu;
+  if (ex) M |= 0x800000u; else ex = 1;
+  if (M == 0) return sign;
+  int p = ex - 150 - s;                      // |v| * 2^-s = M * 2^p
+  int nb = 32 - __clz((int)M);               // bit length of M
+  int e = nb - 1 + p;                        // floor(log2(|v| 2^-s))
+  if (e >= 0) {                              // normal range (>= 1.0)
+    uint32_t r = rne_shift(M, nb - 2);       // 2 significant bits, in [2, 4]
+    if (r == 4) { r = 2; ++e; }
+    if (e > 2) return sign | 0x7u;           // saturate at 6
+    return sign | ((uint32_t)(e + 1) << 1) | (r - 2);
+  }
+  // subnormal: multiples of 0.5; rounding up to 2 lands on the code of 1.0
+  return sign | rne_shift(M, -(p + 1));
+}
+
 // Same code as e4m3_encode_scaled, with fp32 arithmetic and no branches:
 // w = v * 2^-s is exact whenever it matters (|w| < 2^9 inside an MX block;
 // results below the fp32 normal range are far under e4m3's smallest step and

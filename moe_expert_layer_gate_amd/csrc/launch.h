@@ -117,6 +117,12 @@ hipError_t launch_gemm_i8_stream(bool glu, int rg, const Tile* tiles,
 // byte matrices [E, N, Kb] (int8 codes, or two e2m1 codes per byte).
 hipError_t launch_pack_weights(int E, int N, int Kb, const uint8_t* src,
                                uint8_t* dst, hipStream_t s);
+// MXFP4 (e2m1 + e8m0 per 32 along K) of bf16 weights [E, K, N] (N
+// contiguous): codes [E, N, K/2] (low nibble = even k), scales [E, N, K/32].
+// K % 32 == 0.
+hipError_t launch_quant_mxfp4_weights(int E, int K, int N, const uint16_t* w,
+                                      uint8_t* codes, uint8_t* scales,
+                                      hipStream_t s);
 hipError_t launch_quant_i8_rows(bool f32, const void* src, int K, int nrows,
                                 const int32_t* gidx, const int32_t* offs,
                                 int fb, int fe, int gk, int8_t* codes,

@@ -13,9 +13,10 @@ Distributions ("N(0, s)" means standard deviation s):
     bias N(0,1.5) drawn once per seed (heavy expert load imbalance);
   * hidden states x and residual: N(0,1) rounded to the activation dtype;
   * bf16/fp32 expert weights: N(0, w_std) rounded to the weight dtype;
-  * MXFP4 expert weights: e2m1 codes drawn uniformly over all 16 codes and e8m0
-    block scales drawn uniformly from {119, 120, 121} (2^-8..2^-6), which gives
-    an element RMS of about 0.012..0.046, close to N(0, 0.02).
+  * MXFP4 expert weights (W4A8): drawn as bf16 N(0, w_std) like the bf16
+    workloads; each side quantises them to MXFP4 itself (the library with its
+    weight-quantisation call at load time, the oracle with its own MX
+    quantiser), so no quantisation arithmetic lives here.
   * int8 expert weights (W8A8): codes N(0, 32) rounded and clipped to
     [-127, 127] (a per-channel amax near 127, as symmetric quantisation of a
     Gaussian column gives) with one fp32 scale per output channel drawn
@@ -175,10 +176,11 @@ def generate(shape: MoEShape, seed: int = 0, device="cpu",
       logits   fp32 [T, E_tot]
       x        act  [T, H]
       residual act  [T, H] or None
-      w13      [E_loc, H, 2I] (f32/bf16) | uint8 [E_loc, 2I, H/2] (mxfp4 codes)
-      w13_scale None | uint8 [E_loc, 2I, H/32]
-      w2       [E_loc, I, H] (f32/bf16) | uint8 [E_loc, H, I/2]
-      w2_scale None | uint8 [E_loc, H, I/32]
+      w13      [E_loc, H, 2I] f32 / bf16 (bf16 also for mxfp4, quantised by
+               the consumer) | int8 codes [E_loc, 2I, H]
+      w13_scale None | fp32 [E_loc, 2I] (int8)
+      w2       [E_loc, I, H] f32 / bf16 | int8 codes [E_loc, H, I]
+      w2_scale None | fp32 [E_loc, H] (int8)
     Weights are drawn per expert (seeded by global expert id), so an expert's
     weights do not depend on the local range.
     """
@@ -202,8 +204,9 @@ def generate(shape: MoEShape, seed: int = 0, device="cpu",
         return out
     El = shape.E_loc
     experts = range(shape.ffn_begin, shape.ffn_end)
-    if shape.wt in ("f32", "bf16"):
-        wdt = _DT[shape.wt]
+    if shape.wt in ("f32", "bf16", "mxfp4"):
+        # MXFP4 weights are drawn in bf16 and quantised by the consumer
+        wdt = _DT["bf16" if shape.wt == "mxfp4" else shape.wt]
         w13 = torch.empty((El, H, 2 * I), dtype=wdt, device=dev)
         w2 = torch.empty((El, I, H), dtype=wdt, device=dev)
         for i, e in enumerate(experts):
@@ -212,30 +215,6 @@ def generate(shape: MoEShape, seed: int = 0, device="cpu",
             w2[i] = _normal((I, H), shape.w_std, wdt, dev,
                             seed_for(shape, seed, ROLE_W2, e))
         out["w13"], out["w2"] = w13, w2
-    elif shape.wt == "mxfp4":
-        assert H % 32 == 0 and I % 32 == 0
-        w13 = torch.empty((El, 2 * I, H // 2), dtype=torch.uint8, device=dev)
-        w2 = torch.empty((El, H, I // 2), dtype=torch.uint8, device=dev)
-        s13 = torch.empty((El, 2 * I, H // 32), dtype=torch.uint8, device=dev)
-        s2 = torch.empty((El, H, I // 32), dtype=torch.uint8, device=dev)
-        for i, e in enumerate(experts):
-            w13[i] = torch.randint(0, 256, (2 * I, H // 2), device=dev,
-                                   dtype=torch.int32,
-                                   generator=_gen(dev, seed_for(shape, seed, ROLE_W13, e))
-                                   ).to(torch.uint8)
-            w2[i] = torch.randint(0, 256, (H, I // 2), device=dev,
-                                  dtype=torch.int32,
-                                  generator=_gen(dev, seed_for(shape, seed, ROLE_W2, e))
-                                  ).to(torch.uint8)
-            s13[i] = torch.randint(119, 122, (2 * I, H // 32), device=dev,
-                                   dtype=torch.int32,
-                                   generator=_gen(dev, seed_for(shape, seed, ROLE_W13_SCALE, e))
-                                   ).to(torch.uint8)
-            s2[i] = torch.randint(119, 122, (H, I // 32), device=dev,
-                                  dtype=torch.int32,
-                                  generator=_gen(dev, seed_for(shape, seed, ROLE_W2_SCALE, e))
-                                  ).to(torch.uint8)
-        out["w13"], out["w2"], out["w13_scale"], out["w2_scale"] = w13, w2, s13, s2
     elif shape.wt == "int8":
         w13 = torch.empty((El, 2 * I, H), dtype=torch.int8, device=dev)
         w2 = torch.empty((El, H, I), dtype=torch.int8, device=dev)

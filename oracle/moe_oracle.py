@@ -61,7 +61,9 @@ Readings taken where the pages are silent (all listed in the design doc):
     [local_begin, local_end) is over all E_tot ids; copies outside it add 0.
   * fused norm: the residual add is an fp32 add of the two bf16 inputs; the
     RMSNorm is taken of that fp32 sum (not of its bf16 rounding), exactly; the
-    new residual is the sum rounded to bf16.
+    new residual is the sum rounded to bf16; the outputs are the fp32 rounding
+    of the exact y, and the bf16 rounding and MXFP8 quantisation of that fp32
+    value.
   * intermediates are stored in the activation dtype (bf16 or fp32) between
     the two GEMMs, or as MXFP8 / int8 when activations are quantised (the
     fp32-rounded h is quantised); y is stored in the activation dtype;
@@ -101,13 +103,10 @@ def _round_to_precision(x: np.ndarray, mant_bits: int, min_exp: int) -> np.ndarr
     """Round to a binary float with `mant_bits` stored mantissa bits and minimum
     normal exponent `min_exp` (no overflow handling), ties to even."""
     x = np.asarray(x, dtype=np.float64)
-    out = np.zeros_like(x)
-    nz = x != 0
-    _, e = np.frexp(x[nz])                     # |x| = m * 2^e, m in [0.5, 1)
+    _, e = np.frexp(x)                         # |x| = m * 2^e, m in [0.5, 1)
     exp = np.maximum(e - 1, min_exp)           # floor(log2|x|), clamped
     ulp = np.ldexp(1.0, exp - mant_bits)
-    out[nz] = np.round(x[nz] / ulp) * ulp      # np.round: half to even
-    return out
+    return np.round(x / ulp) * ulp             # np.round: half to even; 0 -> 0
 
 
 def round_bf16(x) -> np.ndarray:
@@ -217,16 +216,15 @@ def _elem_encode(v, fmt):
     sign = np.signbit(v).astype(np.int64)
     a = np.abs(v)
     min_normal_exp = 1 - bias
-    r = _round_to_precision(a, m_bits, min_normal_exp)
-    r = np.minimum(r, vmax)
-    code = np.zeros(a.shape, dtype=np.int64)
-    normal = r >= np.ldexp(1.0, min_normal_exp)
-    _, e = np.frexp(r[normal])
-    ex = e - 1
-    man = np.round((r[normal] / np.ldexp(1.0, ex) - 1.0) * (1 << m_bits)).astype(np.int64)
-    code[normal] = ((ex + bias) << m_bits) | man
-    sub = ~normal
-    code[sub] = np.round(r[sub] / np.ldexp(1.0, min_normal_exp - m_bits)).astype(np.int64)
+    r = np.minimum(_round_to_precision(a, m_bits, min_normal_exp), vmax)
+    # normal values: biased exponent and the stored mantissa bits
+    _, e = np.frexp(r)
+    ex = np.maximum(e - 1, min_normal_exp)
+    man = np.round((r / np.ldexp(1.0, ex) - 1.0) * (1 << m_bits)).astype(np.int64)
+    normal_code = ((ex + bias) << m_bits) | man
+    # subnormal values (and zero): multiples of the smallest subnormal step
+    sub_code = np.round(r / np.ldexp(1.0, min_normal_exp - m_bits)).astype(np.int64)
+    code = np.where(r >= np.ldexp(1.0, min_normal_exp), normal_code, sub_code)
     code |= sign << (m_bits + e_bits)
     return code.astype(np.uint8)
 
@@ -580,20 +578,25 @@ def add_rms_norm(x, residual, weight, eps: float):
 
 def add_rms_norm_cast(x, residual, weight, eps: float):
     """[P1] "融合RMSNorm Cast": the normalised hidden states in fp32 (for the
-    router) and in bf16 (for the experts), plus the new residual.
+    router) and in bf16 (for the experts), plus the new residual. The fp32
+    output is the exact y rounded to fp32; the bf16 output is that fp32 value
+    rounded to bf16 (the cast of the fp32 output, not of the exact y).
     Returns (y_f32, y_bf16, residual_out) as fp64 arrays of those values."""
     y, r = add_rms_norm(x, residual, weight, eps)
-    return round_f32(y), round_bf16(y), r
+    y32 = round_f32(y)
+    return y32, round_bf16(y32), r
 
 
 def add_rms_norm_mx_quant(x, residual, weight, eps: float):
     """[P1] "融合RMSNorm MX量化": the normalised hidden states as MXFP8
     (e4m3 codes rounded to nearest even, e8m0 scale per 32 along H), plus the
-    new residual. Returns (codes uint8 [T, H], scales uint8 [T, H/32],
-    residual_out fp64, y fp64 before quantisation)."""
+    new residual. The codes quantise the fp32 value of y (the exact y rounded
+    to fp32), as the dual-output form casts it. Returns (codes uint8 [T, H],
+    scales uint8 [T, H/32], residual_out fp64, y_f32 the quantised values)."""
     y, r = add_rms_norm(x, residual, weight, eps)
-    codes, scales = mx_quant(y, "e4m3")
-    return codes, scales, r, y
+    y32 = round_f32(y)
+    codes, scales = mx_quant(y32, "e4m3")
+    return codes, scales, r, y32
 
 
 def router_logits(y, w_router) -> np.ndarray:

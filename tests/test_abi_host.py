@@ -237,3 +237,43 @@ def test_pack_weights_host_checks(L):
     assert pk(2, 32, 128, ok, ctypes.c_void_p((1 << 30) + 8), None) == 1  # misaligned
     assert pk(2, 32, 128, ok, ctypes.c_void_p((1 << 20) + 4096), None) == 1  # overlap
     assert pk(0, 32, 128, None, None, None) == 0     # nothing to do
+
+
+@pytest.mark.parametrize("kw,layout,status", [
+    (dict(wt="mxfp4", act_q="mxfp8", H=4096, I=1536), "rowmajor", 2),
+    (dict(wt="int8", act_q="int8"), "rowmajor", 2),
+    (dict(), "packed", 2),
+    (dict(act="f32", wt="f32", act_q="f32"), "packed", 2),
+    (dict(wt="mxfp4", act_q="mxfp8", H=4096, I=1536), "packed", 0),
+    (dict(wt="int8", act_q="int8"), "packed", 0),
+    (dict(), "rowmajor", 0),
+])
+def test_weight_layout_declared(L, kw, layout, status):
+    """Quantised weights are read only in the packed order: a problem that
+    declares row-major MXFP4 or int8 weights (or packed bf16 / fp32 ones) is
+    refused before any launch, by every entry point that takes the problem."""
+    p = _p(wt_layout=layout, **kw)
+    st, _ = _query(L, p)
+    assert st == status
+    if status:
+        fake = ctypes.c_void_p(1 << 20)  # never dereferenced
+        assert L.moe_gate_topk(ctypes.byref(p), fake, fake, fake, None) == status
+        n = ctypes.c_size_t(0)
+        assert L.moe_grouped_ffn(ctypes.byref(p), None, None, None, None, None,
+                                 None, None, None, None, ctypes.byref(n),
+                                 None) == status
+
+
+def test_quant_mxfp4_weights_host_checks(L):
+    ok = ctypes.c_void_p(1 << 20)
+    q = L.moe_quant_mxfp4_weights
+    assert q(-1, 64, 16, ok, ok, ok, None) == 1
+    assert q(2, 0, 16, ok, ok, ok, None) == 1
+    assert q(2, 64, 0, ok, ok, ok, None) == 1
+    assert q(2, 48, 16, ok, ok, ok, None) == 2          # K % 32
+    assert q(1 << 10, 1 << 15, 1 << 15, ok, ok, ok, None) == 2  # E*N*K >= 2^40
+    assert q(2, 64, 16, None, ok, ok, None) == 1
+    assert q(2, 64, 16, ok, None, ok, None) == 1
+    assert q(2, 64, 16, ok, ok, None, None) == 1
+    assert q(2, 64, 16, ok, ctypes.c_void_p((1 << 20) + 8), ok, None) == 1
+    assert q(0, 64, 16, None, None, None, None) == 0    # nothing to do

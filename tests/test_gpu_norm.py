@@ -2,13 +2,17 @@
 the CPU oracle, through the C ABI.
 
 Bars: the new residual is bit-exact (an fp32 add of two bf16 values rounded
-to bf16 is the same on both sides); y in fp32 within rel 1e-5 per element
-(fp32 sum of squares, one division, one square root); y in bf16 within one
-bf16 ulp of the exact value; MXFP8: every code decodes to within the MX
-rounding bound of the exact y (half an e4m3 step at the block scale, or the
-saturation error past 448), scale codes equal unless the block maximum sits
-within fp32 noise of a power of two, and codes equal the oracle's own for all
-but a sliver of elements that sit on a rounding midpoint."""
+to bf16 is the same on both sides); y in fp32 within rel 1e-5 per element of
+the exact y (fp32 sum of squares, one division, one square root). The bf16
+and MXFP8 outputs are taken of the fp32 y on both sides, so wherever the
+GPU's fp32 y (from the dual-output call on the same inputs; both calls form
+y with the same code) equals the oracle's fp32 rounding of the exact y, the
+bf16 values and, block by block, the MX codes and scales must be bit-exact.
+Elsewhere -- elements or blocks whose fp32 y differs by rounding, reported
+as a count -- the bf16 value is the rounding of the GPU's own fp32 y, and the
+MX codes decode to within the MX rounding bound of the exact y (half an e4m3
+step at the block scale, or the saturation error past 448) with scales
+within one."""
 import numpy as np
 import pytest
 import torch
@@ -35,42 +39,53 @@ def _host(t):
     return None if t is None else t.double().cpu().numpy()
 
 
+def _bits16(v):
+    return torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).view(torch.int16).numpy()
+
+
 def _check_cast(inp, eps, y32, y16, res):
     ry32, ry16, rres = O.add_rms_norm_cast(_host(inp["x"]), _host(inp["residual"]),
                                            _host(inp["weight"]), eps)
     y, _ = O.add_rms_norm(_host(inp["x"]), _host(inp["residual"]),
                           _host(inp["weight"]), eps)
-    assert np.array_equal(res.view(torch.int16).cpu().numpy(),
-                          torch.from_numpy(rres).to(torch.bfloat16).view(torch.int16).numpy())
+    assert np.array_equal(res.view(torch.int16).cpu().numpy(), _bits16(rres))
     g32 = y32.double().cpu().numpy()
     assert np.all(np.abs(g32 - y) <= 1e-5 * np.abs(y) + 1e-30)
-    g16 = y16.double().cpu().numpy()
-    assert np.all(np.abs(g16 - y) <= bf16_ulp(y))
+    g16 = y16.view(torch.int16).cpu().numpy()
+    same = g32 == ry32
+    assert np.array_equal(g16[same], _bits16(ry16)[same])
+    # where the fp32 values differ, bf16 is the rounding of the GPU's own y
+    assert np.array_equal(g16, y32.cpu().to(torch.bfloat16).view(torch.int16).numpy())
+    print(f"  cast: fp32 y equal to the oracle's in {same.mean():.6f} of "
+          f"{same.size} elements", flush=True)
 
 
-def _check_mx(inp, eps, codes, scales, res):
-    rc, rs, rres, y = O.add_rms_norm_mx_quant(_host(inp["x"]), _host(inp["residual"]),
-                                              _host(inp["weight"]), eps)
-    assert np.array_equal(res.view(torch.int16).cpu().numpy(),
-                          torch.from_numpy(rres).to(torch.bfloat16).view(torch.int16).numpy())
+def _check_mx(inp, eps, codes, scales, res, y32):
+    rc, rs, rres, ry32 = O.add_rms_norm_mx_quant(_host(inp["x"]), _host(inp["residual"]),
+                                                 _host(inp["weight"]), eps)
+    y, _ = O.add_rms_norm(_host(inp["x"]), _host(inp["residual"]),
+                          _host(inp["weight"]), eps)
+    assert np.array_equal(res.view(torch.int16).cpu().numpy(), _bits16(rres))
     gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
     T, H = y.shape
-    # scale codes: equal unless the block max is within fp32 noise of 2^n
-    amax = np.abs(y).reshape(T, H // 32, 32).max(axis=2)
-    frac = np.log2(np.maximum(amax, 1e-300))
-    near = np.abs(frac - np.round(frac)) < 1e-5
+    g32 = y32.double().cpu().numpy()
+    blk_same = (g32 == ry32).reshape(T, H // 32, 32).all(axis=2)
+    # bit-exact codes and scales in every block whose fp32 y agrees
+    el_same = np.repeat(blk_same, 32, axis=1)
+    assert np.array_equal(gs[blk_same], rs[blk_same])
+    assert np.array_equal(gc[el_same], rc[el_same])
+    # the other blocks: scales within one, codes within the MX rounding bound
     ds = gs.astype(np.int64) - rs.astype(np.int64)
-    assert np.all(ds[~near] == 0) and np.all(np.abs(ds[near]) <= 1)
-    # every decoded value within the MX rounding bound of the exact y
+    assert np.all(np.abs(ds) <= 1)
     sc = np.repeat(np.ldexp(1.0, gs.astype(np.int64) - 127), 32, axis=1)
     a = np.abs(y) / sc
     ulp = np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3)
     bound = np.where(a > 448, a - 448, 0.5 * ulp) * sc
     deq = O.mx_dequant(gc, gs, "e4m3")
     assert np.all(np.abs(deq - y) <= bound * (1 + 1e-5) + 1e-6 * np.abs(y))
-    # and the codes are the oracle's own nearly everywhere
-    same = gc == rc
-    assert same.mean() >= 0.999, f"{(~same).sum()} of {same.size} codes differ"
+    print(f"  mx: {int((~blk_same).sum())} of {blk_same.size} blocks with an fp32 "
+          f"y differing from the oracle's; {int((gc != rc).sum())} codes differ there",
+          flush=True)
 
 
 @pytest.mark.parametrize("with_res", [True, False])
@@ -90,8 +105,10 @@ def test_add_rms_norm_mx_quant(T, H, with_res):
     inp = generate_norm(T, H, seed=T * H, device=DEV, residual=with_res)
     codes, scales, res = m.add_rms_norm_mx_quant(inp["x"], inp["residual"],
                                                  inp["weight"], NORM_EPS)
+    y32, _, _ = m.add_rms_norm_cast(inp["x"], inp["residual"], inp["weight"],
+                                    NORM_EPS, want_bf16=False, want_residual=False)
     torch.cuda.synchronize()
-    _check_mx(inp, NORM_EPS, codes, scales, res)
+    _check_mx(inp, NORM_EPS, codes, scales, res, y32)
 
 
 @pytest.mark.parametrize("T,H", FULL)
@@ -104,7 +121,7 @@ def test_add_rms_norm_full_size(T, H):
                                                   inp["weight"], NORM_EPS)
     torch.cuda.synchronize()
     _check_cast(inp, NORM_EPS, y32, y16, res)
-    _check_mx(inp, NORM_EPS, codes, scales, res2)
+    _check_mx(inp, NORM_EPS, codes, scales, res2, y32)
 
 
 def test_add_rms_norm_edges():
@@ -125,7 +142,7 @@ def test_add_rms_norm_edges():
                                                       inp["weight"], eps)
         torch.cuda.synchronize()
         _check_cast(inp, eps, y32, y16, res)
-        _check_mx(inp, eps, codes, scales, res2)
+        _check_mx(inp, eps, codes, scales, res2, y32)
         assert int(scales[0].abs().sum()) == 0
     # only one of the dual outputs; no residual output
     y32, y16, res = m.add_rms_norm_cast(inp["x"], inp["residual"], inp["weight"],

@@ -413,13 +413,20 @@ def test_add_rms_norm_outputs():
     w = _bf16_rows(rng, 1, 128)[0].double().numpy()
     y32, y16, res = O.add_rms_norm_cast(x, r, w, 1e-6)
     y, res2 = O.add_rms_norm(x, r, w, 1e-6)
-    # torch's float32 / bfloat16 conversions of the exact value
-    assert np.array_equal(y32, torch.from_numpy(y).float().double().numpy())
-    assert np.array_equal(y16, torch.from_numpy(y).to(torch.bfloat16).double().numpy())
+    # torch's float32 conversion of the exact value, and torch's bfloat16
+    # conversion of that float32 value
+    t32 = torch.from_numpy(y).float()
+    assert np.array_equal(y32, t32.double().numpy())
+    assert np.array_equal(y16, t32.to(torch.bfloat16).double().numpy())
     assert np.array_equal(res, res2)
     codes, scales, res3, yq = O.add_rms_norm_mx_quant(x, r, w, 1e-6)
     assert codes.shape == (4, 128) and scales.shape == (4, 4)
     assert np.array_equal(res3, res)
+    assert np.array_equal(yq, y32)
+    # the codes are torch's float8_e4m3fn conversion (round to nearest even)
+    # of the fp32 y divided by the block scale
+    c_ref, s_ref = _torch_mxfp8(t32)
+    assert np.array_equal(codes, c_ref) and np.array_equal(scales, s_ref)
     # the MX pair reproduces y to within half an e4m3 step at the block scale
     # (values past 448 at that scale saturate)
     sc = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1)
@@ -428,6 +435,121 @@ def test_add_rms_norm_outputs():
     bound = np.where(a > 448, a - 448, 0.5 * ulp) * sc
     deq = O.mx_dequant(codes, scales, "e4m3")
     assert np.all(np.abs(deq - yq) <= bound * (1 + 1e-12))
+
+
+def test_norm_outputs_round_through_fp32(monkeypatch):
+    """The bf16 and MXFP8 outputs are taken of the fp32 y, not of the exact
+    one: a y just above a rounding midpoint whose fp32 rounding lands on the
+    midpoint itself rounds the other way (ties to even)."""
+    import oracle.moe_oracle as OM
+    y = np.zeros((1, 32))
+    y[0, 0] = 300.0                       # block scale 2^0 for the MX output
+    y[0, 1] = 1.0 + 2.0 ** -8 + 2.0 ** -30   # fp32: 1 + 2^-8, a bf16 midpoint
+    y[0, 2] = 1.0 + 2.0 ** -4 + 2.0 ** -30   # fp32: 1.0625, an e4m3 midpoint
+    monkeypatch.setattr(OM, "add_rms_norm", lambda *a: (y.copy(), np.zeros((1, 32))))
+    y32, y16, _ = O.add_rms_norm_cast(None, None, None, 0.0)
+    assert y32[0, 1] == 1.0 + 2.0 ** -8 and y32[0, 2] == 1.0625
+    # bf16: the exact y would round up to 1 + 2^-7; its fp32 value ties to 1.0
+    assert y16[0, 1] == 1.0
+    codes, scales, _, _ = O.add_rms_norm_mx_quant(None, None, None, 0.0)
+    assert scales[0, 0] == 127
+    # e4m3: the exact y would round up to 1.125 (0x39); 1.0625 ties to 1.0
+    assert codes[0, 2] == 0x38 and codes[0, 1] == 0x38
+
+
+# ----------------------------------------------------------------- W4A8 h
+
+
+def _torch_mxfp8(h32):
+    """MXFP8 of fp32 rows [n, K] written another way: the block exponent from
+    math.frexp of each block's amax, the element codes from torch's
+    float8_e4m3fn conversion (round to nearest even) of the fp32 values
+    divided by 2^s, clamped to +-448 first (torch does not saturate)."""
+    n, K = h32.shape
+    hb = h32.double().reshape(n, K // 32, 32)
+    amax = hb.abs().amax(-1)
+    s = np.zeros((n, K // 32), dtype=np.int64)
+    for i in range(n):
+        for b in range(K // 32):
+            a = float(amax[i, b])
+            s[i, b] = (math.frexp(a)[1] - 1 - 8) if a > 0 else -127
+    s = np.clip(s, -127, 127)
+    scaled = hb / torch.from_numpy(np.ldexp(1.0, s))[..., None]
+    codes = scaled.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.reshape(n, K).numpy(), (s + 127).astype(np.uint8)
+
+
+def _golden_h():
+    g = _load("mx_h_blocks.json")
+
+    def block(name, key, dtype):
+        v = np.zeros(32, dtype=dtype)
+        vals = g["blocks"][name][key]
+        v[:len(vals)] = vals
+        return v
+    rows = g["rows"]
+    h = np.stack([np.concatenate([block(b, "values", np.float64) for b in r]) for r in rows])
+    codes = np.stack([np.concatenate([block(b, "codes", np.int64) for b in r]) for r in rows])
+    deq = np.stack([np.concatenate([block(b, "dequant", np.float64) for b in r]) for r in rows])
+    scales = np.array([[g["blocks"][b]["scale"] for b in r] for r in rows])
+    # negative zeros of the dequantised list
+    for i, r in enumerate(rows):
+        for j, b in enumerate(r):
+            for q, c in enumerate(g["blocks"][b]["codes"]):
+                if c == 128:
+                    deq[i, 32 * j + q] = -0.0
+    return h, codes, scales, deq
+
+
+def test_mxfp8_h_quantisation_golden(monkeypatch):
+    """expert_ffn's W4A8 branch on hand-worked h rows: the SwiGLU output is
+    replaced by the rows of the fixture, w2 is the identity, and the codes,
+    scales, dequantised h and y must be the fixture's."""
+    import oracle.moe_oracle as OM
+    h_rows, codes, scales, deq = _golden_h()
+    n, I = h_rows.shape
+    monkeypatch.setattr(OM, "swiglu", lambda gu: h_rows.copy())
+    a = np.zeros((n, 8))
+    w13 = np.zeros((8, 2 * I))
+    h, (hc, hs), y = O.expert_ffn(a, w13, np.eye(I), act="bf16", act_q="mxfp8")
+    assert np.array_equal(hc.astype(np.int64), codes)
+    assert np.array_equal(hs.astype(np.int64), scales)
+    assert np.array_equal(h, deq) and np.array_equal(np.signbit(h), np.signbit(deq))
+    assert np.array_equal(y, deq)
+
+
+def test_mxfp8_h_matches_torch_float8():
+    """expert_ffn's W4A8 branch against a second formulation in torch: h
+    formed in float64 with torch's chunk and silu, rounded to fp32, blocks of
+    32 along I quantised through float8_e4m3fn; then y = dequantised h @ w2
+    rounded to bf16. Quantising the bf16-rounded h, blocking along the other
+    axis or skipping the quantisation each change codes on these rows."""
+    rng = np.random.default_rng(31)
+    n, H, I = 32, 64, 96
+    a = O.round_bf16(rng.standard_normal((n, H)))
+    w13 = rng.standard_normal((H, 2 * I)) * 0.3
+    w2 = rng.standard_normal((I, 40)) * 0.2
+    h, (hc, hs), y = O.expert_ffn(a, w13, w2, act="bf16", act_q="mxfp8")
+
+    g, u = torch.chunk(torch.from_numpy(a) @ torch.from_numpy(w13), 2, -1)
+    h32 = (torch.nn.functional.silu(g) * u).float()
+    c_ref, s_ref = _torch_mxfp8(h32)
+    assert np.array_equal(hc, c_ref) and np.array_equal(hs, s_ref)
+    dq = (torch.from_numpy(c_ref).view(torch.float8_e4m3fn).double() *
+          torch.from_numpy(np.ldexp(1.0, np.repeat(s_ref.astype(np.int64) - 127, 32, 1))))
+    assert np.array_equal(h, dq.numpy())
+    y_ref = (dq @ torch.from_numpy(w2)).to(torch.bfloat16).double().numpy()
+    # the two fp64 products may differ in their last bits, so the bf16
+    # roundings may differ by one step where the sum sits on a midpoint
+    ulp = np.exp2(np.floor(np.log2(np.abs(y_ref) + 1e-300)) - 7)
+    assert np.all(np.abs(y - y_ref) <= ulp)
+    assert np.mean(y == y_ref) > 0.99
+    # the planted mistakes: bf16 h first, blocks along the rows, no quantising
+    c_bf, _ = _torch_mxfp8(h32.to(torch.bfloat16).float())
+    assert not np.array_equal(c_bf, c_ref)
+    c_t, _ = _torch_mxfp8(h32.T.contiguous())      # blocks of 32 rows
+    assert not np.array_equal(c_t.T, c_ref)
+    assert not np.array_equal(h, h32.double().numpy())
 
 
 # ----------------------------------------------------------------- W8A8 int8
