@@ -23,7 +23,8 @@
  *     MOE_ERR_HIP. Faults inside kernels surface at the caller's next
  *     synchronisation. Nothing is printed; no call aborts.
  *   - Calls keep no mutable global state and may run concurrently on
- *     different streams with different buffers.
+ *     different streams with different buffers (moe_layer_noalloc excepted:
+ *     its scratch is one array per GPU).
  *   - Workspace (hipcub style): when `workspace` is NULL the call stores the
  *     bytes it needs in *workspace_bytes, returns MOE_OK and launches nothing.
  *     Otherwise *workspace_bytes is the size of `workspace`; a buffer that is
@@ -283,6 +284,28 @@ MOE_API moe_status moe_layer_traced(const moe_problem* p, const float* logits,
                                     void* out, void* workspace,
                                     size_t* workspace_bytes, void* stream,
                                     void* const* stage_events, int32_t n_events);
+
+/* moe_layer without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. The layer's intermediates live in a
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB) that the library
+ * holds on every GPU it runs on until the process ends; the call allocates
+ * nothing itself. Same arguments as moe_layer minus the workspace pair, and
+ * the same result bit for bit. A problem whose moe_layer workspace would be
+ * larger than the array (about 1,400 tokens of the Qwen3-30B-A3B shapes) is
+ * refused with MOE_ERR_WORKSPACE before anything is launched. The array of
+ * the current device is used (the stream must belong to it); it is looked up
+ * on the first call on each device. Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (different streams, or
+ * threads) race and must be serialised by the caller. Nothing in the array
+ * needs to start at zero (every call writes what it reads first), so what a
+ * previous call left there is harmless. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+MOE_API moe_status moe_layer_noalloc(const moe_problem* p, const float* logits,
+                                     const void* x, const void* residual,
+                                     const void* w13, const void* w13_scale,
+                                     const void* w2, const void* w2_scale,
+                                     void* out, void* stream);
 
 /* ---------------------------------------------------------------------
  * Upstream fused norm ([P1] "融合算子优化"): the residual add, the RMSNorm in

@@ -23,19 +23,23 @@ __all__ = [
     "init_routing", "ffn_up", "ffn_down", "grouped_ffn", "finalize", "layer",
     "layer_workspace_bytes", "layer_traced", "SYMBOLS", "STAGES",
     "add_rms_norm_cast", "add_rms_norm_mx_quant", "router_logits",
-    "pack_weights", "quant_mxfp4_weights",
+    "pack_weights", "quant_mxfp4_weights", "layer_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
 MOE_F32, MOE_BF16, MOE_MXFP8_E4M3, MOE_MXFP4_E2M1, MOE_INT8 = 0, 1, 2, 3, 4
 MOE_LAYOUT_ROWMAJOR, MOE_LAYOUT_PACKED = 0, 1
+# the static scratch of moe_layer_noalloc (MOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 _LAYOUT = {"rowmajor": MOE_LAYOUT_ROWMAJOR, "packed": MOE_LAYOUT_PACKED}
 _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8_E4M3,
        "mxfp4": MOE_MXFP4_E2M1, "int8": MOE_INT8}
 
 SYMBOLS = ["moe_gate_topk", "moe_init_routing", "moe_grouped_ffn", "moe_ffn_up",
            "moe_ffn_down", "moe_finalize", "moe_layer", "moe_layer_traced",
+           "moe_layer_noalloc",
            "moe_add_rms_norm_cast", "moe_add_rms_norm_mx_quant",
            "moe_router_logits", "moe_pack_weights", "moe_quant_mxfp4_weights",
            "moe_status_string",
@@ -88,6 +92,7 @@ def lib() -> ctypes.CDLL:
         "moe_layer_traced": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _sz, _vp, ctypes.POINTER(ctypes.c_void_p),
                              ctypes.c_int32],
+        "moe_layer_noalloc": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     }
     _i32, _f32 = ctypes.c_int32, ctypes.c_float
     sig["moe_add_rms_norm_cast"] = [_i32, _i32, _vp, _vp, _vp, _f32, _vp, _vp,
@@ -315,6 +320,19 @@ def layer(p: MoeProblem, logits, x, w13, w2, w13_scale=None, w2_scale=None,
                            _ptr(residual), _ptr(w13), _ptr(w13_scale), _ptr(w2),
                            _ptr(w2_scale), _ptr(out), _ptr(workspace),
                            ctypes.byref(n), _stream()))
+    return out
+
+
+def layer_noalloc(p: MoeProblem, logits, x, w13, w2, w13_scale=None,
+                  w2_scale=None, residual=None, out=None):
+    """moe_layer_noalloc: the whole layer with the library's static scratch
+    as its workspace (no allocation by the library; `out` may be passed)."""
+    if out is None:
+        out = torch.empty((p.T, p.H), dtype=_act_dtype(p), device=x.device)
+    _check(lib().moe_layer_noalloc(ctypes.byref(p), _ptr(logits), _ptr(x),
+                                   _ptr(residual), _ptr(w13), _ptr(w13_scale),
+                                   _ptr(w2), _ptr(w2_scale), _ptr(out),
+                                   _stream()))
     return out
 
 

@@ -1,7 +1,16 @@
 // C ABI of the MoE expert layer: argument checks, workspace layout and the
-// launch sequence. No allocation, no host synchronisation, no global state.
+// launch sequence. No allocation and no host synchronisation; the only global
+// state is the per-device address of moe_layer_noalloc's static scratch.
+#include <mutex>
+
 #include "../../include/moe_mi355x.h"
 #include "launch.h"
+
+// Workspace of moe_layer_noalloc, for callers that cannot allocate: one copy
+// on every GPU the library runs on, held until the process ends. Host code
+// never names it directly (on the host the name is only a stand-in); it uses
+// the device address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -247,6 +256,27 @@ moe_status check_weights(const Prob& q, const void* w13, const void* w13s,
   } else if (w13s || w2s) {
     return MOE_ERR_INVALID_ARG;
   }
+  return MOE_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device
+
+// The current device's copy of `scratch`: looked up once per device (with that
+// device current) and kept.
+moe_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+      return MOE_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
   return MOE_OK;
 }
 
@@ -670,6 +700,26 @@ moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
                      size_t* workspace_bytes, void* stream) {
   return moe_layer_traced(p, logits, x, residual, w13, w13_scale, w2, w2_scale,
                           out, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+moe_status moe_layer_noalloc(const moe_problem* p, const float* logits,
+                             const void* x, const void* residual,
+                             const void* w13, const void* w13_scale,
+                             const void* w2, const void* w2_scale, void* out,
+                             void* stream) {
+  // host-side size query first: a problem past the scratch is refused
+  // before anything is looked up or launched
+  size_t need = 0;
+  moe_status st = moe_layer_traced(p, logits, x, residual, w13, w13_scale, w2,
+                                   w2_scale, out, nullptr, &need, stream,
+                                   nullptr, 0);
+  if (st != MOE_OK) return st;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_ptr(&ws)) != MOE_OK) return st;
+  size_t have = MOE_NOALLOC_SCRATCH_BYTES;
+  return moe_layer_traced(p, logits, x, residual, w13, w13_scale, w2, w2_scale,
+                          out, ws, &have, stream, nullptr, 0);
 }
 
 }  // extern "C"
