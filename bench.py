@@ -76,7 +76,7 @@ TRAFFIC = {
     "qwen3_30b_a3b_prefill_skewed_bf16":
         ("gemm_bf16_tiled", "ec4346a119d21336", 594356.3, 49152.0),
     "longcat_flash_zero_experts_bf16":
-        ("gemm_bf16_stream", "eb5dc45129abba45", 13281945.9, 32528.0),
+        ("gemm_bf16_stream", "6943bd7057a67181", 13281051.3, 32528.0),
     "qwen3_235b_a22b_ep_rank_w4a8":
         ("gemm_mx_tiled", "f992f0c5fedf635a", 200173.3, 12804.4),
     "qwen3_30b_a3b_decode_w8a8":
