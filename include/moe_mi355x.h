@@ -285,6 +285,37 @@ MOE_API moe_status moe_layer_traced(const moe_problem* p, const float* logits,
                                     size_t* workspace_bytes, void* stream,
                                     void* const* stage_events, int32_t n_events);
 
+/* Weight prefetch ([P2] "LongCat-Flash inference on Atlas A3 clusters",
+ * section 权重预取: the weights of a memory-bound matmul are fetched ahead
+ * while an earlier, latency-bound operator runs, about HBM bandwidth x that
+ * operator's duration of them; its AFD section does the same for the FFN
+ * side's grouped matmuls in communication gaps). Reads up to max_bytes of the
+ * expert weights the layer's grouped GEMMs will read first -- the heads of
+ * the K ranges their waves start at, for the experts of their first round of
+ * blocks -- so that those lines are in the GPU's caches (the memory-side
+ * cache in front of HBM) when moe_layer / moe_grouped_ffn runs next with the
+ * same problem and weights. For a caller to enqueue on a second stream while
+ * the operators in front of the MoE layer (attention, the fused norm) run.
+ * It writes nothing and changes no result.
+ *   topk_ids  int32 [T, top_k] (the gate's output) or NULL: only the experts
+ *             it routes to are read (ids outside the local range are
+ *             ignored); NULL reads every local expert.
+ *   w13, w2   the layer's weight arguments (as for moe_layer); which: bit 0
+ *             reads w13 (GEMM1), bit 1 w2 (GEMM2), the budget split 2 : 1.
+ *             w2's heads help only when GEMM1 leaves them cached, i.e. when
+ *             the layer's weights are small against the 256 MB cache.
+ *   max_bytes upper bound of the bytes read (>= 0; below 16 reads nothing).
+ * The layer itself does not prefetch: spare blocks of its gate and routing
+ * launches reading ahead were measured to lengthen those latency-bound
+ * kernels by more than the GEMM gained. Checks as for moe_layer (which
+ * outside 0..3 or max_bytes < 0: MOE_ERR_INVALID_ARG; fp32 problems:
+ * MOE_ERR_UNSUPPORTED). */
+MOE_API moe_status moe_prefetch_weights(const moe_problem* p,
+                                        const int32_t* topk_ids,
+                                        const void* w13, const void* w2,
+                                        int32_t which, int64_t max_bytes,
+                                        void* stream);
+
 /* moe_layer without a workspace argument, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation. The layer's intermediates live in a

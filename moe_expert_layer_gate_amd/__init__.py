@@ -23,7 +23,7 @@ __all__ = [
     "init_routing", "ffn_up", "ffn_down", "grouped_ffn", "finalize", "layer",
     "layer_workspace_bytes", "layer_traced", "SYMBOLS", "STAGES",
     "add_rms_norm_cast", "add_rms_norm_mx_quant", "router_logits",
-    "pack_weights", "quant_mxfp4_weights", "layer_noalloc",
+    "pack_weights", "quant_mxfp4_weights", "layer_noalloc", "prefetch_weights",
     "NOALLOC_SCRATCH_BYTES",
 ]
 
@@ -39,7 +39,7 @@ _DT = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8_E4M3,
 
 SYMBOLS = ["moe_gate_topk", "moe_init_routing", "moe_grouped_ffn", "moe_ffn_up",
            "moe_ffn_down", "moe_finalize", "moe_layer", "moe_layer_traced",
-           "moe_layer_noalloc",
+           "moe_layer_noalloc", "moe_prefetch_weights",
            "moe_add_rms_norm_cast", "moe_add_rms_norm_mx_quant",
            "moe_router_logits", "moe_pack_weights", "moe_quant_mxfp4_weights",
            "moe_status_string",
@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
                              _sz, _vp, ctypes.POINTER(ctypes.c_void_p),
                              ctypes.c_int32],
         "moe_layer_noalloc": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+        "moe_prefetch_weights": [_pp, _vp, _vp, _vp, ctypes.c_int32,
+                                 ctypes.c_int64, _vp],
     }
     _i32, _f32 = ctypes.c_int32, ctypes.c_float
     sig["moe_add_rms_norm_cast"] = [_i32, _i32, _vp, _vp, _vp, _f32, _vp, _vp,
@@ -334,6 +336,18 @@ def layer_noalloc(p: MoeProblem, logits, x, w13, w2, w13_scale=None,
                                    _ptr(w2), _ptr(w2_scale), _ptr(out),
                                    _stream()))
     return out
+
+
+def prefetch_weights(p: MoeProblem, w13, w2=None, topk_ids=None,
+                     max_bytes=64 << 20, which=None):
+    """moe_prefetch_weights on the current stream: read ahead up to
+    max_bytes of the weight heads the layer's grouped GEMMs read first
+    (which: 1 = w13, 2 = w2, 3 = both; default w13, and w2 when given)."""
+    if which is None:
+        which = 1 | (2 if w2 is not None else 0)
+    _check(lib().moe_prefetch_weights(ctypes.byref(p), _ptr(topk_ids), _ptr(w13),
+                                      _ptr(w2), int(which), int(max_bytes),
+                                      _stream()))
 
 
 def _norm_args(x, residual, norm_weight):

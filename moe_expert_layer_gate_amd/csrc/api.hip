@@ -107,6 +107,81 @@ long long max_tiles(const Prob& q, int mt) {
   return ne + q.N / mt + 1;
 }
 
+// ---------------------------------------------------------------- prefetch
+
+// Blocks of moe_prefetch_weights (256 threads each).
+constexpr int kPrefetchBlocks = 1024;
+
+// How a grouped GEMM reads one expert's weights: bytes per expert, bytes per
+// K step (every form keeps its weights K-major: bf16 [K, N], packed int8 /
+// e2m1 in 64-byte K chunks of all N columns), steps, the K split its waves
+// start at (streaming kernels), and how many tiles its first round of blocks
+// holds (the experts whose heads are read first).
+struct Geom {
+  long long ebytes = 0, step = 0;
+  int nsteps = 0, nseg = 0, round_tiles = 0;
+};
+
+Geom gemm_geom(const Prob& q, int mt, bool up) {
+  Geom g;
+  const int mtl = (int)max_tiles(q, mt);
+  if (q.El == 0 || mtl == 0 || q.act == MOE_F32) return g;
+  const int K = up ? q.H : q.I, N = up ? 2 * q.I : q.H, Nout = up ? q.I : q.H;
+  const int cus = moe::device_cus();
+  if (q.mx || mt >= 128) {
+    // tiled kernels: 64 bytes of K of every column per step; every (tile,
+    // slab) item walks K from its head, items of every expert run at once
+    const int eb2 = q.mx ? 1 : (q.i8 ? 2 : 4);  // element bytes x 2
+    g.ebytes = (long long)K * N * eb2 / 2;
+    g.step = 64LL * N;
+    g.nsteps = (int)(g.ebytes / g.step);
+    g.nseg = 1;
+    g.round_tiles = q.El;
+  } else if (q.i8) {
+    g.ebytes = (long long)K * N;
+    g.step = 128LL * N;
+    g.nsteps = K / 128;
+    g.nseg = moe::stream_i8_ksplit(up, mtl, K, Nout, mt / 16);
+    g.round_tiles = cus * (8 / g.nseg) / moe::stream_i8_slabs(up, Nout);
+  } else {
+    g.ebytes = (long long)K * N * 2;
+    g.step = 64LL * N;
+    g.nsteps = K / 32;
+    g.nseg = moe::stream_bf16_ksplit(up, mtl, K, Nout, mt / 16);
+    g.round_tiles = cus * (8 / g.nseg) / moe::stream_bf16_slabs(up, Nout);
+  }
+  return g;
+}
+
+// Prefetch of `budget` bytes: bytes [skip, skip + lead) of each K segment of
+// the first `nexp` selected experts (all local experts, or those `ids`
+// routes to), lead = budget / (nexp * segments), within the segments.
+moe::Prefetch make_prefetch(const Geom& g, const void* w, const Prob& q,
+                            const int32_t* ids, int nids, long long skip,
+                            long long budget, int nexp) {
+  moe::Prefetch pf{};
+  if (g.nseg <= 0 || nexp <= 0 || budget < 16 || !w) return pf;
+  const long long segmin = (long long)(g.nsteps / g.nseg) * g.step;
+  long long lead = budget / ((long long)nexp * g.nseg);
+  if (lead > segmin - skip) lead = segmin - skip;
+  lead &= ~15LL;
+  if (lead < 16) return pf;
+  pf.w = (const char*)w;
+  pf.ebytes = g.ebytes;
+  pf.step_bytes = g.step;
+  pf.nsteps = g.nsteps;
+  pf.nseg = g.nseg;
+  pf.skip = (int)skip;
+  pf.lead = (int)lead;
+  pf.nexp = nexp;
+  pf.El = q.El;
+  pf.ids = ids;
+  pf.nids = nids;
+  pf.fb = q.fb;
+  pf.sink = nullptr;
+  return pf;
+}
+
 struct Carve {
   char* base;
   size_t off = 0;
@@ -700,6 +775,44 @@ moe_status moe_layer(const moe_problem* p, const float* logits, const void* x,
                      size_t* workspace_bytes, void* stream) {
   return moe_layer_traced(p, logits, x, residual, w13, w13_scale, w2, w2_scale,
                           out, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+moe_status moe_prefetch_weights(const moe_problem* p, const int32_t* topk_ids,
+                                const void* w13, const void* w2, int32_t which,
+                                int64_t max_bytes, void* stream) {
+  Prob q;
+  moe_status st = check(p, &q);
+  if (st != MOE_OK) return st;
+  if ((which & ~3) || max_bytes < 0) return MOE_ERR_INVALID_ARG;
+  if (q.act == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (q.El == 0 || q.N == 0 || which == 0 || max_bytes < 16) return MOE_OK;
+  if (((which & 1) && !w13) || ((which & 2) && !w2)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(topk_ids, w13, w2)) return MOE_ERR_INVALID_ARG;
+  const int mt = tile_rows(q);
+  // w13 and w2 share the budget in proportion to their sizes (w13 holds
+  // H x 2I elements, w2 I x H: two thirds and one third)
+  long long b13 = 0, b2 = 0;
+  if (which == 3) {
+    b13 = max_bytes / 3 * 2;
+    b2 = max_bytes - b13;
+  } else if (which == 1) {
+    b13 = max_bytes;
+  } else {
+    b2 = max_bytes;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const int nids = topk_ids ? (int)q.N : 0;
+  for (int up = 1; up >= 0; --up) {
+    const long long b = up ? b13 : b2;
+    if (b < 16) continue;
+    const Geom g = gemm_geom(q, mt, up != 0);
+    int nexp = g.round_tiles < q.El ? g.round_tiles : q.El;
+    if (topk_ids && (long long)nexp > q.N) nexp = (int)q.N;
+    const moe::Prefetch pf =
+        make_prefetch(g, up ? w13 : w2, q, topk_ids, nids, 0, b, nexp);
+    MOE_TRY(moe::launch_prefetch(pf, kPrefetchBlocks, s));
+  }
+  return MOE_OK;
 }
 
 moe_status moe_layer_noalloc(const moe_problem* p, const float* logits,

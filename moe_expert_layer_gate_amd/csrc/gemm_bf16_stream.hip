@@ -310,6 +310,16 @@ int stream_ksplit(long long blocks, int steps, int rg) {
   return ks;
 }
 
+int stream_bf16_slabs(bool glu, int Nout) {
+  const int slab = glu ? 128 : 256;
+  return (Nout + slab - 1) / slab;
+}
+
+int stream_bf16_ksplit(bool glu, int max_tiles, int K, int Nout, int rg) {
+  return stream_ksplit((long long)stream_bf16_slabs(glu, Nout) * max_tiles,
+                       K / 32, rg);
+}
+
 hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
                                    const int32_t* tile_count, int max_tiles,
                                    const uint16_t* a, const uint16_t* w,
@@ -317,10 +327,9 @@ hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
                                    const int32_t* gidx, const int32_t* gbase,
                                    int gk, hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
-  const int slab = glu ? 128 : 256;
-  // (max_tiles < 65536: this schedule serves fewer than 64 rows per expert)
-  dim3 grid((Nout + slab - 1) / slab, max_tiles);
-  const int ksplit = stream_ksplit((long long)grid.x * grid.y, K / 32, rg);
+  // (max_tiles < 65536: this schedule serves fewer than 20 rows per expert)
+  dim3 grid(stream_bf16_slabs(glu, Nout), max_tiles);
+  const int ksplit = stream_bf16_ksplit(glu, max_tiles, K, Nout, rg);
   if (glu)
     return rg == 1 ? launch_stream<true, 1>(ksplit, grid, tiles, tile_count, a,
                                             w, out, K, Nw, Nout, gidx, gbase, gk, s)

@@ -240,6 +240,18 @@ hipError_t launch_i8s(int ksplit, dim3 grid, const Tile* tiles,
 
 }  // namespace
 
+int stream_i8_slabs(bool glu, int Nout) {
+  const int slab = glu ? 64 : 128;
+  return (Nout + slab - 1) / slab;
+}
+
+// a step of 128 K moves as many weight bytes per wave (16 KB) as a bf16 step
+// of 32, so the bf16 kernel's split rule applies in these steps
+int stream_i8_ksplit(bool glu, int max_tiles, int K, int Nout, int rg) {
+  return stream_ksplit((long long)stream_i8_slabs(glu, Nout) * max_tiles,
+                       K / 128, rg);
+}
+
 hipError_t launch_gemm_i8_stream(bool glu, int rg, const Tile* tiles,
                                  const int32_t* tile_count, int max_tiles,
                                  const int8_t* a, const float* a_scale,
@@ -248,12 +260,9 @@ hipError_t launch_gemm_i8_stream(bool glu, int rg, const Tile* tiles,
                                  const int32_t* gidx, const int32_t* gbase,
                                  int gk, hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
-  const int slab = glu ? 64 : 128;
-  // (max_tiles < 65536: this schedule serves fewer than 64 rows per expert)
-  dim3 grid((Nout + slab - 1) / slab, max_tiles);
-  // a step of 128 K moves as many weight bytes per wave (16 KB) as a bf16
-  // step of 32, so the bf16 kernel's split rule applies in these steps
-  const int ksplit = stream_ksplit((long long)grid.x * grid.y, K / 128, rg);
+  // (max_tiles < 65536: this schedule serves fewer than 12 rows per expert)
+  dim3 grid(stream_i8_slabs(glu, Nout), max_tiles);
+  const int ksplit = stream_i8_ksplit(glu, max_tiles, K, Nout, rg);
   if (glu)
     return rg == 1 ? launch_i8s<true, 1>(ksplit, grid, tiles, tile_count, a,
                                          a_scale, w, w_scale, out, K, Nw,

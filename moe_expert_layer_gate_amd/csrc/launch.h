@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "prefetch.h"
+
 namespace moe {
 
 // Tile of a grouped GEMM: local expert index and first row (relative to the
@@ -67,6 +69,12 @@ int device_cus();
 // Waves per block that split K in the weight-streaming kernels, for a grid
 // of `blocks` blocks and `steps` K steps of 16 KB of weights per wave.
 int stream_ksplit(long long blocks, int steps, int rg);
+// Column slabs (grid x) and K split of the bf16 / int8 weight-streaming
+// launches (the launchers use these; the weight prefetch follows them).
+int stream_bf16_slabs(bool glu, int Nout);
+int stream_bf16_ksplit(bool glu, int max_tiles, int K, int Nout, int rg);
+int stream_i8_slabs(bool glu, int Nout);
+int stream_i8_ksplit(bool glu, int max_tiles, int K, int Nout, int rg);
 
 // Grouped GEMMs. glu: GEMM1 with SwiGLU epilogue (N = 2*I weight columns,
 // I outputs), else GEMM2 (N outputs). Tiles come from the tile list.
@@ -145,6 +153,9 @@ hipError_t launch_gemm_mx_tiled(bool glu, const Tile* tiles,
                                 void* out, uint8_t* out_scale, int K, int Nw,
                                 int Nout, const int32_t* gidx,
                                 const int32_t* gbase, int gk, hipStream_t s);
+
+// The weight prefetch of pf (prefetch.h) on `blocks` blocks of its own.
+hipError_t launch_prefetch(const Prefetch& pf, int blocks, hipStream_t s);
 
 // Residual add + RMSNorm; mx = 0: fp32 and/or bf16 outputs, mx = 1: MXFP8
 // codes + e8m0 scales. H % 32 == 0, H <= 8192; residual / outputs may be null.

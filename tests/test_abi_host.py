@@ -277,3 +277,22 @@ def test_quant_mxfp4_weights_host_checks(L):
     assert q(2, 64, 16, ok, ok, None, None) == 1
     assert q(2, 64, 16, ok, ctypes.c_void_p((1 << 20) + 8), ok, None) == 1
     assert q(0, 64, 16, None, None, None, None) == 0    # nothing to do
+
+
+def test_prefetch_weights_host_checks(L):
+    ok = ctypes.c_void_p(1 << 20)  # never dereferenced: every case returns first
+    pf = L.moe_prefetch_weights
+    p = _p()
+    assert pf(ctypes.byref(p), None, ok, ok, 4, 1 << 20, None) == 1    # which
+    assert pf(ctypes.byref(p), None, ok, ok, 1, -1, None) == 1         # bytes
+    assert pf(ctypes.byref(p), None, None, ok, 1, 1 << 20, None) == 1  # no w13
+    assert pf(ctypes.byref(p), None, ok, None, 2, 1 << 20, None) == 1  # no w2
+    assert pf(ctypes.byref(p), None, ctypes.c_void_p((1 << 20) + 4), ok, 1,
+              1 << 20, None) == 1                                      # misaligned
+    assert pf(ctypes.byref(_p(act="f32", wt="f32", act_q="f32")), None, ok, ok,
+              1, 1 << 20, None) == 2
+    assert pf(ctypes.byref(_p(top_k=0)), None, ok, ok, 1, 1 << 20, None) == 1
+    # nothing to read: no launch
+    assert pf(ctypes.byref(p), None, None, None, 0, 1 << 20, None) == 0
+    assert pf(ctypes.byref(p), None, ok, ok, 3, 8, None) == 0
+    assert pf(ctypes.byref(_p(T=0)), None, ok, ok, 3, 1 << 20, None) == 0

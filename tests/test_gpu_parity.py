@@ -357,7 +357,9 @@ def test_layer_split_calls_equal_fused():
                  "tiny_fp32", "decode_bf16_small", "decode_w8a8_small",
                  "prefill_w8a8_small", "prefill_w8a8_mid_small",
                  "prefill_long_small", "prefill_w8a8_long_small",
-                 "decode_w8a8_h2048_small", "range_w8a8_small"):
+                 "decode_w8a8_h2048_small", "range_w8a8_small",
+                 "decode_bf16_32row_small", "range_w8a8_stream_small",
+                 "zero_experts_small"):
         shape = SMALL[name]
         inp = generate(shape, seed=6, device=DEV)
         p = m.problem(shape)
@@ -372,6 +374,51 @@ def test_layer_split_calls_equal_fused():
                          inp["residual"])
         torch.cuda.synchronize()
         assert np.array_equal(bits(out), bits(fused)), name
+
+
+@pytest.mark.parametrize("name", ["decode_bf16_small", "decode_w8a8_small",
+                                  "ep_w4a8_small", "prefill_wide_small",
+                                  "zero_experts_small", "decode_bf16_32row_small",
+                                  "range_w8a8_stream_small"])
+def test_prefetch_weights_changes_nothing(name):
+    """moe_prefetch_weights only reads: the layer gives the same bits after
+    it as before, whatever the budget (none, small, past every weight byte),
+    with and without routing ids (ids outside the range among them), for
+    w13, w2 or both."""
+    m = _m()
+    shape = SMALL[name]
+    inp = generate(shape, seed=9, device=DEV)
+    p = m.problem(shape)
+    args = (p, inp["logits"], inp["x"], inp["w13"], inp["w2"], inp["w13_scale"],
+            inp["w2_scale"])
+    want = m.layer(*args, residual=inp["residual"])
+    ids, _ = m.gate_topk(p, inp["logits"])
+    bad = ids.clone()
+    bad[0, 0] = -3
+    bad[-1, -1] = shape.E_tot + 5
+    for topk in (None, ids, bad):
+        for which in (1, 2, 3):
+            for nbytes in (0, 4096, 1 << 20, 1 << 40):
+                m.prefetch_weights(p, inp["w13"], inp["w2"], topk_ids=topk,
+                                   max_bytes=nbytes, which=which)
+    got = m.layer(*args, residual=inp["residual"])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got), bits(want))
+
+
+def test_prefetch_weights_full_size_decode():
+    """The decode workload at full size: prefetch of every expert's w13 heads
+    with the gate's ids, then the layer, equal to the layer alone."""
+    m = _m()
+    shape = get_workload("qwen3_30b_a3b_decode_bf16")
+    inp = generate(shape, seed=3, device=DEV)
+    p = m.problem(shape)
+    want = m.layer(p, inp["logits"], inp["x"], inp["w13"], inp["w2"])
+    ids, _ = m.gate_topk(p, inp["logits"])
+    m.prefetch_weights(p, inp["w13"], topk_ids=ids, max_bytes=96 << 20)
+    got = m.layer(p, inp["logits"], inp["x"], inp["w13"], inp["w2"])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got), bits(want))
 
 
 def test_layer_deterministic():
