@@ -263,19 +263,14 @@ hipError_t launch_gemm_i8_stream(bool glu, int rg, const Tile* tiles,
   // (max_tiles < 65536: this schedule serves fewer than 12 rows per expert)
   dim3 grid(stream_i8_slabs(glu, Nout), max_tiles);
   const int ksplit = stream_i8_ksplit(glu, max_tiles, K, Nout, rg);
+  // 16-row tiles only: below the tiled kernel's switch (12 rows per expert)
+  // 32-row tiles measured 8-12 % slower
+  if (rg != 1) return hipErrorInvalidValue;
   if (glu)
-    return rg == 1 ? launch_i8s<true, 1>(ksplit, grid, tiles, tile_count, a,
-                                         a_scale, w, w_scale, out, K, Nw,
-                                         Nout, gidx, gbase, gk, s)
-                   : launch_i8s<true, 2>(ksplit, grid, tiles, tile_count, a,
-                                         a_scale, w, w_scale, out, K, Nw,
-                                         Nout, gidx, gbase, gk, s);
-  return rg == 1 ? launch_i8s<false, 1>(ksplit, grid, tiles, tile_count, a,
-                                        a_scale, w, w_scale, out, K, Nw, Nout,
-                                        gidx, gbase, gk, s)
-                 : launch_i8s<false, 2>(ksplit, grid, tiles, tile_count, a,
-                                        a_scale, w, w_scale, out, K, Nw, Nout,
-                                        gidx, gbase, gk, s);
+    return launch_i8s<true, 1>(ksplit, grid, tiles, tile_count, a, a_scale, w,
+                               w_scale, out, K, Nw, Nout, gidx, gbase, gk, s);
+  return launch_i8s<false, 1>(ksplit, grid, tiles, tile_count, a, a_scale, w,
+                              w_scale, out, K, Nw, Nout, gidx, gbase, gk, s);
 }
 
 }  // namespace moe

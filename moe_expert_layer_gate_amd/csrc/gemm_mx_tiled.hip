@@ -1,5 +1,7 @@
 // Grouped GEMM, MXFP8 activations x MXFP4 weights on the scaled MFMA,
-// LDS-tiled schedule for prefill-size batches.
+// LDS-tiled schedule: the W4A8 path at every batch size (on the 4096 x 1536
+// experts of the W4A8 workload it beat streaming the weights through
+// registers from a single token on).
 //
 // [P1] "Qwen3-MoE low-latency inference on Atlas A3 / 950 clusters": W4A8
 // (MXFP4 weights, MXFP8 activations) on the prefill path (overview; Prefill
@@ -25,9 +27,11 @@
 //     request however few bytes it moves, so batching cuts the requests of
 //     the scales fourfold (measured: without any scale copies GEMM1 runs
 //     16 % faster); otherwise one 4-byte word per row and step.
-// v_mfma_scale_f32_16x16x128_f8f6f4 operand layout (lane l, q = l/16; see the
-// streaming MX kernel): A row l%16 bytes from K [16q,+16) and [64+16q,+16); B
-// column l%16 bytes from K [32q,+32); scales of K block q. Each wave owns
+// v_mfma_scale_f32_16x16x128_f8f6f4 operand layout on gfx950 (lane l,
+// q = l/16; measured with an in-bounds probe of one instruction): A (8
+// VGPRs) holds row l%16, bytes 0-15 from K [16q, +16) and bytes 16-31 from
+// K [64+16q, +16); B (e2m1, 4 VGPRs) holds column l%16, K [32q, +32); each
+// lane's e8m0 scale is that of K block q (K [32q, +32)) of its row / column. Each wave owns
 // 64 rows x 128 weight columns: 4 x 8 MFMAs per step, 128 fp32 accumulators;
 // 32-row halves past the tile's rows are skipped.
 // GEMM1 tiles hold 128 gate and the 128 matching up columns; a wave takes 64

@@ -107,7 +107,7 @@ hipError_t launch_gemm_i8_tiled(bool glu, int mt, const Tile* tiles,
                                 void* out, int K, int Nw, int Nout,
                                 const int32_t* gidx, const int32_t* gbase,
                                 int gk, hipStream_t s);
-// Same operands, weight-streaming tiles of 16 * rg rows (mt = 16 or 32),
+// Same operands, weight-streaming tiles of 16 rows (rg = 1; mt = 16),
 // K % 128 == 0.
 hipError_t launch_gemm_i8_stream(bool glu, int rg, const Tile* tiles,
                                  const int32_t* tile_count, int max_tiles,
