@@ -84,11 +84,17 @@ size_t act_bytes(const Prob& q) { return q.act == MOE_F32 ? 4 : 2; }
 // the switch bf16 streams 32-row tiles from 8 rows per expert (3-6 % faster
 // than 16-row ones at 8-12 rows), int8 16-row tiles throughout (32-row ones
 // were 8-12 % slower at 8-10 rows).
+// expected rows per expert from which the bf16 / int8 tiled GEMMs take
+// 256-row tiles
+#ifndef MOE_TILE256_AVG
+#define MOE_TILE256_AVG 512
+#endif
+
 int tile_rows(const Prob& q) {
   if (q.act == MOE_F32) return 32;
   if (q.mx) return 128;
   const long long avg = q.E ? q.N / q.E : 0;  // expected rows per expert
-  if (avg >= 512) return 256;
+  if (avg >= MOE_TILE256_AVG) return 256;
   if (avg >= (q.i8 ? 12 : 20)) return 128;
   return q.i8 || avg < 8 ? 16 : 32;
 }
