@@ -78,7 +78,7 @@ TRAFFIC = {
     "longcat_flash_zero_experts_bf16":
         ("gemm_bf16_stream", "eb5ca9dc954f8009", 13284339.7, 32528.0),
     "qwen3_235b_a22b_ep_rank_w4a8":
-        ("gemm_mx_tiled", "3d5c9a1c4de3af59", 168725.7, 12958.6),
+        ("gemm_mx_tiled", "b492aaad15b0855d", 167119.4, 12919.9),
     "qwen3_30b_a3b_decode_w8a8":
         ("gemm_i8_stream", "0a6ed31b3a726a2f", 171399.3, 768.4),
     "qwen3_30b_a3b_prefill_skewed_w8a8":
