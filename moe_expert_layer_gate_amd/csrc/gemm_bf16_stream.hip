@@ -131,8 +131,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
     const uint16_t* pB = we + (size_t)(k0 + 8 * kq) * Nw + ldB;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      st.bA[r] = *(const uint4*)(pA + (size_t)r * Nw);
-      st.bB[r] = *(const uint4*)(pB + (size_t)r * Nw);
+      st.bA[r] = load_stream16(pA + (size_t)r * Nw);
+      st.bB[r] = load_stream16(pB + (size_t)r * Nw);
     }
   };
   auto load_a = [&](Stage& st, int s) {

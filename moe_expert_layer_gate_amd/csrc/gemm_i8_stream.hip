@@ -108,8 +108,8 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_i8_stream_kernel(
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       const int8_t* p = we + frag[gi] + (size_t)(2 * s) * Nw * 64;
-      st.b[gi][0] = *(const uint4*)p;
-      st.b[gi][1] = *(const uint4*)(p + (size_t)Nw * 64);
+      st.b[gi][0] = load_stream16(p);
+      st.b[gi][1] = load_stream16(p + (size_t)Nw * 64);
     }
   };
   auto load_a = [&](Stage& st, int s) {
