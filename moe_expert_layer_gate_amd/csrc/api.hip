@@ -76,16 +76,25 @@ size_t act_bytes(const Prob& q) { return q.act == MOE_F32 ? 4 : 2; }
 // tiles leave half of their waves without rows.) The streaming kernels read
 // an expert's weights once per tile they run, the tiled ones once per 128
 // rows, so the tiled kernels take over from a few rows per expert on: from
-// 12 for int8 and 20 for bf16 (the measured crossovers on the 2048 x 768
-// expert shape; with 6144 x 2048 bf16 experts streaming 32-row tiles was
-// still 4.6 % faster at 16 rows). W4A8 always runs the tiled scaled-MFMA
+// 13 for int8 and 20 for bf16 (the measured crossovers on the 2048 x 768
+// expert shape, with the streamed weights loaded nontemporally: int8 layer
+// 141.2 us streaming vs 146.6 us tiled at 12 rows, 151.9 vs 148.3 us at
+// 14; bf16 239.0 vs 239.2 us at 20 rows, 310.1 vs 244.5 us at 32; with
+// 6144 x 2048 bf16 experts streaming 32-row tiles was still 4.6 % faster
+// at 16 rows). W4A8 always runs the tiled scaled-MFMA
 // kernels, which beat weight streaming on 4096 x 1536 experts from a single
 // token on (1 to 128 tokens of a 32-expert share: 15-26 % faster). Below
 // the switch bf16 streams 32-row tiles from 8 rows per expert (3-6 % faster
 // than 16-row ones at 8-12 rows), int8 16-row tiles throughout (32-row ones
 // were 8-12 % slower at 8-10 rows).
-// expected rows per expert from which the bf16 / int8 tiled GEMMs take
-// 256-row tiles
+// Expected rows per expert from which the bf16 / int8 tiled GEMMs take over
+// from weight streaming, and from which they take 256-row tiles.
+#ifndef MOE_TILED_FROM_BF16
+#define MOE_TILED_FROM_BF16 20
+#endif
+#ifndef MOE_TILED_FROM_I8
+#define MOE_TILED_FROM_I8 13
+#endif
 #ifndef MOE_TILE256_AVG
 #define MOE_TILE256_AVG 512
 #endif
@@ -95,7 +104,7 @@ int tile_rows(const Prob& q) {
   if (q.mx) return 128;
   const long long avg = q.E ? q.N / q.E : 0;  // expected rows per expert
   if (avg >= MOE_TILE256_AVG) return 256;
-  if (avg >= (q.i8 ? 12 : 20)) return 128;
+  if (avg >= (q.i8 ? MOE_TILED_FROM_I8 : MOE_TILED_FROM_BF16)) return 128;
   return q.i8 || avg < 8 ? 16 : 32;
 }
 
