@@ -66,6 +66,11 @@
 // rank: layer 479.6 -> 469.3 us (bf16), 332.0 -> 329.6 us (W8A8), 244.8 ->
 // 240.0 us (W4A8; its GEMM2 65.6 -> 61.9 us), 1530.6 -> 1507.2 us at 16384
 // tokens; groups of 1 (slab-major) or 2 were no better.
+// Weights of single-tile experts copied with the nontemporal hint (0: never).
+#ifndef MOE_TILED_NT_SINGLE
+#define MOE_TILED_NT_SINGLE 1
+#endif
+
 #ifndef MOE_TILED_SLAB_GROUP
 #define MOE_TILED_SLAB_GROUP 3
 #endif
@@ -167,6 +172,9 @@ MOE_DEV void tiled_item(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const char* we = (const char*)w + (size_t)tl.expert * K * Nw * EB;
+  // an expert with one tile is the only reader of its weights: stream them
+  const bool wnt = MOE_TILED_NT_SINGLE &&
+                   __builtin_amdgcn_readfirstlane(tl.count) == 1;
 
   // ---- global -> LDS assignment (per wave instruction: 1 KB contiguous)
   // A, instruction j (0..NA-1): tile rows 16*(wave + NW*j) + lane/4, physical
@@ -246,11 +254,12 @@ MOE_DEV void tiled_item(
     if constexpr (I8) {                                                       \
       const char* bb_ = we + (uint32_t)(s_) * b_step_i8;                      \
       _Pragma("unroll") for (int j = 0; j < NB; ++j)                          \
-        g2lds(bb_, b_off[j], b_dst + o_ + 16 * NW * j * 64);                  \
+        g2lds_w(bb_, b_off[j], b_dst + o_ + 16 * NW * j * 64, wnt);           \
     } else {                                                                  \
       const char* bb_ = we + (size_t)(s_) * b_step;                           \
       _Pragma("unroll") for (int j = 0; j < NB; ++j)                          \
-        g2lds(bb_, b_off[0] + j * b_rowj, b_dst + o_ + 2 * NW * j * B_ROW);   \
+        g2lds_w(bb_, b_off[0] + j * b_rowj, b_dst + o_ + 2 * NW * j * B_ROW,  \
+                wnt);                                                         \
     }                                                                         \
   } while (0)
 

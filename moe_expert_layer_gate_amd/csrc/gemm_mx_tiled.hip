@@ -51,6 +51,11 @@
 // rank: layer 479.6 -> 469.3 us (bf16), 332.0 -> 329.6 us (W8A8), 244.8 ->
 // 240.0 us (W4A8; its GEMM2 65.6 -> 61.9 us), 1530.6 -> 1507.2 us at 16384
 // tokens; groups of 1 (slab-major) or 2 were no better.
+// Weights of single-tile experts copied with the nontemporal hint (0: never).
+#ifndef MOE_MX_NT_SINGLE
+#define MOE_MX_NT_SINGLE 1
+#endif
+
 #ifndef MOE_MX_SLAB_GROUP
 #define MOE_MX_SLAB_GROUP 3
 #endif
@@ -120,6 +125,9 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int KB = K / 32;
   const uint8_t* we = w + (size_t)tl.expert * Nw * (K / 2);
+  // an expert with one tile is the only reader of its weights: stream them
+  const bool wnt = MOE_MX_NT_SINGLE &&
+                   __builtin_amdgcn_readfirstlane(tl.count) == 1;
   const uint8_t* wse = ws + (size_t)tl.expert * Nw * KB;
   // A rows: the tile's rows of the permuted codes, or with a gather index
   // the token rows of the per-token codes (32-bit offsets, checked by the
@@ -179,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
       g2lds(ab_, a_off[j], a_dst + o_ + 32 * j * MBK);                        \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
-      g2lds(bb_, b_off[j], b_dst + o_ + 64 * j * (MBK / 2));                  \
+      g2lds_w(bb_, b_off[j], b_dst + o_ + 64 * j * (MBK / 2), wnt);           \
   } while (0)
   // scales of K steps [SCB*g_, SCB*g_ + SCB) into slot g_ % 2 (1 or 2
   // instructions per wave)
@@ -397,6 +405,9 @@ __global__ __launch_bounds__(256, 2) void gemm_mx32_tiled_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int KB = K / 32;
   const uint8_t* we = w + (size_t)tl.expert * Nw * (K / 2);
+  // an expert with one tile is the only reader of its weights: stream them
+  const bool wnt = MOE_MX_NT_SINGLE &&
+                   __builtin_amdgcn_readfirstlane(tl.count) == 1;
   const uint8_t* wse = ws + (size_t)tl.expert * Nw * KB;
   const uint8_t* a_tile = a + (size_t)tl.row0 * K;
   const uint8_t* as_tile = as + (size_t)tl.row0 * KB;
@@ -433,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx32_tiled_kernel(
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
       g2lds(ab_, a_off[j], a_dst + o_ + 32 * j * MBK);                        \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
-      g2lds(bb_, b_off[j], b_dst + o_ + 64 * j * (MBK / 2));                  \
+      g2lds_w(bb_, b_off[j], b_dst + o_ + 64 * j * (MBK / 2), wnt);           \
   } while (0)
 #define MOE_MX_ISSUE_SCALES(g_)                                               \
   do {                                                                        \

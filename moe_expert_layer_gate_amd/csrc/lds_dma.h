@@ -24,6 +24,27 @@ MOE_DEV void g2lds(const void* base, uint32_t voff, uint32_t lds_wave_base) {
       : "memory");
 }
 
+// The same copy with the nontemporal hint, for weights that no other tile
+// reads (an expert with a single tile): a stream that will not be reused.
+MOE_DEV void g2lds_nt(const void* base, uint32_t voff, uint32_t lds_wave_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1 nt"
+      :
+      : "v"(voff), "s"(base), "s"(lds_wave_base)
+      : "memory");
+}
+
+// Weight copy: nontemporal when nt (a wave-uniform flag), else plain.
+MOE_DEV void g2lds_w(const void* base, uint32_t voff, uint32_t lds_wave_base,
+                     bool nt) {
+  if (nt)
+    g2lds_nt(base, voff, lds_wave_base);
+  else
+    g2lds(base, voff, lds_wave_base);
+}
+
 MOE_DEV uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
