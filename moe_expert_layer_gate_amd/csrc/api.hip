@@ -76,12 +76,13 @@ size_t act_bytes(const Prob& q) { return q.act == MOE_F32 ? 4 : 2; }
 // tiles leave half of their waves without rows.) The streaming kernels read
 // an expert's weights once per tile they run, the tiled ones once per 128
 // rows, so the tiled kernels take over from a few rows per expert on: from
-// 13 for int8 and 20 for bf16 (the measured crossovers on the 2048 x 768
-// expert shape, with the streamed weights loaded nontemporally: int8 layer
-// 141.2 us streaming vs 146.6 us tiled at 12 rows, 151.9 vs 148.3 us at
-// 14; bf16 239.0 vs 239.2 us at 20 rows, 310.1 vs 244.5 us at 32; with
-// 6144 x 2048 bf16 experts streaming 32-row tiles was still 4.6 % faster
-// at 16 rows). W4A8 always runs the tiled scaled-MFMA
+// 10 for int8 and 20 for bf16 (measured with both kinds streaming weights
+// that only they read nontemporally: int8 on the 2048 x 768 expert shape
+// 123.5 us streaming vs 130.6 us tiled at 8 rows, 134.8 vs 132.9 us at 10,
+// 141.1 vs 134.3 us at 12; bf16 on the same shape is 2-5 % faster tiled
+// from 4 rows on (201.5 vs 197.4 us at 4, 210.4 vs 200.9 us at 8), but on
+// 6144 x 2048 experts streaming stays ahead (6090 vs 6340 us at 16 rows),
+// so bf16 switches at 20). W4A8 always runs the tiled scaled-MFMA
 // kernels, which beat weight streaming on 4096 x 1536 experts from a single
 // token on (1 to 128 tokens of a 32-expert share: 15-26 % faster). Below
 // the switch bf16 streams 32-row tiles from 8 rows per expert (3-6 % faster
@@ -93,7 +94,7 @@ size_t act_bytes(const Prob& q) { return q.act == MOE_F32 ? 4 : 2; }
 #define MOE_TILED_FROM_BF16 20
 #endif
 #ifndef MOE_TILED_FROM_I8
-#define MOE_TILED_FROM_I8 13
+#define MOE_TILED_FROM_I8 10
 #endif
 #ifndef MOE_TILE256_AVG
 #define MOE_TILE256_AVG 512

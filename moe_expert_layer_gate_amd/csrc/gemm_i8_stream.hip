@@ -260,10 +260,10 @@ hipError_t launch_gemm_i8_stream(bool glu, int rg, const Tile* tiles,
                                  const int32_t* gidx, const int32_t* gbase,
                                  int gk, hipStream_t s) {
   if (max_tiles == 0) return hipSuccess;
-  // (max_tiles < 65536: this schedule serves fewer than 13 rows per expert)
+  // (max_tiles < 65536: this schedule serves fewer than 10 rows per expert)
   dim3 grid(stream_i8_slabs(glu, Nout), max_tiles);
   const int ksplit = stream_i8_ksplit(glu, max_tiles, K, Nout, rg);
-  // 16-row tiles only: below the tiled kernel's switch (13 rows per expert)
+  // 16-row tiles only: below the tiled kernel's switch (10 rows per expert)
   // 32-row tiles measured 8-12 % slower
   if (rg != 1) return hipErrorInvalidValue;
   if (glu)

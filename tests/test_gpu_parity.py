@@ -84,17 +84,18 @@ SMALL = {
     "prefill_w8a8_long_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_w8a8"),
                                       T=1200, H=384, I=384, n_ffn=8,
                                       local_end=8, top_k=4),
-    # W8A8 with H = 2048: x quantised per token inside the gate kernel
+    # W8A8 with H = 2048: x quantised per token inside the gate kernel; 8
+    # rows per expert (streaming GEMMs)
     "decode_w8a8_h2048_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"),
-                                      T=40, H=2048, I=256, n_ffn=16,
+                                      T=32, H=2048, I=256, n_ffn=16,
                                       local_end=16, top_k=4),
     # W8A8 on an expert range, about 24 rows per expert: 128-row tiles
     "range_w8a8_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"), T=96,
                                H=256, I=256, n_ffn=16, local_begin=4,
                                local_end=10, top_k=4),
-    # W8A8 on an expert range, 10 rows per expert: 16-row streaming tiles
+    # W8A8 on an expert range, 8 rows per expert: 16-row streaming tiles
     "range_w8a8_stream_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"),
-                                      T=40, H=256, I=256, n_ffn=16,
+                                      T=32, H=256, I=256, n_ffn=16,
                                       local_begin=4, local_end=10, top_k=4),
     # bf16 with 16 rows per expert: 32-row streaming tiles
     "decode_bf16_32row_small": scaled(get_workload("qwen3_30b_a3b_decode_bf16"),
