@@ -264,15 +264,10 @@ static hipError_t launch_stream(int ksplit, dim3 grid, const Tile* tiles,
                                 const uint16_t* w, uint16_t* out, int K, int Nw,
                                 int Nout, const int32_t* gidx,
                                 const int32_t* gbase, int gk, hipStream_t s) {
-  switch (ksplit) {
+  switch (ksplit) {  // 1 or 3 (stream_ksplit)
     case 1:
       hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 1>), grid, dim3(64),
                          0, s, tiles, tile_count, a, w, out, K, Nw, Nout, gidx, gbase, gk);
-      break;
-    case 2:
-      hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 2>), grid,
-                         dim3(128), 0, s, tiles, tile_count, a, w, out, K, Nw,
-                         Nout, gidx, gbase, gk);
       break;
     default:
       hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 3>), grid,
@@ -293,21 +288,23 @@ int device_cus() {
 }
 
 // Waves per block that split K. Decode launches have few (tile, slab) blocks;
-// splitting K across up to 3 waves fills the chip, but only as far as every
-// block stays resident in one round and each wave keeps at least 4 steps.
-// At two waves per SIMD a CU holds 8 waves, i.e. floor(8 / k) blocks of k
-// waves: 2 blocks of 3 waves leave two slots empty, so a 3-way split holds
-// 512 blocks per round on 256 CUs, not 2048 / 3 (counting wave slots let
-// the decode GEMM1's 666 blocks spill into a partial second round, which
-// cost it 3-4 %). The grid is sized for the host's upper bound on the tile
-// count; the tiles that exist on the device are typically 3/4 of it.
+// splitting K across 3 waves fills the chip, but only as far as every block
+// stays resident in one round and each wave keeps at least 4 steps. At two
+// waves per SIMD a CU holds 8 waves, i.e. floor(8 / 3) = 2 blocks of 3
+// waves: a 3-way split holds 512 blocks per round on 256 CUs, not 2048 / 3
+// (counting wave slots let the decode GEMM1's 666 blocks spill into a
+// partial second round, which cost it 3-4 %). Beyond that one wave per
+// block: with the weights streamed nontemporally, a 2-way split of the
+// decode GEMMs' 616-822 blocks was 1.5-2.5 % slower than none (Qwen3-30B
+// decode layer 179.2 vs 176.5 us at 32 tokens, 203.3 vs 198.2 us at 64),
+// while at 1-6 tokens the 3-way split stays 0.1-20 us ahead. The grid is
+// sized for the host's upper bound on the tile count; the tiles that exist
+// on the device are typically 3/4 of it.
 int stream_ksplit(long long blocks, int steps, int rg) {
   (void)rg;
-  int ks = 1;
-  for (int k = 2; k <= 3; ++k)
-    if (blocks * 3 / 4 <= (long long)device_cus() * (8 / k) && steps / k >= 4)
-      ks = k;
-  return ks;
+  if (blocks * 3 / 4 <= (long long)device_cus() * (8 / 3) && steps / 3 >= 4)
+    return 3;
+  return 1;
 }
 
 int stream_bf16_slabs(bool glu, int Nout) {

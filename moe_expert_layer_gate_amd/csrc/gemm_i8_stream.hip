@@ -218,16 +218,11 @@ hipError_t launch_i8s(int ksplit, dim3 grid, const Tile* tiles,
                       const float* as, const int8_t* w, const float* ws,
                       void* out, int K, int Nw, int Nout, const int32_t* gidx,
                       const int32_t* gbase, int gk, hipStream_t s) {
-  switch (ksplit) {
+  switch (ksplit) {  // 1 or 3 (stream_ksplit)
     case 1:
       hipLaunchKernelGGL((gemm_i8_stream_kernel<GLU, RG, 1>), grid, dim3(64), 0,
                          s, tiles, tile_count, a, as, w, ws, out, K, Nw, Nout,
                          gidx, gbase, gk);
-      break;
-    case 2:
-      hipLaunchKernelGGL((gemm_i8_stream_kernel<GLU, RG, 2>), grid, dim3(128),
-                         0, s, tiles, tile_count, a, as, w, ws, out, K, Nw,
-                         Nout, gidx, gbase, gk);
       break;
     default:
       hipLaunchKernelGGL((gemm_i8_stream_kernel<GLU, RG, 3>), grid, dim3(192),
