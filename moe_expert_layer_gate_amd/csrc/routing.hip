@@ -96,25 +96,29 @@ __device__ void build_tiles_block(const int32_t* cnt_lds, const int32_t* off_lds
   for (int i = threadIdx.x; i < El; i += blockDim.x)
     tmp[i] = (cnt_lds[fb + i] + mt - 1) / mt;
   __syncthreads();
-  int total = block_exclusive_scan(tmp, El, wsum);
+  const int total = block_exclusive_scan(tmp, El, wsum);
   const int r0 = off_lds[fb];
-  for (int i = threadIdx.x; i < El; i += blockDim.x) {
-    int n = cnt_lds[fb + i];
-    int start = tmp[i];
-    for (int m = 0; m * mt < n; ++m) {
-      int ti = start + m;
-      if (ti >= max_tiles) break;
-      Tile tl;
-      tl.expert = i;
-      tl.row0 = off_lds[fb + i] - r0 + m * mt;
-      tl.rows = min(mt, n - m * mt);
-      tl.first = start;
-      tl.count = (n + mt - 1) / mt;
-      tl.pad[0] = tl.pad[1] = tl.pad[2] = 0;
-      tiles[ti] = tl;
+  // one thread per tile: its expert is the last one whose first tile is at
+  // or before it (experts without tiles share their successor's start)
+  const int nt = min(total, max_tiles);
+  for (int ti = threadIdx.x; ti < nt; ti += blockDim.x) {
+    int lo = 0, hi = El - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tmp[mid] <= ti) lo = mid;
+      else hi = mid - 1;
     }
+    const int n = cnt_lds[fb + lo], m = ti - tmp[lo];
+    Tile tl;
+    tl.expert = lo;
+    tl.row0 = off_lds[fb + lo] - r0 + m * mt;
+    tl.rows = min(mt, n - m * mt);
+    tl.first = tmp[lo];
+    tl.count = (n + mt - 1) / mt;
+    tl.pad[0] = tl.pad[1] = tl.pad[2] = 0;
+    tiles[ti] = tl;
   }
-  if (threadIdx.x == 0) tile_count[0] = min(total, max_tiles);
+  if (threadIdx.x == 0) tile_count[0] = nt;
 }
 
 // Optional per-token quantisation of x riding along with the scan (RowQuant
@@ -164,8 +168,11 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
   while (tpe * 2 * E <= (int)blockDim.x) tpe *= 2;
   while (tpe < (int)blockDim.x && (nchunks + tpe - 1) / tpe > kScanRegs) tpe *= 2;
   const int per = (nchunks + tpe - 1) / tpe;
-  for (int e0 = 0; e0 < E; e0 += blockDim.x / tpe) {
-    const int e = e0 + (int)threadIdx.x / tpe, q = threadIdx.x % tpe;
+  // consecutive threads take consecutive experts of one chunk range, so each
+  // load and store of a wave covers 64 adjacent counts of one chunk row
+  const int epp = (int)blockDim.x / tpe;  // experts per pass
+  for (int e0 = 0; e0 < E; e0 += epp) {
+    const int e = e0 + (int)threadIdx.x % epp, q = (int)threadIdx.x / epp;
     const bool act = e < E;
     const int c0 = q * per, c1 = min(nchunks, c0 + per);
     int sum = 0;
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     __syncthreads();
     if (act) {
       int base = 0;
-      for (int j = 0; j < q; ++j) base += part[threadIdx.x - q + j];
+      for (int j = 0; j < q; ++j) base += part[j * epp + (int)threadIdx.x % epp];
       if (q == tpe - 1) { cnt[e] = base + sum; off[e] = base + sum; counts[e] = base + sum; }
       if (per <= kScanRegs) {
 #pragma unroll
