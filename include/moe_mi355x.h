@@ -273,11 +273,12 @@ MOE_API moe_status moe_layer(const moe_problem* p, const float* logits, const vo
  * after the last. Each of stages 0-7 is at most one kernel launch (a stage
  * with nothing to do launches nothing), except stage 6 for INT8, which
  * quantises h and then runs GEMM2. Where x is quantised once per token
- * (INT8, and MXFP8 with 128-row GEMM tiles), the scan launch of stage 2
- * quantises it beside the scan when routing takes the multi-block path
- * (more than 4096 copies or 1024 experts), else, for E_tot <= 256, the gate
- * launch of stage 0 (int8: only for H = 2048 or 4096); stage 4 is then
- * empty. For performance tooling; results are identical to moe_layer. */
+ * (INT8, and MXFP8 with 128-row GEMM tiles), the gate launch of stage 0
+ * quantises it for E_tot <= 256 (int8: only for H = 2048 or 4096), else
+ * the scan launch of stage 2 when routing takes the multi-block path (more
+ * than 4096 copies or 1024 experts); stage 4 is then empty, and otherwise
+ * holds the quantisation. For performance tooling; results are identical
+ * to moe_layer. */
 MOE_API moe_status moe_layer_traced(const moe_problem* p, const float* logits,
                                     const void* x, const void* residual,
                                     const void* w13, const void* w13_scale,

@@ -89,6 +89,16 @@ SMALL = {
     "decode_w8a8_h2048_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"),
                                       T=32, H=2048, I=256, n_ffn=16,
                                       local_end=16, top_k=4),
+    # W4A8 with 320 experts (the gate launch takes no quantising blocks
+    # above 256) and more than 4096 copies: x quantised beside the scan
+    "ep_w4a8_320e_small": scaled(get_workload("qwen3_235b_a22b_ep_rank_w4a8"),
+                                 T=640, H=256, I=256, n_ffn=320, top_k=8,
+                                 local_begin=64, local_end=96),
+    # the same for W8A8 with 2048-wide rows (each lane keeps its 4 chunks of
+    # 512 in registers)
+    "ep_w8a8_320e_small": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_w8a8"),
+                                 T=640, H=2048, I=256, n_ffn=320, top_k=8,
+                                 local_begin=64, local_end=96),
     # W8A8 on an expert range, about 24 rows per expert: 128-row tiles
     "range_w8a8_small": scaled(get_workload("qwen3_30b_a3b_decode_w8a8"), T=96,
                                H=256, I=256, n_ffn=16, local_begin=4,
