@@ -72,17 +72,17 @@ TRAFFIC = {
     # workload: (kernel source set, sha256[:16] of its sources, FETCH KiB,
     #            WRITE KiB) per GEMM1 dispatch
     "qwen3_30b_a3b_decode_bf16":
-        ("gemm_bf16_stream", "08dea1be81d243a0", 341644.5, 384.0),
+        ("gemm_bf16_stream", "20459705c7982308", 341630.6, 384.0),
     "qwen3_30b_a3b_prefill_skewed_bf16":
-        ("gemm_bf16_tiled", "33eee07361dcb584", 523120.3, 49152.0),
+        ("gemm_bf16_tiled", "52b774f3f8277440", 521906.6, 49152.0),
     "longcat_flash_zero_experts_bf16":
-        ("gemm_bf16_stream", "08dea1be81d243a0", 12854938.8, 32528.0),
+        ("gemm_bf16_stream", "20459705c7982308", 12854819.6, 32528.0),
     "qwen3_235b_a22b_ep_rank_w4a8":
-        ("gemm_mx_tiled", "9db6e23a41832e41", 166490.9, 12909.9),
+        ("gemm_mx_tiled", "406ee714f43fb895", 161412.0, 12866.9),
     "qwen3_30b_a3b_decode_w8a8":
-        ("gemm_i8_stream", "64c0730c3f588b4a", 171196.2, 768.1),
+        ("gemm_i8_stream", "bec598550b7bdc37", 171200.7, 768.0),
     "qwen3_30b_a3b_prefill_skewed_w8a8":
-        ("gemm_bf16_tiled", "33eee07361dcb584", 232546.8, 98304.0),
+        ("gemm_bf16_tiled", "52b774f3f8277440", 228163.1, 98304.0),
 }
 
 
