@@ -89,29 +89,6 @@ MOE_DEV uint32_t rne_shift(uint32_t m, int sh) {
   return q;
 }
 
-// e4m3fn code of v * 2^-s, rounded to nearest (ties to even), saturating at
-// 448, sign kept. Exact integer arithmetic on the fp32 bits of v.
-MOE_DEV uint32_t e4m3_encode_scaled(float v, int s) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  int ex = (int)((u >> 23) & 0xFF);
-  uint32_t M = u & 0x7FFFFFu;
-  if (ex) M |= 0x800000u; else ex = 1;
-  if (M == 0) return sign;
-  int p = ex - 150 - s;                      // |v| * 2^-s = M * 2^p
-  int nb = 32 - __clz((int)M);               // bit length of M
-  int e = nb - 1 + p;                        // floor(log2(|v| 2^-s))
-  if (e >= -6) {                             // e4m3 normal range
-    uint32_t r = rne_shift(M, nb - 4);       // 4 significant bits, in [8,16]
-    if (r == 16) { r = 8; ++e; }
-    if (e > 8 || (e == 8 && r > 14)) return sign | 0x7Eu;   // saturate 448
-    return sign | ((uint32_t)(e + 7) << 3) | (r - 8);
-  }
-  // subnormal: multiples of 2^-9; rounding up to 8 lands on the min normal
-  uint32_t n = rne_shift(M, -(p + 9));
-  return sign | n;
-}
-
 // e8m0 shared exponent of an MXFP4 block: floor(log2(amax)) - 2 (emax of
 // e2m1), clamped to [-127, 127]; an all-zero block gives -127 (code 0).
 MOE_DEV int mx_e2m1_scale_exp(float amax) {
@@ -144,24 +121,27 @@ MOE_DEV uint32_t e2m1_encode_scaled(float v, int s) {
   return sign | rne_shift(M, -(p + 1));
 }
 
-// Same code as e4m3_encode_scaled, with fp32 arithmetic and no branches:
-// w = v * 2^-s is exact whenever it matters (|w| < 2^9 inside an MX block;
-// results below the fp32 normal range are far under e4m3's smallest step and
-// encode as zero either way). Subnormal range (|w| < 2^-6): the magic-number
-// add rounds |w| * 2^9 to an integer ties-to-even, and 8 lands on the code of
-// the smallest normal. Normal range: rounding the fp32 bits at mantissa bit
-// 20 (ties to even) leaves exponent and 3 mantissa bits, rebiased from 127 to
-// 7; codes past 0x7E (448) saturate.
-MOE_DEV uint32_t e4m3_encode_fast(float v, int s) {
-  const float w = __builtin_amdgcn_ldexpf(v, -s);
-  const uint32_t sign = (__float_as_uint(w) >> 24) & 0x80u;
-  const float a = __builtin_fabsf(w);
-  const uint32_t sub = (uint32_t)((a * 512.0f + 8388608.0f) - 8388608.0f);
-  uint32_t u = __float_as_uint(a);
-  u += 0x7FFFFu + ((u >> 20) & 1u);
-  uint32_t nrm = (u >> 20) - (120u << 3);
-  nrm = nrm > 0x7Eu ? 0x7Eu : nrm;
-  return sign | (a < 0.015625f ? sub : nrm);
+// Two e4m3fn codes, of a * 2^-s and b * 2^-s, by the hardware conversion
+// (OCP e4m3, round to nearest even) after clamping to +-448 (saturation):
+// into bytes 0-1 of the result, or with hi into bytes 2-3 keeping bytes 0-1
+// of old. This is the exact rounding (ties to even, saturating at 448, sign
+// kept, subnormals included) wherever |v * 2^-s| < 512, which the MX block
+// scale guarantees: compared on MI355X with an exact integer encoder over
+// every fp32 value of magnitude below 512, with no difference. Not for NaN
+// or infinite inputs.
+MOE_DEV uint32_t e4m3x2_hw(float a, float b, int s, uint32_t old = 0,
+                           bool hi = false) {
+  const float wa =
+      fminf(fmaxf(__builtin_amdgcn_ldexpf(a, -s), -448.0f), 448.0f);
+  const float wb =
+      fminf(fmaxf(__builtin_amdgcn_ldexpf(b, -s), -448.0f), 448.0f);
+  return hi ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(wa, wb, (int)old, true)
+            : (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(wa, wb, (int)old, false);
+}
+
+// Four codes of v[0..3] * 2^-s, v[i] in byte i.
+MOE_DEV uint32_t e4m3x4_hw(const float* v, int s) {
+  return e4m3x2_hw(v[2], v[3], s, e4m3x2_hw(v[0], v[1], s), true);
 }
 
 // ---------------------------------------------------------------- misc

@@ -336,8 +336,9 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
           for (int off = 1; off < 16; off <<= 1)
             amax = fmaxf(amax, __shfl_xor(amax, off));
           const int sx = mx_e4m3_scale_exp(amax);
-          st[r * 64 + 32 * bb + lr] = (uint8_t)e4m3_encode_fast(h0, sx);
-          st[r * 64 + 32 * bb + 16 + lr] = (uint8_t)e4m3_encode_fast(h1, sx);
+          const uint32_t c2 = e4m3x2_hw(h0, h1, sx);
+          st[r * 64 + 32 * bb + lr] = (uint8_t)c2;
+          st[r * 64 + 32 * bb + 16 + lr] = (uint8_t)(c2 >> 8);
           const int row = wm * 64 + r;
           const int cb = c0 + wn * 64 + 32 * bb;
           if (lr == 0 && row < tl.rows && cb < Nout)

@@ -100,11 +100,7 @@ __global__ __launch_bounds__(256) void add_rms_norm_kernel(
       amax = fmaxf(amax, __shfl_xor(amax, 1));
       amax = fmaxf(amax, __shfl_xor(amax, 2));
       const int se = mx_e4m3_scale_exp(amax);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= e4m3_encode_fast(y[i], se) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= e4m3_encode_fast(y[4 + i], se) << (8 * i);
+      const uint32_t lo = e4m3x4_hw(y, se), hi = e4m3x4_hw(y + 4, se);
       if (ok) {
         *(uint2*)(codes + (row + c) * 8) = make_uint2(lo, hi);
         if ((c & 3) == 0) scales[(size_t)t * (H / 32) + (c >> 2)] = (uint8_t)(se + 127);

@@ -130,11 +130,7 @@ MOE_DEV void quant_mx_row_bf16(const uint4* __restrict__ src, int H,
       amax = fmaxf(amax, __shfl_xor(amax, 1));
       amax = fmaxf(amax, __shfl_xor(amax, 2));
       const int s = mx_e4m3_scale_exp(amax);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= e4m3_encode_fast(f[i], s) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= e4m3_encode_fast(f[4 + i], s) << (8 * i);
+      const uint32_t lo = e4m3x4_hw(f, s), hi = e4m3x4_hw(f + 4, s);
       if (c < H / 8) {
         *(uint2*)(dst + (size_t)c * 8) = make_uint2(lo, hi);
         if ((c & 3) == 0) dsc[c >> 2] = (uint8_t)(s + 127);
