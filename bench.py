@@ -72,17 +72,17 @@ TRAFFIC = {
     # workload: (kernel source set, sha256[:16] of its sources, FETCH KiB,
     #            WRITE KiB) per GEMM1 dispatch
     "qwen3_30b_a3b_decode_bf16":
-        ("gemm_bf16_stream", "20459705c7982308", 341630.6, 384.0),
+        ("gemm_bf16_stream", "02e7042387060670", 341630.6, 384.0),
     "qwen3_30b_a3b_prefill_skewed_bf16":
-        ("gemm_bf16_tiled", "52b774f3f8277440", 521906.6, 49152.0),
+        ("gemm_bf16_tiled", "f9d6dd685457c548", 524212.1, 49152.0),
     "longcat_flash_zero_experts_bf16":
-        ("gemm_bf16_stream", "20459705c7982308", 12854819.6, 32528.0),
+        ("gemm_bf16_stream", "02e7042387060670", 12854901.3, 32528.0),
     "qwen3_235b_a22b_ep_rank_w4a8":
-        ("gemm_mx_tiled", "406ee714f43fb895", 161412.0, 12866.9),
+        ("gemm_mx_tiled", "6f2d8e1cf606f5fd", 161229.6, 12879.2),
     "qwen3_30b_a3b_decode_w8a8":
-        ("gemm_i8_stream", "bec598550b7bdc37", 171200.7, 768.0),
+        ("gemm_i8_stream", "6c2db7a115735de1", 171200.7, 768.0),
     "qwen3_30b_a3b_prefill_skewed_w8a8":
-        ("gemm_bf16_tiled", "52b774f3f8277440", 228163.1, 98304.0),
+        ("gemm_bf16_tiled", "f9d6dd685457c548", 226960.0, 98304.0),
 }
 
 
