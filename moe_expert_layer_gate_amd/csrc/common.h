@@ -37,13 +37,18 @@ MOE_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 MOE_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs).
-MOE_DEV uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+// fp32 -> bf16, round to nearest, ties to even (finite inputs), two values
+// per instruction (v_cvt_pk_bf16_f32): lo in bits 0-15, hi in 16-31.
+// Compared on MI355X with the integer rounding (u + 0x7FFF + lsb) >> 16
+// over every finite fp32 value, subnormals included: no difference.
 MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t,
+                            __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+MOE_DEV uint32_t f32_to_bf16_bits(float f) {
+  return pack_bf16x2(f, 0.0f) & 0xFFFFu;
 }
 
 // ---------------------------------------------------------------- wave ops
