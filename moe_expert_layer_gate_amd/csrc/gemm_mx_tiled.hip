@@ -163,6 +163,10 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
                16 * ((lane & 7) ^ (4 * (wave & 1) + (lane >> 4)));
     b_off[j] = (uint32_t)wcol(16 * (4 * j + wave)) / 16 * 1024u + 16u * lane;
   }
+  // A copies whose 8 rows all lie past the tile's rows are skipped: those
+  // LDS rows feed only accumulator rows that are never stored
+  const int na = __builtin_amdgcn_readfirstlane(
+      min(4, (tl.rows - 8 * wave + 31) / 32));
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds0 + 8 * wave * MBK);
   const uint32_t b_dst =
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx_tiled_kernel(
     const uint8_t* bb_ = we + (size_t)(s_) * Nw * (MBK / 2);                  \
     const uint32_t o_ = (st_) * MSTAGE;                                       \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
-      g2lds(ab_, a_off[j], a_dst + o_ + 32 * j * MBK);                        \
+      if (j < na) g2lds(ab_, a_off[j], a_dst + o_ + 32 * j * MBK);            \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
       g2lds_w(bb_, b_off[j], b_dst + o_ + 64 * j * (MBK / 2), wnt);           \
   } while (0)
@@ -425,6 +429,10 @@ __global__ __launch_bounds__(256, 2) void gemm_mx32_tiled_kernel(
                16 * ((lane & 7) ^ (4 * (wave & 1) + (lane >> 4)));
     b_off[j] = (uint32_t)wcol(16 * (4 * j + wave)) / 16 * 1024u + 16u * lane;
   }
+  // A copies whose 8 rows all lie past the tile's rows are skipped: those
+  // LDS rows feed only accumulator rows that are never stored
+  const int na = __builtin_amdgcn_readfirstlane(
+      min(4, (tl.rows - 8 * wave + 31) / 32));
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t a_dst = __builtin_amdgcn_readfirstlane(lds0 + 8 * wave * MBK);
   const uint32_t b_dst =
@@ -443,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mx32_tiled_kernel(
     const uint8_t* bb_ = we + (size_t)(s_) * Nw * (MBK / 2);                  \
     const uint32_t o_ = (st_) * MSTAGE;                                       \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
-      g2lds(ab_, a_off[j], a_dst + o_ + 32 * j * MBK);                        \
+      if (j < na) g2lds(ab_, a_off[j], a_dst + o_ + 32 * j * MBK);            \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                             \
       g2lds_w(bb_, b_off[j], b_dst + o_ + 64 * j * (MBK / 2), wnt);           \
   } while (0)
