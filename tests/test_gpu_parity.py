@@ -202,6 +202,62 @@ def test_init_routing_small(name):
     _routing_case(SMALL[name], seed=3)
 
 
+def _mxfp8_edge_rows(T, H):
+    """bf16 rows whose 32-value blocks sit on the edges of the MXFP8 (e4m3)
+    encoding: with a block maximum of 1 the scale is 2^-8, so values below
+    2^-14 land among the e4m3 subnormals (step 2^-17 before scaling) and the
+    odd multiples of 2^-18 are exact ties between two of them; a maximum of
+    1.96875 scales to 504 and saturates at 448, 1.0625 scales to 272, a tie
+    between the normal codes 256 and 288; negative values and -0; an
+    all-zero block."""
+    tiny = [k * 2.0 ** -18 for k in range(1, 32, 2)]            # ties
+    small = [k * 2.0 ** -17 for k in range(1, 9)]               # subnormals
+    patterns = [
+        [1.0] + tiny + [-v for v in tiny[:15]],
+        [1.0] + small + [-v for v in small] + [2.0 ** -14, -2.0 ** -14] +
+        [2.0 ** -15] * 5 + [-0.0] * 8,
+        [1.96875, -1.96875, 1.875, 1.75] + [0.5, -0.25, 0.125] * 9 + [1.0],
+        [1.0625, -1.0625, 1.0, 1.125] + [0.0] * 28,
+        [0.0] * 32,
+        [-0.0] * 31 + [2.0 ** -126],
+    ]
+    blocks = [np.array(b[:32] + [0.0] * (32 - len(b[:32])), dtype=np.float64)
+              for b in patterns]
+    rows = []
+    for t in range(T):
+        row = np.concatenate([blocks[(t + j) % len(blocks)] * (2.0 ** ((t % 5) - 2))
+                              for j in range(H // 32)])
+        rows.append(row)
+    x = torch.from_numpy(np.stack(rows)).to(torch.bfloat16)
+    assert np.array_equal(x.double().numpy(), np.stack(rows)), "edge values must be bf16"
+    return x
+
+
+def test_mxfp8_quant_edge_values():
+    """MXFP8 codes and scales of x (the per-copy quantisation of the routing
+    gather, the same row routine the gate-side and scan-side quantisers run)
+    bit-exact against the oracle on values chosen at the encoding's edges:
+    subnormal codes, ties to even, saturation, signed zeros, zero blocks."""
+    m = _m()
+    T, H, E, k = 40, 512, 16, 4
+    g = torch.Generator().manual_seed(77)
+    rid, _ = O.gate_topk(torch.randn(T, E, generator=g).numpy(), k)
+    x = _mxfp8_edge_rows(T, H)
+    p = m.problem(T=T, H=H, I=128, n_ffn=E, n_zero=0, top_k=k, local_begin=0,
+                  local_end=E, act="bf16", wt="mxfp4", act_q="mxfp8")
+    r = m.init_routing(p, torch.from_numpy(rid).to(DEV), x.to(DEV))
+    torch.cuda.synchronize()
+    counts, offsets, sc, cp = O.init_routing(rid, E)
+    tok = sc // k
+    codes, scl = O.mx_quant(x.double().numpy()[tok], "e4m3")
+    got_c = r["x_perm"][: T * k].cpu().numpy()
+    got_s = r["x_perm_scale"][: T * k].cpu().numpy()
+    print("edge rows: code mismatches", int((got_c != codes).sum()),
+          "scale mismatches", int((got_s != scl).sum()), flush=True)
+    assert np.array_equal(got_c, codes)
+    assert np.array_equal(got_s, scl)
+
+
 @pytest.mark.parametrize("T,E,k", [(50, 2048, 2), (600, 2048, 64), (64, 1024, 64),
                                    (65, 1024, 64), (4096, 1, 1), (1000, 300, 7),
                                    (4096, 512, 32), (5000, 96, 1)])
