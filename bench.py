@@ -19,8 +19,17 @@ Prints ONE JSON line: whole-step tokens/s plus
 Before the W warm-up steps, untimed steps run for 1 s of wall time so that
 the GPU has reached its working clocks when the (short) timed region starts.
 
+Static expert weights are prepared once before timing, as at model load:
+int8 and MXFP4 weights packed (moe_pack_weights); bf16 weights in the layout
+that suits the model's experts (--wt-layout auto): slab-packed
+(moe_pack_bf16_weights) for the LongCat-shaped experts, whose GEMMs stream
+6144 x 2048 experts in long blocks (layer 6072 -> 5850 us), row-major for
+the Qwen3-30B-A3B ones (slab-packed was 3-4 % slower at decode sizes and
+neutral in prefill). config.wt_layout says which.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--op layer|norm_cast|norm_mx]
+                       [--wt-layout auto|rowmajor|packed]
 
 --op norm_cast / norm_mx time the fused residual add + RMSNorm in front of the
 MoE block instead (dual fp32/bf16 output, or MXFP8), on the workload's T x H
@@ -68,9 +77,16 @@ KERNEL_SOURCES = {
     "gemm_mx_tiled": ["gemm_mx_tiled.hip", "lds_dma.h", "common.h", "launch.h"],
     "gemm_i8_stream": ["gemm_i8_stream.hip", "common.h", "launch.h"],
 }
+# bf16 workloads whose weights bench.py slab-packs by default (measured:
+# the LongCat-shaped layer 6071.9 -> 5849.5 us; the Qwen3-30B-A3B decode
+# layer 181.6 -> 186.6 us at 32 tokens and 199.6 -> 208.0 us at 128, its
+# skewed prefill 464.0 -> 463.8 us, outputs bit-identical)
+BF16_PACKED = {"longcat_flash_zero_experts_bf16"}
+
 TRAFFIC = {
     # workload: (kernel source set, sha256[:16] of its sources, FETCH KiB,
-    #            WRITE KiB) per GEMM1 dispatch
+    #            WRITE KiB) per GEMM1 dispatch, taken with the weight layout
+    #            bench.py uses by default for the workload
     "qwen3_30b_a3b_decode_bf16":
         ("gemm_bf16_stream", "cbea335ea17852cd", 341625.5, 384.0),
     "qwen3_30b_a3b_prefill_skewed_bf16":
@@ -96,9 +112,9 @@ def _sources_sha(kind):
     return h.hexdigest()[:16]
 
 
-def _traffic(workload):
+def _traffic(workload, default_layout=True):
     ent = TRAFFIC.get(workload)
-    if ent is None:
+    if ent is None or not default_layout:
         return None
     kind, sha, fetch_kib, write_kib = ent
     if _sources_sha(kind) != sha:
@@ -150,6 +166,10 @@ def _parse():
                     choices=["layer", "norm_cast", "norm_mx", "router"],
                     help="what one step is: the MoE layer (default) or the "
                          "fused add + RMSNorm in front of it")
+    ap.add_argument("--wt-layout", default="auto",
+                    choices=["auto", "rowmajor", "packed"],
+                    help="layout of bf16 expert weights (auto: the one "
+                         "BF16_PACKED picks for the workload)")
     ap.add_argument("--print-source-sha", action="store_true",
                     help="print the source hashes that key the traffic table")
     return ap.parse_args()
@@ -238,11 +258,14 @@ def _cpu_baseline(shape, inp, target_s):
                                     inp["w2_scale"][i].cpu().numpy())
             return a.T.copy(), b.T.copy()
     else:
-        # one expert's weights fetched from the device when the oracle asks
+        # one expert's row-major weights fetched from the device when the
+        # oracle asks (the GPU path may take them slab-packed)
+        w13 = inp.get("w13_rowmajor", inp["w13"])
+        w2 = inp.get("w2_rowmajor", inp["w2"])
+
         def get(e):
             i = e - fb
-            return (inp["w13"][i].cpu().double().numpy(),
-                    inp["w2"][i].cpu().double().numpy())
+            return (w13[i].cpu().double().numpy(), w2[i].cpu().double().numpy())
     kw = dict(logits=host["logits"].numpy(), x=host["x"].double().numpy(),
               residual=None if host["residual"] is None else host["residual"].double().numpy(),
               get_weights=get, T=shape.T, H=shape.H, I=shape.I,
@@ -319,7 +342,21 @@ def main():
             else:
                 inp[k + "_rowmajor"] = inp[k]
                 inp[k] = m.pack_weights(inp[k])
-    p = m.problem(shape)
+    layout = "rowmajor" if shape.wt == "f32" else "packed"
+    if shape.wt == "bf16":
+        want = args.wt_layout
+        if want == "auto":
+            want = "packed" if shape.name in BF16_PACKED else "rowmajor"
+        if shape.I % 128 or shape.H % 256:
+            want = "rowmajor"  # the slab order needs whole 256-column slabs
+        layout = want
+    if shape.wt == "bf16" and layout == "packed":
+        # static bf16 weights in the slab order, packed once as at model
+        # load (untimed); the CPU baseline keeps the row-major originals
+        for k, glu in (("w13", True), ("w2", False)):
+            inp[k + "_rowmajor"] = inp[k]
+            inp[k] = m.pack_bf16_weights(inp[k], glu=glu)
+    p = m.problem(shape, wt_layout=layout)
     ws = torch.empty(max(m.layer_workspace_bytes(p), 1), dtype=torch.uint8, device=dev)
     dt = torch.float32 if shape.act == "f32" else torch.bfloat16
     out = torch.empty((shape.T, shape.H), dtype=dt, device=dev)
@@ -420,13 +457,15 @@ def main():
         ach = nbytes / dur / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "traffic": _traffic(shape.name)}
+                "traffic": _traffic(shape.name, args.wt_layout == "auto"
+                                    or shape.wt != "bf16")}
     else:
         ach = flops / dur / 1e12
         peak = PEAK_TFLOPS[kind]
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                "traffic": _traffic(shape.name)}
+                "traffic": _traffic(shape.name, args.wt_layout == "auto"
+                                    or shape.wt != "bf16")}
     # both fractions for every workload: the bound one is "frac"; prefill
     # workloads are graded on MFMA peak and sit near the HBM ridge
     peak_f = PEAK_TFLOPS[kind]
@@ -452,7 +491,8 @@ def main():
                    "top_k": shape.top_k,
                    "local_experts": [shape.local_begin, shape.local_end],
                    "act": shape.act, "wt": shape.wt, "act_q": shape.act_q,
-                   "residual": shape.residual, "seed": args.seed},
+                   "wt_layout": layout, "residual": shape.residual,
+                   "seed": args.seed},
         "traced_step_us": round(traced_step_us, 2),
         "stages_us": stage_us,
         "roofline": roof,

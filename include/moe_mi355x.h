@@ -84,7 +84,8 @@ typedef enum moe_dtype {
 /* Layout of the expert weights handed to a call (moe_problem.wt_layout). */
 typedef enum moe_layout {
   MOE_LAYOUT_ROWMAJOR = 0, /* as in "Weight layouts" below, unpacked        */
-  MOE_LAYOUT_PACKED = 1    /* the packed order of moe_pack_weights           */
+  MOE_LAYOUT_PACKED = 1    /* the packed order of moe_pack_weights (MXFP4,
+                              INT8) or moe_pack_bf16_weights (BF16)          */
 } moe_layout;
 
 typedef struct moe_problem {
@@ -102,7 +103,9 @@ typedef struct moe_problem {
                     (dynamic)                                               */
   int32_t wt_layout; /* moe_layout of w13 / w2: MOE_LAYOUT_PACKED for
                         MXFP4_E2M1 and INT8 weights, MOE_LAYOUT_ROWMAJOR for
-                        F32 and BF16; any other pairing is refused with
+                        F32, either for BF16 (packed: the slab order of
+                        moe_pack_bf16_weights, I % 128 == 0 and
+                        H % 256 == 0); any other pairing is refused with
                         MOE_ERR_UNSUPPORTED before anything is launched (the
                         quantised GEMMs read only the packed order: pack
                         row-major MXFP4 / int8 weights once with
@@ -160,6 +163,22 @@ typedef struct moe_problem {
  * contiguous (K-contiguous rows read 64 bytes per column per load
  * otherwise, ~30 % below the streaming rate). moe_pack_weights converts
  * once, e.g. when the weights are loaded.
+ *
+ * Slab-packed weights (BF16 with MOE_LAYOUT_PACKED): the bf16 GEMMs read an
+ * expert's matrix W [K, N] in slabs of 256 columns -- for w13 (N = 2I) slab
+ * j holds the gate columns [128 j, 128 j + 128) and the matching up columns
+ * [I + 128 j, I + 128 j + 128), for w2 (N = H) the columns [256 j, 256 j +
+ * 256) -- and each slab in K steps of 32 rows. Packed, the 32 x 256 block of
+ * step s of slab j is one contiguous 16 KB, in the order [E][N/256][K/32]
+ * [32][256]: element (e, j, s, r, c) = W[e][32 s + r][col_j(c)], col_j(c) =
+ * 128 j + c for c < 128 and I + 128 j + c - 128 otherwise (w13), 256 j + c
+ * (w2). Same element count as row-major, same results bit for bit. Which
+ * layout streams faster depends on the experts (measured on MI355X): row-
+ * major, the blocks reading the slabs of one expert share DRAM rows, which
+ * pays while they run in step (2048 x 768 experts at decode batch sizes:
+ * row-major layer 3-4 % faster); blocks that stream long slabs over several
+ * rounds drift apart, and then contiguous slabs pay (6144 x 2048 experts at
+ * 16 rows each: slab order 4 % faster). Prefill-size batches are neutral.
  */
 
 /* Gating: [P1] "GMM使能和Routing优化 / 快速选择专家" (fused top-k + softmax
@@ -393,6 +412,25 @@ MOE_API moe_status moe_add_rms_norm_mx_quant(int32_t T, int32_t H,
  * Stream-ordered; the caller owns both buffers. */
 MOE_API moe_status moe_pack_weights(int32_t E, int32_t N, int32_t K_bytes,
                                     const void* src, void* dst, void* stream);
+
+/* Packs static bf16 expert weights into the slab order described above
+ * (moe_problem.wt_layout = MOE_LAYOUT_PACKED with BF16 weights); [P2]
+ * "LongCat-Flash inference on Atlas A3 clusters": the decode grouped matmuls
+ * are bound by streaming the expert weights, which the slab order makes
+ * contiguous.
+ *   src  bf16 [E, K, N] row-major (w13 [E_loc, H, 2I] with glu = 1, w2
+ *        [E_loc, I, H] with glu = 0)
+ *   dst  the same E * K * N bf16 values in the slab order; must not overlap
+ *        src
+ * glu = 1 pairs gate column 128 j + c with up column N/2 + 128 j + c in slab
+ * j; glu = 0 takes 256 consecutive columns per slab. E >= 0 (E == 0
+ * launches nothing), K > 0, N > 0, glu 0 or 1 (else MOE_ERR_INVALID_ARG);
+ * K % 32 == 0, N % 256 == 0 and E * K * N < 2^40 (else
+ * MOE_ERR_UNSUPPORTED); pointers 16-byte aligned. Stream-ordered; the
+ * caller owns both buffers. */
+MOE_API moe_status moe_pack_bf16_weights(int32_t E, int32_t K, int32_t N,
+                                         int32_t glu, const void* src,
+                                         void* dst, void* stream);
 
 /* MXFP4 quantisation of bf16 expert weights, the form the W4A8 experts hold
  * ([P1] "MoE EP优化 / AllGather方案(W4A8量化)": MXFP4 weights), for a caller

@@ -23,7 +23,8 @@ __all__ = [
     "init_routing", "ffn_up", "ffn_down", "grouped_ffn", "finalize", "layer",
     "layer_workspace_bytes", "layer_traced", "SYMBOLS", "STAGES",
     "add_rms_norm_cast", "add_rms_norm_mx_quant", "router_logits",
-    "pack_weights", "quant_mxfp4_weights", "layer_noalloc", "prefetch_weights",
+    "pack_weights", "pack_bf16_weights", "quant_mxfp4_weights",
+    "layer_noalloc", "prefetch_weights",
     "NOALLOC_SCRATCH_BYTES",
 ]
 
@@ -41,7 +42,8 @@ SYMBOLS = ["moe_gate_topk", "moe_init_routing", "moe_grouped_ffn", "moe_ffn_up",
            "moe_ffn_down", "moe_finalize", "moe_layer", "moe_layer_traced",
            "moe_layer_noalloc", "moe_prefetch_weights",
            "moe_add_rms_norm_cast", "moe_add_rms_norm_mx_quant",
-           "moe_router_logits", "moe_pack_weights", "moe_quant_mxfp4_weights",
+           "moe_router_logits", "moe_pack_weights", "moe_pack_bf16_weights",
+           "moe_quant_mxfp4_weights",
            "moe_status_string",
            "moe_abi_version"]
 
@@ -103,6 +105,7 @@ def lib() -> ctypes.CDLL:
                                         _vp, _vp, _vp]
     sig["moe_router_logits"] = [_i32, _i32, _i32, _vp, _vp, _vp, _vp]
     sig["moe_pack_weights"] = [_i32, _i32, _i32, _vp, _vp, _vp]
+    sig["moe_pack_bf16_weights"] = [_i32, _i32, _i32, _i32, _vp, _vp, _vp]
     sig["moe_quant_mxfp4_weights"] = [_i32, _i32, _i32, _vp, _vp, _vp, _vp]
     for name, args in sig.items():
         f = getattr(L, name)
@@ -122,7 +125,8 @@ def problem(shape=None, **kw) -> MoeProblem:
     names "f32" / "bf16" / "mxfp4" / "mxfp8" / "int8" / "none") and/or
     keywords. wt_layout ("rowmajor" / "packed") defaults to "packed" for
     MXFP4 and int8 weights (the form pack_weights makes) and "rowmajor"
-    otherwise; the library refuses any other pairing."""
+    otherwise; bf16 weights may also be "packed" (the slab order
+    pack_bf16_weights makes); the library refuses any other pairing."""
     vals = {}
     for n in ("T", "H", "I", "n_ffn", "n_zero", "top_k", "local_begin",
               "local_end", "act", "wt", "act_q", "wt_layout"):
@@ -416,6 +420,21 @@ def pack_weights(w, out=None):
     if out is None:
         out = torch.empty_like(w)
     _check(lib().moe_pack_weights(E, N, Kb, _ptr(w), _ptr(out), _stream()))
+    return out
+
+
+def pack_bf16_weights(w, glu, out=None):
+    """bf16 expert weights [E, K, N] (row-major, N contiguous) -> the slab
+    order the bf16 GEMMs read with wt_layout="packed" (same shape and element
+    count; see moe_pack_bf16_weights). glu: True for w13 (gate and up columns
+    paired per slab), False for w2."""
+    if w.dim() != 3 or w.dtype != torch.bfloat16:
+        raise ValueError("w must be an [E, K, N] bfloat16 tensor")
+    E, K, N = w.shape
+    if out is None:
+        out = torch.empty_like(w)
+    _check(lib().moe_pack_bf16_weights(E, K, N, 1 if glu else 0, _ptr(w),
+                                       _ptr(out), _stream()))
     return out
 
 

@@ -26,6 +26,7 @@ struct Prob {
   long long N;  // T * k copies
   bool mx;      // MXFP8 activations x MXFP4 weights
   bool i8;      // W8A8: int8 activations and weights, fp32 scales
+  bool pk;      // bf16 weights slab-packed (moe_pack_bf16_weights)
 };
 
 moe_status check(const moe_problem* p, Prob* q) {
@@ -50,9 +51,14 @@ moe_status check(const moe_problem* p, Prob* q) {
   r.mx = r.act == MOE_BF16 && r.wt == MOE_MXFP4_E2M1 && r.actq == MOE_MXFP8_E4M3;
   r.i8 = r.act == MOE_BF16 && r.wt == MOE_INT8 && r.actq == MOE_INT8;
   if (!f32 && !bf16 && !r.mx && !r.i8) return MOE_ERR_UNSUPPORTED;
-  // the quantised GEMMs read packed weights only, the others row-major ones
-  if (layout != ((r.mx || r.i8) ? MOE_LAYOUT_PACKED : MOE_LAYOUT_ROWMAJOR))
+  // the quantised GEMMs read packed weights only, the fp32 one row-major
+  // ones, the bf16 ones either (packed: whole 256-column slabs)
+  if (layout != MOE_LAYOUT_ROWMAJOR && layout != MOE_LAYOUT_PACKED)
     return MOE_ERR_UNSUPPORTED;
+  const bool packed = layout == MOE_LAYOUT_PACKED;
+  if ((r.mx || r.i8) ? !packed : (f32 && packed)) return MOE_ERR_UNSUPPORTED;
+  r.pk = bf16 && packed;
+  if (r.pk && (r.I % 128 || r.H % 256)) return MOE_ERR_UNSUPPORTED;
   if (r.mx && (r.H % 128 || r.I % 128)) return MOE_ERR_UNSUPPORTED;
   // int8: K steps of 128; int32 sums of 127 * 127 * K products stay exact;
   // weight offsets (2I * H bytes per expert) fit 32 bits
@@ -128,14 +134,15 @@ long long max_tiles(const Prob& q, int mt) {
 // Blocks of moe_prefetch_weights (256 threads each).
 constexpr int kPrefetchBlocks = 1024;
 
-// How a grouped GEMM reads one expert's weights: bytes per expert, bytes per
-// K step (every form keeps its weights K-major: bf16 [K, N], packed int8 /
-// e2m1 in 64-byte K chunks of all N columns), steps, the K split its waves
-// start at (streaming kernels), and how many tiles its first round of blocks
-// holds (the experts whose heads are read first).
+// How a grouped GEMM reads one expert's weights: bytes per expert, its
+// K-major regions (one for bf16 [K, N] and for packed int8 / e2m1 in 64-byte
+// K chunks of all N columns; the 256-column slabs of slab-packed bf16), bytes
+// per K step of a region, steps, the K split its waves start at (streaming
+// kernels), and how many tiles its first round of blocks holds (the experts
+// whose heads are read first).
 struct Geom {
-  long long ebytes = 0, step = 0;
-  int nsteps = 0, nseg = 0, round_tiles = 0;
+  long long ebytes = 0, step = 0, slab_bytes = 0;
+  int nsteps = 0, nseg = 0, nslab = 1, round_tiles = 0;
 };
 
 Geom gemm_geom(const Prob& q, int mt, bool up) {
@@ -166,6 +173,12 @@ Geom gemm_geom(const Prob& q, int mt, bool up) {
     g.nseg = moe::stream_bf16_ksplit(up, mtl, K, Nout, mt / 16);
     g.round_tiles = cus * (8 / g.nseg) / moe::stream_bf16_slabs(up, Nout);
   }
+  if (q.pk) {
+    // slab-packed bf16: N / 256 slabs of K / 32 steps of 16 KB each
+    g.nslab = N / 256;
+    g.step = 16384;
+    g.slab_bytes = (long long)K * 512;
+  }
   return g;
 }
 
@@ -178,13 +191,15 @@ moe::Prefetch make_prefetch(const Geom& g, const void* w, const Prob& q,
   moe::Prefetch pf{};
   if (g.nseg <= 0 || nexp <= 0 || budget < 16 || !w) return pf;
   const long long segmin = (long long)(g.nsteps / g.nseg) * g.step;
-  long long lead = budget / ((long long)nexp * g.nseg);
+  long long lead = budget / ((long long)nexp * g.nseg * g.nslab);
   if (lead > segmin - skip) lead = segmin - skip;
   lead &= ~15LL;
   if (lead < 16) return pf;
   pf.w = (const char*)w;
   pf.ebytes = g.ebytes;
   pf.step_bytes = g.step;
+  pf.slab_bytes = g.slab_bytes;
+  pf.nslab = g.nslab;
   pf.nsteps = g.nsteps;
   pf.nseg = g.nseg;
   pf.skip = (int)skip;
@@ -280,12 +295,12 @@ moe_status run_up(const Prob& q, int mt, const Tile* tiles,
     MOE_TRY(moe::launch_gemm_bf16_tiled(
         true, mt, tiles, tile_count, mtl, (const uint16_t*)xp,
         (const uint16_t*)w13, (uint16_t*)h, q.H, 2 * q.I, q.I, gidx, gbase,
-        q.k, s));
+        q.k, s, q.pk));
   else
     MOE_TRY(moe::launch_gemm_bf16_stream(
         true, mt / 16, tiles, tile_count, mtl, (const uint16_t*)xp,
         (const uint16_t*)w13, (uint16_t*)h, q.H, 2 * q.I, q.I, gidx, gbase,
-        q.k, s));
+        q.k, s, q.pk));
   return MOE_OK;
 }
 
@@ -328,12 +343,12 @@ moe_status run_down(const Prob& q, int mt, const Tile* tiles,
     MOE_TRY(moe::launch_gemm_bf16_tiled(
         false, mt, tiles, tile_count, mtl, (const uint16_t*)h,
         (const uint16_t*)w2, (uint16_t*)y, q.I, q.H, q.H, nullptr, nullptr,
-        q.k, s));
+        q.k, s, q.pk));
   else
     MOE_TRY(moe::launch_gemm_bf16_stream(
         false, mt / 16, tiles, tile_count, mtl, (const uint16_t*)h,
         (const uint16_t*)w2, (uint16_t*)y, q.I, q.H, q.H, nullptr, nullptr,
-        q.k, s));
+        q.k, s, q.pk));
   return MOE_OK;
 }
 
@@ -624,6 +639,23 @@ moe_status moe_pack_weights(int32_t E, int32_t N, int32_t K_bytes,
                                              (const uint8_t*)src,
                                              (uint8_t*)dst,
                                              (hipStream_t)stream));
+}
+
+moe_status moe_pack_bf16_weights(int32_t E, int32_t K, int32_t N,
+                                 int32_t glu, const void* src, void* dst,
+                                 void* stream) {
+  if (E < 0 || K <= 0 || N <= 0 || (glu != 0 && glu != 1))
+    return MOE_ERR_INVALID_ARG;
+  if (K % 32 || N % 256 || (long long)E * K * N >= (1LL << 40))
+    return MOE_ERR_UNSUPPORTED;
+  if (E == 0) return MOE_OK;
+  if (!src || !dst || !aligned16(src, dst)) return MOE_ERR_INVALID_ARG;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  const uintptr_t n = (uintptr_t)E * K * N * 2;
+  if (a < b + n && b < a + n) return MOE_ERR_INVALID_ARG;  // overlap
+  return hip_status(moe::launch_pack_bf16_weights(
+      E, K, N, glu != 0, (const uint16_t*)src, (uint16_t*)dst,
+      (hipStream_t)stream));
 }
 
 moe_status moe_quant_mxfp4_weights(int32_t E, int32_t K, int32_t N,

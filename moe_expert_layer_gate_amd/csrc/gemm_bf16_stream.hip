@@ -26,6 +26,11 @@
 //   * KSPLIT waves of a block split K; partial sums meet in LDS in one or
 //     two rounds; wave 0 applies SwiGLU / converts and stores 16 bytes per
 //     row and lane.
+//   * PK: the weights come slab-packed (pack_bf16.hip): the 32 x 256 block
+//     a block reads per K step is one contiguous 16 KB, rows of 512 bytes
+//     (the 128 columns of the lane's first group, then those of its second);
+//     the lane's loads and fragments are the same, only their addresses
+//     change.
 // Output D of each MFMA: lane l holds rows 4*(l/16) + 0..3 at column
 // col + 8*(l%16) + i, so a lane owns 8 consecutive columns of 4 rows.
 #include "common.h"
@@ -60,7 +65,7 @@ MOE_DEV u32x4_t column_frag(const uint4 (&r)[8], int i) {
 // Two waves per SIMD: left to itself the compiler spends 288 registers per
 // lane (accumulators in AGPRs) and runs one wave per SIMD, so a decode launch
 // of two thousand waves would take two rounds.
-template <bool GLU, int RG, int KSPLIT>
+template <bool GLU, int RG, int KSPLIT, bool PK>
 __global__ __launch_bounds__(64 * KSPLIT)
 __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
     const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
@@ -126,13 +131,24 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
     u32x4_t af[RG];
   };
   auto load_w = [&](Stage& st, int s) {
-    const int k0 = s * 32;
-    const uint16_t* pA = we + (size_t)(k0 + 8 * kq) * Nw + ldA;
-    const uint16_t* pB = we + (size_t)(k0 + 8 * kq) * Nw + ldB;
+    if constexpr (PK) {
+      // slab blockIdx.x, step s: 16 KB of [32 rows][256 columns]
+      const uint16_t* pA = we + ((size_t)blockIdx.x * nsteps + s) * 8192 +
+                           (8 * kq) * 256 + 8 * g;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      st.bA[r] = load_stream16(pA + (size_t)r * Nw);
-      st.bB[r] = load_stream16(pB + (size_t)r * Nw);
+      for (int r = 0; r < 8; ++r) {
+        st.bA[r] = load_stream16(pA + r * 256);
+        st.bB[r] = load_stream16(pA + r * 256 + 128);
+      }
+    } else {
+      const int k0 = s * 32;
+      const uint16_t* pA = we + (size_t)(k0 + 8 * kq) * Nw + ldA;
+      const uint16_t* pB = we + (size_t)(k0 + 8 * kq) * Nw + ldB;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        st.bA[r] = load_stream16(pA + (size_t)r * Nw);
+        st.bB[r] = load_stream16(pB + (size_t)r * Nw);
+      }
     }
   };
   auto load_a = [&](Stage& st, int s) {
@@ -258,7 +274,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
   }
 }
 
-template <bool GLU, int RG>
+template <bool GLU, int RG, bool PK>
 static hipError_t launch_stream(int ksplit, dim3 grid, const Tile* tiles,
                                 const int32_t* tile_count, const uint16_t* a,
                                 const uint16_t* w, uint16_t* out, int K, int Nw,
@@ -266,16 +282,32 @@ static hipError_t launch_stream(int ksplit, dim3 grid, const Tile* tiles,
                                 const int32_t* gbase, int gk, hipStream_t s) {
   switch (ksplit) {  // 1 or 3 (stream_ksplit)
     case 1:
-      hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 1>), grid, dim3(64),
-                         0, s, tiles, tile_count, a, w, out, K, Nw, Nout, gidx, gbase, gk);
+      hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 1, PK>), grid,
+                         dim3(64), 0, s, tiles, tile_count, a, w, out, K, Nw,
+                         Nout, gidx, gbase, gk);
       break;
     default:
-      hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 3>), grid,
+      hipLaunchKernelGGL((gemm_bf16_stream_kernel<GLU, RG, 3, PK>), grid,
                          dim3(192), 0, s, tiles, tile_count, a, w, out, K, Nw,
                          Nout, gidx, gbase, gk);
       break;
   }
   return hipGetLastError();
+}
+
+template <bool GLU, bool PK>
+static hipError_t launch_stream_rg(int rg, int ksplit, dim3 grid,
+                                   const Tile* tiles, const int32_t* tile_count,
+                                   const uint16_t* a, const uint16_t* w,
+                                   uint16_t* out, int K, int Nw, int Nout,
+                                   const int32_t* gidx, const int32_t* gbase,
+                                   int gk, hipStream_t s) {
+  return rg == 1 ? launch_stream<GLU, 1, PK>(ksplit, grid, tiles, tile_count,
+                                             a, w, out, K, Nw, Nout, gidx,
+                                             gbase, gk, s)
+                 : launch_stream<GLU, 2, PK>(ksplit, grid, tiles, tile_count,
+                                             a, w, out, K, Nw, Nout, gidx,
+                                             gbase, gk, s);
 }
 
 int device_cus() {
@@ -322,20 +354,26 @@ hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
                                    const uint16_t* a, const uint16_t* w,
                                    uint16_t* out, int K, int Nw, int Nout,
                                    const int32_t* gidx, const int32_t* gbase,
-                                   int gk, hipStream_t s) {
+                                   int gk, hipStream_t s, bool pk) {
   if (max_tiles == 0) return hipSuccess;
+  // packed slabs are whole: 256 weight columns, K in steps of 32
+  if (pk && (K % 32 || Nw % 256)) return hipErrorInvalidValue;
   // (max_tiles < 65536: this schedule serves fewer than 20 rows per expert)
   dim3 grid(stream_bf16_slabs(glu, Nout), max_tiles);
   const int ksplit = stream_bf16_ksplit(glu, max_tiles, K, Nout, rg);
   if (glu)
-    return rg == 1 ? launch_stream<true, 1>(ksplit, grid, tiles, tile_count, a,
-                                            w, out, K, Nw, Nout, gidx, gbase, gk, s)
-                   : launch_stream<true, 2>(ksplit, grid, tiles, tile_count, a,
-                                            w, out, K, Nw, Nout, gidx, gbase, gk, s);
-  return rg == 1 ? launch_stream<false, 1>(ksplit, grid, tiles, tile_count, a,
-                                           w, out, K, Nw, Nout, gidx, gbase, gk, s)
-                 : launch_stream<false, 2>(ksplit, grid, tiles, tile_count, a,
-                                           w, out, K, Nw, Nout, gidx, gbase, gk, s);
+    return pk ? launch_stream_rg<true, true>(rg, ksplit, grid, tiles,
+                                             tile_count, a, w, out, K, Nw, Nout,
+                                             gidx, gbase, gk, s)
+              : launch_stream_rg<true, false>(rg, ksplit, grid, tiles,
+                                              tile_count, a, w, out, K, Nw,
+                                              Nout, gidx, gbase, gk, s);
+  return pk ? launch_stream_rg<false, true>(rg, ksplit, grid, tiles,
+                                            tile_count, a, w, out, K, Nw, Nout,
+                                            gidx, gbase, gk, s)
+            : launch_stream_rg<false, false>(rg, ksplit, grid, tiles,
+                                             tile_count, a, w, out, K, Nw,
+                                             Nout, gidx, gbase, gk, s);
 }
 
 }  // namespace moe

@@ -142,11 +142,15 @@ MOE_DEV int swz_b(int k) { return 4 * (k & 3); }
 // sgroup within an expert). smem is the block's LDS ring (plus, for int8, 128 row
 // scales after it); the item starts and ends with every wave past its LDS
 // accesses of the previous item.
+// PKB: bf16 weights slab-packed (pack_bf16.hip): the 32 x 256 block of a
+// K step is one contiguous 16 KB, [k][column] with the tile's columns in
+// order, so the copies read it in place of 32 rows 2N bytes apart (same LDS
+// layout and swizzle).
 // I8: W8A8 -- A int8 codes [rows, K] with one fp32 scale per row (a_scale,
 // indexed like the rows), weights int8 [E_loc, N, K] (K contiguous) with one
 // fp32 scale per output channel (w_scale [E_loc, N]); int32 accumulation,
 // dequantised in the epilogue; GEMM1 stores h in fp32, GEMM2 y in bf16.
-template <bool GLU, class C, bool I8>
+template <bool GLU, class C, bool I8, bool PKB>
 MOE_DEV void tiled_item(
     uint8_t* smem, int L, const Tile* __restrict__ tiles,
     const void* __restrict__ a, const void* __restrict__ w,
@@ -232,7 +236,8 @@ MOE_DEV void tiled_item(
   } else {
     const int kr = 2 * wave + (lane >> 5);
     const int cl = (lane & 31) ^ swz_b(kr);
-    b_off[0] = (uint32_t)(kr * Nw + wcol(8 * cl)) * 2;
+    b_off[0] = PKB ? (uint32_t)(kr * B_ROW + 16 * cl)
+                   : (uint32_t)(kr * Nw + wcol(8 * cl)) * 2;
   }
   const uint32_t a_dst = __builtin_amdgcn_readfirstlane(
       lds_addr(smem + (16 * wave) * (BK * 2)));
@@ -240,9 +245,11 @@ MOE_DEV void tiled_item(
       smem + A_BYTES + (I8 ? 16 * wave * 64 : (2 * wave) * B_ROW)));
   // bytes per K step of B: 32 rows of bf16 [K, N]; for int8 one packed
   // 64-byte K chunk of all N / 16 column groups (32-bit: N * K < 2^31)
-  const size_t b_step = (size_t)BK * Nw * 2;
+  const size_t b_step = PKB ? (size_t)B_BYTES : (size_t)BK * Nw * 2;
+  // packed: this item's slab, K / BK steps of B_BYTES each
+  const char* wsl = we + (PKB ? (size_t)slab * (K / BK) * B_BYTES : 0);
   const uint32_t b_step_i8 = (uint32_t)Nw * 64u;
-  const uint32_t b_rowj = 2u * NW * Nw * 2;     // 2*NW k-rows of B
+  const uint32_t b_rowj = 2u * NW * (PKB ? B_ROW : Nw * 2);  // 2*NW k-rows
 
   // loads of K step s_ into stage st_ (NI instructions per wave)
 #define MOE_TILED_ISSUE(s_, st_)                                              \
@@ -256,7 +263,7 @@ MOE_DEV void tiled_item(
       _Pragma("unroll") for (int j = 0; j < NB; ++j)                          \
         g2lds_w(bb_, b_off[j], b_dst + o_ + 16 * NW * j * 64, wnt);           \
     } else {                                                                  \
-      const char* bb_ = we + (size_t)(s_) * b_step;                           \
+      const char* bb_ = wsl + (size_t)(s_) * b_step;                          \
       _Pragma("unroll") for (int j = 0; j < NB; ++j)                          \
         g2lds_w(bb_, b_off[0] + j * b_rowj, b_dst + o_ + 2 * NW * j * B_ROW,  \
                 wnt);                                                         \
@@ -530,7 +537,7 @@ MOE_DEV void tiled_item(
 // (nj blocks per XCD). The items running at once on an XCD are therefore
 // consecutive: the slabs of a few tiles and the tiles of one expert, whose A
 // rows and weight slabs that XCD's L2 serves to all of them.
-template <bool GLU, class C, bool I8>
+template <bool GLU, class C, bool I8, bool PKB>
 __global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_bf16_tiled_kernel(
     const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_count,
     const void* __restrict__ a, const void* __restrict__ w,
@@ -548,13 +555,13 @@ __global__ __launch_bounds__(C::THREADS, C::BLOCKS_PER_CU) void gemm_bf16_tiled_
   const int lo = xcd * per + min(xcd, rem);
   const int hi = lo + per + (xcd < rem ? 1 : 0);
   for (int L = lo + j; L < hi; L += nj) {
-    tiled_item<GLU, C, I8>(smem, L, tiles, a, w, out, K, Nw, Nout, nslabs,
+    tiled_item<GLU, C, I8, PKB>(smem, L, tiles, a, w, out, K, Nw, Nout, nslabs,
                             sgroup, gidx, gbase, gk, a_scale, w_scale);
     __syncthreads();  // LDS staging of this item read before the next fills
   }
 }
 
-template <class C, bool I8>
+template <class C, bool I8, bool PKB = false>
 static hipError_t launch_tiled(bool glu, const Tile* tiles,
                                const int32_t* tile_count, int max_tiles,
                                const void* a, const void* w, void* out, int K,
@@ -574,11 +581,11 @@ static hipError_t launch_tiled(bool glu, const Tile* tiles,
   nblk = ((nblk + 7) / 8) * 8;
   const dim3 grid((unsigned)nblk), block(C::THREADS);
   if (glu)
-    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<true, C, I8>), grid, block, 0,
+    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<true, C, I8, PKB>), grid, block, 0,
                        s, tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
                        sgroup, gidx, gbase, gk, a_scale, w_scale);
   else
-    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<false, C, I8>), grid, block, 0,
+    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<false, C, I8, PKB>), grid, block, 0,
                        s, tiles, tile_count, a, w, out, K, Nw, Nout, nslabs,
                        sgroup, gidx, gbase, gk, a_scale, w_scale);
   return hipGetLastError();
@@ -589,14 +596,23 @@ hipError_t launch_gemm_bf16_tiled(bool glu, int mt, const Tile* tiles,
                                   const uint16_t* a, const uint16_t* w,
                                   uint16_t* out, int K, int Nw, int Nout,
                                   const int32_t* gidx, const int32_t* gbase,
-                                  int gk, hipStream_t s) {
+                                  int gk, hipStream_t s, bool pk) {
+  // packed slabs are whole: 256 weight columns, K in steps of 32
+  if (pk && (K % BK || Nw % BNW)) return hipErrorInvalidValue;
   if (mt == 256)
-    return launch_tiled<Tiles256, false>(glu, tiles, tile_count, max_tiles, a,
-                                         w, out, K, Nw, Nout, gidx, gbase, gk,
-                                         nullptr, nullptr, s);
-  return launch_tiled<Tiles128, false>(glu, tiles, tile_count, max_tiles, a, w,
-                                       out, K, Nw, Nout, gidx, gbase, gk,
-                                       nullptr, nullptr, s);
+    return pk ? launch_tiled<Tiles256, false, true>(
+                    glu, tiles, tile_count, max_tiles, a, w, out, K, Nw, Nout,
+                    gidx, gbase, gk, nullptr, nullptr, s)
+              : launch_tiled<Tiles256, false>(glu, tiles, tile_count,
+                                              max_tiles, a, w, out, K, Nw, Nout,
+                                              gidx, gbase, gk, nullptr, nullptr,
+                                              s);
+  return pk ? launch_tiled<Tiles128, false, true>(
+                  glu, tiles, tile_count, max_tiles, a, w, out, K, Nw, Nout,
+                  gidx, gbase, gk, nullptr, nullptr, s)
+            : launch_tiled<Tiles128, false>(glu, tiles, tile_count, max_tiles,
+                                            a, w, out, K, Nw, Nout, gidx, gbase,
+                                            gk, nullptr, nullptr, s);
 }
 
 hipError_t launch_gemm_i8_tiled(bool glu, int mt, const Tile* tiles,

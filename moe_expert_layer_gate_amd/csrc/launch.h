@@ -111,15 +111,17 @@ int stream_i8_ksplit(bool glu, int max_tiles, int K, int Nout, int rg);
 
 // Grouped GEMMs. glu: GEMM1 with SwiGLU epilogue (N = 2*I weight columns,
 // I outputs), else GEMM2 (N outputs). Tiles come from the tile list.
-// bf16 activations / bf16 weights [E_loc, K, N]. When gidx is non-NULL the
-// activation row of tile row i is row gidx[gbase[0] + i] / gk of `a` (the
-// gather from x fused into the A loads); otherwise row i of `a`.
+// bf16 activations / bf16 weights [E_loc, K, N], row-major or (pk) slab-
+// packed as launch_pack_bf16_weights writes them (then K % 32 == 0 and
+// N % 256 == 0). When gidx is non-NULL the activation row of tile row i is
+// row gidx[gbase[0] + i] / gk of `a` (the gather from x fused into the A
+// loads); otherwise row i of `a`.
 hipError_t launch_gemm_bf16_stream(bool glu, int rg, const Tile* tiles,
                                    const int32_t* tile_count, int max_tiles,
                                    const uint16_t* a, const uint16_t* w,
                                    uint16_t* out, int K, int Nw, int Nout,
                                    const int32_t* gidx, const int32_t* gbase,
-                                   int gk, hipStream_t s);
+                                   int gk, hipStream_t s, bool pk = false);
 // Same operands, LDS-tiled MFMA tiles of mt = 128 or 256 rows (the tile
 // list's height). With gidx, `a` must span less than 4 GB.
 hipError_t launch_gemm_bf16_tiled(bool glu, int mt, const Tile* tiles,
@@ -127,7 +129,7 @@ hipError_t launch_gemm_bf16_tiled(bool glu, int mt, const Tile* tiles,
                                   const uint16_t* a, const uint16_t* w,
                                   uint16_t* out, int K, int Nw, int Nout,
                                   const int32_t* gidx, const int32_t* gbase,
-                                  int gk, hipStream_t s);
+                                  int gk, hipStream_t s, bool pk = false);
 // W8A8: int8 activations [rows, K] with one fp32 scale per row (a_scale,
 // indexed like the rows of a, through gidx when it is non-NULL), int8
 // weights [E_loc, N, K] with one fp32 scale per output channel
@@ -158,6 +160,12 @@ hipError_t launch_gemm_i8_stream(bool glu, int rg, const Tile* tiles,
 // byte matrices [E, N, Kb] (int8 codes, or two e2m1 codes per byte).
 hipError_t launch_pack_weights(int E, int N, int Kb, const uint8_t* src,
                                uint8_t* dst, hipStream_t s);
+// Slab-packed bf16 weights (pack_bf16.hip) from row-major [E, K, N]:
+// [E][N/256][K/32][32][256]; glu pairs gate column 128 j + c with up column
+// N/2 + 128 j + c in slab j. K % 32 == 0, N % 256 == 0.
+hipError_t launch_pack_bf16_weights(int E, int K, int N, bool glu,
+                                    const uint16_t* src, uint16_t* dst,
+                                    hipStream_t s);
 // MXFP4 (e2m1 + e8m0 per 32 along K) of bf16 weights [E, K, N] (N
 // contiguous): codes [E, N, K/2] (low nibble = even k), scales [E, N, K/32].
 // K % 32 == 0.

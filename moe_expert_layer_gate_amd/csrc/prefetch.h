@@ -9,11 +9,13 @@
 // grouped matmuls in the gaps of communication.
 //
 // What is read: for each of the first `nexp` selected experts (every local
-// expert, or only those some copy routes to, in expert order), bytes
-// [skip, skip + lead) of the head of each of its `nseg` K segments, segment
-// s starting at K step s * nsteps / nseg (steps of `step_bytes` bytes: the
-// consuming GEMM's K steps and K split; its weights are K-major, so a head is
-// contiguous). Those are the bytes the streaming GEMM's waves read first --
+// expert, or only those some copy routes to, in expert order) and each of
+// its `nslab` weight regions (1 for row-major weights; the 256-column slabs
+// of slab-packed bf16 weights, `slab_bytes` apart), bytes [skip, skip +
+// lead) of the head of each of the region's `nseg` K segments, segment s
+// starting at K step s * nsteps / nseg (steps of `step_bytes` bytes: the
+// consuming GEMM's K steps and K split; its weights are K-major within a
+// region, so a head is contiguous). Those are the bytes the streaming GEMM's waves read first --
 // the only ones still in the cache when asked for, since the rest of the
 // weights stream through it meanwhile -- and `nexp` covers the experts of its
 // first round of blocks.
@@ -29,6 +31,8 @@ struct Prefetch {
   const char* w;         // expert 0's weights; expert i at w + i * ebytes
   long long ebytes;      // bytes per expert
   long long step_bytes;  // bytes per K step of the consuming GEMM
+  long long slab_bytes;  // bytes per region (slab) of an expert
+  int nslab;             // regions per expert
   int nsteps;            // K steps per expert
   int nseg;              // K split of the consuming GEMM
   int skip;              // bytes skipped at the head of each segment
@@ -83,22 +87,25 @@ MOE_DEV void prefetch_block(const Prefetch& d, int part, int nparts,
   }
   __syncthreads();
   const int nsel = min((int)wrank[nw], d.nexp);
-  if (d.lead < 16 || nsel <= 0 || d.nseg <= 0) return;  // uniform over the block
+  if (d.lead < 16 || nsel <= 0 || d.nseg <= 0 || d.nslab <= 0)
+    return;  // uniform over the block
   // work in chunks of 64 KB (the last one of a segment head may be shorter):
   // chunk c is chunk c % cps of the read part of segment c / cps, segment
-  // r = j * nseg + sg of the j-th selected expert; lanes take consecutive
-  // 16-byte pieces of a chunk
+  // r = (j * nslab + sl) * nseg + sg of region sl of the j-th selected
+  // expert; lanes take consecutive 16-byte pieces of a chunk
   constexpr int kChunkBytes = 65536;
   const int cps = (d.lead + kChunkBytes - 1) / kChunkBytes;
-  const int nchunks = nsel * d.nseg * cps;
+  const int per_exp = d.nslab * d.nseg;
+  const int nchunks = nsel * per_exp * cps;
   uint32_t fold = 0;
   for (int c = part; c < nchunks; c += nparts) {
     const int r = c / cps;
-    const int j = r / d.nseg;
-    const int sg = r - j * d.nseg;
+    const int j = r / per_exp;
+    const int sl = (r - j * per_exp) / d.nseg;
+    const int sg = r - j * per_exp - sl * d.nseg;
     const int c0 = (c - r * cps) * kChunkBytes;
     const int len = min(kChunkBytes, d.lead - c0);
-    const char* base = d.w + list[j] * d.ebytes +
+    const char* base = d.w + list[j] * d.ebytes + sl * d.slab_bytes +
                        (long long)(sg * d.nsteps / d.nseg) * d.step_bytes +
                        d.skip + c0;
     constexpr int U = 4;  // 16-byte loads in flight per lane

@@ -242,16 +242,20 @@ def test_pack_weights_host_checks(L):
 @pytest.mark.parametrize("kw,layout,status", [
     (dict(wt="mxfp4", act_q="mxfp8", H=4096, I=1536), "rowmajor", 2),
     (dict(wt="int8", act_q="int8"), "rowmajor", 2),
-    (dict(), "packed", 2),
     (dict(act="f32", wt="f32", act_q="f32"), "packed", 2),
+    (dict(I=736), "packed", 2),            # bf16 slabs: I % 128
+    (dict(H=2080, I=768), "packed", 2),    # bf16 slabs: H % 256
     (dict(wt="mxfp4", act_q="mxfp8", H=4096, I=1536), "packed", 0),
     (dict(wt="int8", act_q="int8"), "packed", 0),
+    (dict(), "packed", 0),
     (dict(), "rowmajor", 0),
+    (dict(I=736), "rowmajor", 0),
 ])
 def test_weight_layout_declared(L, kw, layout, status):
-    """Quantised weights are read only in the packed order: a problem that
-    declares row-major MXFP4 or int8 weights (or packed bf16 / fp32 ones) is
-    refused before any launch, by every entry point that takes the problem."""
+    """Quantised weights are read only in the packed order, fp32 ones only
+    row-major, bf16 ones either way (packed: whole 256-column slabs): any
+    other problem is refused before any launch, by every entry point that
+    takes the problem."""
     p = _p(wt_layout=layout, **kw)
     st, _ = _query(L, p)
     assert st == status
@@ -262,6 +266,23 @@ def test_weight_layout_declared(L, kw, layout, status):
         assert L.moe_grouped_ffn(ctypes.byref(p), None, None, None, None, None,
                                  None, None, None, None, ctypes.byref(n),
                                  None) == status
+
+
+def test_pack_bf16_weights_host_checks(L):
+    ok = ctypes.c_void_p(1 << 20)
+    far = ctypes.c_void_p(1 << 34)
+    pk = L.moe_pack_bf16_weights
+    assert pk(-1, 64, 256, 1, ok, far, None) == 1
+    assert pk(2, 0, 256, 1, ok, far, None) == 1
+    assert pk(2, 64, 0, 0, ok, far, None) == 1
+    assert pk(2, 64, 256, 2, ok, far, None) == 1       # glu 0 or 1
+    assert pk(2, 48, 256, 1, ok, far, None) == 2       # K % 32
+    assert pk(2, 64, 384, 0, ok, far, None) == 2       # N % 256
+    assert pk(1 << 12, 1 << 14, 1 << 14, 0, ok, far, None) == 2  # E*K*N >= 2^40
+    assert pk(2, 64, 256, 1, None, far, None) == 1
+    assert pk(2, 64, 256, 1, ok, ctypes.c_void_p((1 << 34) + 8), None) == 1  # misaligned
+    assert pk(2, 64, 256, 1, ok, ctypes.c_void_p((1 << 20) + 4096), None) == 1  # overlap
+    assert pk(0, 64, 256, 1, None, None, None) == 0    # nothing to do
 
 
 def test_quant_mxfp4_weights_host_checks(L):

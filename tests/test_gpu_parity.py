@@ -802,3 +802,124 @@ def test_pack_weights(E, N, Kb, dt):
     # [e][n16][col][c][q][16 bytes] -> [e][c][n16][q][col][16]; lane = 16 q + col
     want = W.transpose(0, 3, 1, 4, 2, 5).reshape(E, N, Kb)
     assert np.array_equal(got.cpu().numpy(), want)
+
+
+# bf16 shapes with whole 256-column slabs (I % 128 == 0, H % 256 == 0), one
+# per bf16 GEMM schedule: 16- and 32-row weight-streaming tiles (K split 3
+# and 1), 128- and 256-row LDS-tiled tiles, identity experts, an expert range
+PACKED_BF16 = {
+    "decode_16row": scaled(get_workload("qwen3_30b_a3b_decode_bf16"), T=16,
+                           H=512, I=384, n_ffn=16, local_end=16, top_k=4),
+    "decode_32row": scaled(get_workload("qwen3_30b_a3b_decode_bf16"), T=32,
+                           H=512, I=384, n_ffn=16, local_end=16, top_k=4),
+    # 8 rows per expert on the decode expert shape: 32-row tiles, no K split
+    "decode_32row_wide": scaled(get_workload("qwen3_30b_a3b_decode_bf16"),
+                                T=128),
+    "prefill_128": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_bf16"),
+                          T=300, H=256, I=256, n_ffn=12, local_end=12, top_k=4),
+    "prefill_256": scaled(get_workload("qwen3_30b_a3b_prefill_skewed_bf16"),
+                          T=1200, H=512, I=256, n_ffn=8, local_end=8, top_k=4),
+    "zero_experts": scaled(get_workload("longcat_flash_zero_experts_bf16"),
+                           T=64, H=512, I=256, n_ffn=24, n_zero=12,
+                           local_end=36, top_k=6),
+    "range": scaled(get_workload("qwen3_30b_a3b_decode_bf16"), T=48, H=768,
+                    I=512, n_ffn=16, local_begin=3, local_end=11, top_k=4),
+}
+
+
+def _packed_inputs(m, inp):
+    """The workload's bf16 weights in the slab order (w13 gate/up paired)."""
+    return (m.pack_bf16_weights(inp["w13"], glu=True),
+            m.pack_bf16_weights(inp["w2"], glu=False))
+
+
+@pytest.mark.parametrize("E,K,N,glu", [(1, 32, 256, True), (3, 96, 512, True),
+                                       (2, 64, 768, False), (2, 2048, 1536, True),
+                                       (2, 768, 2048, False)])
+def test_pack_bf16_weights(E, K, N, glu):
+    """The slab order, element for element: [e][j][s][r][c] holds
+    W[e, 32 s + r, col_j(c)] with col_j(c) = 128 j + c / N/2 + 128 j + c - 128
+    (gate/up pairs) or 256 j + c."""
+    m = _m()
+    _say("pack_bf16", E, K, N, glu)
+    g = torch.Generator().manual_seed(E * 7919 + K + N)
+    w = torch.randint(-32768, 32768, (E, K, N), generator=g,
+                      dtype=torch.int32).to(torch.int16)
+    got = m.pack_bf16_weights(w.view(torch.bfloat16).to(DEV), glu=glu)
+    torch.cuda.synchronize()
+    W = w.numpy()
+    nsl, nst = N // 256, K // 32
+    if glu:
+        gate = W[:, :, : N // 2].reshape(E, nst, 32, nsl, 128)
+        up = W[:, :, N // 2:].reshape(E, nst, 32, nsl, 128)
+        slabs = np.concatenate([gate, up], axis=4)  # [e][s][r][j][256]
+    else:
+        slabs = W.reshape(E, nst, 32, nsl, 256)
+    want = slabs.transpose(0, 3, 1, 2, 4).reshape(E, K, N)
+    assert np.array_equal(got.cpu().view(torch.int16).numpy(), want)
+
+
+@pytest.mark.parametrize("name", list(PACKED_BF16))
+def test_layer_bf16_packed(name):
+    """Slab-packed bf16 weights feed the MFMAs the same operands as row-major
+    ones: the layer's output is bit-identical, and within tolerance of the
+    oracle."""
+    m = _m()
+    shape = PACKED_BF16[name]
+    _say("layer packed bf16", name)
+    inp = generate(shape, seed=4, device=DEV)
+    w13p, w2p = _packed_inputs(m, inp)
+    want = m.layer(m.problem(shape), inp["logits"], inp["x"], inp["w13"],
+                   inp["w2"], residual=inp["residual"])
+    got = m.layer(m.problem(shape, wt_layout="packed"), inp["logits"], inp["x"],
+                  w13p, w2p, residual=inp["residual"])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got), bits(want)), name
+    ref, allow = layer_ref(m, shape, inp)
+    assert_close(to64(got), ref, shape, f"{name} packed", allow=allow)
+
+
+def test_layer_bf16_packed_split_calls_and_prefetch():
+    """The per-stage calls and the weight prefetch take the packed layout
+    too: same bits as the fused layer on row-major weights."""
+    m = _m()
+    for name in ("decode_32row", "prefill_128", "decode_16row"):
+        shape = PACKED_BF16[name]
+        _say("packed split/prefetch", name)
+        inp = generate(shape, seed=5, device=DEV)
+        w13p, w2p = _packed_inputs(m, inp)
+        want = m.layer(m.problem(shape), inp["logits"], inp["x"], inp["w13"],
+                       inp["w2"], residual=inp["residual"])
+        p = m.problem(shape, wt_layout="packed")
+        ids, w = m.gate_topk(p, inp["logits"])
+        for which in (1, 2, 3):
+            for nbytes in (4096, 1 << 20, 1 << 40):
+                m.prefetch_weights(p, w13p, w2p, topk_ids=ids,
+                                   max_bytes=nbytes, which=which)
+        r = m.init_routing(p, ids, inp["x"])
+        h, hs = m.ffn_up(p, r["offsets"], r["x_perm"], r["x_perm_scale"], w13p)
+        y = m.ffn_down(p, r["offsets"], h, hs, w2p)
+        out = m.finalize(p, ids, w, r["copy_pos"], r["offsets"], y, inp["x"],
+                         inp["residual"])
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), bits(want)), name
+
+
+@pytest.mark.parametrize("name", ["longcat_flash_zero_experts_bf16",
+                                  "qwen3_30b_a3b_decode_bf16",
+                                  "qwen3_30b_a3b_prefill_skewed_bf16"])
+def test_layer_full_size_bf16_packed(name):
+    """At the workloads' full sizes, in the configuration bench.py times:
+    the packed layer equals the row-major one bit for bit."""
+    m = _m()
+    shape = get_workload(name)
+    _say("full-size packed", name)
+    inp = generate(shape, seed=0, device=DEV)
+    want = m.layer(m.problem(shape), inp["logits"], inp["x"], inp["w13"],
+                   inp["w2"], residual=inp["residual"])
+    w13p, w2p = _packed_inputs(m, inp)
+    del inp["w13"], inp["w2"]
+    got = m.layer(m.problem(shape, wt_layout="packed"), inp["logits"], inp["x"],
+                  w13p, w2p, residual=inp["residual"])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got), bits(want)), name
