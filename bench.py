@@ -88,17 +88,17 @@ TRAFFIC = {
     #            WRITE KiB) per GEMM1 dispatch, taken with the weight layout
     #            bench.py uses by default for the workload
     "qwen3_30b_a3b_decode_bf16":
-        ("gemm_bf16_stream", "cbea335ea17852cd", 341625.5, 384.0),
+        ("gemm_bf16_stream", "2cf7ce5f704a820a", 341624.4, 384.0),
     "qwen3_30b_a3b_prefill_skewed_bf16":
-        ("gemm_bf16_tiled", "caa5483d71d9f545", 521652.0, 49152.0),
+        ("gemm_bf16_tiled", "6f9a7fe77c7f360a", 521882.2, 49152.0),
     "longcat_flash_zero_experts_bf16":
-        ("gemm_bf16_stream", "cbea335ea17852cd", 12854868.7, 32528.0),
+        ("gemm_bf16_stream", "2cf7ce5f704a820a", 12835728.1, 32528.0),
     "qwen3_235b_a22b_ep_rank_w4a8":
-        ("gemm_mx_tiled", "bd9d57451598c185", 164774.7, 12897.0),
+        ("gemm_mx_tiled", "9837db651f8489a6", 164054.5, 12895.2),
     "qwen3_30b_a3b_decode_w8a8":
-        ("gemm_i8_stream", "cf8e64ada35ec3e7", 171200.6, 768.1),
+        ("gemm_i8_stream", "f183022218c91c87", 171200.5, 768.1),
     "qwen3_30b_a3b_prefill_skewed_w8a8":
-        ("gemm_bf16_tiled", "caa5483d71d9f545", 226378.6, 98304.0),
+        ("gemm_bf16_tiled", "6f9a7fe77c7f360a", 226607.8, 98304.0),
 }
 
 
