@@ -16,7 +16,7 @@ Prints ONE JSON line: whole-step tokens/s plus
   cpu_baseline the CPU oracle timed on the host on a bounded sample of the
                same workload (a reported baseline, not the target).
 
-Before the W warm-up steps, untimed steps run for 1 s of wall time so that
+Before the W warm-up steps, untimed steps run for 2 s of wall time so that
 the GPU has reached its working clocks when the (short) timed region starts.
 
 Static expert weights are prepared once before timing, as at model load:
@@ -136,12 +136,13 @@ def _copy_calibration():
     print(json.dumps({"copy_bytes": n, "dispatches": 5}), flush=True)
 
 
-def _settle(step, seconds=1.0):
+def _settle(step, seconds=2.0):
     """Untimed steps for `seconds` of wall time before the warm-up: the GPU
     reaches its working clocks only after some time under load, and a short
     timed region would otherwise be measured on a ramping clock (the
-    LongCat-shaped layer measured 164.5 k tokens/s after 0.1 s of such steps
-    and 168.5 k after 1 s, on the same box)."""
+    LongCat-shaped layer, row-major weights: 164.5 k tokens/s after 0.1 s of
+    such steps, 168.5 k after 1 s; slab-packed: 174.7 k after 1 s, 179.4 k
+    after 2 s and 179.1 k after 4 s, each pair on one box)."""
     import torch
     t_end = time.perf_counter() + seconds
     while time.perf_counter() < t_end:
