@@ -61,6 +61,27 @@ def test_noalloc_equals_layer_on_two_calls(name):
         assert np.array_equal(bits(got), bits(want)), (name, T)
 
 
+def test_noalloc_packed_bf16_weights():
+    """The slab-packed bf16 layout through the static scratch: equal to
+    moe_layer on row-major weights, on two calls in a row (the second
+    smaller)."""
+    m = _m()
+    shape = scaled(get_workload("longcat_flash_zero_experts_bf16"), T=64,
+                   H=512, I=256, n_ffn=24, n_zero=12, local_end=36, top_k=6)
+    print("noalloc packed bf16", flush=True)
+    for T in (shape.T, 20):
+        sh = shape.replace(T=T)
+        inp = generate(sh, seed=T + 1, device=DEV)
+        want = m.layer(m.problem(sh), inp["logits"], inp["x"], inp["w13"],
+                       inp["w2"], residual=inp["residual"])
+        w13p = m.pack_bf16_weights(inp["w13"], glu=True)
+        w2p = m.pack_bf16_weights(inp["w2"], glu=False)
+        got = m.layer_noalloc(m.problem(sh, wt_layout="packed"), inp["logits"],
+                              inp["x"], w13p, w2p, residual=inp["residual"])
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(got), bits(want)), T
+
+
 def test_noalloc_refuses_problems_past_the_scratch():
     m = _m()
     shape = get_workload("qwen3_30b_a3b_prefill_skewed_bf16")  # T = 4096
