@@ -15,10 +15,10 @@
 // lead) of the head of each of the region's `nseg` K segments, segment s
 // starting at K step s * nsteps / nseg (steps of `step_bytes` bytes: the
 // consuming GEMM's K steps and K split; its weights are K-major within a
-// region, so a head is contiguous). Those are the bytes the streaming GEMM's waves read first --
-// the only ones still in the cache when asked for, since the rest of the
-// weights stream through it meanwhile -- and `nexp` covers the experts of its
-// first round of blocks.
+// region, so a head is contiguous). Those are the bytes the streaming GEMM's
+// waves read first -- the only ones still in the cache when asked for, since
+// the rest of the weights stream through it meanwhile -- and `nexp` covers
+// the experts of its first round of blocks.
 // Nothing is written: the loaded words are folded into one value per lane
 // that is stored only when `sink` is non-null (never, in the library's calls;
 // the conditional store keeps the loads from being optimised away).
