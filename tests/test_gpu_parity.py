@@ -501,11 +501,15 @@ def test_layer_deterministic():
     assert np.array_equal(bits(a), bits(b))
 
 
-def test_expert_range_partials_add_up():
+@pytest.mark.parametrize("name", ["ep_w4a8_small", "qwen3_235b_a22b_ep_rank_w4a8"])
+def test_expert_range_partials_add_up(name):
     """One call per expert-parallel share; the partial sums add up to the
-    full-range layer (the single-GPU stand-in for the reduce-scatter)."""
+    full-range layer (the single-GPU stand-in for the reduce-scatter), on a
+    small W4A8 shape and on the W4A8 rank's full shape (four ranks of 32 of
+    the 128 experts)."""
     m = _m()
-    base = SMALL["ep_w4a8_small"]
+    _say("EP additivity", name)
+    base = SMALL[name] if name in SMALL else get_workload(name)
     full = base.replace(local_begin=0, local_end=base.n_ffn)
     inp = generate(full, seed=8, device=DEV)
     p = m.problem(full)
