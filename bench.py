@@ -306,7 +306,7 @@ def _cpu_baseline(shape, inp, target_s):
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
+        print("bench.py measures one GPU only: the library has no multi-GPU "
               "path (the expert-parallel case is one rank's expert range on "
               "one GPU). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)

@@ -52,7 +52,7 @@ What each function follows:
                    whose expert lies in this rank's range; finalize of a rank gives
                    a partial sum that a later reduce-scatter adds up.
 
-Readings taken where the pages are silent (all listed in the design doc):
+Readings taken where the pages are silent:
   * top-k order: descending logit, ties to the lower expert id; weights are the
     softmax over the k selected logits (equal in exact arithmetic to a softmax
     over all experts followed by renormalising the k selected).
