@@ -317,3 +317,40 @@ def test_prefetch_weights_host_checks(L):
     assert pf(ctypes.byref(p), None, None, None, 0, 1 << 20, None) == 0
     assert pf(ctypes.byref(p), None, ok, ok, 3, 8, None) == 0
     assert pf(ctypes.byref(_p(T=0)), None, ok, ok, 3, 1 << 20, None) == 0
+
+
+def test_header_is_plain_c(L, tmp_path):
+    """include/moe_mi355x.h is a C ABI: a C99 translation unit (strict,
+    warnings as errors) includes it, links against the library and calls
+    into it -- a size query of an invalid problem, which fails on the host
+    before anything touches a GPU."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    src = tmp_path / "abi.c"
+    src.write_text(
+        '#include "moe_mi355x.h"\n'
+        '#include <stdio.h>\n'
+        'int main(void) {\n'
+        '  moe_problem p = {0};\n'
+        '  size_t n = 0;\n'
+        '  moe_status s = moe_layer(&p, 0, 0, 0, 0, 0, 0, 0, 0, 0, &n, 0);\n'
+        '  printf("%d %d %s\\n", (int)s, (int)moe_abi_version(),\n'
+        '         moe_status_string(s));\n'
+        '  return 0;\n'
+        '}\n')
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(m.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic",
+                        "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-L", libdir, "-lmoe_mi355x",
+                        "-Wl,-rpath," + libdir, "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    status, version, text = r.stdout.split(" ", 2)
+    assert int(status) == 1 and int(version) == L.moe_abi_version()
+    assert text.startswith("MOE_ERR_INVALID_ARG")
