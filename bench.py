@@ -88,11 +88,11 @@ TRAFFIC = {
     #            WRITE KiB) per GEMM1 dispatch, taken with the weight layout
     #            bench.py uses by default for the workload
     "qwen3_30b_a3b_decode_bf16":
-        ("gemm_bf16_stream", "2cf7ce5f704a820a", 341624.4, 384.0),
+        ("gemm_bf16_stream", "a94d9ea2fd68934f", 341624.4, 384.0),
     "qwen3_30b_a3b_prefill_skewed_bf16":
         ("gemm_bf16_tiled", "6f9a7fe77c7f360a", 521882.2, 49152.0),
     "longcat_flash_zero_experts_bf16":
-        ("gemm_bf16_stream", "2cf7ce5f704a820a", 12835728.1, 32528.0),
+        ("gemm_bf16_stream", "a94d9ea2fd68934f", 12835682.3, 32528.0),
     "qwen3_235b_a22b_ep_rank_w4a8":
         ("gemm_mx_tiled", "9837db651f8489a6", 164054.5, 12895.2),
     "qwen3_30b_a3b_decode_w8a8":

@@ -237,7 +237,21 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
     if (wave > 0) return;
   }
 
-  // epilogue: lane owns rows 16*rg + 4*kq + e, columns colA + 0..7 (+ colB)
+  // epilogue: lane owns rows 16*rg + 4*kq + e, columns colA + 0..7 (+ colB).
+  // 32-row tiles come with outputs of tens of MB (the LongCat-shaped layer's
+  // y is 100 MB, its h 33 MB), stored while every other wave streams
+  // weights: written nontemporally, its GEMM2 measured 2018 -> 1958 us and
+  // GEMM1 3777 -> 3760 us (layer 5844 -> 5781 us, outputs identical). A
+  // timing-only build without the y stores ran GEMM2 in 1818 us. The
+  // 16-row decode tiles write a few MB, which the next kernel reads from
+  // the caches, and keep plain stores (nontemporal: neutral to 0.5 % slower).
+  constexpr bool NT_OUT = RG == 2;
+  auto store_out = [&](uint16_t* p, uint4 o) {
+    if constexpr (NT_OUT)
+      __builtin_nontemporal_store(u32x4_t{o.x, o.y, o.z, o.w}, (u32x4_t*)p);
+    else
+      *(uint4*)p = o;
+  };
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
 #pragma unroll
@@ -256,7 +270,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
           o.y = pack_bf16x2(hv[2], hv[3]);
           o.z = pack_bf16x2(hv[4], hv[5]);
           o.w = pack_bf16x2(hv[6], hv[7]);
-          *(uint4*)(orow + colA) = o;
+          store_out(orow + colA, o);
         }
       } else {
 #pragma unroll
@@ -267,7 +281,7 @@ __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_bf16_stream_kernel(
           o.y = pack_bf16x2(acc[h][rg][2][e], acc[h][rg][3][e]);
           o.z = pack_bf16x2(acc[h][rg][4][e], acc[h][rg][5][e]);
           o.w = pack_bf16x2(acc[h][rg][6][e], acc[h][rg][7][e]);
-          *(uint4*)(orow + (h == 0 ? colA : colB)) = o;
+          store_out(orow + (h == 0 ? colA : colB), o);
         }
       }
     }
